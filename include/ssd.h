@@ -1,0 +1,215 @@
+/*
+ * ssd.h - C ABI of the MI355X greedy self-speculative decoding library (libssd.so).
+ *
+ * The library runs one decoder-only transformer on one AMD MI355X (gfx950) and
+ * exposes the speculative decode step the way the method states it:
+ *
+ *   prompt -> prefill -> repeat { draft k tokens through a subset of the layers
+ *   (sharing the KV cache) -> verify the k+1 block tokens in one pass through all
+ *   layers -> accept the longest matching prefix plus the verifier's next token
+ *   -> cut the KV cache back to the committed length }.
+ *
+ * Sources: LayerSkip summary page (4.3.1 self-drafting, 4.3.2 self-verification,
+ * 4.3.3 reusing the cache); MLX layer-skip blog ("Code": the middle-layer skip
+ * draft, lossless greedy check); mlx-dflash README ("Architecture": block verify
+ * and greedy cumulative-product accept; "Apple Silicon Optimizations": one host
+ * synchronisation per step, draft cache cropped on rejection); speculative
+ * decoding for MoE models (abstract: per-slot and deduplicated expert reads).
+ *
+ * Conventions for every call:
+ *  - Return value: SSD_OK (0) or a negative ssd_status.  On error the context's
+ *    state is unchanged; ssd_last_error() holds a message (thread-local).
+ *  - Device pointers are plain HIP device addresses (e.g. from torch tensors);
+ *    the library never allocates, frees or resizes them.
+ *  - Host arrays are owned by the caller; their sizes are stated per argument.
+ *  - Work is enqueued on the stream given to ssd_load.  Calls that return host
+ *    data synchronise that stream before returning.
+ *  - Matrices are row-major [out_features, in_features]; element type is the
+ *    cfg dtype (float32, or bf16 stored as uint16 bit patterns).
+ *  - One context is not thread-safe; distinct contexts are independent.
+ */
+#ifndef SSD_H
+#define SSD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SSD_OK = 0,
+    SSD_E_ARG = -1,          /* bad argument: size, token id, pointer, cfg field */
+    SSD_E_STATE = -2,        /* call not allowed in the context's current state */
+    SSD_E_CAPACITY = -3,     /* the pass would write past max_ctx                */
+    SSD_E_HIP = -4,          /* a HIP runtime call failed (see ssd_last_error)  */
+    SSD_E_UNSUPPORTED = -5   /* e.g. non-greedy decoding                        */
+} ssd_status;
+
+/* Context states (ssd_state / ssd_check_transition). */
+enum { SSD_ST_LOADED = 0, SSD_ST_READY = 1, SSD_ST_DRAFTED = 2, SSD_ST_VERIFIED = 3 };
+/* Operations (ssd_check_transition). */
+enum { SSD_OP_PREFILL = 0, SSD_OP_DRAFT = 1, SSD_OP_VERIFY = 2, SSD_OP_VERIFY_BLOCK = 3,
+       SSD_OP_ACCEPT = 4, SSD_OP_RESET = 5 };
+
+enum { SSD_F32 = 0, SSD_BF16 = 1 };
+#define SSD_MAX_FEAT 8
+#define SSD_MAX_BLOCK 32      /* largest verify block (k + 1) a context may declare */
+
+/*
+ * Model and capacity description.  Dense layers: pre-norm RMSNorm, rotary
+ * embedding (rotate-half pairs (i, i+head_dim/2), base rope_theta), grouped-query
+ * attention (query head h reads KV head h*n_kv_heads/n_q_heads), SwiGLU FFN,
+ * untied LM head; no biases (LayerSkip summary, notation section).
+ * MoE (n_experts > 0): layers >= n_dense_layers use top_k of n_experts routed
+ * experts (softmax gate, not renormalised) plus n_shared shared experts, each
+ * an expert_ffn-wide SwiGLU; dense layers then use dense_ffn.
+ * Feature tap (n_feat > 0): each verify pass also outputs
+ * fc . bf16(concat of the residual after layers feat_layers[0..n_feat))
+ * (mlx-dflash README, "Architecture": context features from five layers -> fc).
+ */
+typedef struct {
+    int32_t n_layers, d_model, n_q_heads, n_kv_heads, head_dim, ffn_dim, vocab;
+    int32_t dtype;                 /* SSD_F32 or SSD_BF16 */
+    float rms_eps, rope_theta;
+    int32_t max_ctx;               /* KV capacity in positions */
+    int32_t max_block;             /* largest verify block k+1 (<= SSD_MAX_BLOCK) */
+    int32_t prefill_chunk;         /* rows per prefill pass (multiple of 16, <= 256) */
+    int32_t n_experts, top_k, n_shared, expert_ffn, n_dense_layers, dense_ffn;
+    int32_t moe_dedup;             /* 0: per-slot expert reads, 1: deduplicated */
+    int32_t n_feat, feat_layers[SSD_MAX_FEAT];
+} ssd_cfg;
+
+typedef struct { const void* ptr; int64_t nbytes; } ssd_buf;
+
+typedef struct {
+    int64_t cycles;        /* draft/verify/accept cycles (or plain decode steps) */
+    int64_t drafted;       /* draft tokens proposed */
+    int64_t accepted;      /* draft tokens accepted */
+    int64_t emitted;       /* tokens emitted by the decode loop (after prefill) */
+    int64_t verify_passes; /* verify passes timed in t_verify_ms */
+    double t_prefill_ms, t_draft_ms, t_verify_ms, t_accept_ms, t_decode_ms;
+} ssd_stats;
+
+/* ---- host-only helpers (no HIP call, usable without a GPU) ---------------- */
+
+/* Checks cfg for consistency (divisibility, limits, supported dtypes).  */
+ssd_status ssd_validate_cfg(const ssd_cfg* cfg);
+
+/* Number of weight tensors ssd_load expects, and the element count of tensor i
+ * in the canonical order:
+ *   embed [V,d];
+ *   per layer l: attn_norm [d], wq [Hq*hd,d], wk [Hkv*hd,d], wv [Hkv*hd,d],
+ *     wo [d,Hq*hd], ffn_norm [d], then
+ *     dense layer: w_gate [F,d], w_up [F,d], w_down [d,F]   (F = dense_ffn if MoE)
+ *     MoE layer:   router [E,d], exp_gate [E,Fe,d], exp_up [E,Fe,d],
+ *                  exp_down [E,d,Fe], sh_gate [S,Fe,d], sh_up [S,Fe,d], sh_down [S,d,Fe];
+ *   final_norm [d], lm_head [V,d], fc [d, n_feat*d] (only when n_feat > 0).
+ * Returns -1 for an invalid cfg or index. */
+int32_t ssd_n_weights(const ssd_cfg* cfg);
+int64_t ssd_weight_numel(const ssd_cfg* cfg, int32_t i);
+
+/* Device workspace size in bytes (KV cache, activations, partial results,
+ * rotary tables, token buffers) for cfg; -1 if cfg is invalid. */
+int64_t ssd_workspace_bytes(const ssd_cfg* cfg);
+
+/* Skip mask of the naive layer-skip draft (MLX layer-skip blog, "Code"):
+ * n_skip = max(1, round_half_even(n_layers*frac)), start = (n_layers-n_skip)/2,
+ * mask[l] = 1 for l in [start, start+n_skip).  mask: host array [n_layers]. */
+ssd_status ssd_skip_mask(int32_t n_layers, double frac, uint8_t* mask);
+
+/* State machine: next state of `op` from `state`, or SSD_E_STATE. */
+ssd_status ssd_check_transition(int32_t state, int32_t op, int32_t* next_state);
+
+const char* ssd_strerror(ssd_status s);
+const char* ssd_last_error(void);
+
+/* ---- context ----------------------------------------------------------------- */
+
+typedef struct ssd_ctx ssd_ctx;
+
+/* Binds weights (device buffers, canonical order, n_weights of them, sizes
+ * checked) and a device workspace of at least ssd_workspace_bytes(cfg) bytes,
+ * 256-byte aligned.  hip_stream: a hipStream_t (NULL = the null stream).
+ * Clears the KV cache.  *out receives the context (free with ssd_free). */
+ssd_status ssd_load(const ssd_cfg* cfg, const ssd_buf* weights, int32_t n_weights,
+                    ssd_buf workspace, void* hip_stream, ssd_ctx** out);
+void ssd_free(ssd_ctx* ctx);
+
+/* Back to LOADED: committed length 0, statistics cleared. */
+ssd_status ssd_reset(ssd_ctx* ctx);
+int32_t ssd_state(const ssd_ctx* ctx);
+/* Committed KV length n (positions [0, n) hold full-model entries). */
+int32_t ssd_context_length(const ssd_ctx* ctx);
+
+/* Runs the prompt tokens[0..n) (host, ids in [0,V)) at positions 0..n-1 through
+ * all layers in passes of prefill_chunk rows; *next_tok (host, may be NULL)
+ * receives argmax of the last row's logits (lowest index on ties), which
+ * becomes the pending token t_last at position n.  LOADED -> READY. */
+ssd_status ssd_prefill(ssd_ctx* ctx, const int32_t* tokens, int32_t n, int32_t* next_tok);
+
+/* Draft (LayerSkip summary 4.3.1): k tokens, each through the layers with
+ * skip_mask[l] == 0 only (host array [n_layers]; NULL = no layer skipped),
+ * at positions n..n+k-1, reading and writing the shared KV cache of the kept
+ * layers.  drafts: host [k] or NULL.  READY -> DRAFTED.  Requires
+ * 1 <= k <= max_block-1 and n+k+1 <= max_ctx. */
+ssd_status ssd_draft(ssd_ctx* ctx, const uint8_t* skip_mask, int32_t k, int32_t* drafts);
+
+/* Verify (LayerSkip summary 4.3.2; mlx-dflash "Architecture"): one pass of the
+ * m block tokens [t_last, d_1..d_{m-1}] through all layers at positions
+ * n..n+m-1, overwriting those KV entries.  block == NULL uses the device-
+ * resident block (DRAFTED -> VERIFIED, m must be k+1); a host block [m] is
+ * allowed from READY (READY -> VERIFIED; block[0] normally t_last).
+ * posterior: host [m] or NULL, receives argmax of each row's logits. */
+ssd_status ssd_verify(ssd_ctx* ctx, const int32_t* block, int32_t m, int32_t* posterior);
+
+/* Accept + rollback (mlx-dflash "Architecture" and "Apple Silicon
+ * Optimizations"): a = number of leading drafts equal to the verifier's
+ * predictions; emitted = d_1..d_a, p_a; the committed length becomes n+a+1 and
+ * p_a becomes t_last (entries past the committed length are stale and are
+ * overwritten before any read).  n_accepted, n_emitted: host scalars (may be
+ * NULL); emitted: host [m] or NULL.  VERIFIED -> READY. */
+ssd_status ssd_accept_rollback(ssd_ctx* ctx, int32_t* n_accepted, int32_t* emitted,
+                               int32_t* n_emitted);
+
+/* Whole decode: prefill the prompt, then loop until n_new tokens are produced
+ * (the first one comes from the prefill).  skip_mask == NULL or k == 0: plain
+ * greedy decode (one full pass per token, no host synchronisation per token);
+ * otherwise draft/verify/accept cycles with one host synchronisation each.
+ * greedy must be 1 (greedy acceptance; other decoding -> SSD_E_UNSUPPORTED).
+ * out: host [n_new]; stats: host or NULL.  Leaves the context READY. */
+ssd_status ssd_generate(ssd_ctx* ctx, const int32_t* prompt, int32_t n_prompt, int32_t n_new,
+                        int32_t greedy, const uint8_t* skip_mask, int32_t k,
+                        int32_t* out, ssd_stats* stats);
+
+/* Statistics accumulated since load/reset (per-phase times from HIP events). */
+ssd_status ssd_get_stats(const ssd_ctx* ctx, ssd_stats* stats);
+
+/* ---- test and measurement hooks -------------------------------------------------- */
+
+/* Logits (float32) of the last pass: host [rows * V], rows <= rows of that pass
+ * (prefill keeps only its last row). */
+ssd_status ssd_read_logits(ssd_ctx* ctx, float* host, int32_t rows);
+/* Feature-tap output of the last verify pass: host [rows * d] bf16 bits. */
+ssd_status ssd_read_features(ssd_ctx* ctx, uint16_t* host, int32_t rows);
+/* Injects expert ids for the next passes: host [n_layers][n][top_k] (entries for
+ * dense layers ignored); n == 0 returns to the router's own choice. */
+ssd_status ssd_set_routing(ssd_ctx* ctx, const int32_t* ids, int32_t n);
+/* Routed-expert union size per layer of the last MoE pass: host [n_layers]. */
+ssd_status ssd_read_union(ssd_ctx* ctx, int32_t* host);
+/* Runs the accept kernel on host drafts d[k] and predictions p[k+1];
+ * *a receives the accepted length.  Does not change the context's state. */
+ssd_status ssd_test_accept(ssd_ctx* ctx, const int32_t* d, const int32_t* p, int32_t k, int32_t* a);
+/* Times `iters` back-to-back launches of one layer operation at m rows on the
+ * context's stream with HIP events; *avg_us receives the mean duration.
+ * op: 0 = gate/up GEMM (+SwiGLU), 1 = down GEMM, 2 = qkv GEMM (+RoPE/KV),
+ *     3 = o GEMM, 4 = lm_head GEMM, 5 = attention, 6 = routed-expert FFN.
+ * Uses layer `layer`'s weights; writes only scratch activations and the KV
+ * entries past the committed length. */
+ssd_status ssd_time_op(ssd_ctx* ctx, int32_t op, int32_t layer, int32_t m, int32_t iters,
+                       float* avg_us);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SSD_H */

@@ -1,0 +1,294 @@
+"""Python binding of libssd.so, the MI355X greedy self-speculative decoding
+library (C ABI declared in include/ssd.h).
+
+Argument marshalling only: every step of the decode path runs in the
+library's HIP kernels.  torch provides device memory (weights, workspace) and
+the stream.  Importing this package fails loudly when libssd.so is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libssd.so")
+
+SSD_MAX_FEAT = 8
+SSD_MAX_BLOCK = 32
+ST_LOADED, ST_READY, ST_DRAFTED, ST_VERIFIED = range(4)
+OP_PREFILL, OP_DRAFT, OP_VERIFY, OP_VERIFY_BLOCK, OP_ACCEPT, OP_RESET = range(6)
+OPS = dict(gate_up=0, down=1, qkv=2, o=3, lm_head=4, attention=5, moe=6)
+
+EXPORTS = ["ssd_validate_cfg", "ssd_n_weights", "ssd_weight_numel", "ssd_workspace_bytes",
+           "ssd_skip_mask", "ssd_check_transition", "ssd_strerror", "ssd_last_error",
+           "ssd_load", "ssd_free", "ssd_reset", "ssd_state", "ssd_context_length",
+           "ssd_prefill", "ssd_draft", "ssd_verify", "ssd_accept_rollback", "ssd_generate",
+           "ssd_get_stats", "ssd_read_logits", "ssd_read_features", "ssd_set_routing",
+           "ssd_read_union", "ssd_test_accept", "ssd_time_op"]
+
+
+class Cfg(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("n_layers", "d_model", "n_q_heads", "n_kv_heads", "head_dim", "ffn_dim", "vocab", "dtype")] + \
+               [("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float)] + \
+               [(n, ctypes.c_int32) for n in
+                ("max_ctx", "max_block", "prefill_chunk", "n_experts", "top_k", "n_shared", "expert_ffn",
+                 "n_dense_layers", "dense_ffn", "moe_dedup", "n_feat")] + \
+               [("feat_layers", ctypes.c_int32 * SSD_MAX_FEAT)]
+
+
+class Buf(ctypes.Structure):
+    _fields_ = [("ptr", ctypes.c_void_p), ("nbytes", ctypes.c_int64)]
+
+
+class Stats(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in ("cycles", "drafted", "accepted", "emitted", "verify_passes")] + \
+               [(n, ctypes.c_double) for n in
+                ("t_prefill_ms", "t_draft_ms", "t_verify_ms", "t_accept_ms", "t_decode_ms")]
+
+    def as_dict(self) -> dict:
+        return {n: getattr(self, n) for n, _ in self._fields_}
+
+
+class SSDError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"ssd status {status}: {msg}")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m self_speculative_decoding_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, VP = ctypes.POINTER, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+    pc = P(Cfg)
+    sig = {
+        "ssd_validate_cfg": (I32, [pc]),
+        "ssd_n_weights": (I32, [pc]),
+        "ssd_weight_numel": (I64, [pc, I32]),
+        "ssd_workspace_bytes": (I64, [pc]),
+        "ssd_skip_mask": (I32, [I32, ctypes.c_double, VP]),
+        "ssd_check_transition": (I32, [I32, I32, P(I32)]),
+        "ssd_strerror": (ctypes.c_char_p, [I32]),
+        "ssd_last_error": (ctypes.c_char_p, []),
+        "ssd_load": (I32, [pc, P(Buf), I32, Buf, VP, P(VP)]),
+        "ssd_free": (None, [VP]),
+        "ssd_reset": (I32, [VP]),
+        "ssd_state": (I32, [VP]),
+        "ssd_context_length": (I32, [VP]),
+        "ssd_prefill": (I32, [VP, VP, I32, P(I32)]),
+        "ssd_draft": (I32, [VP, VP, I32, VP]),
+        "ssd_verify": (I32, [VP, VP, I32, VP]),
+        "ssd_accept_rollback": (I32, [VP, P(I32), VP, P(I32)]),
+        "ssd_generate": (I32, [VP, VP, I32, I32, I32, VP, I32, VP, P(Stats)]),
+        "ssd_get_stats": (I32, [VP, P(Stats)]),
+        "ssd_read_logits": (I32, [VP, VP, I32]),
+        "ssd_read_features": (I32, [VP, VP, I32]),
+        "ssd_set_routing": (I32, [VP, VP, I32]),
+        "ssd_read_union": (I32, [VP, VP]),
+        "ssd_test_accept": (I32, [VP, VP, VP, I32, P(I32)]),
+        "ssd_time_op": (I32, [VP, I32, I32, I32, I32, P(ctypes.c_float)]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype, f.argtypes = res, args
+    return lib
+
+
+lib = _load()
+
+
+def _check(status: int):
+    if status != 0:
+        raise SSDError(status, (lib.ssd_last_error() or b"").decode())
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def make_cfg(cfg: dict, max_block: int | None = None, prefill_chunk: int = 128, moe_dedup: int = 0) -> Cfg:
+    """C cfg from a workload dict (keys as in the synth module)."""
+    c = Cfg()
+    for n in ("n_layers", "d_model", "n_q_heads", "n_kv_heads", "head_dim", "vocab", "max_ctx"):
+        setattr(c, n, int(cfg[n]))
+    c.ffn_dim = int(cfg.get("ffn_dim", 0))
+    c.dtype = 1 if cfg["dtype"] == "bf16" else 0
+    c.rms_eps = float(cfg["rms_eps"])
+    c.rope_theta = float(cfg["rope_theta"])
+    c.max_block = int(max_block if max_block is not None else cfg.get("max_block", 17))
+    c.prefill_chunk = int(prefill_chunk)
+    for n in ("n_experts", "top_k", "n_shared", "expert_ffn", "n_dense_layers", "dense_ffn"):
+        setattr(c, n, int(cfg.get(n, 0)))
+    c.moe_dedup = int(moe_dedup)
+    fl = list(cfg.get("feat_layers", ()))
+    c.n_feat = len(fl)
+    for i, l in enumerate(fl):
+        c.feat_layers[i] = int(l)
+    return c
+
+
+def validate_cfg(c: Cfg) -> int:
+    return lib.ssd_validate_cfg(ctypes.byref(c))
+
+
+def workspace_bytes(c: Cfg) -> int:
+    return lib.ssd_workspace_bytes(ctypes.byref(c))
+
+
+def weight_numels(c: Cfg) -> list[int]:
+    n = lib.ssd_n_weights(ctypes.byref(c))
+    if n < 0:
+        _check(validate_cfg(c) or -1)
+    return [lib.ssd_weight_numel(ctypes.byref(c), i) for i in range(n)]
+
+
+def skip_mask(n_layers: int, frac: float) -> np.ndarray:
+    m = np.zeros(n_layers, dtype=np.uint8)
+    _check(lib.ssd_skip_mask(n_layers, float(frac), _ptr(m)))
+    return m
+
+
+def check_transition(state: int, op: int) -> int:
+    nxt = ctypes.c_int32(-1)
+    st = lib.ssd_check_transition(state, op, ctypes.byref(nxt))
+    return nxt.value if st == 0 else st
+
+
+class Engine:
+    """One loaded model on one GPU.
+
+    weights: arrays in the canonical order of include/ssd.h (float32, or uint16
+    bf16 bit patterns), uploaded once to device memory with torch.
+    """
+
+    def __init__(self, cfg: Cfg, weights: list[np.ndarray], device: str = "cuda:0"):
+        import torch
+        self.torch = torch
+        self.cfg = cfg
+        self.device = torch.device(device)
+        numels = weight_numels(cfg)
+        if len(weights) != len(numels):
+            raise ValueError(f"expected {len(numels)} weights, got {len(weights)}")
+        self._w = []
+        bufs = (Buf * len(weights))()
+        for i, (a, n) in enumerate(zip(weights, numels)):
+            a = np.ascontiguousarray(a)
+            if a.size != n:
+                raise ValueError(f"weight {i}: {a.size} elements, expected {n}")
+            host = torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a)
+            t = host.to(self.device)
+            self._w.append(t)
+            bufs[i] = Buf(t.data_ptr(), t.numel() * t.element_size())
+        nb = workspace_bytes(cfg)
+        if nb < 0:
+            _check(validate_cfg(cfg))
+        self._ws = torch.empty(nb, dtype=torch.uint8, device=self.device)
+        self.stream = torch.cuda.current_stream(self.device)
+        ctx = ctypes.c_void_p()
+        torch.cuda.synchronize(self.device)
+        _check(lib.ssd_load(ctypes.byref(cfg), bufs, len(weights), Buf(self._ws.data_ptr(), nb),
+                            ctypes.c_void_p(self.stream.cuda_stream), ctypes.byref(ctx)))
+        self.ctx = ctx
+        self.L, self.V, self.d = cfg.n_layers, cfg.vocab, cfg.d_model
+
+    def close(self):
+        if getattr(self, "ctx", None) is not None and self.ctx.value:
+            lib.ssd_free(self.ctx)
+            self.ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # -- state ------------------------------------------------------------------
+    @property
+    def state(self) -> int:
+        return lib.ssd_state(self.ctx)
+
+    @property
+    def context_length(self) -> int:
+        return lib.ssd_context_length(self.ctx)
+
+    def reset(self):
+        _check(lib.ssd_reset(self.ctx))
+
+    # -- the decode step --------------------------------------------------------------
+    def prefill(self, tokens) -> int:
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        nxt = ctypes.c_int32()
+        _check(lib.ssd_prefill(self.ctx, _ptr(t), len(t), ctypes.byref(nxt)))
+        return nxt.value
+
+    def draft(self, mask, k: int) -> list[int]:
+        m = None if mask is None else np.ascontiguousarray(mask, dtype=np.uint8)
+        out = np.zeros(max(k, 1), dtype=np.int32)
+        _check(lib.ssd_draft(self.ctx, None if m is None else _ptr(m), k, _ptr(out)))
+        return out[:k].tolist()
+
+    def verify(self, block=None, m: int | None = None) -> list[int]:
+        if block is not None:
+            b = np.ascontiguousarray(block, dtype=np.int32)
+            m = len(b)
+        post = np.zeros(m, dtype=np.int32)
+        _check(lib.ssd_verify(self.ctx, None if block is None else _ptr(b), m, _ptr(post)))
+        return post.tolist()
+
+    def accept(self) -> tuple[int, list[int]]:
+        a, ne = ctypes.c_int32(), ctypes.c_int32()
+        em = np.zeros(SSD_MAX_BLOCK + 1, dtype=np.int32)
+        _check(lib.ssd_accept_rollback(self.ctx, ctypes.byref(a), _ptr(em), ctypes.byref(ne)))
+        return a.value, em[:ne.value].tolist()
+
+    def generate(self, prompt, n_new: int, mask=None, k: int = 0, greedy: int = 1):
+        p = np.ascontiguousarray(prompt, dtype=np.int32)
+        out = np.zeros(n_new, dtype=np.int32)
+        st = Stats()
+        m = None if mask is None else np.ascontiguousarray(mask, dtype=np.uint8)
+        _check(lib.ssd_generate(self.ctx, _ptr(p), len(p), n_new, greedy, None if m is None else _ptr(m), k,
+                                _ptr(out), ctypes.byref(st)))
+        return out.tolist(), st.as_dict()
+
+    def stats(self) -> dict:
+        st = Stats()
+        _check(lib.ssd_get_stats(self.ctx, ctypes.byref(st)))
+        return st.as_dict()
+
+    # -- hooks -------------------------------------------------------------------------
+    def read_logits(self, rows: int) -> np.ndarray:
+        out = np.zeros((rows, self.V), dtype=np.float32)
+        _check(lib.ssd_read_logits(self.ctx, _ptr(out), rows))
+        return out
+
+    def read_features(self, rows: int) -> np.ndarray:
+        out = np.zeros((rows, self.d), dtype=np.uint16)
+        _check(lib.ssd_read_features(self.ctx, _ptr(out), rows))
+        return out
+
+    def set_routing(self, ids) -> None:
+        if ids is None:
+            _check(lib.ssd_set_routing(self.ctx, None, 0))
+            return
+        a = np.ascontiguousarray(ids, dtype=np.int32)
+        _check(lib.ssd_set_routing(self.ctx, _ptr(a), a.shape[1]))
+
+    def read_union(self) -> np.ndarray:
+        out = np.zeros(self.L, dtype=np.int32)
+        _check(lib.ssd_read_union(self.ctx, _ptr(out)))
+        return out
+
+    def test_accept(self, d, p) -> int:
+        dd = np.ascontiguousarray(d, dtype=np.int32)
+        pp = np.ascontiguousarray(p, dtype=np.int32)
+        a = ctypes.c_int32()
+        _check(lib.ssd_test_accept(self.ctx, _ptr(dd) if len(dd) else None, _ptr(pp), len(dd), ctypes.byref(a)))
+        return a.value
+
+    def time_op(self, op: str, layer: int, m: int, iters: int) -> float:
+        us = ctypes.c_float()
+        _check(lib.ssd_time_op(self.ctx, OPS[op], layer, m, iters, ctypes.byref(us)))
+        return us.value

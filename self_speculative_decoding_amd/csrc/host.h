@@ -1,0 +1,38 @@
+// Host-only helpers shared by host.cpp and runtime.hip (no HIP calls).
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+#include <vector>
+
+#include "ssd.h"
+
+namespace ssd {
+
+constexpr int kAttPT = 64;   // attention key partition width (kernels.h: ATT_PT)
+
+// Byte offsets of every workspace buffer (256-byte aligned).
+struct Layout {
+  size_t kc = 0, vc = 0, x = 0, xn = 0, q = 0, att = 0, act = 0, logits = 0;
+  size_t part_o = 0, part_ml = 0, counters = 0, rope_cos = 0, rope_sin = 0;
+  size_t block = 0, post = 0, toks = 0, state = 0, result = 0, outlog = 0;
+  size_t tblock = 0, tpost = 0, tstate = 0, tresult = 0, toutlog = 0;
+  size_t tap = 0, feat = 0;
+  size_t m_rlogits = 0, m_ids = 0, m_gates = 0, m_inject = 0, m_slot_out = 0, m_groups = 0, m_union = 0;
+  size_t total = 0;
+  int R = 0;        // rows per pass (multiple of 16)
+  int n_part = 0;   // attention partitions covering max_ctx
+};
+
+ssd_status fail(ssd_status s, const char* fmt, ...);
+const char* last_error();
+void clear_error();
+ssd_status validate(const ssd_cfg* c);
+bool compute_layout(const ssd_cfg& c, Layout& L);
+std::vector<int64_t> weight_table(const ssd_cfg& c);
+bool is_moe_layer(const ssd_cfg& c, int l);
+int layer_ffn(const ssd_cfg& c);
+ssd_status check_transition(int32_t state, int32_t op, int32_t* next);
+ssd_status skip_mask(int32_t n_layers, double frac, uint8_t* mask);
+
+}  // namespace ssd

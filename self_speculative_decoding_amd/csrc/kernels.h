@@ -1,0 +1,94 @@
+// Internal interface between the runtime (runtime.hip) and the gfx950 kernels
+// (kernels.hip).  Not part of the C ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssd {
+
+// Key partition width of the decode attention: partitions are anchored at
+// absolute positions [p*ATT_PT, (p+1)*ATT_PT), so a row's reduction order
+// depends only on its own position, never on the block it is verified in.
+constexpr int ATT_PT = 64;
+constexpr int ROW_TILE = 16;   // rows per MFMA tile / attention row tile
+
+enum Epi {
+  EPI_F32 = 0,     // y[m*ldy + n] = acc                         (logits)
+  EPI_RESID = 1,   // y[m*ldy + n] += acc; optional bf16 tap of the new value
+  EPI_SWIGLU = 2,  // act[m*ldo + n] = silu(acc_gate) * acc_up   (W0 gate, W1 up)
+  EPI_QKV = 3,     // RoPE on q,k; q -> q buffer; k,v -> KV cache at their positions
+  EPI_STORE = 4,   // out[m*ldo + n] = acc in the activation type (feature fc)
+  EPI_MOE = 5,     // per-row routed/shared expert output accumulation (see moe kernels)
+};
+
+struct GemmArgs {
+  const void* X;              // activations [M, K], row stride ldx (elements)
+  int ldx;
+  const void* W0;             // weights [rows, K] row-major
+  const void* W1;
+  const void* W2;
+  int n0, n1;                 // rows of W0 and W1 (QKV: q rows, k rows)
+  int M, N, K;                // N = output columns (SwiGLU: intermediate width)
+  float* y;                   // f32 output / residual
+  int ldy;
+  void* out;                  // activation-typed output (SwiGLU act, STORE)
+  int ldo;
+  void* tap;                  // RESID: optional copy of the new residual (activation type)
+  int ldtap;
+  // QKV epilogue
+  void* q;                    // [M, hq*hd]
+  void* kc;                   // this layer's K cache [hkv][max_ctx][hd]
+  void* vc;
+  const float* cos_t;         // [max_ctx][hd/2]
+  const float* sin_t;
+  const int* state;           // state[0] = committed length n
+  int pos_off;                // row r sits at position state[0] + pos_off + r
+  int hq, hkv, hd, max_ctx;
+};
+
+struct AttnArgs {
+  const void* q;              // [M, hq*hd]
+  const void* kc;             // [hkv][max_ctx][hd]
+  const void* vc;
+  void* out;                  // [M, hq*hd]
+  float* part_o;              // [n_part][R][hq][hd]
+  float* part_ml;             // [n_part][R][hq][2]
+  int* counters;              // [hkv][R/16], zero between launches
+  const int* state;
+  int pos_off, M, R, hq, hkv, hd, max_ctx;
+  float scale_log2;           // log2(e) / sqrt(hd)
+};
+
+// dtype: 0 = f32, 1 = bf16 (uint16 bit patterns)
+hipError_t launch_embed(int dtype, const int* tok, const void* E, float* x, int d, int M, hipStream_t s);
+hipError_t launch_rmsnorm(int dtype, const float* x, int ldx, const void* g, void* y, int ldy, int d,
+                          float eps, int M, hipStream_t s);
+hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t s);
+hipError_t launch_attention(int dtype, const AttnArgs& a, int n_part, hipStream_t s);
+hipError_t launch_argmax(const float* logits, int V, int ld, int* out, int M, hipStream_t s);
+hipError_t launch_accept(int* block, const int* post, int k, int* state, int* outlog, int* result,
+                         hipStream_t s);
+hipError_t launch_set_state(int* state, int idx, int value, hipStream_t s);
+hipError_t launch_copy_tokens(const int* src, int* dst, int n, hipStream_t s);
+
+// MoE (routed experts + shared experts)
+struct MoeArgs {
+  const void* X;              // normalised input [M, d]
+  int M, d, E, top_k, fe, n_shared;
+  const void* router;         // [E, d]
+  const void* eg; const void* eu; const void* ed;   // [E][fe][d], [E][fe][d], [E][d][fe]
+  const void* sg; const void* su; const void* sd;   // [S][fe][d], ...
+  float* rlogits;             // [M, E] f32
+  int* ids;                   // [M, top_k]  (router choice, or injected)
+  float* gates;               // [M, top_k]
+  const int* inject;          // [M, top_k] injected ids or null
+  void* act;                  // [M, top_k + S, fe] activation type
+  float* slot_out;            // [M, top_k + S, d] f32
+  float* resid;               // [M, d] residual (+= combined output)
+  int* groups;                // dedup work list (see kernels)
+  int* union_out;             // [1] union size of this pass
+  int dedup;
+};
+hipError_t launch_moe(int dtype, const MoeArgs& a, hipStream_t s);
+
+}  // namespace ssd

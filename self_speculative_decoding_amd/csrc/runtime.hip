@@ -1,0 +1,664 @@
+// Runtime behind the C ABI: context, weight table, workspace views, the pass
+// driver (prefill / draft / verify), accept + rollback and the decode loops.
+//
+// One pass = embedding -> layers -> final norm -> LM head -> argmax, with every
+// position read from device state (state[0] = committed length n), so the
+// plain greedy loop needs no host synchronisation and a speculative cycle
+// needs exactly one (the accept result), as the mlx-dflash README's
+// "Apple Silicon Optimizations" describe for their engine.
+#include <hip/hip_runtime.h>
+
+#include <chrono>
+#include <cmath>
+#include <cstring>
+#include <vector>
+
+#include "host.h"
+#include "kernels.h"
+
+using namespace ssd;
+
+#define HIPCHK(x)                                                                                    \
+  do {                                                                                               \
+    hipError_t e_ = (x);                                                                             \
+    if (e_ != hipSuccess) return fail(SSD_E_HIP, "%s failed: %s (%s:%d)", #x, hipGetErrorString(e_), \
+                                      __FILE__, __LINE__);                                           \
+  } while (0)
+
+#define SSDCHK(x)                    \
+  do {                               \
+    ssd_status s_ = (x);             \
+    if (s_ != SSD_OK) return s_;     \
+  } while (0)
+
+namespace {
+
+struct LayerW {
+  const void *attn_norm, *wq, *wk, *wv, *wo, *ffn_norm;
+  const void *w_gate, *w_up, *w_down;
+  const void *router, *eg, *eu, *ed, *sg, *su, *sd;
+  bool moe;
+  int ffn;
+  int feat_slot;   // index in feat_layers, or -1
+};
+
+enum { EV_A, EV_B, EV_C, EV_D, EV_N };
+
+}  // namespace
+
+struct ssd_ctx {
+  ssd_cfg cfg;
+  Layout lay;
+  hipStream_t stream;
+  char* ws;
+  size_t esz;
+  const void *embed, *final_norm, *lm_head, *fc;
+  std::vector<LayerW> L;
+  int state = SSD_ST_LOADED;
+  int n = 0;            // host copy of the committed length
+  int k = 0;            // drafts in the current block
+  int head_rows = 0;    // logits rows of the last pass
+  int feat_rows = 0;
+  int moe_inject = 0;   // rows of injected routing (0 = router)
+  int* hbuf = nullptr;  // pinned host scratch
+  hipEvent_t ev[EV_N] = {};
+  ssd_stats st;
+  // device views
+  float *x, *logits, *part_o, *part_ml, *cos_t, *sin_t;
+  void *xn, *q, *att, *act, *kc, *vc, *tap, *feat;
+  int *counters, *block, *post, *toks, *dstate, *result, *outlog;
+  int *tblock, *tpost, *tstate, *tresult, *toutlog;
+  float *m_rlogits, *m_gates, *m_slot_out;
+  int *m_ids, *m_inject, *m_groups, *m_union;
+};
+
+namespace {
+
+inline void* at(ssd_ctx* c, size_t off) { return c->ws + off; }
+
+size_t cache_layer_elems(const ssd_cfg& c) { return (size_t)c.n_kv_heads * c.max_ctx * c.head_dim; }
+
+// One decoder layer over M rows at positions state[0] + pos_off + r.
+ssd_status layer_forward(ssd_ctx* c, int l, int M, int pos_off, bool feats) {
+  const ssd_cfg& g = c->cfg;
+  const LayerW& w = c->L[l];
+  const int d = g.d_model, hq = g.n_q_heads, hkv = g.n_kv_heads, hd = g.head_dim;
+  const int dt = g.dtype;
+  hipStream_t s = c->stream;
+  void* kc = (char*)c->kc + (size_t)l * cache_layer_elems(g) * c->esz;
+  void* vc = (char*)c->vc + (size_t)l * cache_layer_elems(g) * c->esz;
+
+  HIPCHK(launch_rmsnorm(dt, c->x, d, w.attn_norm, c->xn, d, d, g.rms_eps, M, s));
+  {
+    GemmArgs a{};
+    a.X = c->xn; a.ldx = d; a.W0 = w.wq; a.W1 = w.wk; a.W2 = w.wv;
+    a.n0 = hq * hd; a.n1 = hkv * hd; a.M = M; a.N = (hq + 2 * hkv) * hd; a.K = d;
+    a.q = c->q; a.kc = kc; a.vc = vc; a.cos_t = c->cos_t; a.sin_t = c->sin_t;
+    a.state = c->dstate; a.pos_off = pos_off; a.hq = hq; a.hkv = hkv; a.hd = hd; a.max_ctx = g.max_ctx;
+    HIPCHK(launch_gemm(dt, EPI_QKV, a, s));
+  }
+  {
+    AttnArgs a{};
+    a.q = c->q; a.kc = kc; a.vc = vc; a.out = c->att; a.part_o = c->part_o; a.part_ml = c->part_ml;
+    a.counters = c->counters; a.state = c->dstate; a.pos_off = pos_off; a.M = M; a.R = c->lay.R;
+    a.hq = hq; a.hkv = hkv; a.hd = hd; a.max_ctx = g.max_ctx;
+    a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)hd));
+    const int n_part = (c->n + pos_off + M + ATT_PT - 1) / ATT_PT;
+    HIPCHK(launch_attention(dt, a, n_part, s));
+  }
+  {
+    GemmArgs a{};
+    a.X = c->att; a.ldx = hq * hd; a.W0 = w.wo; a.M = M; a.N = d; a.K = hq * hd; a.y = c->x; a.ldy = d;
+    HIPCHK(launch_gemm(dt, EPI_RESID, a, s));
+  }
+  HIPCHK(launch_rmsnorm(dt, c->x, d, w.ffn_norm, c->xn, d, d, g.rms_eps, M, s));
+  if (w.moe) {
+    MoeArgs a{};
+    a.X = c->xn; a.M = M; a.d = d; a.E = g.n_experts; a.top_k = g.top_k; a.fe = g.expert_ffn;
+    a.n_shared = g.n_shared; a.router = w.router; a.eg = w.eg; a.eu = w.eu; a.ed = w.ed;
+    a.sg = w.sg; a.su = w.su; a.sd = w.sd; a.rlogits = c->m_rlogits; a.ids = c->m_ids; a.gates = c->m_gates;
+    a.inject = c->moe_inject ? c->m_inject + (size_t)l * c->lay.R * g.top_k : nullptr;
+    a.act = c->act; a.slot_out = c->m_slot_out; a.resid = c->x; a.groups = c->m_groups;
+    a.union_out = c->m_union + l; a.dedup = g.moe_dedup;
+    HIPCHK(launch_moe(dt, a, s));
+  } else {
+    GemmArgs a{};
+    a.X = c->xn; a.ldx = d; a.W0 = w.w_gate; a.W1 = w.w_up; a.M = M; a.N = w.ffn; a.K = d;
+    a.out = c->act; a.ldo = w.ffn;
+    HIPCHK(launch_gemm(dt, EPI_SWIGLU, a, s));
+    GemmArgs b{};
+    b.X = c->act; b.ldx = w.ffn; b.W0 = w.w_down; b.M = M; b.N = d; b.K = w.ffn; b.y = c->x; b.ldy = d;
+    if (feats && w.feat_slot >= 0) {
+      b.tap = (char*)c->tap + (size_t)w.feat_slot * d * c->esz;
+      b.ldtap = g.n_feat * d;
+    }
+    HIPCHK(launch_gemm(dt, EPI_RESID, b, s));
+  }
+  return SSD_OK;
+}
+
+// Full pass: M tokens from d_tok at positions state[0]+pos_off+r through the
+// layers with skip[l] == 0 (all when skip is NULL); the head runs on rows
+// [head_row0, head_row0+head_rows) and writes argmax to d_arg.
+ssd_status run_pass(ssd_ctx* c, const int* d_tok, int M, int pos_off, const uint8_t* skip, int head_row0,
+                    int head_rows, int* d_arg, bool feats) {
+  const ssd_cfg& g = c->cfg;
+  const int d = g.d_model, dt = g.dtype;
+  hipStream_t s = c->stream;
+  HIPCHK(launch_embed(dt, d_tok, c->embed, c->x, d, M, s));
+  for (int l = 0; l < g.n_layers; ++l) {
+    if (skip && skip[l]) continue;
+    SSDCHK(layer_forward(c, l, M, pos_off, feats));
+  }
+  if (head_rows > 0) {
+    HIPCHK(launch_rmsnorm(dt, c->x + (size_t)head_row0 * d, d, c->final_norm, c->xn, d, d, g.rms_eps, head_rows, s));
+    GemmArgs a{};
+    a.X = c->xn; a.ldx = d; a.W0 = c->lm_head; a.M = head_rows; a.N = g.vocab; a.K = d;
+    a.y = c->logits; a.ldy = g.vocab;
+    HIPCHK(launch_gemm(dt, EPI_F32, a, s));
+    HIPCHK(launch_argmax(c->logits, g.vocab, g.vocab, d_arg, head_rows, s));
+    c->head_rows = head_rows;
+  }
+  if (feats && g.n_feat > 0) {
+    GemmArgs a{};
+    a.X = c->tap; a.ldx = g.n_feat * d; a.W0 = c->fc; a.M = M; a.N = d; a.K = g.n_feat * d;
+    a.out = c->feat; a.ldo = d;
+    HIPCHK(launch_gemm(dt, EPI_STORE, a, s));
+    c->feat_rows = M;
+  }
+  return SSD_OK;
+}
+
+ssd_status check_tokens(const ssd_cfg& g, const int32_t* t, int n) {
+  for (int i = 0; i < n; ++i)
+    if (t[i] < 0 || t[i] >= g.vocab) return fail(SSD_E_ARG, "token %d at index %d outside [0, %d)", t[i], i, g.vocab);
+  return SSD_OK;
+}
+
+ssd_status transition(ssd_ctx* c, int op) {
+  int next;
+  SSDCHK(check_transition(c->state, op, &next));
+  return SSD_OK;
+}
+
+void set_state(ssd_ctx* c, int op) {
+  int next = c->state;
+  check_transition(c->state, op, &next);
+  c->state = next;
+}
+
+float elapsed(hipEvent_t a, hipEvent_t b) {
+  float ms = 0.f;
+  if (hipEventElapsedTime(&ms, a, b) != hipSuccess) return 0.f;
+  return ms;
+}
+
+ssd_status do_prefill(ssd_ctx* c, const int32_t* tokens, int n) {
+  const ssd_cfg& g = c->cfg;
+  hipStream_t s = c->stream;
+  const int P = g.prefill_chunk;
+  c->n = 0;
+  HIPCHK(launch_set_state(c->dstate, 0, 0, s));
+  HIPCHK(launch_set_state(c->dstate, 1, 0, s));
+  for (int s0 = 0; s0 < n; s0 += P) {
+    const int rows = n - s0 < P ? n - s0 : P;
+    HIPCHK(hipMemcpyAsync(c->toks, tokens + s0, rows * sizeof(int32_t), hipMemcpyHostToDevice, s));
+    const bool last = s0 + rows == n;
+    SSDCHK(run_pass(c, c->toks, rows, s0, nullptr, rows - 1, last ? 1 : 0, c->block, false));
+  }
+  HIPCHK(launch_set_state(c->dstate, 0, n, s));
+  HIPCHK(launch_set_state(c->dstate, 1, 1, s));
+  HIPCHK(launch_copy_tokens(c->block, c->outlog, 1, s));
+  c->n = n;
+  return SSD_OK;
+}
+
+ssd_status do_accept(ssd_ctx* c, bool sync, int* a_out, int* nemit_out) {
+  hipStream_t s = c->stream;
+  HIPCHK(launch_accept(c->block, c->post, c->k, c->dstate, c->outlog, c->result, s));
+  if (sync) {
+    HIPCHK(hipMemcpyAsync(c->hbuf, c->result, (c->k + 3) * sizeof(int), hipMemcpyDeviceToHost, s));
+    HIPCHK(hipStreamSynchronize(s));
+    if (a_out) *a_out = c->hbuf[0];
+    if (nemit_out) *nemit_out = c->hbuf[1];
+  }
+  return SSD_OK;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// C ABI
+// ---------------------------------------------------------------------------
+
+extern "C" {
+
+ssd_status ssd_load(const ssd_cfg* cfg, const ssd_buf* weights, int32_t n_weights, ssd_buf workspace,
+                    void* hip_stream, ssd_ctx** out) {
+  clear_error();
+  if (!out) return fail(SSD_E_ARG, "out is NULL");
+  *out = nullptr;
+  SSDCHK(validate(cfg));
+  Layout lay;
+  compute_layout(*cfg, lay);
+  auto table = weight_table(*cfg);
+  if (!weights || n_weights != (int32_t)table.size())
+    return fail(SSD_E_ARG, "expected %d weight buffers, got %d", (int)table.size(), n_weights);
+  const size_t esz = cfg->dtype == SSD_BF16 ? 2 : 4;
+  for (int i = 0; i < n_weights; ++i) {
+    if (!weights[i].ptr) return fail(SSD_E_ARG, "weight %d is NULL", i);
+    if (weights[i].nbytes != (int64_t)(table[i] * esz))
+      return fail(SSD_E_ARG, "weight %d has %lld bytes, expected %lld", i, (long long)weights[i].nbytes,
+                  (long long)(table[i] * esz));
+    if ((uintptr_t)weights[i].ptr % 16) return fail(SSD_E_ARG, "weight %d is not 16-byte aligned", i);
+  }
+  if (!workspace.ptr || workspace.nbytes < (int64_t)lay.total)
+    return fail(SSD_E_ARG, "workspace needs %lld bytes", (long long)lay.total);
+  if ((uintptr_t)workspace.ptr % 256) return fail(SSD_E_ARG, "workspace is not 256-byte aligned");
+
+  ssd_ctx* c = new ssd_ctx();
+  c->cfg = *cfg;
+  c->lay = lay;
+  c->stream = (hipStream_t)hip_stream;
+  c->ws = (char*)workspace.ptr;
+  c->esz = esz;
+  int wi = 0;
+  c->embed = weights[wi++].ptr;
+  for (int l = 0; l < cfg->n_layers; ++l) {
+    LayerW w{};
+    w.attn_norm = weights[wi++].ptr;
+    w.wq = weights[wi++].ptr;
+    w.wk = weights[wi++].ptr;
+    w.wv = weights[wi++].ptr;
+    w.wo = weights[wi++].ptr;
+    w.ffn_norm = weights[wi++].ptr;
+    w.moe = is_moe_layer(*cfg, l);
+    if (w.moe) {
+      w.router = weights[wi++].ptr;
+      w.eg = weights[wi++].ptr;
+      w.eu = weights[wi++].ptr;
+      w.ed = weights[wi++].ptr;
+      w.sg = weights[wi++].ptr;
+      w.su = weights[wi++].ptr;
+      w.sd = weights[wi++].ptr;
+    } else {
+      w.w_gate = weights[wi++].ptr;
+      w.w_up = weights[wi++].ptr;
+      w.w_down = weights[wi++].ptr;
+      w.ffn = layer_ffn(*cfg);
+    }
+    w.feat_slot = -1;
+    for (int i = 0; i < cfg->n_feat; ++i)
+      if (cfg->feat_layers[i] == l) w.feat_slot = i;
+    c->L.push_back(w);
+  }
+  c->final_norm = weights[wi++].ptr;
+  c->lm_head = weights[wi++].ptr;
+  c->fc = cfg->n_feat > 0 ? weights[wi++].ptr : nullptr;
+
+  c->kc = at(c, lay.kc); c->vc = at(c, lay.vc);
+  c->x = (float*)at(c, lay.x); c->xn = at(c, lay.xn); c->q = at(c, lay.q); c->att = at(c, lay.att);
+  c->act = at(c, lay.act); c->logits = (float*)at(c, lay.logits);
+  c->part_o = (float*)at(c, lay.part_o); c->part_ml = (float*)at(c, lay.part_ml);
+  c->counters = (int*)at(c, lay.counters);
+  c->cos_t = (float*)at(c, lay.rope_cos); c->sin_t = (float*)at(c, lay.rope_sin);
+  c->block = (int*)at(c, lay.block); c->post = (int*)at(c, lay.post); c->toks = (int*)at(c, lay.toks);
+  c->dstate = (int*)at(c, lay.state); c->result = (int*)at(c, lay.result); c->outlog = (int*)at(c, lay.outlog);
+  c->tblock = (int*)at(c, lay.tblock); c->tpost = (int*)at(c, lay.tpost); c->tstate = (int*)at(c, lay.tstate);
+  c->tresult = (int*)at(c, lay.tresult); c->toutlog = (int*)at(c, lay.toutlog);
+  c->tap = cfg->n_feat ? at(c, lay.tap) : nullptr;
+  c->feat = cfg->n_feat ? at(c, lay.feat) : nullptr;
+  if (cfg->n_experts > 0) {
+    c->m_rlogits = (float*)at(c, lay.m_rlogits); c->m_ids = (int*)at(c, lay.m_ids);
+    c->m_gates = (float*)at(c, lay.m_gates); c->m_inject = (int*)at(c, lay.m_inject);
+    c->m_slot_out = (float*)at(c, lay.m_slot_out); c->m_groups = (int*)at(c, lay.m_groups);
+    c->m_union = (int*)at(c, lay.m_union);
+  }
+
+  ssd_status st = SSD_OK;
+  auto cleanup = [&](ssd_status s) { ssd_free(c); return s; };
+  // rotary tables, computed in double on the host: angle = pos * theta^(-2i/hd)
+  {
+    const int half = cfg->head_dim / 2;
+    std::vector<float> cs((size_t)cfg->max_ctx * half), sn((size_t)cfg->max_ctx * half);
+    for (int p = 0; p < cfg->max_ctx; ++p)
+      for (int i = 0; i < half; ++i) {
+        const double ang = (double)p * std::pow((double)cfg->rope_theta, -2.0 * i / cfg->head_dim);
+        cs[(size_t)p * half + i] = (float)std::cos(ang);
+        sn[(size_t)p * half + i] = (float)std::sin(ang);
+      }
+    hipError_t e = hipMemsetAsync(c->ws, 0, lay.total, c->stream);
+    if (e == hipSuccess) e = hipMemcpyAsync(c->cos_t, cs.data(), cs.size() * 4, hipMemcpyHostToDevice, c->stream);
+    if (e == hipSuccess) e = hipMemcpyAsync(c->sin_t, sn.data(), sn.size() * 4, hipMemcpyHostToDevice, c->stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
+    if (e == hipSuccess) e = hipHostMalloc((void**)&c->hbuf, 4096, hipHostMallocDefault);
+    for (int i = 0; i < EV_N && e == hipSuccess; ++i) e = hipEventCreate(&c->ev[i]);
+    if (e != hipSuccess) {
+      st = fail(SSD_E_HIP, "load: %s", hipGetErrorString(e));
+      return cleanup(st);
+    }
+  }
+  memset(&c->st, 0, sizeof c->st);
+  *out = c;
+  return SSD_OK;
+}
+
+void ssd_free(ssd_ctx* c) {
+  if (!c) return;
+  (void)hipStreamSynchronize(c->stream);
+  for (int i = 0; i < EV_N; ++i)
+    if (c->ev[i]) (void)hipEventDestroy(c->ev[i]);
+  if (c->hbuf) (void)hipHostFree(c->hbuf);
+  delete c;
+}
+
+ssd_status ssd_reset(ssd_ctx* c) {
+  clear_error();
+  if (!c) return fail(SSD_E_ARG, "ctx is NULL");
+  SSDCHK(transition(c, SSD_OP_RESET));
+  HIPCHK(launch_set_state(c->dstate, 0, 0, c->stream));
+  HIPCHK(launch_set_state(c->dstate, 1, 0, c->stream));
+  HIPCHK(hipStreamSynchronize(c->stream));
+  c->n = 0;
+  c->k = 0;
+  memset(&c->st, 0, sizeof c->st);
+  set_state(c, SSD_OP_RESET);
+  return SSD_OK;
+}
+
+int32_t ssd_state(const ssd_ctx* c) { return c ? c->state : -1; }
+int32_t ssd_context_length(const ssd_ctx* c) { return c ? c->n : -1; }
+
+ssd_status ssd_prefill(ssd_ctx* c, const int32_t* tokens, int32_t n, int32_t* next_tok) {
+  clear_error();
+  if (!c || !tokens) return fail(SSD_E_ARG, "NULL argument");
+  SSDCHK(transition(c, SSD_OP_PREFILL));
+  if (n < 1) return fail(SSD_E_ARG, "empty prompt");
+  if (n + 1 > c->cfg.max_ctx) return fail(SSD_E_CAPACITY, "prompt of %d tokens needs max_ctx > %d", n, n);
+  SSDCHK(check_tokens(c->cfg, tokens, n));
+  auto t0 = std::chrono::steady_clock::now();
+  SSDCHK(do_prefill(c, tokens, n));
+  if (next_tok) HIPCHK(hipMemcpyAsync(c->hbuf, c->block, 4, hipMemcpyDeviceToHost, c->stream));
+  HIPCHK(hipStreamSynchronize(c->stream));
+  if (next_tok) *next_tok = c->hbuf[0];
+  c->st.t_prefill_ms += std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
+  set_state(c, SSD_OP_PREFILL);
+  return SSD_OK;
+}
+
+ssd_status ssd_draft(ssd_ctx* c, const uint8_t* skip_mask, int32_t k, int32_t* drafts) {
+  clear_error();
+  if (!c) return fail(SSD_E_ARG, "ctx is NULL");
+  SSDCHK(transition(c, SSD_OP_DRAFT));
+  if (k < 1 || k + 1 > c->cfg.max_block) return fail(SSD_E_ARG, "k=%d outside [1, max_block-1=%d]", k, c->cfg.max_block - 1);
+  if (c->n + k + 1 > c->cfg.max_ctx) return fail(SSD_E_CAPACITY, "n=%d + k+1=%d exceeds max_ctx=%d", c->n, k + 1, c->cfg.max_ctx);
+  for (int j = 0; j < k; ++j)
+    SSDCHK(run_pass(c, c->block + j, 1, j, skip_mask, 0, 1, c->block + j + 1, false));
+  c->k = k;
+  if (drafts) {
+    HIPCHK(hipMemcpyAsync(c->hbuf, c->block + 1, k * sizeof(int), hipMemcpyDeviceToHost, c->stream));
+    HIPCHK(hipStreamSynchronize(c->stream));
+    memcpy(drafts, c->hbuf, k * sizeof(int));
+  }
+  c->st.drafted += k;
+  set_state(c, SSD_OP_DRAFT);
+  return SSD_OK;
+}
+
+ssd_status ssd_verify(ssd_ctx* c, const int32_t* block, int32_t m, int32_t* posterior) {
+  clear_error();
+  if (!c) return fail(SSD_E_ARG, "ctx is NULL");
+  const int op = block ? SSD_OP_VERIFY_BLOCK : SSD_OP_VERIFY;
+  SSDCHK(transition(c, op));
+  if (block) {
+    if (m < 1 || m > c->cfg.max_block) return fail(SSD_E_ARG, "m=%d outside [1, max_block=%d]", m, c->cfg.max_block);
+    SSDCHK(check_tokens(c->cfg, block, m));
+  } else if (m != c->k + 1) {
+    return fail(SSD_E_ARG, "m=%d but the drafted block has %d tokens", m, c->k + 1);
+  }
+  if (c->n + m + 1 > c->cfg.max_ctx) return fail(SSD_E_CAPACITY, "n=%d + m=%d exceeds max_ctx=%d", c->n, m, c->cfg.max_ctx);
+  if (block) {
+    memcpy(c->hbuf, block, m * sizeof(int));
+    HIPCHK(hipMemcpyAsync(c->block, c->hbuf, m * sizeof(int), hipMemcpyHostToDevice, c->stream));
+    c->k = m - 1;
+  }
+  HIPCHK(hipEventRecord(c->ev[EV_A], c->stream));
+  SSDCHK(run_pass(c, c->block, m, 0, nullptr, 0, m, c->post, true));
+  HIPCHK(hipEventRecord(c->ev[EV_B], c->stream));
+  HIPCHK(hipMemcpyAsync(c->hbuf, c->post, m * sizeof(int), hipMemcpyDeviceToHost, c->stream));
+  HIPCHK(hipStreamSynchronize(c->stream));
+  if (posterior) memcpy(posterior, c->hbuf, m * sizeof(int));
+  c->st.t_verify_ms += elapsed(c->ev[EV_A], c->ev[EV_B]);
+  c->st.verify_passes += 1;
+  set_state(c, op);
+  return SSD_OK;
+}
+
+ssd_status ssd_accept_rollback(ssd_ctx* c, int32_t* n_accepted, int32_t* emitted, int32_t* n_emitted) {
+  clear_error();
+  if (!c) return fail(SSD_E_ARG, "ctx is NULL");
+  SSDCHK(transition(c, SSD_OP_ACCEPT));
+  int a = 0, ne = 0;
+  SSDCHK(do_accept(c, true, &a, &ne));
+  if (n_accepted) *n_accepted = a;
+  if (n_emitted) *n_emitted = ne;
+  if (emitted) memcpy(emitted, c->hbuf + 2, ne * sizeof(int));
+  c->n += ne;
+  c->st.cycles += 1;
+  c->st.accepted += a;
+  c->st.emitted += ne;
+  set_state(c, SSD_OP_ACCEPT);
+  return SSD_OK;
+}
+
+ssd_status ssd_generate(ssd_ctx* c, const int32_t* prompt, int32_t n_prompt, int32_t n_new, int32_t greedy,
+                        const uint8_t* skip_mask, int32_t k, int32_t* out, ssd_stats* stats) {
+  clear_error();
+  if (!c || !prompt || !out) return fail(SSD_E_ARG, "NULL argument");
+  if (greedy != 1) return fail(SSD_E_UNSUPPORTED, "only greedy decoding is supported");
+  if (n_prompt < 1 || n_new < 1) return fail(SSD_E_ARG, "n_prompt and n_new must be positive");
+  const bool spec = skip_mask != nullptr && k > 0;
+  if (spec && k + 1 > c->cfg.max_block) return fail(SSD_E_ARG, "k=%d exceeds max_block-1", k);
+  if (k < 0) return fail(SSD_E_ARG, "negative k");
+  const int kk = spec ? k : 0;
+  if (n_prompt + n_new + kk + 1 > c->cfg.max_ctx)
+    return fail(SSD_E_CAPACITY, "prompt %d + %d new + block %d exceeds max_ctx %d", n_prompt, n_new, kk + 1, c->cfg.max_ctx);
+  SSDCHK(check_tokens(c->cfg, prompt, n_prompt));
+  if (c->state != SSD_ST_LOADED) SSDCHK(ssd_reset(c));
+  memset(&c->st, 0, sizeof c->st);
+  SSDCHK(ssd_prefill(c, prompt, n_prompt, nullptr));
+  hipStream_t s = c->stream;
+  auto t0 = std::chrono::steady_clock::now();
+  int produced = 1;
+  if (!spec) {
+    // plain greedy: one full pass per token, positions and tokens device-resident
+    c->k = 0;
+    HIPCHK(hipEventRecord(c->ev[EV_A], s));
+    for (int i = 1; i < n_new; ++i) {
+      SSDCHK(run_pass(c, c->block, 1, 0, nullptr, 0, 1, c->post, false));
+      SSDCHK(do_accept(c, false, nullptr, nullptr));
+      c->n += 1;
+    }
+    HIPCHK(hipEventRecord(c->ev[EV_B], s));
+    HIPCHK(hipStreamSynchronize(s));
+    produced = n_new;
+    c->st.cycles = n_new - 1;
+    c->st.emitted = n_new - 1;
+    c->st.verify_passes = n_new - 1;
+    c->st.t_verify_ms = elapsed(c->ev[EV_A], c->ev[EV_B]);
+  } else {
+    while (produced < n_new) {
+      HIPCHK(hipEventRecord(c->ev[EV_A], s));
+      for (int j = 0; j < k; ++j)
+        SSDCHK(run_pass(c, c->block + j, 1, j, skip_mask, 0, 1, c->block + j + 1, false));
+      c->k = k;
+      HIPCHK(hipEventRecord(c->ev[EV_B], s));
+      SSDCHK(run_pass(c, c->block, k + 1, 0, nullptr, 0, k + 1, c->post, true));
+      HIPCHK(hipEventRecord(c->ev[EV_C], s));
+      int a = 0, ne = 0;
+      HIPCHK(launch_accept(c->block, c->post, k, c->dstate, c->outlog, c->result, s));
+      HIPCHK(hipEventRecord(c->ev[EV_D], s));
+      HIPCHK(hipMemcpyAsync(c->hbuf, c->result, 2 * sizeof(int), hipMemcpyDeviceToHost, s));
+      HIPCHK(hipStreamSynchronize(s));
+      a = c->hbuf[0];
+      ne = c->hbuf[1];
+      c->n += ne;
+      produced += ne;
+      c->st.cycles += 1;
+      c->st.drafted += k;
+      c->st.accepted += a;
+      c->st.emitted += ne;
+      c->st.verify_passes += 1;
+      c->st.t_draft_ms += elapsed(c->ev[EV_A], c->ev[EV_B]);
+      c->st.t_verify_ms += elapsed(c->ev[EV_B], c->ev[EV_C]);
+      c->st.t_accept_ms += elapsed(c->ev[EV_C], c->ev[EV_D]);
+    }
+  }
+  std::vector<int32_t> tmp(n_new);
+  HIPCHK(hipMemcpyAsync(tmp.data(), c->outlog, n_new * sizeof(int32_t), hipMemcpyDeviceToHost, s));
+  HIPCHK(hipStreamSynchronize(s));
+  c->st.t_decode_ms = std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
+  memcpy(out, tmp.data(), n_new * sizeof(int32_t));
+  c->state = SSD_ST_READY;
+  if (stats) *stats = c->st;
+  return SSD_OK;
+}
+
+ssd_status ssd_get_stats(const ssd_ctx* c, ssd_stats* stats) {
+  if (!c || !stats) return fail(SSD_E_ARG, "NULL argument");
+  *stats = c->st;
+  return SSD_OK;
+}
+
+ssd_status ssd_read_logits(ssd_ctx* c, float* host, int32_t rows) {
+  clear_error();
+  if (!c || !host) return fail(SSD_E_ARG, "NULL argument");
+  if (rows < 1 || rows > c->head_rows) return fail(SSD_E_ARG, "rows=%d but the last pass has %d", rows, c->head_rows);
+  HIPCHK(hipMemcpyAsync(host, c->logits, (size_t)rows * c->cfg.vocab * 4, hipMemcpyDeviceToHost, c->stream));
+  HIPCHK(hipStreamSynchronize(c->stream));
+  return SSD_OK;
+}
+
+ssd_status ssd_read_features(ssd_ctx* c, uint16_t* host, int32_t rows) {
+  clear_error();
+  if (!c || !host) return fail(SSD_E_ARG, "NULL argument");
+  if (c->cfg.n_feat == 0) return fail(SSD_E_UNSUPPORTED, "no feature tap configured");
+  if (c->cfg.dtype != SSD_BF16) return fail(SSD_E_UNSUPPORTED, "features are read as bf16");
+  if (rows < 1 || rows > c->feat_rows) return fail(SSD_E_ARG, "rows=%d but the last verify had %d", rows, c->feat_rows);
+  HIPCHK(hipMemcpyAsync(host, c->feat, (size_t)rows * c->cfg.d_model * 2, hipMemcpyDeviceToHost, c->stream));
+  HIPCHK(hipStreamSynchronize(c->stream));
+  return SSD_OK;
+}
+
+ssd_status ssd_set_routing(ssd_ctx* c, const int32_t* ids, int32_t n) {
+  clear_error();
+  if (!c) return fail(SSD_E_ARG, "ctx is NULL");
+  if (c->cfg.n_experts == 0) return fail(SSD_E_UNSUPPORTED, "not an MoE model");
+  if (n == 0) { c->moe_inject = 0; return SSD_OK; }
+  if (!ids || n < 0 || n > c->lay.R) return fail(SSD_E_ARG, "n=%d outside [0, %d]", n, c->lay.R);
+  const ssd_cfg& g = c->cfg;
+  std::vector<int32_t> buf((size_t)g.n_layers * c->lay.R * g.top_k, 0);
+  for (int l = 0; l < g.n_layers; ++l)
+    for (int t = 0; t < n; ++t)
+      for (int j = 0; j < g.top_k; ++j) {
+        const int32_t e = ids[((size_t)l * n + t) * g.top_k + j];
+        if (is_moe_layer(g, l) && (e < 0 || e >= g.n_experts)) return fail(SSD_E_ARG, "expert id %d out of range", e);
+        buf[((size_t)l * c->lay.R + t) * g.top_k + j] = is_moe_layer(g, l) ? e : 0;
+      }
+  HIPCHK(hipMemcpyAsync(c->m_inject, buf.data(), buf.size() * 4, hipMemcpyHostToDevice, c->stream));
+  HIPCHK(hipStreamSynchronize(c->stream));
+  c->moe_inject = n;
+  return SSD_OK;
+}
+
+ssd_status ssd_read_union(ssd_ctx* c, int32_t* host) {
+  clear_error();
+  if (!c || !host) return fail(SSD_E_ARG, "NULL argument");
+  if (c->cfg.n_experts == 0) return fail(SSD_E_UNSUPPORTED, "not an MoE model");
+  HIPCHK(hipMemcpyAsync(host, c->m_union, c->cfg.n_layers * 4, hipMemcpyDeviceToHost, c->stream));
+  HIPCHK(hipStreamSynchronize(c->stream));
+  return SSD_OK;
+}
+
+ssd_status ssd_test_accept(ssd_ctx* c, const int32_t* d, const int32_t* p, int32_t k, int32_t* a) {
+  clear_error();
+  if (!c || !p || !a || (k > 0 && !d)) return fail(SSD_E_ARG, "NULL argument");
+  if (k < 0 || k + 1 > SSD_MAX_BLOCK) return fail(SSD_E_ARG, "k=%d outside [0, %d]", k, SSD_MAX_BLOCK - 1);
+  int* h = c->hbuf;
+  h[0] = -1;
+  for (int i = 0; i < k; ++i) h[1 + i] = d[i];
+  for (int i = 0; i <= k; ++i) h[64 + i] = p[i];
+  for (int i = 0; i < 16; ++i) h[128 + i] = 0;
+  hipStream_t s = c->stream;
+  HIPCHK(hipMemcpyAsync(c->tblock, h, (k + 1) * 4, hipMemcpyHostToDevice, s));
+  HIPCHK(hipMemcpyAsync(c->tpost, h + 64, (k + 1) * 4, hipMemcpyHostToDevice, s));
+  HIPCHK(hipMemcpyAsync(c->tstate, h + 128, 16 * 4, hipMemcpyHostToDevice, s));
+  HIPCHK(launch_accept(c->tblock, c->tpost, k, c->tstate, c->toutlog, c->tresult, s));
+  HIPCHK(hipMemcpyAsync(h + 256, c->tresult, (k + 3) * 4, hipMemcpyDeviceToHost, s));
+  HIPCHK(hipMemcpyAsync(h + 320, c->tstate, 2 * 4, hipMemcpyDeviceToHost, s));
+  HIPCHK(hipStreamSynchronize(s));
+  *a = h[256];
+  // internal consistency of the kernel's outputs
+  if (h[257] != h[256] + 1 || h[320] != h[257] || h[321] != h[257])
+    return fail(SSD_E_HIP, "accept kernel produced inconsistent counters");
+  return SSD_OK;
+}
+
+ssd_status ssd_time_op(ssd_ctx* c, int32_t op, int32_t layer, int32_t m, int32_t iters, float* avg_us) {
+  clear_error();
+  if (!c || !avg_us) return fail(SSD_E_ARG, "NULL argument");
+  const ssd_cfg& g = c->cfg;
+  if (layer < 0 || layer >= g.n_layers) return fail(SSD_E_ARG, "layer out of range");
+  if (m < 1 || m > c->lay.R) return fail(SSD_E_ARG, "m outside [1, %d]", c->lay.R);
+  if (iters < 1) return fail(SSD_E_ARG, "iters < 1");
+  if (c->n + m + 1 > g.max_ctx) return fail(SSD_E_CAPACITY, "no room past the committed length");
+  const LayerW& w = c->L[layer];
+  const int d = g.d_model, hq = g.n_q_heads, hkv = g.n_kv_heads, hd = g.head_dim, dt = g.dtype;
+  hipStream_t s = c->stream;
+  void* kc = (char*)c->kc + (size_t)layer * cache_layer_elems(g) * c->esz;
+  void* vc = (char*)c->vc + (size_t)layer * cache_layer_elems(g) * c->esz;
+  GemmArgs a{};
+  AttnArgs at{};
+  int epi = -1;
+  switch (op) {
+    case 0:
+      if (w.moe) return fail(SSD_E_ARG, "layer %d is an MoE layer", layer);
+      a.X = c->xn; a.ldx = d; a.W0 = w.w_gate; a.W1 = w.w_up; a.M = m; a.N = w.ffn; a.K = d; a.out = c->act; a.ldo = w.ffn;
+      epi = EPI_SWIGLU; break;
+    case 1:
+      if (w.moe) return fail(SSD_E_ARG, "layer %d is an MoE layer", layer);
+      a.X = c->act; a.ldx = w.ffn; a.W0 = w.w_down; a.M = m; a.N = d; a.K = w.ffn; a.y = c->x; a.ldy = d;
+      epi = EPI_RESID; break;
+    case 2:
+      a.X = c->xn; a.ldx = d; a.W0 = w.wq; a.W1 = w.wk; a.W2 = w.wv; a.n0 = hq * hd; a.n1 = hkv * hd; a.M = m;
+      a.N = (hq + 2 * hkv) * hd; a.K = d; a.q = c->q; a.kc = kc; a.vc = vc; a.cos_t = c->cos_t; a.sin_t = c->sin_t;
+      a.state = c->dstate; a.pos_off = 0; a.hq = hq; a.hkv = hkv; a.hd = hd; a.max_ctx = g.max_ctx;
+      epi = EPI_QKV; break;
+    case 3:
+      a.X = c->att; a.ldx = hq * hd; a.W0 = w.wo; a.M = m; a.N = d; a.K = hq * hd; a.y = c->x; a.ldy = d;
+      epi = EPI_RESID; break;
+    case 4:
+      a.X = c->xn; a.ldx = d; a.W0 = c->lm_head; a.M = m; a.N = g.vocab; a.K = d; a.y = c->logits; a.ldy = g.vocab;
+      if (m > g.max_block) return fail(SSD_E_ARG, "lm_head timing needs m <= max_block");
+      epi = EPI_F32; break;
+    case 5:
+      at.q = c->q; at.kc = kc; at.vc = vc; at.out = c->att; at.part_o = c->part_o; at.part_ml = c->part_ml;
+      at.counters = c->counters; at.state = c->dstate; at.pos_off = 0; at.M = m; at.R = c->lay.R;
+      at.hq = hq; at.hkv = hkv; at.hd = hd; at.max_ctx = g.max_ctx;
+      at.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)hd));
+      break;
+    default:
+      return fail(SSD_E_ARG, "unknown op %d", op);
+  }
+  HIPCHK(hipEventRecord(c->ev[EV_A], s));
+  for (int i = 0; i < iters; ++i) {
+    if (op == 5) HIPCHK(launch_attention(dt, at, (c->n + m + ATT_PT - 1) / ATT_PT, s));
+    else HIPCHK(launch_gemm(dt, epi, a, s));
+  }
+  HIPCHK(hipEventRecord(c->ev[EV_B], s));
+  HIPCHK(hipStreamSynchronize(s));
+  *avg_us = elapsed(c->ev[EV_A], c->ev[EV_B]) * 1000.f / iters;
+  return SSD_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,91 @@
+"""C-ABI library: loads, exports every declared symbol, and its host-only
+logic (configuration checks, weight table, layout, skip mask, state machine)
+behaves as documented.  No GPU needed: nothing here launches a kernel."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import skip_mask as oracle_skip_mask
+from _common import ROOT
+
+ssd = pytest.importorskip("self_speculative_decoding_amd")
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "ssd.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssd_[a-z_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(ssd.LIB_PATH)
+    names = _declared()
+    assert len(names) >= 20
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(ssd.EXPORTS) == names
+
+
+@pytest.mark.parametrize("name", ["tiny", "qwen3-4b", "llama-8b", "qwen3-8b", "dsv2-lite"])
+def test_workload_cfgs_validate_and_weight_table_matches(name):
+    cfg = synth.config(name)
+    c = ssd.make_cfg(cfg)
+    assert ssd.validate_cfg(c) == 0, ssd.lib.ssd_last_error()
+    numels = ssd.weight_numels(c)
+    specs = synth.weight_specs(cfg)
+    assert numels == [int(np.prod(s)) for _, s, _ in specs]
+    assert ssd.workspace_bytes(c) > 0
+
+
+def test_llama8b_weight_bytes():
+    # 32 layers x 436.2 MB + embedding and LM head of 1.05 GB each
+    assert abs(synth.weight_bytes(synth.config("llama-8b")) / 1e9 - 16.06) < 0.01
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("n_kv_heads", 3, -1), ("head_dim", 96, -5), ("dtype", 7, -1), ("max_block", 0, -1),
+    ("max_block", 33, -1), ("prefill_chunk", 24, -1), ("vocab", 4100, -5), ("rms_eps", 0.0, -1),
+])
+def test_validate_rejects(field, value, status):
+    c = ssd.make_cfg(synth.config("llama-8b"))
+    setattr(c, field, value)
+    assert ssd.validate_cfg(c) == status
+    assert ssd.workspace_bytes(c) == -1
+    assert ssd.lib.ssd_last_error()
+
+
+def test_null_cfg():
+    assert ssd.lib.ssd_validate_cfg(None) == -1
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 7, 32, 36, 80])
+@pytest.mark.parametrize("frac", [0.0, 0.1, 0.2, 0.25, 0.3, 0.4, 0.5, 0.9, 1.0])
+def test_skip_mask_matches_oracle(n, frac):
+    assert ssd.skip_mask(n, frac).tolist() == oracle_skip_mask(n, frac)
+
+
+def test_skip_mask_rejects():
+    m = np.zeros(4, np.uint8)
+    assert ssd.lib.ssd_skip_mask(0, 0.5, m.ctypes.data_as(ctypes.c_void_p)) == -1
+    assert ssd.lib.ssd_skip_mask(4, 1.5, m.ctypes.data_as(ctypes.c_void_p)) == -1
+    assert ssd.lib.ssd_skip_mask(4, 0.5, None) == -1
+
+
+def test_state_machine():
+    L, R, D, V = ssd.ST_LOADED, ssd.ST_READY, ssd.ST_DRAFTED, ssd.ST_VERIFIED
+    ok = {(L, ssd.OP_PREFILL): R, (R, ssd.OP_DRAFT): D, (D, ssd.OP_VERIFY): V,
+          (R, ssd.OP_VERIFY_BLOCK): V, (V, ssd.OP_ACCEPT): R}
+    for s in (L, R, D, V):
+        assert ssd.check_transition(s, ssd.OP_RESET) == L
+        for op in (ssd.OP_PREFILL, ssd.OP_DRAFT, ssd.OP_VERIFY, ssd.OP_VERIFY_BLOCK, ssd.OP_ACCEPT):
+            assert ssd.check_transition(s, op) == ok.get((s, op), -2), (s, op)
+    assert ssd.check_transition(L, 99) == -1
+
+
+def test_strerror():
+    for s in (0, -1, -2, -3, -4, -5):
+        assert ssd.lib.ssd_strerror(s)
