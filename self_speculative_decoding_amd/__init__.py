@@ -59,6 +59,10 @@ class SSDError(RuntimeError):
 
 
 def _load():
+    # torch first: its HIP runtime (SONAME libamdhip64.so.7) is then the one
+    # libssd.so binds to, so the process has a single HIP runtime and device
+    # pointers from torch are valid inside the library.
+    import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with `python -m self_speculative_decoding_amd.build`")
     lib = ctypes.CDLL(LIB_PATH)
