@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""Greedy self-speculative decode benchmark on one MI355X.
+
+Workload (default): Llama-3.1-8B-shaped bf16 decoder with seeded random
+weights, a 1024-token uniform-random prompt and 512 greedy tokens; the draft
+skips the contiguous middle 20 % of the layers and proposes k=3 tokens per
+cycle.  A step is one whole decode (prefill + 512 tokens through
+draft/verify/accept cycles).  ``value`` is decode tokens per second after the
+prefill (tokens after the first / decode wall time).
+
+Also reported: plain greedy tok/s measured back-to-back in the same process
+(speedup = self-spec / greedy), the verify pass's HBM bandwidth (algorithmic
+bytes of weights + KV per pass / HIP-event time of the pass), the roofline
+of the dominant kernel (the gate/up GEMM at the verify width, timed with HIP
+events on the library's stream), the skip x k sweep, and the CPU oracle's
+decode rate on a bounded sample.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama-8b]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0   # MI355X HBM3E peak
+
+
+def log(msg: str) -> None:
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def weight_bytes_per_pass(cfg: dict) -> int:
+    """Weights one full pass streams: every layer matrix plus the LM head
+    (the embedding table is gathered, M rows only)."""
+    import synth
+    eb = 2 if cfg["dtype"] == "bf16" else 4
+    tot = 0
+    for name, shape, kind in synth.weight_specs(cfg):
+        if name in ("embed", "fc") or kind == "gain":
+            continue
+        n = 1
+        for s in shape:
+            n *= s
+        tot += n * eb
+    return tot
+
+
+def pass_bytes(cfg: dict, M: int, ctx: float, layers: int | None = None, head: bool = True) -> float:
+    """Algorithmic HBM bytes of one pass of M rows ending at context ctx:
+    weights once, K and V of positions [0, ctx) read once per layer, K/V of
+    the M new rows written, logits written."""
+    eb = 2 if cfg["dtype"] == "bf16" else 4
+    L = cfg["n_layers"]
+    per_layer_w = (weight_bytes_per_pass(cfg) - cfg["vocab"] * cfg["d_model"] * eb) / L
+    nl = L if layers is None else layers
+    kv_tok = 2 * cfg["n_kv_heads"] * cfg["head_dim"] * eb
+    b = nl * (per_layer_w + kv_tok * ctx + kv_tok * M)
+    if head:
+        b += cfg["vocab"] * cfg["d_model"] * eb + M * cfg["vocab"] * 4
+    return b
+
+
+def cpu_baseline(cfg, weights, prompt, budget_s: float) -> dict:
+    """The oracle (float64 CPU decoder) timed on this host: greedy decode steps
+    after a short prompt, until about budget_s seconds of decode work."""
+    import numpy as np
+    from oracle import Model
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    log("cpu baseline: building the oracle model")
+    m = Model(cfg, weights)
+    short = prompt[:8]
+    cache, n, last = m.prefill(short)
+    tok = int(np.argmax(last))
+    t0 = time.perf_counter()
+    steps = 0
+    while True:
+        lg = m.forward([tok], n, cache)[0]
+        n += 1
+        steps += 1
+        tok = int(np.argmax(lg))
+        el = time.perf_counter() - t0
+        log(f"cpu baseline: decode step {steps} at {el:.1f}s")
+        if el >= budget_s or steps >= 64:
+            break
+    del m
+    return {"value": steps / el, "unit": "tok/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{steps} float64 greedy decode steps of the same model after an 8-token prompt "
+                      f"(context <= {8 + steps}); weight conversion and prefill excluded"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="llama-8b", choices=["llama-8b", "qwen3-4b", "tiny"])
+    ap.add_argument("--skip", type=float, default=None, help="draft skip fraction (default: workload's)")
+    ap.add_argument("--k", type=int, default=None, help="draft length (default: workload's)")
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--n-new", type=int, default=None, help="tokens per decode (default: workload's)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: the decode path has no multi-GPU mode "
+              "(pass --gpus 1)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import synth
+    from self_speculative_decoding_amd import Engine, make_cfg, skip_mask
+
+    cfg = synth.config(args.workload)
+    frac = args.skip if args.skip is not None else cfg.get("skip_frac", 0.5)
+    k = args.k if args.k is not None else cfg["k"]
+    ks = list(cfg.get("ks", (k,)))
+    fracs = list(cfg.get("skip_fracs", (frac,)))
+    n_new, P = args.n_new or cfg["n_new"], cfg["prompt_len"]
+    log(f"workload {args.workload}: generating weights")
+    t = time.perf_counter()
+    weights = synth.make_weights(cfg)
+    prompt = synth.make_prompt(cfg)
+    log(f"weights ready in {time.perf_counter() - t:.1f}s; uploading")
+    eng = Engine(make_cfg(cfg, max_block=max(ks + [k]) + 1, prefill_chunk=256),
+                 [weights[n] for n, _, _ in synth.weight_specs(cfg)])
+    mask = skip_mask(cfg["n_layers"], frac)
+    skipped = [int(i) for i in np.nonzero(mask)[0]]
+    log(f"draft skips layers {skipped[0]}..{skipped[-1]} ({len(skipped)} of {cfg['n_layers']}), k={k}")
+
+    for w in range(args.warmup):
+        eng.generate(prompt, n_new, mask, k)
+        eng.generate(prompt, n_new)
+        log(f"warmup {w + 1}/{args.warmup} done")
+
+    # ---- timed region: K self-speculative decodes ----
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    dec_ms = ver_ms = dr_ms = 0.0
+    vpasses = cycles = acc = drafted = 0
+    spec_out = None
+    for i in range(args.steps):
+        out, st = eng.generate(prompt, n_new, mask, k)
+        spec_out = out
+        dec_ms += st["t_decode_ms"]
+        ver_ms += st["t_verify_ms"]
+        dr_ms += st["t_draft_ms"]
+        vpasses += st["verify_passes"]
+        cycles += st["cycles"]
+        acc += st["accepted"]
+        drafted += st["drafted"]
+        log(f"step {i + 1}/{args.steps}: {(n_new - 1) / st['t_decode_ms'] * 1e3:.1f} tok/s, "
+            f"{st['cycles']} cycles, {st['accepted']}/{st['drafted']} drafts accepted")
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    value = args.steps * (n_new - 1) / (dec_ms / 1e3)
+
+    # ---- plain greedy, back to back ----
+    base_ms = base_pass_ms = 0.0
+    base_passes = 0
+    base_out = None
+    for i in range(args.steps):
+        out, st = eng.generate(prompt, n_new)
+        base_out = out
+        base_ms += st["t_decode_ms"]
+        base_pass_ms += st["t_verify_ms"]
+        base_passes += st["verify_passes"]
+    base_tps = args.steps * (n_new - 1) / (base_ms / 1e3)
+    lossless = spec_out == base_out
+    log(f"greedy {base_tps:.1f} tok/s; self-spec {value:.1f} tok/s; lossless={lossless}")
+
+    # ---- verify-pass bandwidth ----
+    avg_ctx = P + n_new / 2.0
+    vb = pass_bytes(cfg, k + 1, avg_ctx)
+    v_ms = ver_ms / max(vpasses, 1)
+    v_gbs = vb / (v_ms / 1e3) / 1e9
+    bb = pass_bytes(cfg, 1, avg_ctx)
+    b_ms = base_pass_ms / max(base_passes, 1)
+    b_gbs = bb / (b_ms / 1e3) / 1e9
+
+    # ---- dominant kernel: gate/up GEMM (+SwiGLU) at the verify width ----
+    ops = {}
+    for op in ("gate_up", "down", "qkv", "o", "attention", "lm_head"):
+        for m in (1, k + 1):
+            ops[f"{op}_m{m}"] = round(eng.time_op(op, 0, m, 50), 2)
+    d, F = cfg["d_model"], cfg["ffn_dim"]
+    gu_bytes = 2 * F * d * 2
+    gu_us = eng.time_op("gate_up", 0, k + 1, 200)
+    roof = {"bound": "hbm", "kernel": "gemm_bf16_kernel<EPI_SWIGLU> (gate/up GEMM + SwiGLU)",
+            "m": k + 1, "achieved": round(gu_bytes / (gu_us * 1e-6) / 1e9, 1), "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": round(gu_bytes / (gu_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+            "traffic": None, "bytes_per_launch": gu_bytes, "avg_us": round(gu_us, 2)}
+    log(f"gate/up GEMM m={k + 1}: {gu_us:.1f} us = {roof['achieved']:.0f} GB/s")
+
+    # ---- skip x k sweep (one decode each) ----
+    sweep = []
+    if not args.no_sweep and len(fracs) * len(ks) > 1:
+        for f in fracs:
+            m_ = skip_mask(cfg["n_layers"], f)
+            for kk in ks:
+                out, st = eng.generate(prompt, n_new, m_, kk)
+                tps = (n_new - 1) / (st["t_decode_ms"] / 1e3)
+                sweep.append({"skip": f, "k": kk, "tok_s": round(tps, 2), "speedup": round(tps / base_tps, 4),
+                              "acceptance": round(st["accepted"] / max(st["drafted"], 1), 4),
+                              "tokens_per_cycle": round(st["emitted"] / max(st["cycles"], 1), 3),
+                              "verify_ms": round(st["t_verify_ms"] / max(st["verify_passes"], 1), 3),
+                              "draft_step_ms": round(st["t_draft_ms"] / max(st["drafted"], 1), 3),
+                              "lossless": out == base_out})
+                log(f"sweep skip={f} k={kk}: {tps:.1f} tok/s ({tps / base_tps:.3f}x)")
+    eng.close()
+    del eng
+    torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(cfg, weights, prompt, args.cpu_budget)
+
+    skipped_desc = f"{skipped[0]}-{skipped[-1]}"
+    line = {
+        "metric": "greedy self-spec decode tok/s + verify-pass HBM GB/s (% of peak), 8B-shaped bf16",
+        "value": round(value, 2), "unit": "tok/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 1), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": cfg["dtype"], "data": "synthetic",
+        "config": {"workload": f"{args.workload}-shaped {cfg['dtype']} random-init decoder, {P}-token uniform "
+                               f"prompt, {n_new} greedy tokens, self-spec middle skip {frac:.0%} "
+                               f"(layers {skipped_desc}), k={k}",
+                   "prompt_len": P, "n_new": n_new, "skip_frac": frac, "k": k, "parallelism": "none"},
+        "greedy_tok_s": round(base_tps, 2), "speedup": round(value / base_tps, 4), "lossless": lossless,
+        "acceptance": round(acc / max(drafted, 1), 4), "tokens_per_cycle": round(args.steps * (n_new - 1) / max(cycles, 1), 3),
+        "verify_pass": {"m": k + 1, "ms": round(v_ms, 4), "bytes": int(vb), "gbs": round(v_gbs, 1),
+                        "frac": round(v_gbs / PEAK_HBM_GBS, 4), "avg_ctx": avg_ctx},
+        "decode_pass_m1": {"ms": round(b_ms, 4), "bytes": int(bb), "gbs": round(b_gbs, 1),
+                           "frac": round(b_gbs / PEAK_HBM_GBS, 4)},
+        "draft_step_ms": round(dr_ms / max(drafted, 1), 4),
+        "roofline": roof, "ops_us": ops, "sweep": sweep, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -182,6 +182,13 @@ ssd_status ssd_generate(ssd_ctx* ctx, const int32_t* prompt, int32_t n_prompt, i
                         int32_t greedy, const uint8_t* skip_mask, int32_t k,
                         int32_t* out, ssd_stats* stats);
 
+/* Options: SSD_OPT_GRAPHS (default 1) replays each decode-loop pass (draft
+ * step, verify, plain decode step) as a HIP graph captured on first use;
+ * 0 launches every kernel directly.  Both give bitwise-identical results.
+ * hip_stream must not be the null stream while graphs are on. */
+enum { SSD_OPT_GRAPHS = 0 };
+ssd_status ssd_set_option(ssd_ctx* ctx, int32_t option, int32_t value);
+
 /* Statistics accumulated since load/reset (per-phase times from HIP events). */
 ssd_status ssd_get_stats(const ssd_ctx* ctx, ssd_stats* stats);
 

@@ -26,7 +26,7 @@ EXPORTS = ["ssd_validate_cfg", "ssd_n_weights", "ssd_weight_numel", "ssd_workspa
            "ssd_load", "ssd_free", "ssd_reset", "ssd_state", "ssd_context_length",
            "ssd_prefill", "ssd_draft", "ssd_verify", "ssd_accept_rollback", "ssd_generate",
            "ssd_get_stats", "ssd_read_logits", "ssd_read_features", "ssd_set_routing",
-           "ssd_read_union", "ssd_test_accept", "ssd_time_op"]
+           "ssd_read_union", "ssd_test_accept", "ssd_time_op", "ssd_set_option"]
 
 
 class Cfg(ctypes.Structure):
@@ -64,7 +64,7 @@ def _load():
     # pointers from torch are valid inside the library.
     import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m self_speculative_decoding_amd.build`")
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python self_speculative_decoding_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     P, I32, I64, VP = ctypes.POINTER, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
     pc = P(Cfg)
@@ -94,6 +94,7 @@ def _load():
         "ssd_read_union": (I32, [VP, VP]),
         "ssd_test_accept": (I32, [VP, VP, VP, I32, P(I32)]),
         "ssd_time_op": (I32, [VP, I32, I32, I32, I32, P(ctypes.c_float)]),
+        "ssd_set_option": (I32, [VP, I32, I32]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -190,7 +191,9 @@ class Engine:
         if nb < 0:
             _check(validate_cfg(cfg))
         self._ws = torch.empty(nb, dtype=torch.uint8, device=self.device)
-        self.stream = torch.cuda.current_stream(self.device)
+        # a stream of the library's own (default priority): graphs cannot be
+        # captured on the null stream
+        self.stream = torch.cuda.Stream(self.device)
         ctx = ctypes.c_void_p()
         torch.cuda.synchronize(self.device)
         _check(lib.ssd_load(ctypes.byref(cfg), bufs, len(weights), Buf(self._ws.data_ptr(), nb),
@@ -220,6 +223,9 @@ class Engine:
 
     def reset(self):
         _check(lib.ssd_reset(self.ctx))
+
+    def set_graphs(self, on: bool):
+        _check(lib.ssd_set_option(self.ctx, 0, 1 if on else 0))
 
     # -- the decode step --------------------------------------------------------------
     def prefill(self, tokens) -> int:

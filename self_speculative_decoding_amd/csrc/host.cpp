@@ -76,7 +76,8 @@ ssd_status validate(const ssd_cfg* cp) {
   if (c.max_block < 1 || c.max_block > SSD_MAX_BLOCK) return fail(SSD_E_ARG, "max_block must be in [1, %d]", SSD_MAX_BLOCK);
   if (c.prefill_chunk < 16 || c.prefill_chunk > 256 || c.prefill_chunk % 16)
     return fail(SSD_E_ARG, "prefill_chunk must be a multiple of 16 in [16, 256]");
-  if (c.max_ctx < 2 || c.max_ctx > (1 << 20)) return fail(SSD_E_ARG, "max_ctx out of range");
+  // the attention combine holds one partition of kAttPT keys per lane of a 128-lane workgroup
+  if (c.max_ctx < 2 || c.max_ctx > 128 * kAttPT) return fail(SSD_E_ARG, "max_ctx must be in [2, %d]", 128 * kAttPT);
   if (c.n_experts < 0 || c.n_shared < 0 || c.n_dense_layers < 0 || c.n_feat < 0)
     return fail(SSD_E_ARG, "negative count");
   if (c.n_experts > 0) {
@@ -95,6 +96,8 @@ ssd_status validate(const ssd_cfg* cp) {
     if (is_moe_layer(c, c.feat_layers[i])) return fail(SSD_E_UNSUPPORTED, "feature tap on an MoE layer");
   }
   // kernel shape requirements
+  if (c.d_model % 4 || c.d_model > 16384) return fail(SSD_E_UNSUPPORTED, "d_model must be a multiple of 4 and <= 16384");
+  if (c.vocab > 16 * 16384) return fail(SSD_E_UNSUPPORTED, "vocab must be <= 262144");
   const int64_t qo = (int64_t)c.n_q_heads * c.head_dim;
   const int f = layer_ffn(c);
   if (c.dtype == SSD_BF16) {
@@ -137,6 +140,8 @@ bool compute_layout(const ssd_cfg& c, Layout& L) {
   }
   L.act = take((size_t)R * fact * esz);
   L.logits = take((size_t)c.max_block * c.vocab * 4);
+  L.amax_v = take((size_t)c.max_block * (c.vocab / 16 + 1) * 4);
+  L.amax_i = take((size_t)c.max_block * (c.vocab / 16 + 1) * 4);
   L.part_o = take((size_t)L.n_part * R * hq * hd * 4);
   L.part_ml = take((size_t)L.n_part * R * hq * 2 * 4);
   L.counters = take((size_t)hkv * (R / 16) * 4);

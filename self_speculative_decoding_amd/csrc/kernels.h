@@ -19,6 +19,7 @@ enum Epi {
   EPI_QKV = 3,     // RoPE on q,k; q -> q buffer; k,v -> KV cache at their positions
   EPI_STORE = 4,   // out[m*ldo + n] = acc in the activation type (feature fc)
   EPI_MOE = 5,     // per-row routed/shared expert output accumulation (see moe kernels)
+  EPI_LOGITS = 6,  // EPI_F32 plus per-16-column (max, lowest index) pairs for the argmax
 };
 
 struct GemmArgs {
@@ -44,6 +45,9 @@ struct GemmArgs {
   const int* state;           // state[0] = committed length n
   int pos_off;                // row r sits at position state[0] + pos_off + r
   int hq, hkv, hd, max_ctx;
+  // LOGITS epilogue: per-tile argmax partials [M][N/16]
+  float* amax_v;
+  int* amax_i;
 };
 
 struct AttnArgs {
@@ -66,6 +70,7 @@ hipError_t launch_rmsnorm(int dtype, const float* x, int ldx, const void* g, voi
 hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t s);
 hipError_t launch_attention(int dtype, const AttnArgs& a, int n_part, hipStream_t s);
 hipError_t launch_argmax(const float* logits, int V, int ld, int* out, int M, hipStream_t s);
+hipError_t launch_argmax_tiles(const float* pv, const int* pi, int nt, int* out, int M, hipStream_t s);
 hipError_t launch_accept(int* block, const int* post, int k, int* state, int* outlog, int* result,
                          hipStream_t s);
 hipError_t launch_set_state(int* state, int idx, int value, hipStream_t s);

@@ -54,20 +54,45 @@ __global__ __launch_bounds__(256) void embed_kernel(const int* __restrict__ tok,
 // ---------------------------------------------------------------------------
 
 template <typename E>
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ x, int ldx,
-                                                      const E* __restrict__ g, E* __restrict__ y,
-                                                      int ldy, int d, float eps) {
-  __shared__ float ws[4];
+__global__ __launch_bounds__(1024) void rmsnorm_kernel(const float* __restrict__ x, int ldx,
+                                                       const E* __restrict__ g, E* __restrict__ y,
+                                                       int ldy, int d, float eps) {
+  // lanes own 4 consecutive elements: i = 4*(t + 1024*j); d is a multiple of 4
+  __shared__ float ws[16];
   const float* xr = x + (size_t)blockIdx.x * ldx;
+  constexpr int J = 4;   // d <= 16384
+  float4 v[J];
   float s = 0.f;
-  for (int i = threadIdx.x; i < d; i += 256) s = fmaf(xr[i], xr[i], s);
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int i = 4 * (threadIdx.x + 1024 * j);
+    v[j] = i < d ? *(const float4*)(xr + i) : float4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    s = fmaf(v[j].x, v[j].x, s);
+    s = fmaf(v[j].y, v[j].y, s);
+    s = fmaf(v[j].z, v[j].z, s);
+    s = fmaf(v[j].w, v[j].w, s);
+  }
   s = wave_sum(s);
   if ((threadIdx.x & 63) == 0) ws[threadIdx.x >> 6] = s;
   __syncthreads();
-  s = ((ws[0] + ws[1]) + ws[2]) + ws[3];
+  s = 0.f;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) s += ws[w];
   const float r = 1.0f / sqrtf(s / (float)d + eps);
   E* yr = y + (size_t)blockIdx.x * ldy;
-  for (int i = threadIdx.x; i < d; i += 256) yr[i] = fromf<E>(xr[i] * r * tof(g[i]));
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int i = 4 * (threadIdx.x + 1024 * j);
+    if (i < d) {
+      yr[i] = fromf<E>(v[j].x * r * tof(g[i]));
+      yr[i + 1] = fromf<E>(v[j].y * r * tof(g[i + 1]));
+      yr[i + 2] = fromf<E>(v[j].z * r * tof(g[i + 2]));
+      yr[i + 3] = fromf<E>(v[j].w * r * tof(g[i + 3]));
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -77,6 +102,8 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
 template <typename E>
 __device__ __forceinline__ void epi_single(const GemmArgs& a, int epi, int m, int n, float v) {
   if (epi == EPI_F32) {
+    a.y[(size_t)m * a.ldy + n] = v;
+  } else if (epi == EPI_LOGITS) {
     a.y[(size_t)m * a.ldy + n] = v;
   } else if (epi == EPI_RESID) {
     const float r = a.y[(size_t)m * a.ldy + n] + v;
@@ -122,9 +149,10 @@ __device__ __forceinline__ void epi_v_single(const GemmArgs& a, int m, int vh, i
 // bf16 skinny GEMM on MFMA 16x16x32 (weight streaming)
 //
 // Y[M,N] = X[M,K] . W[N,K]^T, M padded to 16-row tiles (grid.y).  A workgroup
-// of 4 waves owns NW 16-column tiles; the waves split K into 4 contiguous
-// quarters, each accumulating its MFMA K-steps in order, and the quarters are
-// added in wave order through LDS.  The per-element arithmetic is therefore a
+// of KW waves owns NW 16-column tiles; the waves split K into KW contiguous
+// ranges, each accumulating its MFMA K-steps in order, and the ranges are
+// added in wave order through LDS.  KW depends on N only (8 waves for narrow
+// GEMMs, to keep enough loads in flight; 4 for the LM head).  The per-element arithmetic is therefore a
 // function of (shape, row data) only.  Each lane streams 16-byte pieces of
 // weight rows; U K-steps of loads are issued before their MFMAs.
 //
@@ -156,8 +184,8 @@ __device__ __forceinline__ const uint16_t* gemm_row(const GemmArgs& a, int t, in
   return W + (size_t)(t * 16 + c) * a.K;
 }
 
-template <int EPI, int NW>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
+template <int EPI, int NW, int KW>
+__global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane & 15, kg = lane >> 4;
   const int t = blockIdx.x, mt = blockIdx.y;
@@ -170,7 +198,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
   for (int j = 0; j < NW; ++j) wr[j] = gemm_row<EPI, NW>(a, t, j, c, &head, &dim) + kg * 8;
 
   const int S = a.K >> 5;
-  const int s0 = (S * wave) >> 2, s1 = (S * (wave + 1)) >> 2;
+  const int s0 = (S * wave) / KW, s1 = (S * (wave + 1)) / KW;
   f32x4 acc[NW];
 #pragma unroll
   for (int j = 0; j < NW; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -202,7 +230,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
     }
   }
 
-  __shared__ f32x4 red[3][NW][64];
+  __shared__ f32x4 red[KW - 1][NW][64];
   if (wave > 0) {
 #pragma unroll
     for (int j = 0; j < NW; ++j) red[wave - 1][j][lane] = acc[j];
@@ -210,7 +238,9 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
   __syncthreads();
   if (wave != 0) return;
 #pragma unroll
-  for (int j = 0; j < NW; ++j) acc[j] = ((acc[j] + red[0][j][lane]) + red[1][j][lane]) + red[2][j][lane];
+  for (int w = 0; w < KW - 1; ++w)
+#pragma unroll
+    for (int j = 0; j < NW; ++j) acc[j] = acc[j] + red[w][j][lane];
 
   if (EPI == EPI_QKV) {
     const bool rot = head < a.hq + a.hkv;
@@ -231,8 +261,23 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = mt * 16 + 4 * kg + i;
-      if (m >= a.M) continue;
       const int n = t * 16 + c;
+      if (EPI == EPI_LOGITS) {
+        // (max, lowest index) over this tile's 16 columns, fixed butterfly
+        float bv = acc[0][i];
+        int bi = n;
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {
+          const float ov = __shfl_xor(bv, o);
+          const int oi = __shfl_xor(bi, o);
+          if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+        }
+        if (m < a.M && c == 0) {
+          a.amax_v[(size_t)m * gridDim.x + t] = bv;
+          a.amax_i[(size_t)m * gridDim.x + t] = bi;
+        }
+      }
+      if (m >= a.M) continue;
       if (EPI == EPI_SWIGLU) epi_swiglu<uint16_t>(a, m, n, acc[0][i], acc[1][i]);
       else epi_single<uint16_t>(a, EPI, m, n, acc[0][i]);
     }
@@ -308,9 +353,8 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
 // vector, each holding a fixed slice of head dims: a dot product is the
 // in-order slice sum followed by a fixed butterfly over the TPQ lanes, so all
 // lanes hold all PT scores.  Keys past the row's own position are excluded by
-// select.  Per-partition (max, sum, P.V) go to a partial buffer; the last
-// workgroup of a (kv head, tile) to finish (atomic ticket) combines the
-// partitions 0..pos/PT of each row in partition order.
+// select.  Per-partition (max, sum, P.V) go to a partial buffer that
+// attn_combine_kernel reduces in partition order.
 // ---------------------------------------------------------------------------
 
 template <typename E, int HD, int G>
@@ -323,7 +367,6 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) E Ks[PT * HD];
   __shared__ __attribute__((aligned(16))) E Vs[PT * HD];
   __shared__ float S[QV][PT + 1];
-  __shared__ int ticket;
 
   const int p = blockIdx.x, kvh = blockIdx.y, mt = blockIdx.z;
   const int tid = threadIdx.x;
@@ -414,42 +457,174 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     }
   }
 
-  // the last workgroup of this (kv head, row tile) to finish combines the partitions
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) ticket = atomicAdd(a.counters + kvh * (a.R / ROW_TILE) + mt, 1);
-  __syncthreads();
-  if (ticket != (int)gridDim.x - 1) return;
-  __threadfence();
-  if (tid == 0) a.counters[kvh * (a.R / ROW_TILE) + mt] = 0;
+}
 
-  if (r < nrows) {
-    const int np = pos / PT + 1;
-    float M = -INFINITY;
-    for (int pp = 0; pp < np; ++pp)
-      M = fmaxf(M, a.part_ml[(((size_t)pp * a.R + row) * a.hq + head) * 2]);
-    float L = 0.f, o[SL];
+// bf16 attention partition on MFMA 16x16x32.
+//
+// Same partitioning and output as attn_kernel.  Query vectors qi = r*G + g of
+// the row tile form up to four 16-row MFMA tiles (one per wave).  S = Q.K^T
+// takes Q fragments from the q buffer and K fragments straight from the
+// cache rows; the row max and sum of each query are a fixed butterfly over the
+// 16 lanes holding its keys; P is rounded to bf16 (the row sum uses the
+// rounded values) and O = P.V reads P and a transposed V tile from LDS.
+// Every output element is produced by the same instruction sequence for any
+// number of rows in the pass.
+template <int G>
+__global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
+  constexpr int HD = 128, PT = ATT_PT, PS = PT + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[HD][PS];
+  __shared__ __attribute__((aligned(16))) uint16_t Ps[4][16][PS];
+  const int p = blockIdx.x, kvh = blockIdx.y, mt = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = lane & 15, kg = lane >> 4;
+  const int base = a.state[0] + a.pos_off;
+  const int row0 = mt * ROW_TILE;
+  const int nrows = min(ROW_TILE, a.M - row0);
+  const int key0 = p * PT;
+  const int maxpos = base + row0 + nrows - 1;
+  if (key0 > maxpos) return;   // whole workgroup: no row reaches this partition
+  const uint4 zero = {0u, 0u, 0u, 0u};
+
+  // V tile, transposed into LDS (keys past the last row's position read as 0)
+  const uint16_t* vb = (const uint16_t*)a.vc + ((size_t)kvh * a.max_ctx + key0) * HD;
+  for (int e = tid; e < PT * HD / 8; e += 256) {
+    const int key = e / (HD / 8), d0 = (e % (HD / 8)) * 8;
+    uint4 v = key0 + key <= maxpos ? *(const uint4*)(vb + (size_t)key * HD + d0) : zero;
+    const uint16_t* pv = (const uint16_t*)&v;
 #pragma unroll
-    for (int d = 0; d < SL; ++d) o[d] = 0.f;
-    for (int pp = 0; pp < np; ++pp) {
-      const float* pm = a.part_ml + (((size_t)pp * a.R + row) * a.hq + head) * 2;
-      const float w = exp2f(pm[0] - M);
-      L += w * pm[1];
-      const float* po = a.part_o + (((size_t)pp * a.R + row) * a.hq + head) * HD + sub * SL;
-#pragma unroll
-      for (int d = 0; d < SL; ++d) o[d] += w * po[d];
-    }
-    const float inv = 1.0f / L;
-    E* out = (E*)a.out + (size_t)row * a.hq * HD + (size_t)head * HD + sub * SL;
-#pragma unroll
-    for (int d = 0; d < SL; ++d) out[d] = fromf<E>(o[d] * inv);
+    for (int j = 0; j < 8; ++j) Vt[d0 + j][key] = pv[j];
   }
+
+  // S = Q . K^T for this wave's 16 query vectors x 64 keys
+  const int QV = nrows * G;
+  const int qi = wave * 16 + c;
+  const bool qv = qi < QV;
+  const int qr = qi / G, qg = qi % G;
+  const uint16_t* qp = (const uint16_t*)a.q + (size_t)(row0 + (qv ? qr : 0)) * a.hq * HD +
+                       (size_t)(kvh * G + qg) * HD + kg * 8;
+  uint4 qa[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) qa[ks] = qv ? *(const uint4*)(qp + ks * 32) : zero;
+  const uint16_t* kb = (const uint16_t*)a.kc + ((size_t)kvh * a.max_ctx + key0) * HD + kg * 8;
+  f32x4 s[4];
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) {
+    s[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int key = kt * 16 + c;
+    const bool kv = key0 + key <= maxpos;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const uint4 kf = kv ? *(const uint4*)(kb + (size_t)key * HD + ks * 32) : zero;
+      s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[ks]),
+                                                      __builtin_bit_cast(bf16x8, kf), s[kt], 0, 0, 0);
+    }
+  }
+  // lane holds S[query 4*kg+i][key kt*16+c]
+  float mx[4], l[4];
+  int pos_i[4];
+  bool row_ok[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q2 = wave * 16 + 4 * kg + i;
+    row_ok[i] = q2 < QV;
+    pos_i[i] = base + row0 + q2 / G;
+    float m = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      const bool valid = row_ok[i] && key0 + kt * 16 + c <= pos_i[i];
+      m = valid ? fmaxf(m, s[kt][i] * a.scale_log2) : m;
+    }
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+    mx[i] = m;
+    float sum = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      const bool valid = row_ok[i] && key0 + kt * 16 + c <= pos_i[i];
+      const uint16_t pb = valid ? f2bf(exp2f(s[kt][i] * a.scale_log2 - m)) : (uint16_t)0;
+      sum += bf2f(pb);
+      Ps[wave][4 * kg + i][kt * 16 + c] = pb;
+    }
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) sum += __shfl_xor(sum, o);
+    l[i] = sum;
+  }
+  __syncthreads();
+
+  // O = P . V
+  f32x4 o[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const uint4 pa = *(const uint4*)&Ps[wave][c][ks * 32 + kg * 8];
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const uint4 vf = *(const uint4*)&Vt[dt * 16 + c][ks * 32 + kg * 8];
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pa),
+                                                      __builtin_bit_cast(bf16x8, vf), o[dt], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (!row_ok[i] || key0 > pos_i[i]) continue;
+    const int q2 = wave * 16 + 4 * kg + i;
+    const int row = row0 + q2 / G, head = kvh * G + q2 % G;
+    const size_t ph = ((size_t)p * a.R + row) * a.hq + head;
+    float* po = a.part_o + ph * HD;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) po[dt * 16 + c] = o[dt][i];
+    if (c == 0) {
+      a.part_ml[ph * 2] = mx[i];
+      a.part_ml[ph * 2 + 1] = l[i];
+    }
+  }
+}
+
+// Combine of the attention partitions: one workgroup per (row, head), one
+// lane per head dim.  Row r at position pos uses partitions 0..pos/PT, added
+// in partition order with weights exp2(m_p - max m).
+template <typename E>
+__global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
+  __shared__ float sm[128], sl[128];
+  const int row = blockIdx.x, head = blockIdx.y, t = threadIdx.x;
+  const int pos = a.state[0] + a.pos_off + row;
+  const int np = pos / ATT_PT + 1;
+  if (t < np) {
+    const float* pm = a.part_ml + (((size_t)t * a.R + row) * a.hq + head) * 2;
+    sm[t] = pm[0];
+    sl[t] = pm[1];
+  }
+  __syncthreads();
+  float M = -INFINITY;
+  for (int pp = 0; pp < np; ++pp) M = fmaxf(M, sm[pp]);
+  float L = 0.f;
+  for (int pp = 0; pp < np; ++pp) L += exp2f(sm[pp] - M) * sl[pp];
+  if (t >= a.hd) return;
+  const size_t stride = (size_t)a.R * a.hq * a.hd;
+  const float* po = a.part_o + ((size_t)row * a.hq + head) * a.hd + t;
+  float acc = 0.f;
+  int pp = 0;
+  for (; pp + 8 <= np; pp += 8) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = po[(size_t)(pp + j) * stride];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc += exp2f(sm[pp + j] - M) * v[j];
+  }
+  for (; pp < np; ++pp) acc += exp2f(sm[pp] - M) * po[(size_t)pp * stride];
+  ((E*)a.out)[(size_t)row * a.hq * a.hd + (size_t)head * a.hd + t] = fromf<E>(acc / L);
 }
 
 // ---------------------------------------------------------------------------
 // argmax per row (lowest index among equal maxima)
 // ---------------------------------------------------------------------------
 
+__device__ __forceinline__ void amax_merge(float& bv, int& bi, float ov, int oi) {
+  if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+}
+
+// plain row scan (float32 models)
 __global__ __launch_bounds__(1024) void argmax_kernel(const float* __restrict__ L, int V, int ld,
                                                       int* __restrict__ out) {
   __shared__ float bv[16];
@@ -462,16 +637,41 @@ __global__ __launch_bounds__(1024) void argmax_kernel(const float* __restrict__ 
     if (x > best) { best = x; idx = v; }
   }
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float ob = __shfl_xor(best, o);
-    const int oi = __shfl_xor(idx, o);
-    if (ob > best || (ob == best && oi < idx)) { best = ob; idx = oi; }
-  }
+  for (int o = 32; o > 0; o >>= 1) amax_merge(best, idx, __shfl_xor(best, o), __shfl_xor(idx, o));
   if ((threadIdx.x & 63) == 0) { bv[threadIdx.x >> 6] = best; bi[threadIdx.x >> 6] = idx; }
   __syncthreads();
   if (threadIdx.x == 0) {
-    for (int w = 1; w < 16; ++w)
-      if (bv[w] > best || (bv[w] == best && bi[w] < idx)) { best = bv[w]; idx = bi[w]; }
+    for (int w = 1; w < 16; ++w) amax_merge(best, idx, bv[w], bi[w]);
+    out[blockIdx.x] = idx == 0x7fffffff ? 0 : idx;
+  }
+}
+
+// reduce of the per-tile (max, index) pairs written by the LM head epilogue
+__global__ __launch_bounds__(1024) void argmax_tiles_kernel(const float* __restrict__ pv, const int* __restrict__ pi,
+                                                            int nt, int* __restrict__ out) {
+  __shared__ float bv[16];
+  __shared__ int bi[16];
+  const float* rv = pv + (size_t)blockIdx.x * nt;
+  const int* ri = pi + (size_t)blockIdx.x * nt;
+  constexpr int J = 16;   // nt <= 16384
+  float v[J];
+  int id[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int t = threadIdx.x + 1024 * j;
+    v[j] = t < nt ? rv[t] : -INFINITY;
+    id[j] = t < nt ? ri[t] : 0x7fffffff;
+  }
+  float best = v[0];
+  int idx = id[0];
+#pragma unroll
+  for (int j = 1; j < J; ++j) amax_merge(best, idx, v[j], id[j]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) amax_merge(best, idx, __shfl_xor(best, o), __shfl_xor(idx, o));
+  if ((threadIdx.x & 63) == 0) { bv[threadIdx.x >> 6] = best; bi[threadIdx.x >> 6] = idx; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < 16; ++w) amax_merge(best, idx, bv[w], bi[w]);
     out[blockIdx.x] = idx == 0x7fffffff ? 0 : idx;
   }
 }
@@ -524,8 +724,8 @@ hipError_t launch_embed(int dtype, const int* tok, const void* E, float* x, int 
 
 hipError_t launch_rmsnorm(int dtype, const float* x, int ldx, const void* g, void* y, int ldy, int d, float eps,
                           int M, hipStream_t s) {
-  if (dtype) rmsnorm_kernel<uint16_t><<<M, 256, 0, s>>>(x, ldx, (const uint16_t*)g, (uint16_t*)y, ldy, d, eps);
-  else rmsnorm_kernel<float><<<M, 256, 0, s>>>(x, ldx, (const float*)g, (float*)y, ldy, d, eps);
+  if (dtype) rmsnorm_kernel<uint16_t><<<M, 1024, 0, s>>>(x, ldx, (const uint16_t*)g, (uint16_t*)y, ldy, d, eps);
+  else rmsnorm_kernel<float><<<M, 1024, 0, s>>>(x, ldx, (const float*)g, (float*)y, ldy, d, eps);
   return hipGetLastError();
 }
 
@@ -536,14 +736,22 @@ hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t s) {
     if (epi == EPI_QKV) tiles = (a.hq + 2 * a.hkv) * a.hd / 16;
     else tiles = a.N / 16;
     dim3 grid(tiles, mt);
+    const bool wide = tiles >= 1024;   // a function of N only
+#define SSD_G(E, NW)                                                      \
+  case E:                                                                 \
+    if (wide) gemm_bf16_kernel<E, NW, 4><<<grid, 256, 0, s>>>(a);         \
+    else gemm_bf16_kernel<E, NW, 8><<<grid, 512, 0, s>>>(a);              \
+    break;
     switch (epi) {
-      case EPI_F32: gemm_bf16_kernel<EPI_F32, 1><<<grid, 256, 0, s>>>(a); break;
-      case EPI_RESID: gemm_bf16_kernel<EPI_RESID, 1><<<grid, 256, 0, s>>>(a); break;
-      case EPI_SWIGLU: gemm_bf16_kernel<EPI_SWIGLU, 2><<<grid, 256, 0, s>>>(a); break;
-      case EPI_QKV: gemm_bf16_kernel<EPI_QKV, 1><<<grid, 256, 0, s>>>(a); break;
-      case EPI_STORE: gemm_bf16_kernel<EPI_STORE, 1><<<grid, 256, 0, s>>>(a); break;
+      SSD_G(EPI_F32, 1)
+      SSD_G(EPI_LOGITS, 1)
+      SSD_G(EPI_RESID, 1)
+      SSD_G(EPI_SWIGLU, 2)
+      SSD_G(EPI_QKV, 1)
+      SSD_G(EPI_STORE, 1)
       default: return hipErrorInvalidValue;
     }
+#undef SSD_G
   } else {
     int npairs;
     if (epi == EPI_QKV) npairs = (a.hq + 2 * a.hkv) * (a.hd / 2);
@@ -566,11 +774,19 @@ template <typename E>
 static hipError_t attn_dispatch(const AttnArgs& a, int n_part, int hd, hipStream_t s) {
   const int G = a.hq / a.hkv;
   dim3 grid(n_part, a.hkv, (a.M + ROW_TILE - 1) / ROW_TILE);
+  bool done = false;
+  if (sizeof(E) == 2 && hd == 128) {
+    if (G == 1) { attn_mfma_kernel<1><<<grid, 256, 0, s>>>(a); done = true; }
+    if (G == 2) { attn_mfma_kernel<2><<<grid, 256, 0, s>>>(a); done = true; }
+    if (G == 4) { attn_mfma_kernel<4><<<grid, 256, 0, s>>>(a); done = true; }
+  }
 #define SSD_ATT(HDv, Gv) \
-  if (hd == HDv && G == Gv) { attn_kernel<E, HDv, Gv><<<grid, 256, 0, s>>>(a); return hipGetLastError(); }
+  if (!done && hd == HDv && G == Gv) { attn_kernel<E, HDv, Gv><<<grid, 256, 0, s>>>(a); done = true; }
   SSD_ATT(64, 1) SSD_ATT(64, 2) SSD_ATT(64, 4) SSD_ATT(128, 1) SSD_ATT(128, 2) SSD_ATT(128, 4)
 #undef SSD_ATT
-  return hipErrorInvalidValue;
+  if (!done) return hipErrorInvalidValue;
+  attn_combine_kernel<E><<<dim3(a.M, a.hq), 128, 0, s>>>(a);
+  return hipGetLastError();
 }
 
 hipError_t launch_attention(int dtype, const AttnArgs& a, int n_part, hipStream_t s) {
@@ -579,6 +795,11 @@ hipError_t launch_attention(int dtype, const AttnArgs& a, int n_part, hipStream_
 
 hipError_t launch_argmax(const float* logits, int V, int ld, int* out, int M, hipStream_t s) {
   argmax_kernel<<<M, 1024, 0, s>>>(logits, V, ld, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_argmax_tiles(const float* pv, const int* pi, int nt, int* out, int M, hipStream_t s) {
+  argmax_tiles_kernel<<<M, 1024, 0, s>>>(pv, pi, nt, out);
   return hipGetLastError();
 }
 

@@ -11,6 +11,8 @@
 #include <chrono>
 #include <cmath>
 #include <cstring>
+#include <map>
+#include <string>
 #include <vector>
 
 #include "host.h"
@@ -44,6 +46,11 @@ struct LayerW {
 
 enum { EV_A, EV_B, EV_C, EV_D, EV_N };
 
+struct GraphEntry {
+  hipGraph_t graph;
+  hipGraphExec_t exec;
+};
+
 }  // namespace
 
 struct ssd_ctx {
@@ -63,8 +70,13 @@ struct ssd_ctx {
   int* hbuf = nullptr;  // pinned host scratch
   hipEvent_t ev[EV_N] = {};
   ssd_stats st;
+  // decode/draft/verify passes captured as HIP graphs, keyed by their launch shape
+  std::map<std::string, GraphEntry> graphs;
+  bool use_graphs = true;
+  bool capturing = false;
   // device views
-  float *x, *logits, *part_o, *part_ml, *cos_t, *sin_t;
+  float *x, *logits, *part_o, *part_ml, *cos_t, *sin_t, *amax_v;
+  int* amax_i;
   void *xn, *q, *att, *act, *kc, *vc, *tap, *feat;
   int *counters, *block, *post, *toks, *dstate, *result, *outlog;
   int *tblock, *tpost, *tstate, *tresult, *toutlog;
@@ -103,7 +115,9 @@ ssd_status layer_forward(ssd_ctx* c, int l, int M, int pos_off, bool feats) {
     a.counters = c->counters; a.state = c->dstate; a.pos_off = pos_off; a.M = M; a.R = c->lay.R;
     a.hq = hq; a.hkv = hkv; a.hd = hd; a.max_ctx = g.max_ctx;
     a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)hd));
-    const int n_part = (c->n + pos_off + M + ATT_PT - 1) / ATT_PT;
+    // a captured pass covers every partition up to max_ctx; workgroups past
+    // the last row's position exit at once
+    const int n_part = c->capturing ? c->lay.n_part : (c->n + pos_off + M + ATT_PT - 1) / ATT_PT;
     HIPCHK(launch_attention(dt, a, n_part, s));
   }
   {
@@ -155,8 +169,15 @@ ssd_status run_pass(ssd_ctx* c, const int* d_tok, int M, int pos_off, const uint
     GemmArgs a{};
     a.X = c->xn; a.ldx = d; a.W0 = c->lm_head; a.M = head_rows; a.N = g.vocab; a.K = d;
     a.y = c->logits; a.ldy = g.vocab;
-    HIPCHK(launch_gemm(dt, EPI_F32, a, s));
-    HIPCHK(launch_argmax(c->logits, g.vocab, g.vocab, d_arg, head_rows, s));
+    if (dt == SSD_BF16) {
+      // the LM head epilogue leaves (max, index) per 16 columns; reduce those
+      a.amax_v = c->amax_v; a.amax_i = c->amax_i;
+      HIPCHK(launch_gemm(dt, EPI_LOGITS, a, s));
+      HIPCHK(launch_argmax_tiles(c->amax_v, c->amax_i, g.vocab / 16, d_arg, head_rows, s));
+    } else {
+      HIPCHK(launch_gemm(dt, EPI_F32, a, s));
+      HIPCHK(launch_argmax(c->logits, g.vocab, g.vocab, d_arg, head_rows, s));
+    }
     c->head_rows = head_rows;
   }
   if (feats && g.n_feat > 0) {
@@ -166,6 +187,50 @@ ssd_status run_pass(ssd_ctx* c, const int* d_tok, int M, int pos_off, const uint
     HIPCHK(launch_gemm(dt, EPI_STORE, a, s));
     c->feat_rows = M;
   }
+  return SSD_OK;
+}
+
+void destroy_graphs(ssd_ctx* c) {
+  for (auto& kv : c->graphs) {
+    (void)hipGraphExecDestroy(kv.second.exec);
+    (void)hipGraphDestroy(kv.second.graph);
+  }
+  c->graphs.clear();
+}
+
+// One decode-loop pass (draft step, verify or plain decode step) with its head
+// on all M rows.  Replays a HIP graph captured on first use: every position is
+// read from device state, so one graph serves every context length.
+ssd_status decode_pass(ssd_ctx* c, const int* tok, int M, int pos_off, const uint8_t* skip, int* arg, bool feats) {
+  if (!c->use_graphs) return run_pass(c, tok, M, pos_off, skip, 0, M, arg, feats);
+  std::string key;
+  key.reserve(64 + c->cfg.n_layers);
+  const intptr_t parts[5] = {M, pos_off, (intptr_t)tok, (intptr_t)arg, feats ? 1 : 0};
+  key.append((const char*)parts, sizeof parts);
+  if (skip) key.append((const char*)skip, c->cfg.n_layers);
+  auto it = c->graphs.find(key);
+  if (it == c->graphs.end()) {
+    GraphEntry ge{};
+    HIPCHK(hipStreamBeginCapture(c->stream, hipStreamCaptureModeThreadLocal));
+    c->capturing = true;
+    const ssd_status st = run_pass(c, tok, M, pos_off, skip, 0, M, arg, feats);
+    c->capturing = false;
+    const hipError_t ee = hipStreamEndCapture(c->stream, &ge.graph);
+    if (st != SSD_OK) {
+      if (ee == hipSuccess) (void)hipGraphDestroy(ge.graph);
+      return st;
+    }
+    HIPCHK(ee);
+    const hipError_t ie = hipGraphInstantiate(&ge.exec, ge.graph, nullptr, nullptr, 0);
+    if (ie != hipSuccess) {
+      (void)hipGraphDestroy(ge.graph);
+      return fail(SSD_E_HIP, "hipGraphInstantiate: %s", hipGetErrorString(ie));
+    }
+    it = c->graphs.emplace(key, ge).first;
+  }
+  HIPCHK(hipGraphLaunch(it->second.exec, c->stream));
+  c->head_rows = M;
+  if (feats && c->cfg.n_feat > 0) c->feat_rows = M;
   return SSD_OK;
 }
 
@@ -299,6 +364,7 @@ ssd_status ssd_load(const ssd_cfg* cfg, const ssd_buf* weights, int32_t n_weight
   c->kc = at(c, lay.kc); c->vc = at(c, lay.vc);
   c->x = (float*)at(c, lay.x); c->xn = at(c, lay.xn); c->q = at(c, lay.q); c->att = at(c, lay.att);
   c->act = at(c, lay.act); c->logits = (float*)at(c, lay.logits);
+  c->amax_v = (float*)at(c, lay.amax_v); c->amax_i = (int*)at(c, lay.amax_i);
   c->part_o = (float*)at(c, lay.part_o); c->part_ml = (float*)at(c, lay.part_ml);
   c->counters = (int*)at(c, lay.counters);
   c->cos_t = (float*)at(c, lay.rope_cos); c->sin_t = (float*)at(c, lay.rope_sin);
@@ -346,6 +412,7 @@ ssd_status ssd_load(const ssd_cfg* cfg, const ssd_buf* weights, int32_t n_weight
 void ssd_free(ssd_ctx* c) {
   if (!c) return;
   (void)hipStreamSynchronize(c->stream);
+  destroy_graphs(c);
   for (int i = 0; i < EV_N; ++i)
     if (c->ev[i]) (void)hipEventDestroy(c->ev[i]);
   if (c->hbuf) (void)hipHostFree(c->hbuf);
@@ -393,7 +460,7 @@ ssd_status ssd_draft(ssd_ctx* c, const uint8_t* skip_mask, int32_t k, int32_t* d
   if (k < 1 || k + 1 > c->cfg.max_block) return fail(SSD_E_ARG, "k=%d outside [1, max_block-1=%d]", k, c->cfg.max_block - 1);
   if (c->n + k + 1 > c->cfg.max_ctx) return fail(SSD_E_CAPACITY, "n=%d + k+1=%d exceeds max_ctx=%d", c->n, k + 1, c->cfg.max_ctx);
   for (int j = 0; j < k; ++j)
-    SSDCHK(run_pass(c, c->block + j, 1, j, skip_mask, 0, 1, c->block + j + 1, false));
+    SSDCHK(decode_pass(c, c->block + j, 1, j, skip_mask, c->block + j + 1, false));
   c->k = k;
   if (drafts) {
     HIPCHK(hipMemcpyAsync(c->hbuf, c->block + 1, k * sizeof(int), hipMemcpyDeviceToHost, c->stream));
@@ -423,7 +490,7 @@ ssd_status ssd_verify(ssd_ctx* c, const int32_t* block, int32_t m, int32_t* post
     c->k = m - 1;
   }
   HIPCHK(hipEventRecord(c->ev[EV_A], c->stream));
-  SSDCHK(run_pass(c, c->block, m, 0, nullptr, 0, m, c->post, true));
+  SSDCHK(decode_pass(c, c->block, m, 0, nullptr, c->post, true));
   HIPCHK(hipEventRecord(c->ev[EV_B], c->stream));
   HIPCHK(hipMemcpyAsync(c->hbuf, c->post, m * sizeof(int), hipMemcpyDeviceToHost, c->stream));
   HIPCHK(hipStreamSynchronize(c->stream));
@@ -475,7 +542,7 @@ ssd_status ssd_generate(ssd_ctx* c, const int32_t* prompt, int32_t n_prompt, int
     c->k = 0;
     HIPCHK(hipEventRecord(c->ev[EV_A], s));
     for (int i = 1; i < n_new; ++i) {
-      SSDCHK(run_pass(c, c->block, 1, 0, nullptr, 0, 1, c->post, false));
+      SSDCHK(decode_pass(c, c->block, 1, 0, nullptr, c->post, false));
       SSDCHK(do_accept(c, false, nullptr, nullptr));
       c->n += 1;
     }
@@ -490,10 +557,10 @@ ssd_status ssd_generate(ssd_ctx* c, const int32_t* prompt, int32_t n_prompt, int
     while (produced < n_new) {
       HIPCHK(hipEventRecord(c->ev[EV_A], s));
       for (int j = 0; j < k; ++j)
-        SSDCHK(run_pass(c, c->block + j, 1, j, skip_mask, 0, 1, c->block + j + 1, false));
+        SSDCHK(decode_pass(c, c->block + j, 1, j, skip_mask, c->block + j + 1, false));
       c->k = k;
       HIPCHK(hipEventRecord(c->ev[EV_B], s));
-      SSDCHK(run_pass(c, c->block, k + 1, 0, nullptr, 0, k + 1, c->post, true));
+      SSDCHK(decode_pass(c, c->block, k + 1, 0, nullptr, c->post, true));
       HIPCHK(hipEventRecord(c->ev[EV_C], s));
       int a = 0, ne = 0;
       HIPCHK(launch_accept(c->block, c->post, k, c->dstate, c->outlog, c->result, s));
@@ -521,6 +588,16 @@ ssd_status ssd_generate(ssd_ctx* c, const int32_t* prompt, int32_t n_prompt, int
   memcpy(out, tmp.data(), n_new * sizeof(int32_t));
   c->state = SSD_ST_READY;
   if (stats) *stats = c->st;
+  return SSD_OK;
+}
+
+ssd_status ssd_set_option(ssd_ctx* c, int32_t option, int32_t value) {
+  clear_error();
+  if (!c) return fail(SSD_E_ARG, "ctx is NULL");
+  if (option != SSD_OPT_GRAPHS) return fail(SSD_E_ARG, "unknown option %d", option);
+  HIPCHK(hipStreamSynchronize(c->stream));
+  destroy_graphs(c);
+  c->use_graphs = value != 0;
   return SSD_OK;
 }
 
@@ -639,8 +716,9 @@ ssd_status ssd_time_op(ssd_ctx* c, int32_t op, int32_t layer, int32_t m, int32_t
       epi = EPI_RESID; break;
     case 4:
       a.X = c->xn; a.ldx = d; a.W0 = c->lm_head; a.M = m; a.N = g.vocab; a.K = d; a.y = c->logits; a.ldy = g.vocab;
+      a.amax_v = c->amax_v; a.amax_i = c->amax_i;
       if (m > g.max_block) return fail(SSD_E_ARG, "lm_head timing needs m <= max_block");
-      epi = EPI_F32; break;
+      epi = dt == SSD_BF16 ? EPI_LOGITS : EPI_F32; break;
     case 5:
       at.q = c->q; at.kc = kc; at.vc = vc; at.out = c->att; at.part_o = c->part_o; at.part_ml = c->part_ml;
       at.counters = c->counters; at.state = c->dstate; at.pos_off = 0; at.M = m; at.R = c->lay.R;

@@ -5,9 +5,9 @@ weights, prompts, the synthetic MoE routing trace and the random parts of the
 geometric-prefix verify blocks.  It contains none of the decoding method's
 arithmetic, and it imports neither the oracle nor the HIP binding.
 
-Weights are drawn N(0, 0.02) per tensor from
-``numpy.random.Generator(PCG64(SeedSequence([seed, tensor_id, chunk])))``
-(norm gains are 1).  bf16 configurations draw float32 and store the
+Weight matrices are uniform with standard deviation 0.02, drawn per tensor
+chunk from ``numpy.random.Generator(PCG64(SeedSequence([seed, tensor_id,
+chunk])))`` (norm gains are 1).  bf16 configurations draw float32 and store the
 round-to-nearest-even bf16 bit pattern (uint16); float32 configurations
 store float32.  Prompts are uniform over the vocabulary.
 """
@@ -89,7 +89,7 @@ def is_moe_layer(cfg: dict, layer: int) -> bool:
 def weight_specs(cfg: dict) -> list[tuple[str, tuple[int, ...], str]]:
     """(name, shape, kind) in the canonical order the C ABI expects.
 
-    kind is "gain" (filled with ones) or "mat" (random N(0, 0.02)).
+    kind is "gain" (filled with ones) or "mat" (random, standard deviation 0.02).
     Matrices are row-major [out_features, in_features].
     """
     d, hd = cfg["d_model"], cfg["head_dim"]
@@ -138,45 +138,55 @@ _CHUNK = 1 << 24  # elements per independently seeded chunk
 def _f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
     """Round float32 to the nearest bf16 (ties to even); returns uint16 bits."""
     u = a.view(np.uint32)
-    rounding = ((u >> 16) & 1) + np.uint32(0x7FFF)
-    return ((u + rounding) >> 16).astype(np.uint16)
+    r = u >> 16
+    r &= np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += u
+    r >>= 16
+    return r.astype(np.uint16)
 
 
-def _draw(seed: int, tid: int, shape, bf16: bool, scale: float) -> np.ndarray:
-    n = int(np.prod(shape))
-    out = np.empty(n, dtype=np.uint16 if bf16 else np.float32)
-    for c0 in range(0, n, _CHUNK):
-        c1 = min(n, c0 + _CHUNK)
-        g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, tid, c0 // _CHUNK])))
-        v = g.standard_normal(c1 - c0, dtype=np.float32)
-        v *= np.float32(0.02 * scale)
-        out[c0:c1] = _f32_to_bf16_bits(v) if bf16 else v
-    return out.reshape(shape)
+_UNIFORM_HALF_WIDTH = 0.02 * 3.0 ** 0.5   # U(-a, a) has standard deviation 0.02
+
+
+def _fill_chunk(flat: np.ndarray, seed: int, tid: int, chunk: int, bf16: bool, scale: float) -> None:
+    c0 = chunk * _CHUNK
+    c1 = min(flat.size, c0 + _CHUNK)
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, tid, chunk])))
+    v = g.random(c1 - c0, dtype=np.float32)
+    v *= np.float32(2.0 * _UNIFORM_HALF_WIDTH * scale)
+    v -= np.float32(_UNIFORM_HALF_WIDTH * scale)
+    flat[c0:c1] = _f32_to_bf16_bits(v) if bf16 else v
 
 
 def make_weights(cfg: dict, seed: int = 0, threads: int | None = None) -> dict[str, np.ndarray]:
     """All weights of ``cfg``: name -> float32 array (f32 configs) or uint16 bf16 bits.
 
-    Layers listed in cfg["out_scale"] have both residual-writing matrices
-    (wo and w_down) scaled by the given factor before storage.
+    Matrices are uniform on (-0.02*sqrt(3), 0.02*sqrt(3)) (standard deviation
+    0.02), drawn in independently seeded chunks of 2^24 elements; norm gains
+    are 1.  Layers listed in cfg["out_scale"] have both residual-writing
+    matrices (wo and w_down) scaled by the given factor.
     """
     bf16 = cfg["dtype"] == "bf16"
-    specs = weight_specs(cfg)
     one = np.uint16(0x3F80) if bf16 else np.float32(1.0)
-
-    def job(item):
-        tid, (name, shape, kind) = item
+    out, jobs = {}, []
+    for tid, (name, shape, kind) in enumerate(weight_specs(cfg)):
         if kind == "gain":
-            return name, np.full(shape, one, dtype=np.uint16 if bf16 else np.float32)
+            out[name] = np.full(shape, one, dtype=np.uint16 if bf16 else np.float32)
+            continue
         scale = 1.0
         if name.endswith(".wo") or name.endswith(".w_down"):
             layer = int(name[1:name.index(".")])
             scale = float(cfg["out_scale"].get(layer, 1.0))
-        return name, _draw(seed, tid, shape, bf16, scale)
-
+        arr = np.empty(shape, dtype=np.uint16 if bf16 else np.float32)
+        out[name] = arr
+        flat = arr.reshape(-1)
+        for chunk in range((flat.size + _CHUNK - 1) // _CHUNK):
+            jobs.append((flat, tid, chunk, scale))
     threads = threads or min(16, os.cpu_count() or 1)
     with ThreadPoolExecutor(threads) as ex:
-        return dict(ex.map(job, enumerate(specs)))
+        list(ex.map(lambda j: _fill_chunk(j[0], seed, j[1], j[2], bf16, j[3]), jobs))
+    return out
 
 
 def make_prompt(cfg: dict, seed: int = 0, length: int | None = None) -> np.ndarray:

@@ -233,3 +233,42 @@ def test_small_bf16_prefill_chunking_invariant(small):
     _, _, last = ora.prefill(prompt)
     assert np.max(np.abs(gl - last)) <= 3e-2
     assert t == int(np.argmax(gl))
+
+
+def test_small_bf16_graph_replays_match_eager(small):
+    """Captured passes replayed many times (with eager prefill work and host
+    synchronisation between replays) give exactly the eager results."""
+    from self_speculative_decoding_amd import skip_mask
+    cfg, w, eng, _ = small
+    prompt, N = synth.make_prompt(cfg), 40
+    mask = skip_mask(cfg["n_layers"], 0.5)
+    try:
+        eng.set_graphs(False)
+        base_e, _ = eng.generate(prompt, N)
+        spec_e, _ = eng.generate(prompt, N, mask, 3)
+        toks_e, rows_e = _stepwise(eng, prompt, 12)
+        eng.set_graphs(True)
+        for rep in range(3):
+            base_g, _ = eng.generate(prompt, N)
+            spec_g, _ = eng.generate(prompt, N, mask, 3)
+            toks_g, rows_g = _stepwise(eng, prompt, 12)
+            assert base_g == base_e and spec_g == spec_e, rep
+            assert toks_g == toks_e and np.array_equal(rows_g, rows_e), rep
+    finally:
+        eng.set_graphs(True)
+
+
+def test_tiny_graph_and_eager_agree(tiny):
+    cfg, w, eng, _ = tiny
+    prompt = synth.make_prompt(cfg)
+    mask = np.zeros(cfg["n_layers"], np.uint8)
+    mask[[1, 2]] = 1
+    try:
+        eng.set_graphs(False)
+        e1, s1 = eng.generate(prompt, 48, mask, 3)
+        eng.set_graphs(True)
+        g1, s2 = eng.generate(prompt, 48, mask, 3)
+        g2, _ = eng.generate(prompt, 48, mask, 3)
+        assert e1 == g1 == g2 and s1["accepted"] == s2["accepted"]
+    finally:
+        eng.set_graphs(True)
