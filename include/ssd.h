@@ -211,8 +211,10 @@ ssd_status ssd_test_accept(ssd_ctx* ctx, const int32_t* d, const int32_t* p, int
  * context's stream with HIP events; *avg_us receives the mean duration.
  * op: 0 = gate/up GEMM (+SwiGLU), 1 = down GEMM, 2 = qkv GEMM (+RoPE/KV),
  *     3 = o GEMM, 4 = lm_head GEMM, 5 = attention, 6 = routed-expert FFN.
- * Uses layer `layer`'s weights; writes only scratch activations and the KV
- * entries past the committed length. */
+ * Launch i uses the weights of the i-th layer (cyclically, starting at
+ * `layer`, among layers of the same kind), so consecutive launches stream
+ * different weights as a real pass does.  Writes only scratch activations and
+ * KV entries past the committed length. */
 ssd_status ssd_time_op(ssd_ctx* ctx, int32_t op, int32_t layer, int32_t m, int32_t iters,
                        float* avg_us);
 

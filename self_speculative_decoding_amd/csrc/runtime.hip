@@ -689,49 +689,58 @@ ssd_status ssd_time_op(ssd_ctx* c, int32_t op, int32_t layer, int32_t m, int32_t
   if (m < 1 || m > c->lay.R) return fail(SSD_E_ARG, "m outside [1, %d]", c->lay.R);
   if (iters < 1) return fail(SSD_E_ARG, "iters < 1");
   if (c->n + m + 1 > g.max_ctx) return fail(SSD_E_CAPACITY, "no room past the committed length");
-  const LayerW& w = c->L[layer];
+  if (op < 0 || op > 5) return fail(SSD_E_ARG, "unknown op %d", op);
+  if (op == 4 && m > g.max_block) return fail(SSD_E_ARG, "lm_head timing needs m <= max_block");
   const int d = g.d_model, hq = g.n_q_heads, hkv = g.n_kv_heads, hd = g.head_dim, dt = g.dtype;
   hipStream_t s = c->stream;
-  void* kc = (char*)c->kc + (size_t)layer * cache_layer_elems(g) * c->esz;
-  void* vc = (char*)c->vc + (size_t)layer * cache_layer_elems(g) * c->esz;
-  GemmArgs a{};
-  AttnArgs at{};
-  int epi = -1;
-  switch (op) {
-    case 0:
-      if (w.moe) return fail(SSD_E_ARG, "layer %d is an MoE layer", layer);
-      a.X = c->xn; a.ldx = d; a.W0 = w.w_gate; a.W1 = w.w_up; a.M = m; a.N = w.ffn; a.K = d; a.out = c->act; a.ldo = w.ffn;
-      epi = EPI_SWIGLU; break;
-    case 1:
-      if (w.moe) return fail(SSD_E_ARG, "layer %d is an MoE layer", layer);
-      a.X = c->act; a.ldx = w.ffn; a.W0 = w.w_down; a.M = m; a.N = d; a.K = w.ffn; a.y = c->x; a.ldy = d;
-      epi = EPI_RESID; break;
-    case 2:
-      a.X = c->xn; a.ldx = d; a.W0 = w.wq; a.W1 = w.wk; a.W2 = w.wv; a.n0 = hq * hd; a.n1 = hkv * hd; a.M = m;
-      a.N = (hq + 2 * hkv) * hd; a.K = d; a.q = c->q; a.kc = kc; a.vc = vc; a.cos_t = c->cos_t; a.sin_t = c->sin_t;
-      a.state = c->dstate; a.pos_off = 0; a.hq = hq; a.hkv = hkv; a.hd = hd; a.max_ctx = g.max_ctx;
-      epi = EPI_QKV; break;
-    case 3:
-      a.X = c->att; a.ldx = hq * hd; a.W0 = w.wo; a.M = m; a.N = d; a.K = hq * hd; a.y = c->x; a.ldy = d;
-      epi = EPI_RESID; break;
-    case 4:
-      a.X = c->xn; a.ldx = d; a.W0 = c->lm_head; a.M = m; a.N = g.vocab; a.K = d; a.y = c->logits; a.ldy = g.vocab;
-      a.amax_v = c->amax_v; a.amax_i = c->amax_i;
-      if (m > g.max_block) return fail(SSD_E_ARG, "lm_head timing needs m <= max_block");
-      epi = dt == SSD_BF16 ? EPI_LOGITS : EPI_F32; break;
-    case 5:
+  // layers of the same kind as `layer`, visited in turn so that consecutive
+  // launches stream different weights (as a real pass does) instead of
+  // re-reading one matrix that the on-die caches could hold
+  std::vector<int> ring;
+  for (int i = 0; i < g.n_layers; ++i) {
+    const int l = (layer + i) % g.n_layers;
+    if (c->L[l].moe == c->L[layer].moe) ring.push_back(l);
+  }
+  if ((op == 0 || op == 1) && c->L[layer].moe) return fail(SSD_E_ARG, "layer %d is an MoE layer", layer);
+  HIPCHK(hipEventRecord(c->ev[EV_A], s));
+  for (int it = 0; it < iters; ++it) {
+    const int l = ring[it % ring.size()];
+    const LayerW& w = c->L[l];
+    void* kc = (char*)c->kc + (size_t)l * cache_layer_elems(g) * c->esz;
+    void* vc = (char*)c->vc + (size_t)l * cache_layer_elems(g) * c->esz;
+    GemmArgs a{};
+    int epi = -1;
+    switch (op) {
+      case 0:
+        a.X = c->xn; a.ldx = d; a.W0 = w.w_gate; a.W1 = w.w_up; a.M = m; a.N = w.ffn; a.K = d; a.out = c->act; a.ldo = w.ffn;
+        epi = EPI_SWIGLU; break;
+      case 1:
+        a.X = c->act; a.ldx = w.ffn; a.W0 = w.w_down; a.M = m; a.N = d; a.K = w.ffn; a.y = c->x; a.ldy = d;
+        epi = EPI_RESID; break;
+      case 2:
+        a.X = c->xn; a.ldx = d; a.W0 = w.wq; a.W1 = w.wk; a.W2 = w.wv; a.n0 = hq * hd; a.n1 = hkv * hd; a.M = m;
+        a.N = (hq + 2 * hkv) * hd; a.K = d; a.q = c->q; a.kc = kc; a.vc = vc; a.cos_t = c->cos_t; a.sin_t = c->sin_t;
+        a.state = c->dstate; a.pos_off = 0; a.hq = hq; a.hkv = hkv; a.hd = hd; a.max_ctx = g.max_ctx;
+        epi = EPI_QKV; break;
+      case 3:
+        a.X = c->att; a.ldx = hq * hd; a.W0 = w.wo; a.M = m; a.N = d; a.K = hq * hd; a.y = c->x; a.ldy = d;
+        epi = EPI_RESID; break;
+      case 4:
+        a.X = c->xn; a.ldx = d; a.W0 = c->lm_head; a.M = m; a.N = g.vocab; a.K = d; a.y = c->logits; a.ldy = g.vocab;
+        a.amax_v = c->amax_v; a.amax_i = c->amax_i;
+        epi = dt == SSD_BF16 ? EPI_LOGITS : EPI_F32; break;
+      default: break;
+    }
+    if (op == 5) {
+      AttnArgs at{};
       at.q = c->q; at.kc = kc; at.vc = vc; at.out = c->att; at.part_o = c->part_o; at.part_ml = c->part_ml;
       at.counters = c->counters; at.state = c->dstate; at.pos_off = 0; at.M = m; at.R = c->lay.R;
       at.hq = hq; at.hkv = hkv; at.hd = hd; at.max_ctx = g.max_ctx;
       at.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)hd));
-      break;
-    default:
-      return fail(SSD_E_ARG, "unknown op %d", op);
-  }
-  HIPCHK(hipEventRecord(c->ev[EV_A], s));
-  for (int i = 0; i < iters; ++i) {
-    if (op == 5) HIPCHK(launch_attention(dt, at, (c->n + m + ATT_PT - 1) / ATT_PT, s));
-    else HIPCHK(launch_gemm(dt, epi, a, s));
+      HIPCHK(launch_attention(dt, at, (c->n + m + ATT_PT - 1) / ATT_PT, s));
+    } else {
+      HIPCHK(launch_gemm(dt, epi, a, s));
+    }
   }
   HIPCHK(hipEventRecord(c->ev[EV_B], s));
   HIPCHK(hipStreamSynchronize(s));
