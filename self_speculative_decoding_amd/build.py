@@ -14,7 +14,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libssd.so")
 BUILD = os.path.join(PKG, "_build")
 
-SOURCES = ["kernels.hip", "runtime.hip", "host.cpp"]
+SOURCES = ["kernels.hip", "moe.hip", "runtime.hip", "host.cpp"]
 # Packed-FP32 instructions are switched off for all device code.
 DEVICE_FLAGS = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-fPIC", "-std=c++17", "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-function"]
@@ -47,7 +47,7 @@ def build(verbose: bool = False) -> str:
     with ThreadPoolExecutor(len(SOURCES)) as ex:
         objs = list(ex.map(compile_one, SOURCES))
     tmp = LIB + ".tmp"
-    cmd = [hipcc, *DEVICE_FLAGS, "-shared", "-fPIC", *objs, "-o", tmp]
+    cmd = [hipcc, *DEVICE_FLAGS, "-shared", "-fPIC", "-Wl,--no-undefined", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}{r.stderr}")

@@ -82,6 +82,8 @@ ssd_status validate(const ssd_cfg* cp) {
     return fail(SSD_E_ARG, "negative count");
   if (c.n_experts > 0) {
     if (c.n_experts > 64) return fail(SSD_E_UNSUPPORTED, "at most 64 routed experts");
+    if (c.dtype != SSD_BF16) return fail(SSD_E_UNSUPPORTED, "MoE layers run in bf16");
+    if (c.n_experts % 16) return fail(SSD_E_UNSUPPORTED, "n_experts must be a multiple of 16");
     if (c.top_k < 1 || c.top_k > c.n_experts || c.top_k > 8) return fail(SSD_E_ARG, "top_k must be in [1, min(8, n_experts)]");
     if (c.expert_ffn < 1) return fail(SSD_E_ARG, "expert_ffn must be positive");
     if (c.n_dense_layers > c.n_layers) return fail(SSD_E_ARG, "n_dense_layers > n_layers");
@@ -169,7 +171,8 @@ bool compute_layout(const ssd_cfg& c, Layout& L) {
     L.m_gates = take((size_t)R * c.top_k * 4);
     L.m_inject = take((size_t)c.n_layers * R * c.top_k * 4);
     L.m_slot_out = take((size_t)R * slots * d * 4);
-    L.m_groups = take((size_t)(c.n_experts * 2 + 2 + R * c.top_k * 2 + 64) * 4);
+    const size_t max_units = (size_t)R * c.top_k + (size_t)((R + 15) / 16) * c.n_shared;
+    L.m_groups = take((16 + max_units * 18) * 4);
     L.m_union = take((size_t)c.n_layers * 4);
   }
   L.total = off;

@@ -6,36 +6,9 @@
 // bitwise-identical logits, which is what makes greedy self-speculation emit
 // exactly the plain greedy sequence on the GPU (MLX layer-skip blog, "Code":
 // the lossless check; mlx-dflash README: bit-for-bit parity with greedy).
-#include "kernels.h"
-
-#include <math.h>
+#include "device.h"
 
 namespace ssd {
-
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(4))) float f32x4;
-
-// ---------------------------------------------------------------------------
-// element helpers (bf16 is carried as uint16 bit patterns)
-// ---------------------------------------------------------------------------
-
-__device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
-__device__ __forceinline__ uint16_t f2bf(float f) {   // nearest, ties to even
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-__device__ __forceinline__ float tof(float v) { return v; }
-__device__ __forceinline__ float tof(uint16_t v) { return bf2f(v); }
-template <typename E> __device__ __forceinline__ E fromf(float v);
-template <> __device__ __forceinline__ float fromf<float>(float v) { return v; }
-template <> __device__ __forceinline__ uint16_t fromf<uint16_t>(float v) { return f2bf(v); }
-
-__device__ __forceinline__ float wave_sum(float v) {   // fixed butterfly, same result in all lanes
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
 
 // ---------------------------------------------------------------------------
 // embedding gather: x[m, :] = E[tok[m], :] as float32 (residual stream)
@@ -161,9 +134,6 @@ __device__ __forceinline__ void epi_v_single(const GemmArgs& a, int m, int vh, i
 // 4*(lane/16) .. +3.
 // ---------------------------------------------------------------------------
 
-constexpr int GEMM_U = 8;
-
-__device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *(const uint4*)p; }
 
 template <int EPI, int NW>
 __device__ __forceinline__ const uint16_t* gemm_row(const GemmArgs& a, int t, int j, int c, int* head_out,
@@ -202,33 +172,7 @@ __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
   f32x4 acc[NW];
 #pragma unroll
   for (int j = 0; j < NW; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const uint4 zero = {0u, 0u, 0u, 0u};
-
-  int s = s0;
-  for (; s + GEMM_U <= s1; s += GEMM_U) {
-    uint4 xa[GEMM_U], wb[NW][GEMM_U];
-#pragma unroll
-    for (int u = 0; u < GEMM_U; ++u) {
-#pragma unroll
-      for (int j = 0; j < NW; ++j) wb[j][u] = ld16(wr[j] + (size_t)(s + u) * 32);
-      xa[u] = av_ok ? ld16(xr + (size_t)(s + u) * 32) : zero;
-    }
-#pragma unroll
-    for (int u = 0; u < GEMM_U; ++u)
-#pragma unroll
-      for (int j = 0; j < NW; ++j)
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa[u]),
-                                                         __builtin_bit_cast(bf16x8, wb[j][u]), acc[j], 0, 0, 0);
-  }
-  for (; s < s1; ++s) {
-    uint4 xa = av_ok ? ld16(xr + (size_t)s * 32) : zero;
-#pragma unroll
-    for (int j = 0; j < NW; ++j) {
-      uint4 wb = ld16(wr[j] + (size_t)s * 32);
-      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa),
-                                                       __builtin_bit_cast(bf16x8, wb), acc[j], 0, 0, 0);
-    }
-  }
+  mfma_stream<NW>(xr, av_ok, wr, s0, s1, acc);
 
   __shared__ f32x4 red[KW - 1][NW][64];
   if (wave > 0) {
@@ -819,6 +763,5 @@ hipError_t launch_copy_tokens(const int* src, int* dst, int n, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_moe(int, const MoeArgs&, hipStream_t) { return hipErrorNotSupported; }
 
 }  // namespace ssd

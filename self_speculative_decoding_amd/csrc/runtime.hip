@@ -90,6 +90,19 @@ inline void* at(ssd_ctx* c, size_t off) { return c->ws + off; }
 
 size_t cache_layer_elems(const ssd_cfg& c) { return (size_t)c.n_kv_heads * c.max_ctx * c.head_dim; }
 
+MoeArgs moe_args(ssd_ctx* c, int l, int M) {
+  const ssd_cfg& g = c->cfg;
+  const LayerW& w = c->L[l];
+  MoeArgs a{};
+  a.X = c->xn; a.M = M; a.d = g.d_model; a.E = g.n_experts; a.top_k = g.top_k; a.fe = g.expert_ffn;
+  a.n_shared = g.n_shared; a.router = w.router; a.eg = w.eg; a.eu = w.eu; a.ed = w.ed;
+  a.sg = w.sg; a.su = w.su; a.sd = w.sd; a.rlogits = c->m_rlogits; a.ids = c->m_ids; a.gates = c->m_gates;
+  a.inject = c->moe_inject ? c->m_inject + (size_t)l * c->lay.R * g.top_k : nullptr;
+  a.act = c->act; a.slot_out = c->m_slot_out; a.resid = c->x; a.groups = c->m_groups;
+  a.union_out = c->m_union + l; a.dedup = g.moe_dedup;
+  return a;
+}
+
 // One decoder layer over M rows at positions state[0] + pos_off + r.
 ssd_status layer_forward(ssd_ctx* c, int l, int M, int pos_off, bool feats) {
   const ssd_cfg& g = c->cfg;
@@ -127,14 +140,7 @@ ssd_status layer_forward(ssd_ctx* c, int l, int M, int pos_off, bool feats) {
   }
   HIPCHK(launch_rmsnorm(dt, c->x, d, w.ffn_norm, c->xn, d, d, g.rms_eps, M, s));
   if (w.moe) {
-    MoeArgs a{};
-    a.X = c->xn; a.M = M; a.d = d; a.E = g.n_experts; a.top_k = g.top_k; a.fe = g.expert_ffn;
-    a.n_shared = g.n_shared; a.router = w.router; a.eg = w.eg; a.eu = w.eu; a.ed = w.ed;
-    a.sg = w.sg; a.su = w.su; a.sd = w.sd; a.rlogits = c->m_rlogits; a.ids = c->m_ids; a.gates = c->m_gates;
-    a.inject = c->moe_inject ? c->m_inject + (size_t)l * c->lay.R * g.top_k : nullptr;
-    a.act = c->act; a.slot_out = c->m_slot_out; a.resid = c->x; a.groups = c->m_groups;
-    a.union_out = c->m_union + l; a.dedup = g.moe_dedup;
-    HIPCHK(launch_moe(dt, a, s));
+    const MoeArgs a = moe_args(c, l, M);    HIPCHK(launch_moe(dt, a, s));
   } else {
     GemmArgs a{};
     a.X = c->xn; a.ldx = d; a.W0 = w.w_gate; a.W1 = w.w_up; a.M = M; a.N = w.ffn; a.K = d;
@@ -159,6 +165,8 @@ ssd_status run_pass(ssd_ctx* c, const int* d_tok, int M, int pos_off, const uint
   const ssd_cfg& g = c->cfg;
   const int d = g.d_model, dt = g.dtype;
   hipStream_t s = c->stream;
+  if (c->moe_inject && M > c->moe_inject)
+    return fail(SSD_E_ARG, "pass of %d rows but routing was injected for %d", M, c->moe_inject);
   HIPCHK(launch_embed(dt, d_tok, c->embed, c->x, d, M, s));
   for (int l = 0; l < g.n_layers; ++l) {
     if (skip && skip[l]) continue;
@@ -689,7 +697,9 @@ ssd_status ssd_time_op(ssd_ctx* c, int32_t op, int32_t layer, int32_t m, int32_t
   if (m < 1 || m > c->lay.R) return fail(SSD_E_ARG, "m outside [1, %d]", c->lay.R);
   if (iters < 1) return fail(SSD_E_ARG, "iters < 1");
   if (c->n + m + 1 > g.max_ctx) return fail(SSD_E_CAPACITY, "no room past the committed length");
-  if (op < 0 || op > 5) return fail(SSD_E_ARG, "unknown op %d", op);
+  if (op < 0 || op > 6) return fail(SSD_E_ARG, "unknown op %d", op);
+  if (op == 6 && !c->L[layer].moe) return fail(SSD_E_ARG, "layer %d is not an MoE layer", layer);
+  if (op == 6 && c->moe_inject && m > c->moe_inject) return fail(SSD_E_ARG, "m exceeds the injected routing rows");
   if (op == 4 && m > g.max_block) return fail(SSD_E_ARG, "lm_head timing needs m <= max_block");
   const int d = g.d_model, hq = g.n_q_heads, hkv = g.n_kv_heads, hd = g.head_dim, dt = g.dtype;
   hipStream_t s = c->stream;
@@ -731,7 +741,9 @@ ssd_status ssd_time_op(ssd_ctx* c, int32_t op, int32_t layer, int32_t m, int32_t
         epi = dt == SSD_BF16 ? EPI_LOGITS : EPI_F32; break;
       default: break;
     }
-    if (op == 5) {
+    if (op == 6) {
+      HIPCHK(launch_moe(dt, moe_args(c, l, m), s));
+    } else if (op == 5) {
       AttnArgs at{};
       at.q = c->q; at.kc = kc; at.vc = vc; at.out = c->att; at.part_o = c->part_o; at.part_ml = c->part_ml;
       at.counters = c->counters; at.state = c->dstate; at.pos_off = 0; at.M = m; at.R = c->lay.R;

@@ -272,3 +272,61 @@ def test_tiny_graph_and_eager_agree(tiny):
         assert e1 == g1 == g2 and s1["accepted"] == s2["accepted"]
     finally:
         eng.set_graphs(True)
+
+
+# ---------------------------------------------------------------------------
+# feature tap + fc, and geometric-prefix verify blocks
+# ---------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def feat():
+    cfg = synth.config("qwen3-8b", n_layers=4, d_model=512, n_q_heads=8, n_kv_heads=2,
+                       ffn_dim=1024, vocab=2048, max_ctx=400, prompt_len=200, cid=51,
+                       feat_layers=(1, 3))
+    w = synth.make_weights(cfg, seed=4)
+    print("[feat] building engine", flush=True)
+    eng = engine(cfg, w, max_block=17, prefill_chunk=128)
+    yield cfg, w, eng, Model(cfg, w)
+    eng.close()
+
+
+def test_feature_tap_matches_oracle(feat):
+    from _common import bf16_bits_to_f32
+    from oracle.model import Cache
+    cfg, w, eng, ora = feat
+    prompt = synth.make_prompt(cfg)
+    eng.reset()
+    t = eng.prefill(prompt)
+    block = [t] + list(synth.make_tokens(cfg["vocab"], 15, seed=4, stream=9))
+    eng.verify(block)
+    got = bf16_bits_to_f32(eng.read_features(16))
+    cache = Cache(cfg)
+    ora.forward(prompt, 0, cache)
+    lg = ora.forward(block, len(prompt), cache)
+    ref = ora.features
+    err = np.max(np.abs(got - ref))
+    print(f"[feat] max |dfeature| = {err:.3e} (scale {np.max(np.abs(ref)):.2f})")
+    assert err <= 3e-2 * max(1.0, float(np.max(np.abs(ref))))
+    assert np.max(np.abs(eng.read_logits(16) - lg)) <= 3e-2
+    eng.accept()
+
+
+def test_geometric_blocks_accept_exactly_the_correct_prefix(feat):
+    cfg, w, eng, _ = feat
+    prompt = synth.make_prompt(cfg)
+    true, _ = eng.generate(prompt, 120)          # the target's own greedy continuation
+    eng.reset()
+    t = eng.prefill(prompt)
+    assert t == true[0]
+    pos = 0
+    for s in range(12):
+        rest = np.array(true[pos + 1:pos + 16], dtype=np.int32)
+        if len(rest) < 15:
+            break
+        d, m = synth.make_geometric_block(rest, cfg["vocab"], 0.7, 16, seed=4, stream=s)
+        post = eng.verify([true[pos]] + list(d))
+        a, em = eng.accept()
+        assert a == m, (s, a, m)
+        assert em == list(true[pos + 1:pos + a + 2])
+        pos += a + 1
+        assert eng.context_length == len(prompt) + pos
