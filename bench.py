@@ -98,18 +98,133 @@ def cpu_baseline(cfg, weights, prompt, budget_s: float) -> dict:
                       f"(context <= {8 + steps}); weight conversion and prefill excluded"}
 
 
+def bench_verify_blocks(args) -> int:
+    """Qwen3-8B-shaped target verifying 16-token blocks at context 2048 with the
+    five-layer feature tap + fc on; drafts carry a geometric(p) correct prefix.
+    Reports the verify pass time, its HBM bandwidth and tokens per verify."""
+    import numpy as np
+    import synth
+    from self_speculative_decoding_amd import Engine, make_cfg
+    cfg = synth.config("qwen3-8b")
+    B, P = cfg["block"], cfg["prompt_len"]
+    log("qwen3-8b: generating weights")
+    w = synth.make_weights(cfg)
+    prompt = synth.make_prompt(cfg)
+    eng = Engine(make_cfg(cfg, max_block=B, prefill_chunk=256), [w[n] for n, _, _ in synth.weight_specs(cfg)])
+    n_cont = 400
+    true, _ = eng.generate(prompt, n_cont)
+    log("greedy continuation ready")
+    fc_bytes = cfg["d_model"] * len(cfg["feat_layers"]) * cfg["d_model"] * 2
+    res = []
+    for p in cfg["geo_p"]:
+        eng.reset()
+        eng.prefill(prompt)
+        pos, a_list, ms = 0, [], []
+        s = 0
+        while pos + B < n_cont and s < args.blocks:
+            d, m = synth.make_geometric_block(np.array(true[pos + 1:pos + B], np.int32), cfg["vocab"], p, B,
+                                              seed=0, stream=1000 * int(p * 10) + s)
+            st0 = eng.stats()
+            eng.verify([true[pos]] + list(d))
+            st1 = eng.stats()
+            a, _ = eng.accept()
+            if a != m:
+                raise RuntimeError(f"accepted {a} but the block had a correct prefix of {m}")
+            ms.append(st1["t_verify_ms"] - st0["t_verify_ms"])
+            a_list.append(a)
+            pos += a + 1
+            s += 1
+        ms = ms[1:] if len(ms) > 1 else ms        # first replay captures the graph
+        v_ms = float(np.mean(ms))
+        vb = pass_bytes(cfg, B, P + pos / 2) + fc_bytes
+        res.append({"p": p, "blocks": s, "tokens_per_verify": round(float(np.mean(a_list)) + 1, 3),
+                    "expected_tokens_per_verify": round((1 - p ** B) / (1 - p), 3),
+                    "verify_ms": round(v_ms, 4), "gbs": round(vb / v_ms / 1e6, 1),
+                    "frac": round(vb / v_ms / 1e6 / PEAK_HBM_GBS, 4),
+                    "tok_s": round((float(np.mean(a_list)) + 1) / v_ms * 1e3, 1)})
+        log(f"p={p}: {res[-1]}")
+    eng.close()
+    line = {"metric": "verify-pass HBM GB/s (% of peak), 16-token blocks, Qwen3-8B-shaped bf16 + feature tap",
+            "value": res[-1]["gbs"], "unit": "GB/s", "n_gpus": 1, "higher_is_better": True, "dtype": "bf16",
+            "data": "synthetic", "vs_baseline": None,
+            "config": {"workload": f"qwen3-8b-shaped bf16 random-init target, {P}-token prompt, verify blocks of {B} "
+                                   f"with geometric correct prefix, feature tap layers {list(cfg['feat_layers'])} + fc"},
+            "by_p": res}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def bench_moe(args) -> int:
+    """DeepSeek-V2-Lite-shaped MoE verify passes of n = 1..8 tokens with the
+    synthetic routing trace: per-slot vs deduplicated expert reads, whole pass
+    and one layer's expert operation alone (fitted bandwidths, u(n), r(n))."""
+    import numpy as np
+    import synth
+    from self_speculative_decoding_amd import Engine, make_cfg
+    cfg = synth.config("dsv2-lite")
+    L, E, K = cfg["n_layers"], cfg["n_experts"], cfg["top_k"]
+    eb = cfg["expert_ffn"] * cfg["d_model"] * 3 * 2             # one expert's gate/up/down bytes
+    log("dsv2-lite: generating weights")
+    w = synth.make_weights(cfg)
+    prompt = synth.make_prompt(cfg)
+    eng = Engine(make_cfg(cfg, max_block=9, prefill_chunk=256), [w[n] for n, _, _ in synth.weight_specs(cfg)])
+    rows = []
+    for n in cfg["pass_sizes"]:
+        trace = synth.make_routing_trace(L, n, E, K, seed=0, stream=n)
+        ubar = float(np.mean([len(set(trace[l].reshape(-1).tolist())) for l in range(cfg["n_dense_layers"], L)])) / (K * n)
+        r = {"n": n, "u_bar": round(ubar, 4)}
+        for mode, dedup in (("per_slot", 0), ("dedup", 1)):
+            eng.set_moe_dedup(dedup)
+            eng.set_routing(None)
+            eng.reset()
+            eng.prefill(prompt)
+            eng.set_routing(trace)
+            block = list(synth.make_tokens(cfg["vocab"], n, seed=0, stream=100 + n))
+            times = []
+            for it in range(args.passes):
+                st0 = eng.stats()
+                eng.verify(block)
+                st1 = eng.stats()
+                eng.accept()
+                times.append(st1["t_verify_ms"] - st0["t_verify_ms"])
+            r[f"{mode}_pass_ms"] = round(float(np.mean(times[1:])), 4)
+            us = eng.time_op("moe", cfg["n_dense_layers"], n, 52)
+            unions = eng.read_union()
+            req = (K * n if dedup == 0 else ubar * K * n) * eb + cfg["n_shared"] * eb
+            r[f"{mode}_layer_us"] = round(us, 2)
+            r[f"{mode}_layer_gbs"] = round(req / us / 1e3, 1)
+        r["r"] = round(r["dedup_layer_gbs"] / r["per_slot_layer_gbs"], 4)
+        rows.append(r)
+        log(f"n={n}: {r}")
+    eng.close()
+    pred = next((r["n"] for r in rows if r["u_bar"] < r["r"]), None)
+    meas = next((r["n"] for r in rows if r["dedup_pass_ms"] < r["per_slot_pass_ms"]), None)
+    line = {"metric": "MoE verify pass ms, per-slot vs deduplicated expert reads, DeepSeek-V2-Lite-shaped bf16",
+            "value": rows[-1]["dedup_pass_ms"], "unit": "ms", "n_gpus": 1, "higher_is_better": False,
+            "dtype": "bf16", "data": "synthetic", "vs_baseline": None,
+            "config": {"workload": "dsv2-lite-shaped bf16 MoE (27 layers, 64 experts top-6 + 2 shared, expert "
+                                   "FFN 1408), verify passes of n=1..8 tokens, synthetic routing trace "
+                                   "(reuse of the previous token's expert with probability 0.5)"},
+            "predicted_crossover_n": pred, "measured_crossover_n": meas, "by_n": rows}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--workload", default="llama-8b", choices=["llama-8b", "qwen3-4b", "tiny"])
+    ap.add_argument("--workload", default="llama-8b",
+                    choices=["llama-8b", "qwen3-4b", "tiny", "qwen3-8b", "dsv2-lite"])
     ap.add_argument("--skip", type=float, default=None, help="draft skip fraction (default: workload's)")
     ap.add_argument("--k", type=int, default=None, help="draft length (default: workload's)")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--n-new", type=int, default=None, help="tokens per decode (default: workload's)")
+    ap.add_argument("--blocks", type=int, default=40, help="verify blocks per p (qwen3-8b)")
+    ap.add_argument("--passes", type=int, default=12, help="verify passes per n and mode (dsv2-lite)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -123,6 +238,10 @@ def main() -> int:
     import synth
     from self_speculative_decoding_amd import Engine, make_cfg, skip_mask
 
+    if args.workload == "qwen3-8b":
+        return bench_verify_blocks(args)
+    if args.workload == "dsv2-lite":
+        return bench_moe(args)
     cfg = synth.config(args.workload)
     frac = args.skip if args.skip is not None else cfg.get("skip_frac", 0.5)
     k = args.k if args.k is not None else cfg["k"]

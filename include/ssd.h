@@ -185,8 +185,13 @@ ssd_status ssd_generate(ssd_ctx* ctx, const int32_t* prompt, int32_t n_prompt, i
 /* Options: SSD_OPT_GRAPHS (default 1) replays each decode-loop pass (draft
  * step, verify, plain decode step) as a HIP graph captured on first use;
  * 0 launches every kernel directly.  Both give bitwise-identical results.
- * hip_stream must not be the null stream while graphs are on. */
-enum { SSD_OPT_GRAPHS = 0 };
+ * hip_stream must not be the null stream while graphs are on.
+ * SSD_OPT_MOE_DEDUP switches an MoE model between per-slot (0) and
+ * deduplicated (1) expert reads (speculative decoding for MoE models,
+ * abstract); outputs are bitwise identical.
+ * SSD_OPT_TRACE (default 0): decode-loop passes also record the float32
+ * residual after every layer (ssd_read_trace); a test hook. */
+enum { SSD_OPT_GRAPHS = 0, SSD_OPT_MOE_DEDUP = 1, SSD_OPT_TRACE = 2 };
 ssd_status ssd_set_option(ssd_ctx* ctx, int32_t option, int32_t value);
 
 /* Statistics accumulated since load/reset (per-phase times from HIP events). */
@@ -197,6 +202,12 @@ ssd_status ssd_get_stats(const ssd_ctx* ctx, ssd_stats* stats);
 /* Logits (float32) of the last pass: host [rows * V], rows <= rows of that pass
  * (prefill keeps only its last row). */
 ssd_status ssd_read_logits(ssd_ctx* ctx, float* host, int32_t rows);
+/* Residual after every layer of the last decode-loop pass (SSD_OPT_TRACE on):
+ * host [n_layers * rows * d] float32, layer-major. */
+ssd_status ssd_read_trace(ssd_ctx* ctx, float* host, int32_t rows);
+/* KV cache entries of one layer, positions [pos0, pos0+n): host k and v,
+ * each [n_kv_heads * n * head_dim] in the cfg dtype (bf16 bits or float32). */
+ssd_status ssd_read_kv(ssd_ctx* ctx, int32_t layer, int32_t pos0, int32_t n, void* k_host, void* v_host);
 /* Feature-tap output of the last verify pass: host [rows * d] bf16 bits. */
 ssd_status ssd_read_features(ssd_ctx* ctx, uint16_t* host, int32_t rows);
 /* Injects expert ids for the next passes: host [n_layers][n][top_k] (entries for

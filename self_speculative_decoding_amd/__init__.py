@@ -26,7 +26,8 @@ EXPORTS = ["ssd_validate_cfg", "ssd_n_weights", "ssd_weight_numel", "ssd_workspa
            "ssd_load", "ssd_free", "ssd_reset", "ssd_state", "ssd_context_length",
            "ssd_prefill", "ssd_draft", "ssd_verify", "ssd_accept_rollback", "ssd_generate",
            "ssd_get_stats", "ssd_read_logits", "ssd_read_features", "ssd_set_routing",
-           "ssd_read_union", "ssd_test_accept", "ssd_time_op", "ssd_set_option"]
+           "ssd_read_union", "ssd_test_accept", "ssd_time_op", "ssd_set_option", "ssd_read_trace",
+           "ssd_read_kv"]
 
 
 class Cfg(ctypes.Structure):
@@ -95,6 +96,8 @@ def _load():
         "ssd_test_accept": (I32, [VP, VP, VP, I32, P(I32)]),
         "ssd_time_op": (I32, [VP, I32, I32, I32, I32, P(ctypes.c_float)]),
         "ssd_set_option": (I32, [VP, I32, I32]),
+        "ssd_read_trace": (I32, [VP, VP, I32]),
+        "ssd_read_kv": (I32, [VP, I32, I32, I32, VP, VP]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -226,6 +229,25 @@ class Engine:
 
     def set_graphs(self, on: bool):
         _check(lib.ssd_set_option(self.ctx, 0, 1 if on else 0))
+
+    def set_moe_dedup(self, on: bool):
+        _check(lib.ssd_set_option(self.ctx, 1, 1 if on else 0))
+
+    def set_trace(self, on: bool):
+        _check(lib.ssd_set_option(self.ctx, 2, 1 if on else 0))
+
+    def read_trace(self, rows: int) -> np.ndarray:
+        out = np.zeros((self.L, rows, self.d), dtype=np.float32)
+        _check(lib.ssd_read_trace(self.ctx, _ptr(out), rows))
+        return out
+
+    def read_kv(self, layer: int, pos0: int, n: int):
+        """K and V of one layer, [n_kv_heads, n, head_dim], cfg dtype."""
+        dt = np.uint16 if self.cfg.dtype == 1 else np.float32
+        k = np.zeros((self.cfg.n_kv_heads, n, self.cfg.head_dim), dtype=dt)
+        v = np.zeros_like(k)
+        _check(lib.ssd_read_kv(self.ctx, layer, pos0, n, _ptr(k), _ptr(v)))
+        return k, v
 
     # -- the decode step --------------------------------------------------------------
     def prefill(self, tokens) -> int:

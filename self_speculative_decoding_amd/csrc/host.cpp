@@ -143,6 +143,7 @@ bool compute_layout(const ssd_cfg& c, Layout& L) {
   L.act = take((size_t)R * fact * esz);
   L.logits = take((size_t)c.max_block * c.vocab * 4);
   L.amax_v = take((size_t)c.max_block * (c.vocab / 16 + 1) * 4);
+  L.trace = take((size_t)c.n_layers * c.max_block * d * 4);
   L.amax_i = take((size_t)c.max_block * (c.vocab / 16 + 1) * 4);
   L.part_o = take((size_t)L.n_part * R * hq * hd * 4);
   L.part_ml = take((size_t)L.n_part * R * hq * 2 * 4);

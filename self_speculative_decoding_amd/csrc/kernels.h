@@ -75,6 +75,7 @@ hipError_t launch_accept(int* block, const int* post, int k, int* state, int* ou
                          hipStream_t s);
 hipError_t launch_set_state(int* state, int idx, int value, hipStream_t s);
 hipError_t launch_copy_tokens(const int* src, int* dst, int n, hipStream_t s);
+hipError_t launch_copy_f32(const float* src, float* dst, int n, hipStream_t s);
 
 // MoE (routed experts + shared experts)
 struct MoeArgs {

@@ -409,8 +409,8 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 // the row tile form up to four 16-row MFMA tiles (one per wave).  S = Q.K^T
 // takes Q fragments from the q buffer and K fragments straight from the
 // cache rows; the row max and sum of each query are a fixed butterfly over the
-// 16 lanes holding its keys; P is rounded to bf16 (the row sum uses the
-// rounded values) and O = P.V reads P and a transposed V tile from LDS.
+// 16 lanes holding its keys; P is split into bf16 hi + lo parts and
+// O = P_hi.V + P_lo.V reads them and a transposed V tile from LDS.
 // Every output element is produced by the same instruction sequence for any
 // number of rows in the pass.
 template <int G>
@@ -418,6 +418,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
   constexpr int HD = 128, PT = ATT_PT, PS = PT + 8;
   __shared__ __attribute__((aligned(16))) uint16_t Vt[HD][PS];
   __shared__ __attribute__((aligned(16))) uint16_t Ps[4][16][PS];
+  __shared__ __attribute__((aligned(16))) uint16_t Pl[4][16][PS];
   const int p = blockIdx.x, kvh = blockIdx.y, mt = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 15, kg = lane >> 4;
@@ -485,9 +486,12 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
       const bool valid = row_ok[i] && key0 + kt * 16 + c <= pos_i[i];
-      const uint16_t pb = valid ? f2bf(exp2f(s[kt][i] * a.scale_log2 - m)) : (uint16_t)0;
-      sum += bf2f(pb);
-      Ps[wave][4 * kg + i][kt * 16 + c] = pb;
+      const float pv = valid ? exp2f(s[kt][i] * a.scale_log2 - m) : 0.f;
+      sum += pv;
+      // P = hi + lo, both bf16: the P.V products keep ~16 significant bits
+      const uint16_t hi = f2bf(pv);
+      Ps[wave][4 * kg + i][kt * 16 + c] = hi;
+      Pl[wave][4 * kg + i][kt * 16 + c] = f2bf(pv - bf2f(hi));
     }
 #pragma unroll
     for (int o = 1; o < 16; o <<= 1) sum += __shfl_xor(sum, o);
@@ -502,10 +506,13 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
     const uint4 pa = *(const uint4*)&Ps[wave][c][ks * 32 + kg * 8];
+    const uint4 pl = *(const uint4*)&Pl[wave][c][ks * 32 + kg * 8];
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
       const uint4 vf = *(const uint4*)&Vt[dt * 16 + c][ks * 32 + kg * 8];
       o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pa),
+                                                      __builtin_bit_cast(bf16x8, vf), o[dt], 0, 0, 0);
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pl),
                                                       __builtin_bit_cast(bf16x8, vf), o[dt], 0, 0, 0);
     }
   }
@@ -652,6 +659,11 @@ __global__ __launch_bounds__(64) void accept_kernel(int* block, const int* post,
 
 __global__ void set_state_kernel(int* state, int idx, int value) { state[idx] = value; }
 
+__global__ __launch_bounds__(256) void copy_f32_kernel(const float* __restrict__ src, float* __restrict__ dst, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) dst[i] = src[i];
+}
+
 __global__ void copy_tokens_kernel(const int* src, int* dst, int n) {
   for (int i = threadIdx.x; i < n; i += blockDim.x) dst[i] = src[i];
 }
@@ -755,6 +767,11 @@ hipError_t launch_accept(int* block, const int* post, int k, int* state, int* ou
 
 hipError_t launch_set_state(int* state, int idx, int value, hipStream_t s) {
   set_state_kernel<<<1, 1, 0, s>>>(state, idx, value);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_f32(const float* src, float* dst, int n, hipStream_t s) {
+  copy_f32_kernel<<<(n + 255) / 256, 256, 0, s>>>(src, dst, n);
   return hipGetLastError();
 }
 

@@ -74,6 +74,8 @@ struct ssd_ctx {
   std::map<std::string, GraphEntry> graphs;
   bool use_graphs = true;
   bool capturing = false;
+  bool trace_on = false;   // record the residual after every layer of decode-loop passes
+  float* trace = nullptr;
   // device views
   float *x, *logits, *part_o, *part_ml, *cos_t, *sin_t, *amax_v;
   int* amax_i;
@@ -154,6 +156,8 @@ ssd_status layer_forward(ssd_ctx* c, int l, int M, int pos_off, bool feats) {
     }
     HIPCHK(launch_gemm(dt, EPI_RESID, b, s));
   }
+  if (c->trace_on && M <= g.max_block)
+    HIPCHK(launch_copy_f32(c->x, c->trace + (size_t)l * g.max_block * d, M * d, s));
   return SSD_OK;
 }
 
@@ -373,6 +377,7 @@ ssd_status ssd_load(const ssd_cfg* cfg, const ssd_buf* weights, int32_t n_weight
   c->x = (float*)at(c, lay.x); c->xn = at(c, lay.xn); c->q = at(c, lay.q); c->att = at(c, lay.att);
   c->act = at(c, lay.act); c->logits = (float*)at(c, lay.logits);
   c->amax_v = (float*)at(c, lay.amax_v); c->amax_i = (int*)at(c, lay.amax_i);
+  c->trace = (float*)at(c, lay.trace);
   c->part_o = (float*)at(c, lay.part_o); c->part_ml = (float*)at(c, lay.part_ml);
   c->counters = (int*)at(c, lay.counters);
   c->cos_t = (float*)at(c, lay.rope_cos); c->sin_t = (float*)at(c, lay.rope_sin);
@@ -602,10 +607,14 @@ ssd_status ssd_generate(ssd_ctx* c, const int32_t* prompt, int32_t n_prompt, int
 ssd_status ssd_set_option(ssd_ctx* c, int32_t option, int32_t value) {
   clear_error();
   if (!c) return fail(SSD_E_ARG, "ctx is NULL");
-  if (option != SSD_OPT_GRAPHS) return fail(SSD_E_ARG, "unknown option %d", option);
+  if (option != SSD_OPT_GRAPHS && option != SSD_OPT_MOE_DEDUP && option != SSD_OPT_TRACE)
+    return fail(SSD_E_ARG, "unknown option %d", option);
+  if (option == SSD_OPT_MOE_DEDUP && c->cfg.n_experts == 0) return fail(SSD_E_UNSUPPORTED, "not an MoE model");
   HIPCHK(hipStreamSynchronize(c->stream));
   destroy_graphs(c);
-  c->use_graphs = value != 0;
+  if (option == SSD_OPT_GRAPHS) c->use_graphs = value != 0;
+  else if (option == SSD_OPT_TRACE) c->trace_on = value != 0;
+  else c->cfg.moe_dedup = value != 0;
   return SSD_OK;
 }
 
@@ -620,6 +629,36 @@ ssd_status ssd_read_logits(ssd_ctx* c, float* host, int32_t rows) {
   if (!c || !host) return fail(SSD_E_ARG, "NULL argument");
   if (rows < 1 || rows > c->head_rows) return fail(SSD_E_ARG, "rows=%d but the last pass has %d", rows, c->head_rows);
   HIPCHK(hipMemcpyAsync(host, c->logits, (size_t)rows * c->cfg.vocab * 4, hipMemcpyDeviceToHost, c->stream));
+  HIPCHK(hipStreamSynchronize(c->stream));
+  return SSD_OK;
+}
+
+ssd_status ssd_read_trace(ssd_ctx* c, float* host, int32_t rows) {
+  clear_error();
+  if (!c || !host) return fail(SSD_E_ARG, "NULL argument");
+  if (!c->trace_on) return fail(SSD_E_STATE, "residual trace is off (SSD_OPT_TRACE)");
+  if (rows < 1 || rows > c->head_rows || rows > c->cfg.max_block)
+    return fail(SSD_E_ARG, "rows=%d but the last pass has %d", rows, c->head_rows);
+  const size_t d = c->cfg.d_model;
+  for (int l = 0; l < c->cfg.n_layers; ++l)
+    HIPCHK(hipMemcpyAsync(host + (size_t)l * rows * d, c->trace + (size_t)l * c->cfg.max_block * d,
+                          rows * d * 4, hipMemcpyDeviceToHost, c->stream));
+  HIPCHK(hipStreamSynchronize(c->stream));
+  return SSD_OK;
+}
+
+ssd_status ssd_read_kv(ssd_ctx* c, int32_t layer, int32_t pos0, int32_t n, void* k_host, void* v_host) {
+  clear_error();
+  if (!c || !k_host || !v_host) return fail(SSD_E_ARG, "NULL argument");
+  const ssd_cfg& g = c->cfg;
+  if (layer < 0 || layer >= g.n_layers || pos0 < 0 || n < 1 || pos0 + n > g.max_ctx)
+    return fail(SSD_E_ARG, "layer/positions out of range");
+  const size_t hd = g.head_dim, row = hd * c->esz;
+  for (int h = 0; h < g.n_kv_heads; ++h) {
+    const size_t off = (((size_t)layer * g.n_kv_heads + h) * g.max_ctx + pos0) * row;
+    HIPCHK(hipMemcpyAsync((char*)k_host + (size_t)h * n * row, (char*)c->kc + off, n * row, hipMemcpyDeviceToHost, c->stream));
+    HIPCHK(hipMemcpyAsync((char*)v_host + (size_t)h * n * row, (char*)c->vc + off, n * row, hipMemcpyDeviceToHost, c->stream));
+  }
   HIPCHK(hipStreamSynchronize(c->stream));
   return SSD_OK;
 }
