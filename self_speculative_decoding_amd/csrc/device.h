@@ -71,4 +71,44 @@ __device__ __forceinline__ void mfma_stream(const uint16_t* xr, bool xok, const 
   }
 }
 
+// As mfma_stream for MT 16-row tiles sharing every weight fragment.
+template <int NW, int MT>
+__device__ __forceinline__ void mfma_stream_mt(const uint16_t* const* xr, const bool* xok, const uint16_t* const* wr,
+                                               int s0, int s1, f32x4 (*acc)[NW]) {
+  constexpr int U = 4;
+  const uint4 zero = {0u, 0u, 0u, 0u};
+  int s = s0;
+  for (; s + U <= s1; s += U) {
+    uint4 xa[MT][U], wb[NW][U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int j = 0; j < NW; ++j) wb[j][u] = ld16(wr[j] + (size_t)(s + u) * 32);
+#pragma unroll
+      for (int r = 0; r < MT; ++r) xa[r][u] = xok[r] ? ld16(xr[r] + (size_t)(s + u) * 32) : zero;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int r = 0; r < MT; ++r)
+#pragma unroll
+        for (int j = 0; j < NW; ++j)
+          acc[r][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa[r][u]),
+                                                              __builtin_bit_cast(bf16x8, wb[j][u]), acc[r][j], 0, 0, 0);
+  }
+  for (; s < s1; ++s) {
+    uint4 wb[NW];
+#pragma unroll
+    for (int j = 0; j < NW; ++j) wb[j] = ld16(wr[j] + (size_t)s * 32);
+#pragma unroll
+    for (int r = 0; r < MT; ++r) {
+      const uint4 xa = xok[r] ? ld16(xr[r] + (size_t)s * 32) : zero;
+#pragma unroll
+      for (int j = 0; j < NW; ++j)
+        acc[r][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa),
+                                                            __builtin_bit_cast(bf16x8, wb[j]), acc[r][j], 0, 0, 0);
+    }
+  }
+}
+
 }  // namespace ssd

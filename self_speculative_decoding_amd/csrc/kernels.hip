@@ -154,14 +154,19 @@ __device__ __forceinline__ const uint16_t* gemm_row(const GemmArgs& a, int t, in
   return W + (size_t)(t * 16 + c) * a.K;
 }
 
-template <int EPI, int NW, int KW>
+template <int EPI, int NW, int KW, int MT>
 __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane & 15, kg = lane >> 4;
-  const int t = blockIdx.x, mt = blockIdx.y;
-  const int am = mt * 16 + c;
-  const bool av_ok = am < a.M;
-  const uint16_t* xr = (const uint16_t*)a.X + (size_t)(av_ok ? am : 0) * a.ldx + kg * 8;
+  const int t = blockIdx.x;
+  const uint16_t* xr[MT];
+  bool av_ok[MT];
+#pragma unroll
+  for (int r = 0; r < MT; ++r) {
+    const int am = (blockIdx.y * MT + r) * 16 + c;
+    av_ok[r] = am < a.M;
+    xr[r] = (const uint16_t*)a.X + (size_t)(av_ok[r] ? am : 0) * a.ldx + kg * 8;
+  }
   const uint16_t* wr[NW];
   int head = 0, dim = 0;
 #pragma unroll
@@ -169,61 +174,72 @@ __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
 
   const int S = a.K >> 5;
   const int s0 = (S * wave) / KW, s1 = (S * (wave + 1)) / KW;
-  f32x4 acc[NW];
+  f32x4 acc[MT][NW];
 #pragma unroll
-  for (int j = 0; j < NW; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  mfma_stream<NW>(xr, av_ok, wr, s0, s1, acc);
+  for (int r = 0; r < MT; ++r)
+#pragma unroll
+    for (int j = 0; j < NW; ++j) acc[r][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (MT == 1) mfma_stream<NW>(xr[0], av_ok[0], wr, s0, s1, acc[0]);
+  else mfma_stream_mt<NW, MT>(xr, av_ok, wr, s0, s1, acc);
 
-  __shared__ f32x4 red[KW - 1][NW][64];
+  __shared__ f32x4 red[KW - 1][MT][NW][64];
   if (wave > 0) {
 #pragma unroll
-    for (int j = 0; j < NW; ++j) red[wave - 1][j][lane] = acc[j];
+    for (int r = 0; r < MT; ++r)
+#pragma unroll
+      for (int j = 0; j < NW; ++j) red[wave - 1][r][j][lane] = acc[r][j];
   }
   __syncthreads();
   if (wave != 0) return;
 #pragma unroll
   for (int w = 0; w < KW - 1; ++w)
 #pragma unroll
-    for (int j = 0; j < NW; ++j) acc[j] = acc[j] + red[w][j][lane];
+    for (int r = 0; r < MT; ++r)
+#pragma unroll
+      for (int j = 0; j < NW; ++j) acc[r][j] = acc[r][j] + red[w][r][j][lane];
 
-  if (EPI == EPI_QKV) {
-    const bool rot = head < a.hq + a.hkv;
-    float part[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) part[i] = __shfl_xor(acc[0][i], 8);
+  for (int r = 0; r < MT; ++r) {
+    const int mt = blockIdx.y * MT + r;
+    if (EPI == EPI_QKV) {
+      const bool rot = head < a.hq + a.hkv;
+      float part[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = mt * 16 + 4 * kg + i;
-      if (m >= a.M) continue;
-      if (rot) {
-        if (c < 8) epi_qkv_pair<uint16_t>(a, m, head, dim, acc[0][i], part[i]);
-      } else {
-        epi_v_single<uint16_t>(a, m, head - a.hq - a.hkv, dim, acc[0][i]);
-      }
-    }
-  } else {
+      for (int i = 0; i < 4; ++i) part[i] = __shfl_xor(acc[r][0][i], 8);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = mt * 16 + 4 * kg + i;
-      const int n = t * 16 + c;
-      if (EPI == EPI_LOGITS) {
-        // (max, lowest index) over this tile's 16 columns, fixed butterfly
-        float bv = acc[0][i];
-        int bi = n;
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) {
-          const float ov = __shfl_xor(bv, o);
-          const int oi = __shfl_xor(bi, o);
-          if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-        }
-        if (m < a.M && c == 0) {
-          a.amax_v[(size_t)m * gridDim.x + t] = bv;
-          a.amax_i[(size_t)m * gridDim.x + t] = bi;
+      for (int i = 0; i < 4; ++i) {
+        const int m = mt * 16 + 4 * kg + i;
+        if (m >= a.M) continue;
+        if (rot) {
+          if (c < 8) epi_qkv_pair<uint16_t>(a, m, head, dim, acc[r][0][i], part[i]);
+        } else {
+          epi_v_single<uint16_t>(a, m, head - a.hq - a.hkv, dim, acc[r][0][i]);
         }
       }
-      if (m >= a.M) continue;
-      if (EPI == EPI_SWIGLU) epi_swiglu<uint16_t>(a, m, n, acc[0][i], acc[1][i]);
-      else epi_single<uint16_t>(a, EPI, m, n, acc[0][i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = mt * 16 + 4 * kg + i;
+        const int n = t * 16 + c;
+        if (EPI == EPI_LOGITS) {
+          // (max, lowest index) over this tile's 16 columns, fixed butterfly
+          float bv = acc[r][0][i];
+          int bi = n;
+#pragma unroll
+          for (int o = 1; o < 16; o <<= 1) {
+            const float ov = __shfl_xor(bv, o);
+            const int oi = __shfl_xor(bi, o);
+            if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+          }
+          if (m < a.M && c == 0) {
+            a.amax_v[(size_t)m * gridDim.x + t] = bv;
+            a.amax_i[(size_t)m * gridDim.x + t] = bi;
+          }
+        }
+        if (m >= a.M) continue;
+        if (EPI == EPI_SWIGLU) epi_swiglu<uint16_t>(a, m, n, acc[r][0][i], acc[r][NW - 1][i]);
+        else epi_single<uint16_t>(a, EPI, m, n, acc[r][0][i]);
+      }
     }
   }
 }
@@ -693,10 +709,15 @@ hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t s) {
     else tiles = a.N / 16;
     dim3 grid(tiles, mt);
     const bool wide = tiles >= 1024;   // a function of N only
-#define SSD_G(E, NW)                                                      \
-  case E:                                                                 \
-    if (wide) gemm_bf16_kernel<E, NW, 4><<<grid, 256, 0, s>>>(a);         \
-    else gemm_bf16_kernel<E, NW, 8><<<grid, 512, 0, s>>>(a);              \
+    // decode-loop passes (M <= 16): one 16-row tile per workgroup; longer
+    // passes (prefill chunks): 4 row tiles per workgroup share each weight load
+    const bool multi = a.M > 16;
+    const dim3 grid_mt(tiles, (a.M + 63) / 64);
+#define SSD_G(E, NW)                                                                 \
+  case E:                                                                            \
+    if (multi) gemm_bf16_kernel<E, NW, 4, 4><<<grid_mt, 256, 0, s>>>(a);             \
+    else if (wide) gemm_bf16_kernel<E, NW, 4, 1><<<grid, 256, 0, s>>>(a);            \
+    else gemm_bf16_kernel<E, NW, 8, 1><<<grid, 512, 0, s>>>(a);                      \
     break;
     switch (epi) {
       SSD_G(EPI_F32, 1)

@@ -49,7 +49,7 @@ CONFIGS = {
                      d_model=4096, n_q_heads=32, n_kv_heads=8, head_dim=128,
                      ffn_dim=12288, vocab=151936, dtype="bf16", prompt_len=2048,
                      block=16, geo_p=(0.5, 0.7, 0.9),
-                     feat_layers=(1, 9, 17, 25, 33), max_ctx=2048 + 17 + 16),
+                     feat_layers=(1, 9, 17, 25, 33), max_ctx=2048 + 448),
     # DeepSeek-V2-Lite-shaped MoE bf16
     "dsv2-lite": dict(_DENSE_DEFAULTS, name="dsv2-lite", cid=4, n_layers=27,
                       d_model=2048, n_q_heads=16, n_kv_heads=4, head_dim=128,
