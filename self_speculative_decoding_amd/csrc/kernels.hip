@@ -709,9 +709,10 @@ hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t s) {
     else tiles = a.N / 16;
     dim3 grid(tiles, mt);
     const bool wide = tiles >= 1024;   // a function of N only
-    // decode-loop passes (M <= 16): one 16-row tile per workgroup; longer
-    // passes (prefill chunks): 4 row tiles per workgroup share each weight load
-    const bool multi = a.M > 16;
+    // decode-loop passes (M <= SSD_MAX_BLOCK rows) always take the one-tile
+    // kernel, so a row's arithmetic never depends on the pass width; longer
+    // passes (prefill chunks) let 4 row tiles share each weight load
+    const bool multi = a.M > 32;
     const dim3 grid_mt(tiles, (a.M + 63) / 64);
 #define SSD_G(E, NW)                                                                 \
   case E:                                                                            \
