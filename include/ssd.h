@@ -221,7 +221,9 @@ ssd_status ssd_test_accept(ssd_ctx* ctx, const int32_t* d, const int32_t* p, int
 /* Times `iters` back-to-back launches of one layer operation at m rows on the
  * context's stream with HIP events; *avg_us receives the mean duration.
  * op: 0 = gate/up GEMM (+SwiGLU), 1 = down GEMM, 2 = qkv GEMM (+RoPE/KV),
- *     3 = o GEMM, 4 = lm_head GEMM, 5 = attention, 6 = routed-expert FFN.
+ *     3 = o GEMM, 4 = lm_head GEMM, 5 = attention, 6 = MoE expert FFN
+ *     (router, grouping, expert GEMMs, combine), 7 = streaming read of the LM
+ *     head matrix with 256*m workgroups (achievable HBM read bandwidth).
  * Launch i uses the weights of the i-th layer (cyclically, starting at
  * `layer`, among layers of the same kind), so consecutive launches stream
  * different weights as a real pass does.  Writes only scratch activations and

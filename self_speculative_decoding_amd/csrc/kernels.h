@@ -74,6 +74,7 @@ hipError_t launch_argmax_tiles(const float* pv, const int* pi, int nt, int* out,
 hipError_t launch_accept(int* block, const int* post, int k, int* state, int* outlog, int* result,
                          hipStream_t s);
 hipError_t launch_set_state(int* state, int idx, int value, hipStream_t s);
+hipError_t launch_read_probe(const void* src, size_t bytes, unsigned* sink, int blocks, hipStream_t s);
 hipError_t launch_copy_tokens(const int* src, int* dst, int n, hipStream_t s);
 hipError_t launch_copy_f32(const float* src, float* dst, int n, hipStream_t s);
 

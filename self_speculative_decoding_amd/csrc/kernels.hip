@@ -675,6 +675,28 @@ __global__ __launch_bounds__(64) void accept_kernel(int* block, const int* post,
 
 __global__ void set_state_kernel(int* state, int idx, int value) { state[idx] = value; }
 
+// Streaming read of n16 16-byte words (achievable HBM read bandwidth): each
+// lane keeps 8 loads in flight; one XOR per workgroup lands in sink.
+__global__ __launch_bounds__(256) void read_probe_kernel(const uint4* __restrict__ src, size_t n16,
+                                                         unsigned* __restrict__ sink) {
+  const size_t stride = (size_t)gridDim.x * 256;
+  unsigned acc = 0;
+  size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  for (; i + 7 * stride < n16; i += 8 * stride) {
+    uint4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = src[i + j * stride];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
+  }
+  for (; i < n16; i += stride) {
+    const uint4 v = src[i];
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  acc = __reduce_xor_sync(0xffffffffffffffffull, acc);
+  if (threadIdx.x == 0) sink[blockIdx.x] = acc;
+}
+
 __global__ __launch_bounds__(256) void copy_f32_kernel(const float* __restrict__ src, float* __restrict__ dst, int n) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i < n) dst[i] = src[i];
@@ -784,6 +806,11 @@ hipError_t launch_argmax_tiles(const float* pv, const int* pi, int nt, int* out,
 hipError_t launch_accept(int* block, const int* post, int k, int* state, int* outlog, int* result,
                          hipStream_t s) {
   accept_kernel<<<1, 64, 0, s>>>(block, post, k, state, outlog, result);
+  return hipGetLastError();
+}
+
+hipError_t launch_read_probe(const void* src, size_t bytes, unsigned* sink, int blocks, hipStream_t s) {
+  read_probe_kernel<<<blocks, 256, 0, s>>>((const uint4*)src, bytes / 16, sink);
   return hipGetLastError();
 }
 

@@ -734,9 +734,11 @@ ssd_status ssd_time_op(ssd_ctx* c, int32_t op, int32_t layer, int32_t m, int32_t
   const ssd_cfg& g = c->cfg;
   if (layer < 0 || layer >= g.n_layers) return fail(SSD_E_ARG, "layer out of range");
   if (m < 1 || m > c->lay.R) return fail(SSD_E_ARG, "m outside [1, %d]", c->lay.R);
+  if (op == 7 && (size_t)256 * m > (size_t)c->cfg.max_block * (c->cfg.vocab / 16 + 1))
+    return fail(SSD_E_ARG, "too many probe workgroups for the sink buffer");
   if (iters < 1) return fail(SSD_E_ARG, "iters < 1");
   if (c->n + m + 1 > g.max_ctx) return fail(SSD_E_CAPACITY, "no room past the committed length");
-  if (op < 0 || op > 6) return fail(SSD_E_ARG, "unknown op %d", op);
+  if (op < 0 || op > 7) return fail(SSD_E_ARG, "unknown op %d", op);
   if (op == 6 && !c->L[layer].moe) return fail(SSD_E_ARG, "layer %d is not an MoE layer", layer);
   if (op == 6 && c->moe_inject && m > c->moe_inject) return fail(SSD_E_ARG, "m exceeds the injected routing rows");
   if (op == 4 && m > g.max_block) return fail(SSD_E_ARG, "lm_head timing needs m <= max_block");
@@ -780,7 +782,11 @@ ssd_status ssd_time_op(ssd_ctx* c, int32_t op, int32_t layer, int32_t m, int32_t
         epi = dt == SSD_BF16 ? EPI_LOGITS : EPI_F32; break;
       default: break;
     }
-    if (op == 6) {
+    if (op == 7) {
+      // read probe over the LM head matrix; m = workgroups per CU (x256)
+      const size_t bytes = (size_t)g.vocab * d * c->esz;
+      HIPCHK(launch_read_probe(c->lm_head, bytes, (unsigned*)c->amax_i, 256 * m, s));
+    } else if (op == 6) {
       HIPCHK(launch_moe(dt, moe_args(c, l, m), s));
     } else if (op == 5) {
       AttnArgs at{};
