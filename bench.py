@@ -66,6 +66,27 @@ def pass_bytes(cfg: dict, M: int, ctx: float, layers: int | None = None, head: b
     return b
 
 
+def measured_traffic() -> float | None:
+    """HBM bytes per launch of the gate/up GEMM from the committed hardware-
+    counter summary, or None when the kernel sources changed since."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "gemm_swiglu_llama8b_traffic.txt")
+    try:
+        txt = open(path).read()
+    except OSError:
+        return None
+    csrc = os.path.join(ROOT, "self_speculative_decoding_amd", "csrc")
+    sha = hashlib.sha256(open(os.path.join(csrc, "kernels.hip"), "rb").read() +
+                         open(os.path.join(csrc, "device.h"), "rb").read()).hexdigest()
+    rec_sha = nbytes = None
+    for line in txt.splitlines():
+        if line.startswith("kernel source sha256"):
+            rec_sha = line.split(":")[-1].strip()
+        if line.startswith("counter bytes per launch:"):
+            nbytes = float(line.split(":")[1].split()[0])
+    return nbytes if rec_sha == sha else None
+
+
 def cpu_baseline(cfg, weights, prompt, budget_s: float) -> dict:
     """The oracle (float64 CPU decoder) timed on this host: greedy decode steps
     after a short prompt, until about budget_s seconds of decode work."""
@@ -96,6 +117,28 @@ def cpu_baseline(cfg, weights, prompt, budget_s: float) -> dict:
     return {"value": steps / el, "unit": "tok/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{steps} float64 greedy decode steps of the same model after an 8-token prompt "
                       f"(context <= {8 + steps}); weight conversion and prefill excluded"}
+
+
+def bench_pmc_probe(args) -> int:
+    """Kernel sequence for `rocprofv3 --pmc` runs: 3 plain copies of 128 MiB
+    (counter calibration), then 24 gate/up GEMM launches at m = 4 over the
+    layers of a 4-layer model with the headline widths (940 MB of weights, more
+    than the on-die caches hold), then 3 read probes of the 1.05 GB LM head."""
+    import synth
+    from self_speculative_decoding_amd import Engine, make_cfg
+    cfg = synth.config("llama-8b", n_layers=4)
+    w = synth.make_weights(cfg)
+    eng = Engine(make_cfg(cfg, max_block=6, prefill_chunk=256), [w[n] for n, _, _ in synth.weight_specs(cfg)])
+    eng.prefill(synth.make_prompt(cfg)[:64])
+    res = {"copy_probe_us": eng.time_op("copy_probe", 0, 128, 3),
+           "gate_up_m4_us": eng.time_op("gate_up", 0, 4, 24),
+           "read_probe_us": eng.time_op("read_probe", 0, 4, 3)}
+    eng.close()
+    res["copy_bytes"] = 128 << 20
+    res["gate_up_bytes"] = 2 * cfg["ffn_dim"] * cfg["d_model"] * 2
+    res["read_probe_gbs"] = round(cfg["vocab"] * cfg["d_model"] * 2 / res["read_probe_us"] / 1e3, 1)
+    print(json.dumps(res), flush=True)
+    return 0
 
 
 def bench_verify_blocks(args) -> int:
@@ -225,6 +268,9 @@ def main() -> int:
     ap.add_argument("--n-new", type=int, default=None, help="tokens per decode (default: workload's)")
     ap.add_argument("--blocks", type=int, default=40, help="verify blocks per p (qwen3-8b)")
     ap.add_argument("--passes", type=int, default=12, help="verify passes per n and mode (dsv2-lite)")
+    ap.add_argument("--pmc-probe", action="store_true",
+                    help="short fixed kernel sequence for hardware-counter runs (copy probe, read probe, "
+                         "gate/up GEMM at m=4 on a 4-layer model of the headline widths)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -238,6 +284,8 @@ def main() -> int:
     import synth
     from self_speculative_decoding_amd import Engine, make_cfg, skip_mask
 
+    if args.pmc_probe:
+        return bench_pmc_probe(args)
     if args.workload == "qwen3-8b":
         return bench_verify_blocks(args)
     if args.workload == "dsv2-lite":
@@ -320,7 +368,8 @@ def main() -> int:
     roof = {"bound": "hbm", "kernel": "gemm_bf16_kernel<EPI_SWIGLU> (gate/up GEMM + SwiGLU)",
             "m": k + 1, "achieved": round(gu_bytes / (gu_us * 1e-6) / 1e9, 1), "peak": PEAK_HBM_GBS,
             "unit": "GB/s", "frac": round(gu_bytes / (gu_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
-            "traffic": None, "bytes_per_launch": gu_bytes, "avg_us": round(gu_us, 2)}
+            "traffic": measured_traffic() if args.workload == "llama-8b" else None,
+            "bytes_per_launch": gu_bytes, "avg_us": round(gu_us, 2)}
     log(f"gate/up GEMM m={k + 1}: {gu_us:.1f} us = {roof['achieved']:.0f} GB/s")
 
     # ---- skip x k sweep (one decode each) ----

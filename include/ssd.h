@@ -223,7 +223,9 @@ ssd_status ssd_test_accept(ssd_ctx* ctx, const int32_t* d, const int32_t* p, int
  * op: 0 = gate/up GEMM (+SwiGLU), 1 = down GEMM, 2 = qkv GEMM (+RoPE/KV),
  *     3 = o GEMM, 4 = lm_head GEMM, 5 = attention, 6 = MoE expert FFN
  *     (router, grouping, expert GEMMs, combine), 7 = streaming read of the LM
- *     head matrix with 256*m workgroups (achievable HBM read bandwidth).
+ *     head matrix with 256*m workgroups (achievable HBM read bandwidth),
+ *     8 = plain float32 copy of m MiB (capped by the buffers) from the LM head
+ *     matrix into scratch (a known-size read + write for counter calibration).
  * Launch i uses the weights of the i-th layer (cyclically, starting at
  * `layer`, among layers of the same kind), so consecutive launches stream
  * different weights as a real pass does.  Writes only scratch activations and

@@ -19,7 +19,7 @@ SSD_MAX_FEAT = 8
 SSD_MAX_BLOCK = 32
 ST_LOADED, ST_READY, ST_DRAFTED, ST_VERIFIED = range(4)
 OP_PREFILL, OP_DRAFT, OP_VERIFY, OP_VERIFY_BLOCK, OP_ACCEPT, OP_RESET = range(6)
-OPS = dict(gate_up=0, down=1, qkv=2, o=3, lm_head=4, attention=5, moe=6, read_probe=7)
+OPS = dict(gate_up=0, down=1, qkv=2, o=3, lm_head=4, attention=5, moe=6, read_probe=7, copy_probe=8)
 
 EXPORTS = ["ssd_validate_cfg", "ssd_n_weights", "ssd_weight_numel", "ssd_workspace_bytes",
            "ssd_skip_mask", "ssd_check_transition", "ssd_strerror", "ssd_last_error",

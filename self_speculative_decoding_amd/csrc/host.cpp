@@ -145,7 +145,8 @@ bool compute_layout(const ssd_cfg& c, Layout& L) {
   L.amax_v = take((size_t)c.max_block * (c.vocab / 16 + 1) * 4);
   L.trace = take((size_t)c.n_layers * c.max_block * d * 4);
   L.amax_i = take((size_t)c.max_block * (c.vocab / 16 + 1) * 4);
-  L.part_o = take((size_t)L.n_part * R * hq * hd * 4);
+  L.part_o_bytes = (size_t)L.n_part * R * hq * hd * 4;
+  L.part_o = take(L.part_o_bytes);
   L.part_ml = take((size_t)L.n_part * R * hq * 2 * 4);
   L.counters = take((size_t)hkv * (R / 16) * 4);
   L.rope_cos = take((size_t)c.max_ctx * (hd / 2) * 4);

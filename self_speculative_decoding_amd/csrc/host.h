@@ -22,6 +22,7 @@ struct Layout {
   size_t total = 0;
   int R = 0;        // rows per pass (multiple of 16)
   int n_part = 0;   // attention partitions covering max_ctx
+  size_t part_o_bytes = 0;
 };
 
 ssd_status fail(ssd_status s, const char* fmt, ...);

@@ -8,6 +8,7 @@
 // "Apple Silicon Optimizations" describe for their engine.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <chrono>
 #include <cmath>
 #include <cstring>
@@ -738,7 +739,7 @@ ssd_status ssd_time_op(ssd_ctx* c, int32_t op, int32_t layer, int32_t m, int32_t
     return fail(SSD_E_ARG, "too many probe workgroups for the sink buffer");
   if (iters < 1) return fail(SSD_E_ARG, "iters < 1");
   if (c->n + m + 1 > g.max_ctx) return fail(SSD_E_CAPACITY, "no room past the committed length");
-  if (op < 0 || op > 7) return fail(SSD_E_ARG, "unknown op %d", op);
+  if (op < 0 || op > 8) return fail(SSD_E_ARG, "unknown op %d", op);
   if (op == 6 && !c->L[layer].moe) return fail(SSD_E_ARG, "layer %d is not an MoE layer", layer);
   if (op == 6 && c->moe_inject && m > c->moe_inject) return fail(SSD_E_ARG, "m exceeds the injected routing rows");
   if (op == 4 && m > g.max_block) return fail(SSD_E_ARG, "lm_head timing needs m <= max_block");
@@ -782,7 +783,11 @@ ssd_status ssd_time_op(ssd_ctx* c, int32_t op, int32_t layer, int32_t m, int32_t
         epi = dt == SSD_BF16 ? EPI_LOGITS : EPI_F32; break;
       default: break;
     }
-    if (op == 7) {
+    if (op == 8) {
+      // plain copy of m MiB from the LM head matrix into the attention partial buffer
+      const size_t bytes = std::min(std::min((size_t)m << 20, c->lay.part_o_bytes), (size_t)g.vocab * d * c->esz);
+      HIPCHK(launch_copy_f32((const float*)c->lm_head, c->part_o, (int)(bytes / 4), s));
+    } else if (op == 7) {
       // read probe over the LM head matrix; m = workgroups per CU (x256)
       const size_t bytes = (size_t)g.vocab * d * c->esz;
       HIPCHK(launch_read_probe(c->lm_head, bytes, (unsigned*)c->amax_i, 256 * m, s));
