@@ -31,42 +31,62 @@ __device__ __forceinline__ float wave_sum(float v) {   // fixed butterfly, same 
   return v;
 }
 
-// MFMA weight-streaming GEMM tile step count issued ahead of their MFMAs
-constexpr int GEMM_U = 8;
 
 __device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *(const uint4*)p; }
 
-// One wave's share of a 16-row x (NW x 16)-column MFMA tile: K-steps
-// [s0, s1) of 32 elements, accumulated in order.  xr: this lane's A row at its
-// 8-element K group (A rows past the valid ones load zeros); wr[j]: this
-// lane's weight row of tile j at the same K group.
-template <int NW>
-__device__ __forceinline__ void mfma_stream(const uint16_t* xr, bool xok, const uint16_t* const* wr, int s0, int s1,
+// Weights are read once per pass: nontemporal loads stream them without
+// allocating in the caches (measured: 7.1 vs 6.3 TB/s for a plain read).
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld16_nt(const uint16_t* p) {
+  const u32x4 t = __builtin_nontemporal_load((const u32x4*)p);
+  return uint4{t[0], t[1], t[2], t[3]};
+}
+
+// One wave's share of a 16-row x (NW x 16)-column MFMA tile: K-chunks
+// [c0, c1) of 64 elements, accumulated in order.  In each chunk lane group g
+// (lane/16) reads 32 contiguous bytes (elements 16g..16g+15) of its A row
+// and its weight rows, so the four groups cover every 128-byte line of a row;
+// the chunk is two MFMA K-steps, the first over elements 16g..16g+7 of every
+// group, the second over 16g+8..16g+15 (A and B permuted alike).
+// xr: this lane's A row at element 16g; wr[j]: weight row of tile j at 16g.
+template <int NW, bool NT>
+__device__ __forceinline__ void mfma_stream(const uint16_t* xr, bool xok, const uint16_t* const* wr, int c0, int c1,
                                             f32x4* acc) {
+  constexpr int U = 4;   // chunks per batch of loads
   const uint4 zero = {0u, 0u, 0u, 0u};
-  int s = s0;
-  for (; s + GEMM_U <= s1; s += GEMM_U) {
-    uint4 xa[GEMM_U], wb[NW][GEMM_U];
+  auto ldw = [](const uint16_t* p) { return NT ? ld16_nt(p) : ld16(p); };
+  int s = c0;
+  for (; s + U <= c1; s += U) {
+    uint4 xa[U][2], wb[NW][U][2];
 #pragma unroll
-    for (int u = 0; u < GEMM_U; ++u) {
+    for (int u = 0; u < U; ++u) {
 #pragma unroll
-      for (int j = 0; j < NW; ++j) wb[j][u] = ld16(wr[j] + (size_t)(s + u) * 32);
-      xa[u] = xok ? ld16(xr + (size_t)(s + u) * 32) : zero;
+      for (int j = 0; j < NW; ++j) {
+        wb[j][u][0] = ldw(wr[j] + (size_t)(s + u) * 64);
+        wb[j][u][1] = ldw(wr[j] + (size_t)(s + u) * 64 + 8);
+      }
+      xa[u][0] = xok ? ld16(xr + (size_t)(s + u) * 64) : zero;
+      xa[u][1] = xok ? ld16(xr + (size_t)(s + u) * 64 + 8) : zero;
     }
 #pragma unroll
-    for (int u = 0; u < GEMM_U; ++u)
+    for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int j = 0; j < NW; ++j)
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa[u]),
-                                                         __builtin_bit_cast(bf16x8, wb[j][u]), acc[j], 0, 0, 0);
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int j = 0; j < NW; ++j)
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa[u][h]),
+                                                           __builtin_bit_cast(bf16x8, wb[j][u][h]), acc[j], 0, 0, 0);
   }
-  for (; s < s1; ++s) {
-    const uint4 xa = xok ? ld16(xr + (size_t)s * 32) : zero;
+  for (; s < c1; ++s) {
 #pragma unroll
-    for (int j = 0; j < NW; ++j) {
-      const uint4 wb = ld16(wr[j] + (size_t)s * 32);
-      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa),
-                                                       __builtin_bit_cast(bf16x8, wb), acc[j], 0, 0, 0);
+    for (int h = 0; h < 2; ++h) {
+      const uint4 xa = xok ? ld16(xr + (size_t)s * 64 + 8 * h) : zero;
+#pragma unroll
+      for (int j = 0; j < NW; ++j) {
+        const uint4 wb = ldw(wr[j] + (size_t)s * 64 + 8 * h);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa),
+                                                         __builtin_bit_cast(bf16x8, wb), acc[j], 0, 0, 0);
+      }
     }
   }
 }
@@ -74,40 +94,25 @@ __device__ __forceinline__ void mfma_stream(const uint16_t* xr, bool xok, const 
 // As mfma_stream for MT 16-row tiles sharing every weight fragment.
 template <int NW, int MT>
 __device__ __forceinline__ void mfma_stream_mt(const uint16_t* const* xr, const bool* xok, const uint16_t* const* wr,
-                                               int s0, int s1, f32x4 (*acc)[NW]) {
-  constexpr int U = 4;
+                                               int c0, int c1, f32x4 (*acc)[NW]) {
   const uint4 zero = {0u, 0u, 0u, 0u};
-  int s = s0;
-  for (; s + U <= s1; s += U) {
-    uint4 xa[MT][U], wb[NW][U];
+  for (int s = c0; s < c1; ++s) {
+    uint4 wb[NW][2], xa[MT][2];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int h = 0; h < 2; ++h) {
 #pragma unroll
-      for (int j = 0; j < NW; ++j) wb[j][u] = ld16(wr[j] + (size_t)(s + u) * 32);
+      for (int j = 0; j < NW; ++j) wb[j][h] = ld16(wr[j] + (size_t)s * 64 + 8 * h);
 #pragma unroll
-      for (int r = 0; r < MT; ++r) xa[r][u] = xok[r] ? ld16(xr[r] + (size_t)(s + u) * 32) : zero;
+      for (int r = 0; r < MT; ++r) xa[r][h] = xok[r] ? ld16(xr[r] + (size_t)s * 64 + 8 * h) : zero;
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int r = 0; r < MT; ++r)
 #pragma unroll
         for (int j = 0; j < NW; ++j)
-          acc[r][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa[r][u]),
-                                                              __builtin_bit_cast(bf16x8, wb[j][u]), acc[r][j], 0, 0, 0);
-  }
-  for (; s < s1; ++s) {
-    uint4 wb[NW];
-#pragma unroll
-    for (int j = 0; j < NW; ++j) wb[j] = ld16(wr[j] + (size_t)s * 32);
-#pragma unroll
-    for (int r = 0; r < MT; ++r) {
-      const uint4 xa = xok[r] ? ld16(xr[r] + (size_t)s * 32) : zero;
-#pragma unroll
-      for (int j = 0; j < NW; ++j)
-        acc[r][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa),
-                                                            __builtin_bit_cast(bf16x8, wb[j]), acc[r][j], 0, 0, 0);
-    }
+          acc[r][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa[r][h]),
+                                                              __builtin_bit_cast(bf16x8, wb[j][h]), acc[r][j], 0, 0, 0);
   }
 }
 

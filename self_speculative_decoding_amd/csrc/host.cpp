@@ -103,12 +103,12 @@ ssd_status validate(const ssd_cfg* cp) {
   const int64_t qo = (int64_t)c.n_q_heads * c.head_dim;
   const int f = layer_ffn(c);
   if (c.dtype == SSD_BF16) {
-    auto k32 = [](int64_t v) { return v % 32 == 0; };
+    auto k32 = [](int64_t v) { return v % 64 == 0; };   // GEMM K runs in 64-element chunks
     auto n16 = [](int64_t v) { return v % 16 == 0; };
-    if (!k32(c.d_model) || !k32(qo)) return fail(SSD_E_UNSUPPORTED, "bf16: d_model and heads*head_dim must be multiples of 32");
+    if (!k32(c.d_model) || !k32(qo)) return fail(SSD_E_UNSUPPORTED, "bf16: d_model and heads*head_dim must be multiples of 64");
     if (!n16(c.vocab)) return fail(SSD_E_UNSUPPORTED, "bf16: vocab must be a multiple of 16");
-    if (f > 0 && (!k32(f))) return fail(SSD_E_UNSUPPORTED, "bf16: FFN width must be a multiple of 32");
-    if (c.n_experts > 0 && !k32(c.expert_ffn)) return fail(SSD_E_UNSUPPORTED, "bf16: expert_ffn must be a multiple of 32");
+    if (f > 0 && (!k32(f))) return fail(SSD_E_UNSUPPORTED, "bf16: FFN width must be a multiple of 64");
+    if (c.n_experts > 0 && !k32(c.expert_ffn)) return fail(SSD_E_UNSUPPORTED, "bf16: expert_ffn must be a multiple of 64");
   } else {
     if (c.d_model % 2 || c.vocab % 2 || qo % 2) return fail(SSD_E_UNSUPPORTED, "f32: d_model, vocab, heads*head_dim must be even");
     if (c.n_experts > 0 && c.expert_ffn % 2) return fail(SSD_E_UNSUPPORTED, "f32: expert_ffn must be even");

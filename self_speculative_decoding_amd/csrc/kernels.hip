@@ -165,21 +165,21 @@ __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
   for (int r = 0; r < MT; ++r) {
     const int am = (blockIdx.y * MT + r) * 16 + c;
     av_ok[r] = am < a.M;
-    xr[r] = (const uint16_t*)a.X + (size_t)(av_ok[r] ? am : 0) * a.ldx + kg * 8;
+    xr[r] = (const uint16_t*)a.X + (size_t)(av_ok[r] ? am : 0) * a.ldx + kg * 16;
   }
   const uint16_t* wr[NW];
   int head = 0, dim = 0;
 #pragma unroll
-  for (int j = 0; j < NW; ++j) wr[j] = gemm_row<EPI, NW>(a, t, j, c, &head, &dim) + kg * 8;
+  for (int j = 0; j < NW; ++j) wr[j] = gemm_row<EPI, NW>(a, t, j, c, &head, &dim) + kg * 16;
 
-  const int S = a.K >> 5;
+  const int S = a.K >> 6;   // 64-element chunks
   const int s0 = (S * wave) / KW, s1 = (S * (wave + 1)) / KW;
   f32x4 acc[MT][NW];
 #pragma unroll
   for (int r = 0; r < MT; ++r)
 #pragma unroll
     for (int j = 0; j < NW; ++j) acc[r][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (MT == 1) mfma_stream<NW>(xr[0], av_ok[0], wr, s0, s1, acc[0]);
+  if (MT == 1) mfma_stream<NW, false>(xr[0], av_ok[0], wr, s0, s1, acc[0]);
   else mfma_stream_mt<NW, MT>(xr, av_ok, wr, s0, s1, acc);
 
   __shared__ f32x4 red[KW - 1][MT][NW][64];

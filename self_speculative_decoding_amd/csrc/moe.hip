@@ -152,21 +152,21 @@ __global__ __launch_bounds__(256) void moe_gemm_kernel(MoeArgs a) {
   int K;
   if (PHASE == 0) {
     K = a.d;
-    xr = (const uint16_t*)a.X + (size_t)(code / slots) * a.d + kg * 8;
+    xr = (const uint16_t*)a.X + (size_t)(code / slots) * a.d + kg * 16;
     const size_t eo = (size_t)e * a.fe * a.d;
-    wr[0] = (const uint16_t*)(sh ? a.sg : a.eg) + eo + (size_t)(t * 16 + c) * a.d + kg * 8;
-    wr[NW - 1] = (const uint16_t*)(sh ? a.su : a.eu) + eo + (size_t)(t * 16 + c) * a.d + kg * 8;
+    wr[0] = (const uint16_t*)(sh ? a.sg : a.eg) + eo + (size_t)(t * 16 + c) * a.d + kg * 16;
+    wr[NW - 1] = (const uint16_t*)(sh ? a.su : a.eu) + eo + (size_t)(t * 16 + c) * a.d + kg * 16;
   } else {
     K = a.fe;
-    xr = (const uint16_t*)a.act + (size_t)code * a.fe + kg * 8;
-    wr[0] = (const uint16_t*)(sh ? a.sd : a.ed) + (size_t)e * a.d * a.fe + (size_t)(t * 16 + c) * a.fe + kg * 8;
+    xr = (const uint16_t*)a.act + (size_t)code * a.fe + kg * 16;
+    wr[0] = (const uint16_t*)(sh ? a.sd : a.ed) + (size_t)e * a.d * a.fe + (size_t)(t * 16 + c) * a.fe + kg * 16;
   }
-  const int S = K >> 5;
+  const int S = K >> 6;   // 64-element chunks
   const int s0 = (S * wave) >> 2, s1 = (S * (wave + 1)) >> 2;
   f32x4 acc[NW];
 #pragma unroll
   for (int j = 0; j < NW; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  mfma_stream<NW>(xr, ok, wr, s0, s1, acc);
+  mfma_stream<NW, false>(xr, ok, wr, s0, s1, acc);
 
   __shared__ f32x4 red[3][NW][64];
   if (wave > 0) {
