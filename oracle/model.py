@@ -126,6 +126,17 @@ class Model:
         """x [M, in] times W [out, in] transposed."""
         return x @ W.astype(np.float64, copy=False).T
 
+    def normed_lin(self, x: np.ndarray, g: np.ndarray, Ws) -> list[np.ndarray]:
+        """RMSNorm with gain g followed by products with each W of Ws.
+
+        Exact arithmetic gives lin(rmsnorm(x, g), W).  The stored operand is
+        the gain-scaled input x * g (rounded like every stored matrix input)
+        and the 1/rms factor multiplies the product: the normalisation is a
+        per-row scalar, so it commutes with the product."""
+        rstd = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + self.eps)
+        xg = self.rn(x * g)
+        return [self.lin(xg, W) * rstd for W in Ws]
+
     # -- blocks --------------------------------------------------------------
 
     def embed(self, tokens) -> np.ndarray:
@@ -135,10 +146,10 @@ class Model:
         w, p = self.w, f"l{l}."
         M = x.shape[0]
         pos = np.arange(pos0, pos0 + M)
-        n1 = self.rn(rmsnorm(x, w[p + "attn_norm"], self.eps))
-        q = self.lin(n1, w[p + "wq"]).reshape(M, self.hq, self.hd)
-        k = self.lin(n1, w[p + "wk"]).reshape(M, self.hkv, self.hd)
-        v = self.lin(n1, w[p + "wv"]).reshape(M, self.hkv, self.hd)
+        q, k, v = self.normed_lin(x, w[p + "attn_norm"], [w[p + "wq"], w[p + "wk"], w[p + "wv"]])
+        q = q.reshape(M, self.hq, self.hd)
+        k = k.reshape(M, self.hkv, self.hd)
+        v = v.reshape(M, self.hkv, self.hd)
         q = self.rn(rope(q, pos, self.theta))
         k = self.rn(rope(k, pos, self.theta))
         v = self.rn(v)
@@ -155,9 +166,11 @@ class Model:
         att = self.rn(out.reshape(M, self.hq * self.hd))
         return x + self.lin(att, w[p + "wo"])
 
-    def dense_ffn(self, l: int, n2: np.ndarray) -> np.ndarray:
+    def dense_ffn(self, l: int, h: np.ndarray) -> np.ndarray:
+        """SwiGLU feed-forward of the normed residual h (ffn_norm folded in)."""
         w, p = self.w, f"l{l}."
-        act = self.rn(silu(self.lin(n2, w[p + "w_gate"])) * self.lin(n2, w[p + "w_up"]))
+        gate, up = self.normed_lin(h, w[p + "ffn_norm"], [w[p + "w_gate"], w[p + "w_up"]])
+        act = self.rn(silu(gate) * up)
         return self.lin(act, w[p + "w_down"])
 
     def expert(self, l: int, e: int, rows: np.ndarray, shared: bool = False) -> np.ndarray:
@@ -197,13 +210,14 @@ class Model:
 
     def layer(self, l: int, x: np.ndarray, pos0: int, cache: Cache, dedup: bool = False) -> np.ndarray:
         h = self.attention_block(l, x, pos0, cache)
-        n2 = self.rn(rmsnorm(h, self.w[f"l{l}.ffn_norm"], self.eps))
         if self.cfg["n_experts"] > 0 and l >= self.cfg["n_dense_layers"]:
+            # router and experts share one normed input
+            n2 = self.rn(rmsnorm(h, self.w[f"l{l}.ffn_norm"], self.eps))
             return h + self.moe_ffn(l, n2, dedup)
-        return h + self.dense_ffn(l, n2)
+        return h + self.dense_ffn(l, h)
 
     def head(self, x: np.ndarray) -> np.ndarray:
-        return self.lin(self.rn(rmsnorm(x, self.w["final_norm"], self.eps)), self.w["lm_head"])
+        return self.normed_lin(x, self.w["final_norm"], [self.w["lm_head"]])[0]
 
     def forward(self, tokens, pos0: int, cache: Cache, layers=None, dedup: bool = False) -> np.ndarray:
         """Logits [M, V] for tokens at positions pos0..pos0+M-1, writing the

@@ -49,10 +49,9 @@ __device__ __forceinline__ uint4 ld16_nt(const uint16_t* p) {
 // the chunk is two MFMA K-steps, the first over elements 16g..16g+7 of every
 // group, the second over 16g+8..16g+15 (A and B permuted alike).
 // xr: this lane's A row at element 16g; wr[j]: weight row of tile j at 16g.
-template <int NW, bool NT>
+template <int NW, bool NT, int U>
 __device__ __forceinline__ void mfma_stream(const uint16_t* xr, bool xok, const uint16_t* const* wr, int c0, int c1,
                                             f32x4* acc) {
-  constexpr int U = 4;   // chunks per batch of loads
   const uint4 zero = {0u, 0u, 0u, 0u};
   auto ldw = [](const uint16_t* p) { return NT ? ld16_nt(p) : ld16(p); };
   int s = c0;

@@ -133,6 +133,7 @@ bool compute_layout(const ssd_cfg& c, Layout& L) {
   L.vc = take(cache);
   L.x = take((size_t)R * d * 4);
   L.xn = take((size_t)R * d * esz);
+  L.ss = take((size_t)R * (d / 16) * 4);   // folded-norm partial sums of squares
   L.q = take((size_t)R * hq * hd * esz);
   L.att = take((size_t)R * hq * hd * esz);
   size_t fact = (size_t)layer_ffn(c);

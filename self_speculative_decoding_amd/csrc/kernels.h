@@ -48,6 +48,18 @@ struct GemmArgs {
   // LOGITS epilogue: per-tile argmax partials [M][N/16]
   float* amax_v;
   int* amax_i;
+  // RMSNorm folded into the GEMMs (bf16 models).  A consumer GEMM (QKV,
+  // gate/up, LM head) reads X = bf16(x * gain) and scales its float
+  // accumulator by rstd = 1/sqrt(mean(x^2) + eps), summing the per-16-column
+  // partial sums of squares ss_in [M][nss] the producer left.  The producer
+  // (residual epilogue) writes those partials (ss_out [M][N/16]) and the next
+  // consumer's input xg_out = bf16(x_new * gain_next) [M][N].
+  const float* ss_in;
+  int nss;
+  float eps;
+  float* ss_out;
+  void* xg_out;
+  const void* gain_next;
 };
 
 struct AttnArgs {
@@ -65,6 +77,10 @@ struct AttnArgs {
 
 // dtype: 0 = f32, 1 = bf16 (uint16 bit patterns)
 hipError_t launch_embed(int dtype, const int* tok, const void* E, float* x, int d, int M, hipStream_t s);
+// bf16 embedding that also leaves the folded-RMSNorm inputs of the first layer:
+// xg = bf16(x * gain) and per-16-column sums of squares ss [M][d/16]
+hipError_t launch_embed_norm(const int* tok, const void* E, float* x, int d, int M, const void* gain, void* xg,
+                             float* ss, hipStream_t s);
 hipError_t launch_rmsnorm(int dtype, const float* x, int ldx, const void* g, void* y, int ldy, int d,
                           float eps, int M, hipStream_t s);
 hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t s);
@@ -95,6 +111,10 @@ struct MoeArgs {
   int* groups;                // dedup work list (see kernels)
   int* union_out;             // [1] union size of this pass
   int dedup;
+  // folded RMSNorm of the next GEMM (see GemmArgs): written when ss_out != 0
+  float* ss_out;              // [M, d/16]
+  void* xg_out;               // [M, d] bf16(x * gain_next)
+  const void* gain_next;      // [d]
 };
 hipError_t launch_moe(int dtype, const MoeArgs& a, hipStream_t s);
 

@@ -8,6 +8,14 @@
 // the lossless check; mlx-dflash README: bit-for-bit parity with greedy).
 #include "device.h"
 
+// load-batch depth (64-element chunks) of the decode GEMMs; build-time tuning
+#ifndef SSD_GEMM_U1
+#define SSD_GEMM_U1 4
+#endif
+#ifndef SSD_GEMM_U2
+#define SSD_GEMM_U2 2
+#endif
+
 namespace ssd {
 
 // ---------------------------------------------------------------------------
@@ -20,6 +28,23 @@ __global__ __launch_bounds__(256) void embed_kernel(const int* __restrict__ tok,
   const int m = blockIdx.x;
   const E* row = emb + (size_t)tok[m] * d;
   for (int i = threadIdx.x; i < d; i += 256) x[(size_t)m * d + i] = tof(row[i]);
+}
+
+__global__ __launch_bounds__(256) void embed_norm_kernel(const int* __restrict__ tok, const uint16_t* __restrict__ emb,
+                                                         float* __restrict__ x, int d, const uint16_t* __restrict__ g,
+                                                         uint16_t* __restrict__ xg, float* __restrict__ ss) {
+  const int m = blockIdx.x;
+  const uint16_t* row = emb + (size_t)tok[m] * d;
+  for (int c0 = threadIdx.x * 16; c0 < d; c0 += 256 * 16) {
+    float q = 0.f;
+    for (int j = 0; j < 16; ++j) {
+      const float v = bf2f(row[c0 + j]);
+      x[(size_t)m * d + c0 + j] = v;
+      xg[(size_t)m * d + c0 + j] = f2bf(v * bf2f(g[c0 + j]));
+      q = fmaf(v, v, q);
+    }
+    ss[(size_t)m * (d / 16) + c0 / 16] = q;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -135,6 +160,23 @@ __device__ __forceinline__ void epi_v_single(const GemmArgs& a, int m, int vh, i
 // ---------------------------------------------------------------------------
 
 
+// Row m's sum-of-squares partials (one per 16 columns, nss of them): lane l
+// holds partials 4l..4l+3; partials from 256 on are added after, 64 apart.
+// The order is fixed by nss alone, whatever the pass width.
+__device__ __forceinline__ float4 ss_part(const GemmArgs& a, int m, bool row_ok, int lane) {
+  if (!row_ok || m >= a.M || 4 * lane >= a.nss) return make_float4(0.f, 0.f, 0.f, 0.f);
+  return *(const float4*)(a.ss_in + (size_t)m * a.nss + 4 * lane);
+}
+
+__device__ __forceinline__ float ss_rstd(const GemmArgs& a, int m, bool row_ok, int lane, float4 v) {
+  float s = ((v.x + v.y) + v.z) + v.w;
+  if (row_ok && m < a.M)
+    for (int p = 256 + lane; p < a.nss; p += 64) s += a.ss_in[(size_t)m * a.nss + p];
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) s += __shfl_xor(s, o);
+  return 1.0f / sqrtf(s / (float)a.K + a.eps);
+}
+
 template <int EPI, int NW>
 __device__ __forceinline__ const uint16_t* gemm_row(const GemmArgs& a, int t, int j, int c, int* head_out,
                                                     int* dim_out) {
@@ -174,15 +216,40 @@ __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
 
   const int S = a.K >> 6;   // 64-element chunks
   const int s0 = (S * wave) / KW, s1 = (S * (wave + 1)) / KW;
+
+  // folded RMSNorm: wave w owns tile rows w, w + KW, ...  One-tile launches
+  // load the rows' sum-of-squares partials before the weight stream so the
+  // loads overlap it; multi-tile launches load them afterwards.
+  constexpr int RPW = (16 * MT + KW - 1) / KW;   // rows per wave
+  constexpr int RPRE = MT == 1 ? RPW : 1;
+  const bool fold = a.ss_in != nullptr;
+  float4 ssv[RPRE];
+  if (MT == 1 && fold) {
+#pragma unroll
+    for (int r = 0; r < RPRE; ++r) ssv[r] = ss_part(a, blockIdx.y * 16 + wave + r * KW, r * KW + wave < 16, lane);
+  }
   f32x4 acc[MT][NW];
 #pragma unroll
   for (int r = 0; r < MT; ++r)
 #pragma unroll
     for (int j = 0; j < NW; ++j) acc[r][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (MT == 1) mfma_stream<NW, false>(xr[0], av_ok[0], wr, s0, s1, acc[0]);
+  // chunks per batch of loads (fewer for the two-matrix gate/up GEMM keeps
+  // its register count, and so the workgroups resident per CU, in check)
+  if (MT == 1) mfma_stream<NW, false, NW == 2 ? SSD_GEMM_U2 : SSD_GEMM_U1>(xr[0], av_ok[0], wr, s0, s1, acc[0]);
   else mfma_stream_mt<NW, MT>(xr, av_ok, wr, s0, s1, acc);
 
   __shared__ f32x4 red[KW - 1][MT][NW][64];
+  __shared__ float rs[16 * MT];
+  if (fold) {
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      const int row = r * KW + wave;
+      const int m = blockIdx.y * 16 * MT + row;
+      const float4 v = MT == 1 ? ssv[r < RPRE ? r : 0] : ss_part(a, m, row < 16 * MT, lane);
+      const float f = ss_rstd(a, m, row < 16 * MT, lane, v);
+      if (lane == 0 && row < 16 * MT) rs[row] = f;
+    }
+  }
   if (wave > 0) {
 #pragma unroll
     for (int r = 0; r < MT; ++r)
@@ -197,6 +264,17 @@ __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
     for (int r = 0; r < MT; ++r)
 #pragma unroll
       for (int j = 0; j < NW; ++j) acc[r][j] = acc[r][j] + red[w][r][j][lane];
+  if (fold) {
+    // rows of this lane's accumulators: 4*kg + i of each 16-row tile
+#pragma unroll
+    for (int r = 0; r < MT; ++r)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float f = rs[r * 16 + 4 * kg + i];
+#pragma unroll
+        for (int j = 0; j < NW; ++j) acc[r][j][i] *= f;
+      }
+  }
 
 #pragma unroll
   for (int r = 0; r < MT; ++r) {
@@ -235,6 +313,21 @@ __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
             a.amax_v[(size_t)m * gridDim.x + t] = bv;
             a.amax_i[(size_t)m * gridDim.x + t] = bi;
           }
+        }
+        if (EPI == EPI_RESID && a.ss_out) {
+          // new residual, its sum of squares over this tile's 16 columns and
+          // bf16(x * gain) for the GEMM that consumes it
+          const float xv = m < a.M ? a.y[(size_t)m * a.ldy + n] + acc[r][0][i] : 0.f;
+          float sq = xv * xv;
+#pragma unroll
+          for (int o = 1; o < 16; o <<= 1) sq += __shfl_xor(sq, o);
+          if (m < a.M) {
+            a.y[(size_t)m * a.ldy + n] = xv;
+            if (a.tap) ((uint16_t*)a.tap)[(size_t)m * a.ldtap + n] = f2bf(xv);
+            ((uint16_t*)a.xg_out)[(size_t)m * a.ldy + n] = f2bf(xv * bf2f(((const uint16_t*)a.gain_next)[n]));
+            if (c == 0) a.ss_out[(size_t)m * gridDim.x + t] = sq;
+          }
+          continue;
         }
         if (m >= a.M) continue;
         if (EPI == EPI_SWIGLU) epi_swiglu<uint16_t>(a, m, n, acc[r][0][i], acc[r][NW - 1][i]);
@@ -713,6 +806,12 @@ __global__ void copy_tokens_kernel(const int* src, int* dst, int n) {
 hipError_t launch_embed(int dtype, const int* tok, const void* E, float* x, int d, int M, hipStream_t s) {
   if (dtype) embed_kernel<uint16_t><<<M, 256, 0, s>>>(tok, (const uint16_t*)E, x, d);
   else embed_kernel<float><<<M, 256, 0, s>>>(tok, (const float*)E, x, d);
+  return hipGetLastError();
+}
+
+hipError_t launch_embed_norm(const int* tok, const void* E, float* x, int d, int M, const void* gain, void* xg,
+                             float* ss, hipStream_t s) {
+  embed_norm_kernel<<<M, 256, 0, s>>>(tok, (const uint16_t*)E, x, d, (const uint16_t*)gain, (uint16_t*)xg, ss);
   return hipGetLastError();
 }
 

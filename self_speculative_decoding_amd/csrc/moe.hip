@@ -166,7 +166,7 @@ __global__ __launch_bounds__(256) void moe_gemm_kernel(MoeArgs a) {
   f32x4 acc[NW];
 #pragma unroll
   for (int j = 0; j < NW; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  mfma_stream<NW, false>(xr, ok, wr, s0, s1, acc);
+  mfma_stream<NW, false, 4>(xr, ok, wr, s0, s1, acc);
 
   __shared__ f32x4 red[3][NW][64];
   if (wave > 0) {
@@ -193,15 +193,26 @@ __global__ __launch_bounds__(256) void moe_gemm_kernel(MoeArgs a) {
 }
 
 // x[m] += sum_j gate[m][j] * y[m][j] + sum_s y[m][top_k + s], in slot order.
+// A thread owns 16 consecutive columns; with ss_out set it also leaves their
+// sum of squares and bf16(x * gain_next) for the next layer's folded norm.
 __global__ __launch_bounds__(256) void moe_combine_kernel(MoeArgs a) {
   const int m = blockIdx.x;
   const int slots = a.top_k + a.n_shared;
   const float* y = a.slot_out + (size_t)m * slots * a.d;
-  for (int i = threadIdx.x; i < a.d; i += 256) {
-    float acc = 0.f;
-    for (int j = 0; j < a.top_k; ++j) acc += a.gates[(size_t)m * a.top_k + j] * y[(size_t)j * a.d + i];
-    for (int s = 0; s < a.n_shared; ++s) acc += y[(size_t)(a.top_k + s) * a.d + i];
-    a.resid[(size_t)m * a.d + i] += acc;
+  for (int c0 = threadIdx.x * 16; c0 < a.d; c0 += 256 * 16) {
+    float q = 0.f;
+    for (int i = c0; i < c0 + 16; ++i) {
+      float acc = 0.f;
+      for (int j = 0; j < a.top_k; ++j) acc += a.gates[(size_t)m * a.top_k + j] * y[(size_t)j * a.d + i];
+      for (int s = 0; s < a.n_shared; ++s) acc += y[(size_t)(a.top_k + s) * a.d + i];
+      const float xv = a.resid[(size_t)m * a.d + i] + acc;
+      a.resid[(size_t)m * a.d + i] = xv;
+      if (a.ss_out) {
+        q = fmaf(xv, xv, q);
+        ((uint16_t*)a.xg_out)[(size_t)m * a.d + i] = f2bf(xv * bf2f(((const uint16_t*)a.gain_next)[i]));
+      }
+    }
+    if (a.ss_out) a.ss_out[(size_t)m * (a.d / 16) + c0 / 16] = q;
   }
 }
 

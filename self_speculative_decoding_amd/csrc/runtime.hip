@@ -78,7 +78,7 @@ struct ssd_ctx {
   bool trace_on = false;   // record the residual after every layer of decode-loop passes
   float* trace = nullptr;
   // device views
-  float *x, *logits, *part_o, *part_ml, *cos_t, *sin_t, *amax_v;
+  float *x, *ss, *logits, *part_o, *part_ml, *cos_t, *sin_t, *amax_v;
   int* amax_i;
   void *xn, *q, *att, *act, *kc, *vc, *tap, *feat;
   int *counters, *block, *post, *toks, *dstate, *result, *outlog;
@@ -106,23 +106,51 @@ MoeArgs moe_args(ssd_ctx* c, int l, int M) {
   return a;
 }
 
+// bf16 models fold every RMSNorm that feeds a dense GEMM (QKV, gate/up, LM
+// head) into that GEMM: the residual's producer leaves xn = bf16(x * gain) and
+// per-16-column sums of squares in ss, and the GEMM scales its product by
+// 1/rms.  The MoE feed-forward keeps a standalone norm (router and experts
+// share its output).
+void fold_in(ssd_ctx* c, GemmArgs& a, int row0) {
+  const int d = c->cfg.d_model;
+  a.ss_in = c->ss + (size_t)row0 * (d / 16);
+  a.nss = d / 16;
+  a.eps = c->cfg.rms_eps;
+}
+
+void fold_out(ssd_ctx* c, GemmArgs& a, const void* gain_next) {
+  a.ss_out = c->ss;
+  a.xg_out = c->xn;
+  a.gain_next = gain_next;
+}
+
+// Gain of the norm that follows layer l in this pass: attn_norm of the next
+// layer that runs, else the final norm.
+const void* next_gain(ssd_ctx* c, int l, const uint8_t* skip) {
+  for (int j = l + 1; j < c->cfg.n_layers; ++j)
+    if (!(skip && skip[j])) return c->L[j].attn_norm;
+  return c->final_norm;
+}
+
 // One decoder layer over M rows at positions state[0] + pos_off + r.
-ssd_status layer_forward(ssd_ctx* c, int l, int M, int pos_off, bool feats) {
+ssd_status layer_forward(ssd_ctx* c, int l, int M, int pos_off, bool feats, const void* gain_next) {
   const ssd_cfg& g = c->cfg;
   const LayerW& w = c->L[l];
   const int d = g.d_model, hq = g.n_q_heads, hkv = g.n_kv_heads, hd = g.head_dim;
   const int dt = g.dtype;
+  const bool fold = dt == SSD_BF16;
   hipStream_t s = c->stream;
   void* kc = (char*)c->kc + (size_t)l * cache_layer_elems(g) * c->esz;
   void* vc = (char*)c->vc + (size_t)l * cache_layer_elems(g) * c->esz;
 
-  HIPCHK(launch_rmsnorm(dt, c->x, d, w.attn_norm, c->xn, d, d, g.rms_eps, M, s));
+  if (!fold) HIPCHK(launch_rmsnorm(dt, c->x, d, w.attn_norm, c->xn, d, d, g.rms_eps, M, s));
   {
     GemmArgs a{};
     a.X = c->xn; a.ldx = d; a.W0 = w.wq; a.W1 = w.wk; a.W2 = w.wv;
     a.n0 = hq * hd; a.n1 = hkv * hd; a.M = M; a.N = (hq + 2 * hkv) * hd; a.K = d;
     a.q = c->q; a.kc = kc; a.vc = vc; a.cos_t = c->cos_t; a.sin_t = c->sin_t;
     a.state = c->dstate; a.pos_off = pos_off; a.hq = hq; a.hkv = hkv; a.hd = hd; a.max_ctx = g.max_ctx;
+    if (fold) fold_in(c, a, 0);
     HIPCHK(launch_gemm(dt, EPI_QKV, a, s));
   }
   {
@@ -139,15 +167,20 @@ ssd_status layer_forward(ssd_ctx* c, int l, int M, int pos_off, bool feats) {
   {
     GemmArgs a{};
     a.X = c->att; a.ldx = hq * hd; a.W0 = w.wo; a.M = M; a.N = d; a.K = hq * hd; a.y = c->x; a.ldy = d;
+    if (fold && !w.moe) fold_out(c, a, w.ffn_norm);
     HIPCHK(launch_gemm(dt, EPI_RESID, a, s));
   }
-  HIPCHK(launch_rmsnorm(dt, c->x, d, w.ffn_norm, c->xn, d, d, g.rms_eps, M, s));
   if (w.moe) {
-    const MoeArgs a = moe_args(c, l, M);    HIPCHK(launch_moe(dt, a, s));
+    HIPCHK(launch_rmsnorm(dt, c->x, d, w.ffn_norm, c->xn, d, d, g.rms_eps, M, s));
+    MoeArgs a = moe_args(c, l, M);
+    a.ss_out = c->ss; a.xg_out = c->xn; a.gain_next = gain_next;
+    HIPCHK(launch_moe(dt, a, s));
   } else {
+    if (!fold) HIPCHK(launch_rmsnorm(dt, c->x, d, w.ffn_norm, c->xn, d, d, g.rms_eps, M, s));
     GemmArgs a{};
     a.X = c->xn; a.ldx = d; a.W0 = w.w_gate; a.W1 = w.w_up; a.M = M; a.N = w.ffn; a.K = d;
     a.out = c->act; a.ldo = w.ffn;
+    if (fold) fold_in(c, a, 0);
     HIPCHK(launch_gemm(dt, EPI_SWIGLU, a, s));
     GemmArgs b{};
     b.X = c->act; b.ldx = w.ffn; b.W0 = w.w_down; b.M = M; b.N = d; b.K = w.ffn; b.y = c->x; b.ldy = d;
@@ -155,6 +188,7 @@ ssd_status layer_forward(ssd_ctx* c, int l, int M, int pos_off, bool feats) {
       b.tap = (char*)c->tap + (size_t)w.feat_slot * d * c->esz;
       b.ldtap = g.n_feat * d;
     }
+    if (fold) fold_out(c, b, gain_next);
     HIPCHK(launch_gemm(dt, EPI_RESID, b, s));
   }
   if (c->trace_on && M <= g.max_block)
@@ -169,21 +203,26 @@ ssd_status run_pass(ssd_ctx* c, const int* d_tok, int M, int pos_off, const uint
                     int head_rows, int* d_arg, bool feats) {
   const ssd_cfg& g = c->cfg;
   const int d = g.d_model, dt = g.dtype;
+  const bool fold = dt == SSD_BF16;
   hipStream_t s = c->stream;
   if (c->moe_inject && M > c->moe_inject)
     return fail(SSD_E_ARG, "pass of %d rows but routing was injected for %d", M, c->moe_inject);
-  HIPCHK(launch_embed(dt, d_tok, c->embed, c->x, d, M, s));
+  if (fold) HIPCHK(launch_embed_norm(d_tok, c->embed, c->x, d, M, next_gain(c, -1, skip), c->xn, c->ss, s));
+  else HIPCHK(launch_embed(dt, d_tok, c->embed, c->x, d, M, s));
   for (int l = 0; l < g.n_layers; ++l) {
     if (skip && skip[l]) continue;
-    SSDCHK(layer_forward(c, l, M, pos_off, feats));
+    SSDCHK(layer_forward(c, l, M, pos_off, feats, next_gain(c, l, skip)));
   }
   if (head_rows > 0) {
-    HIPCHK(launch_rmsnorm(dt, c->x + (size_t)head_row0 * d, d, c->final_norm, c->xn, d, d, g.rms_eps, head_rows, s));
+    if (!fold)
+      HIPCHK(launch_rmsnorm(dt, c->x + (size_t)head_row0 * d, d, c->final_norm, c->xn, d, d, g.rms_eps, head_rows, s));
     GemmArgs a{};
-    a.X = c->xn; a.ldx = d; a.W0 = c->lm_head; a.M = head_rows; a.N = g.vocab; a.K = d;
+    a.X = fold ? (const void*)((const uint16_t*)c->xn + (size_t)head_row0 * d) : c->xn;
+    a.ldx = d; a.W0 = c->lm_head; a.M = head_rows; a.N = g.vocab; a.K = d;
     a.y = c->logits; a.ldy = g.vocab;
     if (dt == SSD_BF16) {
       // the LM head epilogue leaves (max, index) per 16 columns; reduce those
+      fold_in(c, a, head_row0);
       a.amax_v = c->amax_v; a.amax_i = c->amax_i;
       HIPCHK(launch_gemm(dt, EPI_LOGITS, a, s));
       HIPCHK(launch_argmax_tiles(c->amax_v, c->amax_i, g.vocab / 16, d_arg, head_rows, s));
@@ -375,7 +414,7 @@ ssd_status ssd_load(const ssd_cfg* cfg, const ssd_buf* weights, int32_t n_weight
   c->fc = cfg->n_feat > 0 ? weights[wi++].ptr : nullptr;
 
   c->kc = at(c, lay.kc); c->vc = at(c, lay.vc);
-  c->x = (float*)at(c, lay.x); c->xn = at(c, lay.xn); c->q = at(c, lay.q); c->att = at(c, lay.att);
+  c->x = (float*)at(c, lay.x); c->ss = (float*)at(c, lay.ss); c->xn = at(c, lay.xn); c->q = at(c, lay.q); c->att = at(c, lay.att);
   c->act = at(c, lay.act); c->logits = (float*)at(c, lay.logits);
   c->amax_v = (float*)at(c, lay.amax_v); c->amax_i = (int*)at(c, lay.amax_i);
   c->trace = (float*)at(c, lay.trace);
@@ -801,6 +840,9 @@ ssd_status ssd_time_op(ssd_ctx* c, int32_t op, int32_t layer, int32_t m, int32_t
       at.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)hd));
       HIPCHK(launch_attention(dt, at, (c->n + m + ATT_PT - 1) / ATT_PT, s));
     } else {
+      // bf16 GEMMs carry their folded-norm work as in a pass
+      if (dt == SSD_BF16 && (op == 0 || op == 2 || op == 4)) fold_in(c, a, 0);
+      if (dt == SSD_BF16 && (op == 1 || op == 3)) fold_out(c, a, w.ffn_norm);
       HIPCHK(launch_gemm(dt, epi, a, s));
     }
   }
