@@ -8,12 +8,27 @@
 // the lossless check; mlx-dflash README: bit-for-bit parity with greedy).
 #include "device.h"
 
-// load-batch depth (64-element chunks) of the decode GEMMs; build-time tuning
+// Build-time tuning of the decode GEMMs: load-batch depth in 64-element
+// chunks (U1 one-matrix, U2 gate/up; the batch depth does not change the
+// accumulation order) and waves per workgroup (gate/up; other
+// GEMMs with fewer than 1024 column tiles; wider GEMMs such as the LM head).
 #ifndef SSD_GEMM_U1
 #define SSD_GEMM_U1 4
 #endif
 #ifndef SSD_GEMM_U2
 #define SSD_GEMM_U2 2
+#endif
+#ifndef SSD_GEMM_U1_LONGK   // one-matrix GEMMs with K >= 8192 (the FFN down projection)
+#define SSD_GEMM_U1_LONGK 2
+#endif
+#ifndef SSD_KW_SWIGLU
+#define SSD_KW_SWIGLU 8
+#endif
+#ifndef SSD_KW_NARROW
+#define SSD_KW_NARROW 8
+#endif
+#ifndef SSD_KW_WIDE
+#define SSD_KW_WIDE 4
 #endif
 
 namespace ssd {
@@ -120,9 +135,9 @@ __device__ __forceinline__ void epi_swiglu(const GemmArgs& a, int m, int n, floa
 
 // (v0, v1) are dims (i, i + hd/2) of output head `head` of [q | k | v]
 template <typename E>
-__device__ __forceinline__ void epi_qkv_pair(const GemmArgs& a, int m, int head, int i, float v0, float v1) {
+__device__ __forceinline__ void epi_qkv_pair(const GemmArgs& a, int base, int m, int head, int i, float v0, float v1) {
   const int half = a.hd >> 1;
-  const int pos = a.state[0] + a.pos_off + m;
+  const int pos = base + m;
   if (head < a.hq + a.hkv) {
     const float c = a.cos_t[(size_t)pos * half + i], s = a.sin_t[(size_t)pos * half + i];
     const float o0 = v0 * c - v1 * s, o1 = v1 * c + v0 * s;
@@ -138,8 +153,8 @@ __device__ __forceinline__ void epi_qkv_pair(const GemmArgs& a, int m, int head,
 }
 
 template <typename E>
-__device__ __forceinline__ void epi_v_single(const GemmArgs& a, int m, int vh, int dim, float v) {
-  const int pos = a.state[0] + a.pos_off + m;
+__device__ __forceinline__ void epi_v_single(const GemmArgs& a, int base, int m, int vh, int dim, float v) {
+  const int pos = base + m;
   ((E*)a.vc)[((size_t)vh * a.max_ctx + pos) * a.hd + dim] = fromf<E>(v);
 }
 
@@ -217,6 +232,19 @@ __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
   const int S = a.K >> 6;   // 64-element chunks
   const int s0 = (S * wave) / KW, s1 = (S * (wave + 1)) / KW;
 
+  // Epilogue inputs fetched before the weight stream so that their latency
+  // hides behind it: the position base (QKV) and, for one-tile launches, the
+  // residual entries wave 0 will update.
+  const int base = EPI == EPI_QKV ? a.state[0] + a.pos_off : 0;
+  float yv[4] = {0.f, 0.f, 0.f, 0.f};
+  if (EPI == EPI_RESID && MT == 1 && wave == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = blockIdx.y * 16 + 4 * kg + i;
+      if (m < a.M) yv[i] = a.y[(size_t)m * a.ldy + t * 16 + c];
+    }
+  }
+
   // folded RMSNorm: wave w owns tile rows w, w + KW, ...  One-tile launches
   // load the rows' sum-of-squares partials before the weight stream so the
   // loads overlap it; multi-tile launches load them afterwards.
@@ -235,7 +263,10 @@ __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
     for (int j = 0; j < NW; ++j) acc[r][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   // chunks per batch of loads (fewer for the two-matrix gate/up GEMM keeps
   // its register count, and so the workgroups resident per CU, in check)
-  if (MT == 1) mfma_stream<NW, false, NW == 2 ? SSD_GEMM_U2 : SSD_GEMM_U1>(xr[0], av_ok[0], wr, s0, s1, acc[0]);
+  if (MT == 1 && NW == 1 && a.K >= 8192)
+    mfma_stream<NW, false, SSD_GEMM_U1_LONGK>(xr[0], av_ok[0], wr, s0, s1, acc[0]);
+  else if (MT == 1)
+    mfma_stream<NW, false, NW == 2 ? SSD_GEMM_U2 : SSD_GEMM_U1>(xr[0], av_ok[0], wr, s0, s1, acc[0]);
   else mfma_stream_mt<NW, MT>(xr, av_ok, wr, s0, s1, acc);
 
   __shared__ f32x4 red[KW - 1][MT][NW][64];
@@ -289,9 +320,9 @@ __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
         const int m = mt * 16 + 4 * kg + i;
         if (m >= a.M) continue;
         if (rot) {
-          if (c < 8) epi_qkv_pair<uint16_t>(a, m, head, dim, acc[r][0][i], part[i]);
+          if (c < 8) epi_qkv_pair<uint16_t>(a, base, m, head, dim, acc[r][0][i], part[i]);
         } else {
-          epi_v_single<uint16_t>(a, m, head - a.hq - a.hkv, dim, acc[r][0][i]);
+          epi_v_single<uint16_t>(a, base, m, head - a.hq - a.hkv, dim, acc[r][0][i]);
         }
       }
     } else {
@@ -317,7 +348,7 @@ __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
         if (EPI == EPI_RESID && a.ss_out) {
           // new residual, its sum of squares over this tile's 16 columns and
           // bf16(x * gain) for the GEMM that consumes it
-          const float xv = m < a.M ? a.y[(size_t)m * a.ldy + n] + acc[r][0][i] : 0.f;
+          const float xv = m < a.M ? (MT == 1 ? yv[i] : a.y[(size_t)m * a.ldy + n]) + acc[r][0][i] : 0.f;
           float sq = xv * xv;
 #pragma unroll
           for (int o = 1; o < 16; o <<= 1) sq += __shfl_xor(sq, o);
@@ -331,7 +362,11 @@ __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
         }
         if (m >= a.M) continue;
         if (EPI == EPI_SWIGLU) epi_swiglu<uint16_t>(a, m, n, acc[r][0][i], acc[r][NW - 1][i]);
-        else epi_single<uint16_t>(a, EPI, m, n, acc[r][0][i]);
+        else if (EPI == EPI_RESID && MT == 1) {
+          const float xv = yv[i] + acc[r][0][i];
+          a.y[(size_t)m * a.ldy + n] = xv;
+          if (a.tap) ((uint16_t*)a.tap)[(size_t)m * a.ldtap + n] = f2bf(xv);
+        } else epi_single<uint16_t>(a, EPI, m, n, acc[r][0][i]);
       }
     }
   }
@@ -387,7 +422,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
     s0 = wave_sum(s0);
     s1 = wave_sum(s1);
     if (lane == 0) {
-      if (EPI == EPI_QKV) epi_qkv_pair<float>(a, m, head, i, s0, s1);
+      if (EPI == EPI_QKV) epi_qkv_pair<float>(a, a.state[0] + a.pos_off, m, head, i, s0, s1);
       else if (EPI == EPI_SWIGLU) epi_swiglu<float>(a, m, pi, s0, s1);
       else {
         epi_single<float>(a, EPI, m, 2 * pi, s0);
@@ -531,47 +566,69 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
   const int p = blockIdx.x, kvh = blockIdx.y, mt = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 15, kg = lane >> 4;
-  const int base = a.state[0] + a.pos_off;
+  const int st0 = a.state[0];   // position load issued first, used late
   const int row0 = mt * ROW_TILE;
   const int nrows = min(ROW_TILE, a.M - row0);
   const int key0 = p * PT;
-  const int maxpos = base + row0 + nrows - 1;
-  if (key0 > maxpos) return;   // whole workgroup: no row reaches this partition
-  const uint4 zero = {0u, 0u, 0u, 0u};
 
-  // V tile, transposed into LDS (keys past the last row's position read as 0)
-  const uint16_t* vb = (const uint16_t*)a.vc + ((size_t)kvh * a.max_ctx + key0) * HD;
-  for (int e = tid; e < PT * HD / 8; e += 256) {
-    const int key = e / (HD / 8), d0 = (e % (HD / 8)) * 8;
-    uint4 v = key0 + key <= maxpos ? *(const uint4*)(vb + (size_t)key * HD + d0) : zero;
-    const uint16_t* pv = (const uint16_t*)&v;
+  // Every global load of the workgroup is issued up front and unconditionally
+  // (addresses clamped into the cache), before the position is known: the V
+  // tile (into registers, transposed into LDS after S), the Q fragments and
+  // the K fragments.  There is no early exit: a workgroup past every row's
+  // position runs through and stores nothing, so the loads never wait for
+  // the position.  Keys past the last row's position are masked after.
+  const uint16_t* vb = (const uint16_t*)a.vc + (size_t)kvh * a.max_ctx * HD;
+  constexpr int VL = PT * HD / 8 / 256;   // uint4 pieces of V per thread
+  uint4 vv[VL];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) Vt[d0 + j][key] = pv[j];
+  for (int i = 0; i < VL; ++i) {
+    const int e = tid + 256 * i, key = min(key0 + e / (HD / 8), a.max_ctx - 1), d0 = (e % (HD / 8)) * 8;
+    vv[i] = *(const uint4*)(vb + (size_t)key * HD + d0);
   }
-
-  // S = Q . K^T for this wave's 16 query vectors x 64 keys
   const int QV = nrows * G;
   const int qi = wave * 16 + c;
   const bool qv = qi < QV;
   const int qr = qi / G, qg = qi % G;
   const uint16_t* qp = (const uint16_t*)a.q + (size_t)(row0 + (qv ? qr : 0)) * a.hq * HD +
-                       (size_t)(kvh * G + qg) * HD + kg * 8;
+                       (size_t)(kvh * G + (qv ? qg : 0)) * HD + kg * 8;
   uint4 qa[4];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) qa[ks] = qv ? *(const uint4*)(qp + ks * 32) : zero;
-  const uint16_t* kb = (const uint16_t*)a.kc + ((size_t)kvh * a.max_ctx + key0) * HD + kg * 8;
+  for (int ks = 0; ks < 4; ++ks) qa[ks] = *(const uint4*)(qp + ks * 32);
+  const uint16_t* kb = (const uint16_t*)a.kc + (size_t)kvh * a.max_ctx * HD + kg * 8;
+  uint4 kf[4][4];
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) {
+    const int key = min(key0 + kt * 16 + c, a.max_ctx - 1);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) kf[kt][ks] = *(const uint4*)(kb + (size_t)key * HD + ks * 32);
+  }
+  const int base = st0 + a.pos_off;
+  const int maxpos = base + row0 + nrows - 1;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    qa[ks].x = qv ? qa[ks].x : 0u;
+    qa[ks].y = qv ? qa[ks].y : 0u;
+    qa[ks].z = qv ? qa[ks].z : 0u;
+    qa[ks].w = qv ? qa[ks].w : 0u;
+  }
+#pragma unroll
+  for (int i = 0; i < VL; ++i) {
+    const bool keep = key0 + (tid + 256 * i) / (HD / 8) <= maxpos;   // P is 0 past it; keep 0 * V finite
+    vv[i].x = keep ? vv[i].x : 0u;
+    vv[i].y = keep ? vv[i].y : 0u;
+    vv[i].z = keep ? vv[i].z : 0u;
+    vv[i].w = keep ? vv[i].w : 0u;
+  }
+
+  // S = Q . K^T for this wave's 16 query vectors x 64 keys
   f32x4 s[4];
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt) {
     s[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int key = kt * 16 + c;
-    const bool kv = key0 + key <= maxpos;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const uint4 kf = kv ? *(const uint4*)(kb + (size_t)key * HD + ks * 32) : zero;
+    for (int ks = 0; ks < 4; ++ks)
       s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[ks]),
-                                                      __builtin_bit_cast(bf16x8, kf), s[kt], 0, 0, 0);
-    }
+                                                      __builtin_bit_cast(bf16x8, kf[kt][ks]), s[kt], 0, 0, 0);
   }
   // lane holds S[query 4*kg+i][key kt*16+c]
   float mx[4], l[4];
@@ -605,6 +662,13 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
     for (int o = 1; o < 16; o <<= 1) sum += __shfl_xor(sum, o);
     l[i] = sum;
+  }
+#pragma unroll
+  for (int i = 0; i < VL; ++i) {
+    const int e = tid + 256 * i, key = e / (HD / 8), d0 = (e % (HD / 8)) * 8;
+    const uint32_t wds[4] = {vv[i].x, vv[i].y, vv[i].z, vv[i].w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) Vt[d0 + j][key] = (uint16_t)(wds[j >> 1] >> (16 * (j & 1)));
   }
   __syncthreads();
 
@@ -643,36 +707,46 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
 
 // Combine of the attention partitions: one workgroup per (row, head), one
 // lane per head dim.  Row r at position pos uses partitions 0..pos/PT, added
-// in partition order with weights exp2(m_p - max m).
+// in partition order with weights exp2(m_p - max m).  The partial outputs are
+// loaded (up to 32 at a time) together with the (m, l) pairs.
 template <typename E>
 __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
+  constexpr int B = 32;
   __shared__ float sm[128], sl[128];
   const int row = blockIdx.x, head = blockIdx.y, t = threadIdx.x;
-  const int pos = a.state[0] + a.pos_off + row;
-  const int np = pos / ATT_PT + 1;
-  if (t < np) {
-    const float* pm = a.part_ml + (((size_t)t * a.R + row) * a.hq + head) * 2;
+  const int st0 = a.state[0];   // position load issued first, used late
+  const int npmax = (a.max_ctx + ATT_PT - 1) / ATT_PT;   // partitions allocated
+  const size_t stride = (size_t)a.R * a.hq * a.hd;
+  const float* po = a.part_o + ((size_t)row * a.hq + head) * a.hd + (t < a.hd ? t : 0);
+  // first loads issued unconditionally (indexes clamped to the allocation)
+  // before the position is known
+  float v[B];
+#pragma unroll
+  for (int j = 0; j < B; ++j) v[j] = po[(size_t)min(j, npmax - 1) * stride];
+  const float* pm = a.part_ml + (((size_t)min(t, npmax - 1) * a.R + row) * a.hq + head) * 2;
+  if (t < npmax) {   // entries past the row's partitions are never read
     sm[t] = pm[0];
     sl[t] = pm[1];
   }
+  const int pos = st0 + a.pos_off + row;
+  const int np = pos / ATT_PT + 1;
   __syncthreads();
   float M = -INFINITY;
   for (int pp = 0; pp < np; ++pp) M = fmaxf(M, sm[pp]);
   float L = 0.f;
   for (int pp = 0; pp < np; ++pp) L += exp2f(sm[pp] - M) * sl[pp];
   if (t >= a.hd) return;
-  const size_t stride = (size_t)a.R * a.hq * a.hd;
-  const float* po = a.part_o + ((size_t)row * a.hq + head) * a.hd + t;
   float acc = 0.f;
-  int pp = 0;
-  for (; pp + 8 <= np; pp += 8) {
-    float v[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = po[(size_t)(pp + j) * stride];
+  for (int j = 0; j < B; ++j)
+    if (j < np) acc += exp2f(sm[j] - M) * v[j];
+  for (int p0 = B; p0 < np; p0 += B) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc += exp2f(sm[pp + j] - M) * v[j];
+    for (int j = 0; j < B; ++j) v[j] = p0 + j < np ? po[(size_t)(p0 + j) * stride] : 0.f;
+#pragma unroll
+    for (int j = 0; j < B; ++j)
+      if (p0 + j < np) acc += exp2f(sm[p0 + j] - M) * v[j];
   }
-  for (; pp < np; ++pp) acc += exp2f(sm[pp] - M) * po[(size_t)pp * stride];
   ((E*)a.out)[(size_t)row * a.hq * a.hd + (size_t)head * a.hd + t] = fromf<E>(acc / L);
 }
 
@@ -835,19 +909,19 @@ hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t s) {
     // passes (prefill chunks) let 4 row tiles share each weight load
     const bool multi = a.M > 32;
     const dim3 grid_mt(tiles, (a.M + 63) / 64);
-#define SSD_G(E, NW)                                                                 \
-  case E:                                                                            \
-    if (multi) gemm_bf16_kernel<E, NW, 4, 4><<<grid_mt, 256, 0, s>>>(a);             \
-    else if (wide) gemm_bf16_kernel<E, NW, 4, 1><<<grid, 256, 0, s>>>(a);            \
-    else gemm_bf16_kernel<E, NW, 8, 1><<<grid, 512, 0, s>>>(a);                      \
+#define SSD_G(E, NW, KWN)                                                                         \
+  case E:                                                                                         \
+    if (multi) gemm_bf16_kernel<E, NW, 4, 4><<<grid_mt, 256, 0, s>>>(a);                          \
+    else if (wide) gemm_bf16_kernel<E, NW, SSD_KW_WIDE, 1><<<grid, 64 * SSD_KW_WIDE, 0, s>>>(a);   \
+    else gemm_bf16_kernel<E, NW, KWN, 1><<<grid, 64 * KWN, 0, s>>>(a);                            \
     break;
     switch (epi) {
-      SSD_G(EPI_F32, 1)
-      SSD_G(EPI_LOGITS, 1)
-      SSD_G(EPI_RESID, 1)
-      SSD_G(EPI_SWIGLU, 2)
-      SSD_G(EPI_QKV, 1)
-      SSD_G(EPI_STORE, 1)
+      SSD_G(EPI_F32, 1, SSD_KW_NARROW)
+      SSD_G(EPI_LOGITS, 1, SSD_KW_NARROW)
+      SSD_G(EPI_RESID, 1, SSD_KW_NARROW)
+      SSD_G(EPI_SWIGLU, 2, SSD_KW_SWIGLU)
+      SSD_G(EPI_QKV, 1, SSD_KW_NARROW)
+      SSD_G(EPI_STORE, 1, SSD_KW_NARROW)
       default: return hipErrorInvalidValue;
     }
 #undef SSD_G

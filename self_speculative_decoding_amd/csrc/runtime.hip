@@ -75,6 +75,7 @@ struct ssd_ctx {
   std::map<std::string, GraphEntry> graphs;
   bool use_graphs = true;
   bool capturing = false;
+  int cap_part = 0;        // attention partitions of the pass being captured
   bool trace_on = false;   // record the residual after every layer of decode-loop passes
   float* trace = nullptr;
   // device views
@@ -88,6 +89,8 @@ struct ssd_ctx {
 };
 
 namespace {
+
+constexpr int kCtxBucket = 512;   // positions per graph context bucket (multiple of ATT_PT)
 
 inline void* at(ssd_ctx* c, size_t off) { return c->ws + off; }
 
@@ -159,9 +162,9 @@ ssd_status layer_forward(ssd_ctx* c, int l, int M, int pos_off, bool feats, cons
     a.counters = c->counters; a.state = c->dstate; a.pos_off = pos_off; a.M = M; a.R = c->lay.R;
     a.hq = hq; a.hkv = hkv; a.hd = hd; a.max_ctx = g.max_ctx;
     a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)hd));
-    // a captured pass covers every partition up to max_ctx; workgroups past
-    // the last row's position exit at once
-    const int n_part = c->capturing ? c->lay.n_part : (c->n + pos_off + M + ATT_PT - 1) / ATT_PT;
+    // a captured pass covers the partitions of its context bucket; workgroups
+    // past the last row's position store nothing
+    const int n_part = c->capturing ? c->cap_part : (c->n + pos_off + M + ATT_PT - 1) / ATT_PT;
     HIPCHK(launch_attention(dt, a, n_part, s));
   }
   {
@@ -255,14 +258,19 @@ void destroy_graphs(ssd_ctx* c) {
 // read from device state, so one graph serves every context length.
 ssd_status decode_pass(ssd_ctx* c, const int* tok, int M, int pos_off, const uint8_t* skip, int* arg, bool feats) {
   if (!c->use_graphs) return run_pass(c, tok, M, pos_off, skip, 0, M, arg, feats);
+  // Graphs are keyed by the context bucket (kCtxBucket positions) holding
+  // the pass's last row: the attention grid covers that bucket, so a replay
+  // never launches more than one bucket's worth of idle partitions.
+  const int bucket = (c->n + pos_off + M + kCtxBucket - 1) / kCtxBucket;
   std::string key;
   key.reserve(64 + c->cfg.n_layers);
-  const intptr_t parts[5] = {M, pos_off, (intptr_t)tok, (intptr_t)arg, feats ? 1 : 0};
+  const intptr_t parts[6] = {M, pos_off, (intptr_t)tok, (intptr_t)arg, feats ? 1 : 0, bucket};
   key.append((const char*)parts, sizeof parts);
   if (skip) key.append((const char*)skip, c->cfg.n_layers);
   auto it = c->graphs.find(key);
   if (it == c->graphs.end()) {
     GraphEntry ge{};
+    c->cap_part = std::min(c->lay.n_part, bucket * kCtxBucket / ATT_PT);
     HIPCHK(hipStreamBeginCapture(c->stream, hipStreamCaptureModeThreadLocal));
     c->capturing = true;
     const ssd_status st = run_pass(c, tok, M, pos_off, skip, 0, M, arg, feats);
