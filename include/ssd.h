@@ -109,8 +109,15 @@ ssd_status ssd_validate_cfg(const ssd_cfg* cfg);
 int32_t ssd_n_weights(const ssd_cfg* cfg);
 int64_t ssd_weight_numel(const ssd_cfg* cfg, int32_t i);
 
+/* 1 if the context reads weight tensor i after ssd_load returns, 0 if the
+ * caller may free it then, -1 for an invalid cfg or index.  bf16 models copy
+ * every matrix (all but embed and the norm gains) into the workspace at load,
+ * in the tile order their GEMMs stream; float32 models keep every buffer. */
+int32_t ssd_weight_retained(const ssd_cfg* cfg, int32_t i);
+
 /* Device workspace size in bytes (KV cache, activations, partial results,
- * rotary tables, token buffers) for cfg; -1 if cfg is invalid. */
+ * rotary tables, token buffers and, for bf16 models, the packed copy of the
+ * weight matrices) for cfg; -1 if cfg is invalid. */
 int64_t ssd_workspace_bytes(const ssd_cfg* cfg);
 
 /* Skip mask of the naive layer-skip draft (MLX layer-skip blog, "Code"):
@@ -131,7 +138,10 @@ typedef struct ssd_ctx ssd_ctx;
 /* Binds weights (device buffers, canonical order, n_weights of them, sizes
  * checked) and a device workspace of at least ssd_workspace_bytes(cfg) bytes,
  * 256-byte aligned.  hip_stream: a hipStream_t (NULL = the null stream).
- * Clears the KV cache.  *out receives the context (free with ssd_free). */
+ * Clears the KV cache; for bf16 models packs the weight matrices into the
+ * workspace (synchronously) after which the buffers ssd_weight_retained
+ * reports as 0 are no longer read.  *out receives the context (free with
+ * ssd_free). */
 ssd_status ssd_load(const ssd_cfg* cfg, const ssd_buf* weights, int32_t n_weights,
                     ssd_buf workspace, void* hip_stream, ssd_ctx** out);
 void ssd_free(ssd_ctx* ctx);

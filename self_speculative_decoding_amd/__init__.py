@@ -21,7 +21,7 @@ ST_LOADED, ST_READY, ST_DRAFTED, ST_VERIFIED = range(4)
 OP_PREFILL, OP_DRAFT, OP_VERIFY, OP_VERIFY_BLOCK, OP_ACCEPT, OP_RESET = range(6)
 OPS = dict(gate_up=0, down=1, qkv=2, o=3, lm_head=4, attention=5, moe=6, read_probe=7, copy_probe=8)
 
-EXPORTS = ["ssd_validate_cfg", "ssd_n_weights", "ssd_weight_numel", "ssd_workspace_bytes",
+EXPORTS = ["ssd_validate_cfg", "ssd_n_weights", "ssd_weight_numel", "ssd_weight_retained", "ssd_workspace_bytes",
            "ssd_skip_mask", "ssd_check_transition", "ssd_strerror", "ssd_last_error",
            "ssd_load", "ssd_free", "ssd_reset", "ssd_state", "ssd_context_length",
            "ssd_prefill", "ssd_draft", "ssd_verify", "ssd_accept_rollback", "ssd_generate",
@@ -73,6 +73,7 @@ def _load():
         "ssd_validate_cfg": (I32, [pc]),
         "ssd_n_weights": (I32, [pc]),
         "ssd_weight_numel": (I64, [pc, I32]),
+        "ssd_weight_retained": (I32, [pc, I32]),
         "ssd_workspace_bytes": (I64, [pc]),
         "ssd_skip_mask": (I32, [I32, ctypes.c_double, VP]),
         "ssd_check_transition": (I32, [I32, I32, P(I32)]),
@@ -202,6 +203,10 @@ class Engine:
         _check(lib.ssd_load(ctypes.byref(cfg), bufs, len(weights), Buf(self._ws.data_ptr(), nb),
                             ctypes.c_void_p(self.stream.cuda_stream), ctypes.byref(ctx)))
         self.ctx = ctx
+        # matrices the library copied into its packed layout are not read again
+        for i in range(len(self._w)):
+            if lib.ssd_weight_retained(ctypes.byref(cfg), i) == 0:
+                self._w[i] = None
         self.L, self.V, self.d = cfg.n_layers, cfg.vocab, cfg.d_model
 
     def close(self):

@@ -35,23 +35,36 @@ __device__ __forceinline__ float wave_sum(float v) {   // fixed butterfly, same 
 __device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *(const uint4*)p; }
 
 // Weights are read once per pass: nontemporal loads stream them without
-// allocating in the caches (measured: 7.1 vs 6.3 TB/s for a plain read).
+// allocating in the caches.
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 ld16_nt(const uint16_t* p) {
   const u32x4 t = __builtin_nontemporal_load((const u32x4*)p);
   return uint4{t[0], t[1], t[2], t[3]};
 }
 
+// Packed weight tiles.  A bf16 GEMM weight [N, K] is stored as tiles of 16
+// rows (output columns) x 64 K-elements, 1024 elements = 2 KB each, the tiles
+// of one row tile consecutive in K.  Inside a tile, element (row c, k) with
+// k = 16g + 8h + j (g < 4, h < 2, j < 8) sits at h*512 + (16g + c)*8 + j: lane
+// l = 16g + c of a wave reads its MFMA B fragment for K-step h as the 16 bytes
+// at h*512 + 8l, so each load instruction of a wave reads 1 KB contiguous.
+// The gate and up matrices of a SwiGLU are interleaved tile by tile (gate
+// chunk s, up chunk s, gate chunk s+1, ...) so one wave streams one region.
+constexpr int PACK_TILE = 1024;   // elements per packed tile
+
 // One wave's share of a 16-row x (NW x 16)-column MFMA tile: K-chunks
 // [c0, c1) of 64 elements, accumulated in order.  In each chunk lane group g
-// (lane/16) reads 32 contiguous bytes (elements 16g..16g+15) of its A row
-// and its weight rows, so the four groups cover every 128-byte line of a row;
+// (lane/16) reads 32 contiguous bytes (elements 16g..16g+15) of its A row;
 // the chunk is two MFMA K-steps, the first over elements 16g..16g+7 of every
 // group, the second over 16g+8..16g+15 (A and B permuted alike).
-// xr: this lane's A row at element 16g; wr[j]: weight row of tile j at 16g.
+// xr: this lane's A row at element 16g; wr[j]: packed tile j of this
+// workgroup at chunk 0 plus 8*lane; consecutive chunks of a tile are NW
+// tiles apart (interleaved pairs).  U chunks of loads are issued before their
+// MFMAs; weights are read with nontemporal loads (read once per pass).
 template <int NW, bool NT, int U>
 __device__ __forceinline__ void mfma_stream(const uint16_t* xr, bool xok, const uint16_t* const* wr, int c0, int c1,
                                             f32x4* acc) {
+  constexpr size_t CS = (size_t)NW * PACK_TILE;
   const uint4 zero = {0u, 0u, 0u, 0u};
   auto ldw = [](const uint16_t* p) { return NT ? ld16_nt(p) : ld16(p); };
   int s = c0;
@@ -61,8 +74,8 @@ __device__ __forceinline__ void mfma_stream(const uint16_t* xr, bool xok, const 
     for (int u = 0; u < U; ++u) {
 #pragma unroll
       for (int j = 0; j < NW; ++j) {
-        wb[j][u][0] = ldw(wr[j] + (size_t)(s + u) * 64);
-        wb[j][u][1] = ldw(wr[j] + (size_t)(s + u) * 64 + 8);
+        wb[j][u][0] = ldw(wr[j] + (size_t)(s + u) * CS);
+        wb[j][u][1] = ldw(wr[j] + (size_t)(s + u) * CS + PACK_TILE / 2);
       }
       xa[u][0] = xok ? ld16(xr + (size_t)(s + u) * 64) : zero;
       xa[u][1] = xok ? ld16(xr + (size_t)(s + u) * 64 + 8) : zero;
@@ -82,7 +95,7 @@ __device__ __forceinline__ void mfma_stream(const uint16_t* xr, bool xok, const 
       const uint4 xa = xok ? ld16(xr + (size_t)s * 64 + 8 * h) : zero;
 #pragma unroll
       for (int j = 0; j < NW; ++j) {
-        const uint4 wb = ldw(wr[j] + (size_t)s * 64 + 8 * h);
+        const uint4 wb = ldw(wr[j] + (size_t)s * CS + h * (PACK_TILE / 2));
         acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa),
                                                          __builtin_bit_cast(bf16x8, wb), acc[j], 0, 0, 0);
       }
@@ -94,13 +107,14 @@ __device__ __forceinline__ void mfma_stream(const uint16_t* xr, bool xok, const 
 template <int NW, int MT>
 __device__ __forceinline__ void mfma_stream_mt(const uint16_t* const* xr, const bool* xok, const uint16_t* const* wr,
                                                int c0, int c1, f32x4 (*acc)[NW]) {
+  constexpr size_t CS = (size_t)NW * PACK_TILE;
   const uint4 zero = {0u, 0u, 0u, 0u};
   for (int s = c0; s < c1; ++s) {
     uint4 wb[NW][2], xa[MT][2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
 #pragma unroll
-      for (int j = 0; j < NW; ++j) wb[j][h] = ld16(wr[j] + (size_t)s * 64 + 8 * h);
+      for (int j = 0; j < NW; ++j) wb[j][h] = ld16(wr[j] + (size_t)s * CS + h * (PACK_TILE / 2));
 #pragma unroll
       for (int r = 0; r < MT; ++r) xa[r][h] = xok[r] ? ld16(xr[r] + (size_t)s * 64 + 8 * h) : zero;
     }

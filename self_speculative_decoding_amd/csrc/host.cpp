@@ -29,37 +29,50 @@ bool is_moe_layer(const ssd_cfg& c, int l) { return c.n_experts > 0 && l >= c.n_
 
 int layer_ffn(const ssd_cfg& c) { return c.n_experts > 0 ? c.dense_ffn : c.ffn_dim; }
 
-std::vector<int64_t> weight_table(const ssd_cfg& c) {
+std::vector<int64_t> weight_table(const ssd_cfg& c, std::vector<char>* gemm) {
   const int64_t d = c.d_model, hd = c.head_dim, hq = c.n_q_heads, hkv = c.n_kv_heads;
   std::vector<int64_t> t;
-  t.push_back((int64_t)c.vocab * d);
+  std::vector<char> g;
+  auto add = [&](int64_t n, bool is_gemm) { t.push_back(n); g.push_back(is_gemm); };
+  add((int64_t)c.vocab * d, false);
   for (int l = 0; l < c.n_layers; ++l) {
-    t.push_back(d);
-    t.push_back(hq * hd * d);
-    t.push_back(hkv * hd * d);
-    t.push_back(hkv * hd * d);
-    t.push_back(d * hq * hd);
-    t.push_back(d);
+    add(d, false);
+    add(hq * hd * d, true);
+    add(hkv * hd * d, true);
+    add(hkv * hd * d, true);
+    add(d * hq * hd, true);
+    add(d, false);
     if (is_moe_layer(c, l)) {
       const int64_t e = c.n_experts, fe = c.expert_ffn, s = c.n_shared;
-      t.push_back(e * d);
-      t.push_back(e * fe * d);
-      t.push_back(e * fe * d);
-      t.push_back(e * d * fe);
-      t.push_back(s * fe * d);
-      t.push_back(s * fe * d);
-      t.push_back(s * d * fe);
+      add(e * d, true);
+      add(e * fe * d, true);
+      add(e * fe * d, true);
+      add(e * d * fe, true);
+      add(s * fe * d, true);
+      add(s * fe * d, true);
+      add(s * d * fe, true);
     } else {
       const int64_t f = layer_ffn(c);
-      t.push_back(f * d);
-      t.push_back(f * d);
-      t.push_back(d * f);
+      add(f * d, true);
+      add(f * d, true);
+      add(d * f, true);
     }
   }
-  t.push_back(d);
-  t.push_back((int64_t)c.vocab * d);
-  if (c.n_feat > 0) t.push_back(d * c.n_feat * d);
+  add(d, false);
+  add((int64_t)c.vocab * d, true);
+  if (c.n_feat > 0) add(d * c.n_feat * d, true);
+  if (gemm) *gemm = g;
   return t;
+}
+
+int64_t packed_elems(const ssd_cfg& c) {
+  if (c.dtype != SSD_BF16) return 0;
+  std::vector<char> g;
+  const auto t = weight_table(c, &g);
+  int64_t n = 0;
+  for (size_t i = 0; i < t.size(); ++i)
+    if (g[i]) n += t[i];
+  return n;
 }
 
 ssd_status validate(const ssd_cfg* cp) {
@@ -178,6 +191,7 @@ bool compute_layout(const ssd_cfg& c, Layout& L) {
     L.m_groups = take((16 + max_units * 18) * 4);
     L.m_union = take((size_t)c.n_layers * 4);
   }
+  L.wpack = take((size_t)packed_elems(c) * 2);   // bf16 GEMM weights in the packed tile layout
   L.total = off;
   return true;
 }
@@ -238,6 +252,14 @@ int64_t ssd_weight_numel(const ssd_cfg* cfg, int32_t i) {
   auto t = ssd::weight_table(*cfg);
   if (i < 0 || i >= (int32_t)t.size()) return -1;
   return t[i];
+}
+
+int32_t ssd_weight_retained(const ssd_cfg* cfg, int32_t i) {
+  if (ssd::validate(cfg) != SSD_OK) return -1;
+  std::vector<char> g;
+  auto t = ssd::weight_table(*cfg, &g);
+  if (i < 0 || i >= (int32_t)t.size()) return -1;
+  return cfg->dtype == SSD_BF16 && g[i] ? 0 : 1;
 }
 
 int64_t ssd_workspace_bytes(const ssd_cfg* cfg) {

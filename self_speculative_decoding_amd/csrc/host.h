@@ -17,7 +17,7 @@ struct Layout {
   size_t part_o = 0, part_ml = 0, counters = 0, rope_cos = 0, rope_sin = 0;
   size_t block = 0, post = 0, toks = 0, state = 0, result = 0, outlog = 0;
   size_t tblock = 0, tpost = 0, tstate = 0, tresult = 0, toutlog = 0;
-  size_t tap = 0, feat = 0, amax_v = 0, amax_i = 0, trace = 0;
+  size_t tap = 0, feat = 0, amax_v = 0, amax_i = 0, trace = 0, wpack = 0;
   size_t m_rlogits = 0, m_ids = 0, m_gates = 0, m_inject = 0, m_slot_out = 0, m_groups = 0, m_union = 0;
   size_t total = 0;
   int R = 0;        // rows per pass (multiple of 16)
@@ -30,7 +30,10 @@ const char* last_error();
 void clear_error();
 ssd_status validate(const ssd_cfg* c);
 bool compute_layout(const ssd_cfg& c, Layout& L);
-std::vector<int64_t> weight_table(const ssd_cfg& c);
+// element counts of the weight tensors in ssd_load order; gemm (optional)
+// flags the matrices the bf16 GEMMs read (packed at load)
+std::vector<int64_t> weight_table(const ssd_cfg& c, std::vector<char>* gemm = nullptr);
+int64_t packed_elems(const ssd_cfg& c);
 bool is_moe_layer(const ssd_cfg& c, int l);
 int layer_ffn(const ssd_cfg& c);
 ssd_status check_transition(int32_t state, int32_t op, int32_t* next);

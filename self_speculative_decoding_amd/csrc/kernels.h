@@ -99,8 +99,8 @@ struct MoeArgs {
   const void* X;              // normalised input [M, d]
   int M, d, E, top_k, fe, n_shared;
   const void* router;         // [E, d]
-  const void* eg; const void* eu; const void* ed;   // [E][fe][d], [E][fe][d], [E][d][fe]
-  const void* sg; const void* su; const void* sd;   // [S][fe][d], ...
+  const void* eg; const void* ed;   // packed: per expert gate/up interleaved [fe x d], down [d x fe]
+  const void* sg; const void* sd;   // shared experts, same layout
   float* rlogits;             // [M, E] f32
   int* ids;                   // [M, top_k]  (router choice, or injected)
   float* gates;               // [M, top_k]
@@ -117,5 +117,16 @@ struct MoeArgs {
   const void* gain_next;      // [d]
 };
 hipError_t launch_moe(int dtype, const MoeArgs& a, hipStream_t s);
+
+// Packing of a row-major bf16 weight [N, K] into the tile layout the bf16
+// GEMMs stream (see device.h).  mode 0: rows of src0 in order; mode 1: the
+// QKV GEMM's rows gathered from src0 = wq, src1 = wk, src2 = wv; pair: the
+// tiles of src0 and src1 (same shape) interleaved one by one (gate/up).
+struct PackArgs {
+  const void* src0; const void* src1; const void* src2;
+  void* dst;
+  int N, K, mode, pair, hq, hkv, hd;
+};
+hipError_t launch_pack(const PackArgs& p, hipStream_t s);
 
 }  // namespace ssd

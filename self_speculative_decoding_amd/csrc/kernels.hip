@@ -21,6 +21,9 @@
 #ifndef SSD_GEMM_U1_LONGK   // one-matrix GEMMs with K >= 8192 (the FFN down projection)
 #define SSD_GEMM_U1_LONGK 2
 #endif
+#ifndef SSD_GEMM_UW         // GEMMs with >= 1024 column tiles (the LM head)
+#define SSD_GEMM_UW 2
+#endif
 #ifndef SSD_KW_SWIGLU
 #define SSD_KW_SWIGLU 8
 #endif
@@ -28,7 +31,7 @@
 #define SSD_KW_NARROW 8
 #endif
 #ifndef SSD_KW_WIDE
-#define SSD_KW_WIDE 4
+#define SSD_KW_WIDE 8
 #endif
 
 namespace ssd {
@@ -152,6 +155,19 @@ __device__ __forceinline__ void epi_qkv_pair(const GemmArgs& a, int base, int m,
   }
 }
 
+// as epi_qkv_pair for a q or k head, with the rotary cos/sin already loaded
+template <typename E>
+__device__ __forceinline__ void epi_qkv_rot(const GemmArgs& a, int base, int m, int head, int i, float v0, float v1,
+                                            float c, float s) {
+  const int half = a.hd >> 1;
+  const int pos = base + m;
+  const float o0 = v0 * c - v1 * s, o1 = v1 * c + v0 * s;
+  E* dst = head < a.hq ? (E*)a.q + (size_t)m * a.hq * a.hd + (size_t)head * a.hd
+                       : (E*)a.kc + ((size_t)(head - a.hq) * a.max_ctx + pos) * a.hd;
+  dst[i] = fromf<E>(o0);
+  dst[i + half] = fromf<E>(o1);
+}
+
 template <typename E>
 __device__ __forceinline__ void epi_v_single(const GemmArgs& a, int base, int m, int vh, int dim, float v) {
   const int pos = base + m;
@@ -192,26 +208,17 @@ __device__ __forceinline__ float ss_rstd(const GemmArgs& a, int m, bool row_ok, 
   return 1.0f / sqrtf(s / (float)a.K + a.eps);
 }
 
-template <int EPI, int NW>
-__device__ __forceinline__ const uint16_t* gemm_row(const GemmArgs& a, int t, int j, int c, int* head_out,
-                                                    int* dim_out) {
-  if (EPI == EPI_QKV) {
-    const int col0 = t * 16;
-    const int head = col0 / a.hd, jj = (col0 % a.hd) / 16, half = a.hd >> 1;
-    int dim;
-    if (head < a.hq + a.hkv) dim = c < 8 ? 8 * jj + c : half + 8 * jj + (c - 8);
-    else dim = 16 * jj + c;
-    *head_out = head;
-    *dim_out = dim;
-    if (head < a.hq) return (const uint16_t*)a.W0 + ((size_t)head * a.hd + dim) * a.K;
-    if (head < a.hq + a.hkv) return (const uint16_t*)a.W1 + ((size_t)(head - a.hq) * a.hd + dim) * a.K;
-    return (const uint16_t*)a.W2 + ((size_t)(head - a.hq - a.hkv) * a.hd + dim) * a.K;
-  }
-  const uint16_t* W = (const uint16_t*)(j == 0 ? a.W0 : a.W1);
-  return W + (size_t)(t * 16 + c) * a.K;
+// Output head and head dim of lane c in column tile t of the QKV GEMM.  Its
+// packed weight rows put the RoPE pair (i, i + hd/2) of a q or k head on
+// lanes c and c^8: tile columns 8jj..8jj+7 and hd/2+8jj..+7 of the head.
+__device__ __forceinline__ void qkv_col(const GemmArgs& a, int t, int c, int* head_out, int* dim_out) {
+  const int col0 = t * 16;
+  const int head = col0 / a.hd, jj = (col0 % a.hd) / 16, half = a.hd >> 1;
+  *head_out = head;
+  *dim_out = head < a.hq + a.hkv ? (c < 8 ? 8 * jj + c : half + 8 * jj + (c - 8)) : 16 * jj + c;
 }
 
-template <int EPI, int NW, int KW, int MT>
+template <int EPI, int NW, int KW, int MT, int U>
 __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane & 15, kg = lane >> 4;
@@ -224,12 +231,15 @@ __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
     av_ok[r] = am < a.M;
     xr[r] = (const uint16_t*)a.X + (size_t)(av_ok[r] ? am : 0) * a.ldx + kg * 16;
   }
-  const uint16_t* wr[NW];
-  int head = 0, dim = 0;
-#pragma unroll
-  for (int j = 0; j < NW; ++j) wr[j] = gemm_row<EPI, NW>(a, t, j, c, &head, &dim) + kg * 16;
-
   const int S = a.K >> 6;   // 64-element chunks
+  // packed weight tiles of this column tile (gate/up interleaved when NW = 2)
+  const uint16_t* wr[NW];
+#pragma unroll
+  for (int j = 0; j < NW; ++j)
+    wr[j] = (const uint16_t*)a.W0 + ((size_t)t * S * NW + j) * PACK_TILE + 8 * lane;
+  int head = 0, dim = 0;
+  if (EPI == EPI_QKV) qkv_col(a, t, c, &head, &dim);
+
   const int s0 = (S * wave) / KW, s1 = (S * (wave + 1)) / KW;
 
   // Epilogue inputs fetched before the weight stream so that their latency
@@ -263,10 +273,27 @@ __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
     for (int j = 0; j < NW; ++j) acc[r][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   // chunks per batch of loads (fewer for the two-matrix gate/up GEMM keeps
   // its register count, and so the workgroups resident per CU, in check)
-  if (MT == 1 && NW == 1 && a.K >= 8192)
-    mfma_stream<NW, false, SSD_GEMM_U1_LONGK>(xr[0], av_ok[0], wr, s0, s1, acc[0]);
-  else if (MT == 1)
-    mfma_stream<NW, false, NW == 2 ? SSD_GEMM_U2 : SSD_GEMM_U1>(xr[0], av_ok[0], wr, s0, s1, acc[0]);
+  float rc[4] = {0.f, 0.f, 0.f, 0.f}, rsn[4] = {0.f, 0.f, 0.f, 0.f};   // RoPE cos/sin (QKV)
+  if (MT == 1 && EPI == EPI_QKV) {
+    // first load batch, then the rotary table entries of wave 0's epilogue
+    // (they need the position), then the rest of the K range
+    const int sm = min(s0 + U, s1);
+    mfma_stream<NW, true, U>(xr[0], av_ok[0], wr, s0, sm, acc[0]);
+    if (wave == 0 && head < a.hq + a.hkv && c < 8) {
+      const int half = a.hd >> 1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = blockIdx.y * 16 + 4 * kg + i;
+        if (m < a.M) {
+          rc[i] = a.cos_t[(size_t)(base + m) * half + dim];
+          rsn[i] = a.sin_t[(size_t)(base + m) * half + dim];
+        }
+      }
+    }
+    mfma_stream<NW, true, U>(xr[0], av_ok[0], wr, sm, s1, acc[0]);
+  } else if (MT == 1) {
+    mfma_stream<NW, true, U>(xr[0], av_ok[0], wr, s0, s1, acc[0]);
+  }
   else mfma_stream_mt<NW, MT>(xr, av_ok, wr, s0, s1, acc);
 
   __shared__ f32x4 red[KW - 1][MT][NW][64];
@@ -320,7 +347,8 @@ __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
         const int m = mt * 16 + 4 * kg + i;
         if (m >= a.M) continue;
         if (rot) {
-          if (c < 8) epi_qkv_pair<uint16_t>(a, base, m, head, dim, acc[r][0][i], part[i]);
+          if (c < 8 && MT == 1) epi_qkv_rot<uint16_t>(a, base, m, head, dim, acc[r][0][i], part[i], rc[i], rsn[i]);
+          else if (c < 8) epi_qkv_pair<uint16_t>(a, base, m, head, dim, acc[r][0][i], part[i]);
         } else {
           epi_v_single<uint16_t>(a, base, m, head - a.hq - a.hkv, dim, acc[r][0][i]);
         }
@@ -370,6 +398,37 @@ __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
       }
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// weight packing (load time): one workgroup per packed tile, 16 bytes per thread
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(128) void pack_kernel(PackArgs p) {
+  const int t = blockIdx.x, s = blockIdx.y, which = blockIdx.z;
+  const int l = threadIdx.x & 63, h = threadIdx.x >> 6, g = l >> 4, c = l & 15;
+  const uint16_t* src;
+  size_t row;
+  if (p.mode == 1) {
+    const int col0 = t * 16;
+    const int head = col0 / p.hd, jj = (col0 % p.hd) / 16, half = p.hd >> 1;
+    const int dim = head < p.hq + p.hkv ? (c < 8 ? 8 * jj + c : half + 8 * jj + (c - 8)) : 16 * jj + c;
+    if (head < p.hq) { src = (const uint16_t*)p.src0; row = (size_t)head * p.hd + dim; }
+    else if (head < p.hq + p.hkv) { src = (const uint16_t*)p.src1; row = (size_t)(head - p.hq) * p.hd + dim; }
+    else { src = (const uint16_t*)p.src2; row = (size_t)(head - p.hq - p.hkv) * p.hd + dim; }
+  } else {
+    src = (const uint16_t*)(which ? p.src1 : p.src0);
+    row = (size_t)t * 16 + c;
+  }
+  const uint4 v = *(const uint4*)(src + row * p.K + (size_t)s * 64 + 16 * g + 8 * h);
+  const size_t tile = ((size_t)t * (p.K / 64) + s) * (p.pair ? 2 : 1) + which;
+  *(uint4*)((uint16_t*)p.dst + tile * PACK_TILE + h * (PACK_TILE / 2) + 8 * l) = v;
+}
+
+hipError_t launch_pack(const PackArgs& p, hipStream_t s) {
+  if (p.N % 16 || p.K % 64 || p.N <= 0 || p.K <= 0) return hipErrorInvalidValue;
+  pack_kernel<<<dim3(p.N / 16, p.K / 64, p.pair ? 2 : 1), 128, 0, s>>>(p);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -909,19 +968,20 @@ hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t s) {
     // passes (prefill chunks) let 4 row tiles share each weight load
     const bool multi = a.M > 32;
     const dim3 grid_mt(tiles, (a.M + 63) / 64);
-#define SSD_G(E, NW, KWN)                                                                         \
-  case E:                                                                                         \
-    if (multi) gemm_bf16_kernel<E, NW, 4, 4><<<grid_mt, 256, 0, s>>>(a);                          \
-    else if (wide) gemm_bf16_kernel<E, NW, SSD_KW_WIDE, 1><<<grid, 64 * SSD_KW_WIDE, 0, s>>>(a);   \
-    else gemm_bf16_kernel<E, NW, KWN, 1><<<grid, 64 * KWN, 0, s>>>(a);                            \
+#define SSD_G(E, NW, KWN, UN)                                                                         \
+  case E:                                                                                             \
+    if (multi) gemm_bf16_kernel<E, NW, 4, 4, 1><<<grid_mt, 256, 0, s>>>(a);                           \
+    else if (wide) gemm_bf16_kernel<E, NW, SSD_KW_WIDE, 1, SSD_GEMM_UW><<<grid, 64 * SSD_KW_WIDE, 0, s>>>(a); \
+    else if (NW == 1 && a.K >= 8192) gemm_bf16_kernel<E, NW, KWN, 1, SSD_GEMM_U1_LONGK><<<grid, 64 * KWN, 0, s>>>(a); \
+    else gemm_bf16_kernel<E, NW, KWN, 1, UN><<<grid, 64 * KWN, 0, s>>>(a);                            \
     break;
     switch (epi) {
-      SSD_G(EPI_F32, 1, SSD_KW_NARROW)
-      SSD_G(EPI_LOGITS, 1, SSD_KW_NARROW)
-      SSD_G(EPI_RESID, 1, SSD_KW_NARROW)
-      SSD_G(EPI_SWIGLU, 2, SSD_KW_SWIGLU)
-      SSD_G(EPI_QKV, 1, SSD_KW_NARROW)
-      SSD_G(EPI_STORE, 1, SSD_KW_NARROW)
+      SSD_G(EPI_F32, 1, SSD_KW_NARROW, SSD_GEMM_U1)
+      SSD_G(EPI_LOGITS, 1, SSD_KW_NARROW, SSD_GEMM_U1)
+      SSD_G(EPI_RESID, 1, SSD_KW_NARROW, SSD_GEMM_U1)
+      SSD_G(EPI_SWIGLU, 2, SSD_KW_SWIGLU, SSD_GEMM_U2)
+      SSD_G(EPI_QKV, 1, SSD_KW_NARROW, SSD_GEMM_U1)
+      SSD_G(EPI_STORE, 1, SSD_KW_NARROW, SSD_GEMM_U1)
       default: return hipErrorInvalidValue;
     }
 #undef SSD_G

@@ -147,26 +147,29 @@ __global__ __launch_bounds__(256) void moe_gemm_kernel(MoeArgs a) {
   const int slots = a.top_k + a.n_shared;
   const bool ok = c < nr;
   const int code = ok ? u[2 + c] : 0;
+  // packed expert weights: per expert, gate/up interleaved [fe/16 tiles] or
+  // down [d/16 tiles], tiles of 16 rows x 64 K-elements
   const uint16_t* xr;
   const uint16_t* wr[NW];
   int K;
   if (PHASE == 0) {
     K = a.d;
     xr = (const uint16_t*)a.X + (size_t)(code / slots) * a.d + kg * 16;
-    const size_t eo = (size_t)e * a.fe * a.d;
-    wr[0] = (const uint16_t*)(sh ? a.sg : a.eg) + eo + (size_t)(t * 16 + c) * a.d + kg * 16;
-    wr[NW - 1] = (const uint16_t*)(sh ? a.su : a.eu) + eo + (size_t)(t * 16 + c) * a.d + kg * 16;
+    const uint16_t* ex = (const uint16_t*)(sh ? a.sg : a.eg) + (size_t)e * 2 * a.fe * a.d;
+#pragma unroll
+    for (int j = 0; j < NW; ++j) wr[j] = ex + ((size_t)t * (K >> 6) * 2 + j) * PACK_TILE + 8 * lane;
   } else {
     K = a.fe;
     xr = (const uint16_t*)a.act + (size_t)code * a.fe + kg * 16;
-    wr[0] = (const uint16_t*)(sh ? a.sd : a.ed) + (size_t)e * a.d * a.fe + (size_t)(t * 16 + c) * a.fe + kg * 16;
+    const uint16_t* ex = (const uint16_t*)(sh ? a.sd : a.ed) + (size_t)e * a.d * a.fe;
+    wr[0] = ex + (size_t)t * (K >> 6) * PACK_TILE + 8 * lane;
   }
   const int S = K >> 6;   // 64-element chunks
   const int s0 = (S * wave) >> 2, s1 = (S * (wave + 1)) >> 2;
   f32x4 acc[NW];
 #pragma unroll
   for (int j = 0; j < NW; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  mfma_stream<NW, false, 4>(xr, ok, wr, s0, s1, acc);
+  mfma_stream<NW, true, 4>(xr, ok, wr, s0, s1, acc);
 
   __shared__ f32x4 red[3][NW][64];
   if (wave > 0) {

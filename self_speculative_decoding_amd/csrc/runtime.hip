@@ -101,8 +101,8 @@ MoeArgs moe_args(ssd_ctx* c, int l, int M) {
   const LayerW& w = c->L[l];
   MoeArgs a{};
   a.X = c->xn; a.M = M; a.d = g.d_model; a.E = g.n_experts; a.top_k = g.top_k; a.fe = g.expert_ffn;
-  a.n_shared = g.n_shared; a.router = w.router; a.eg = w.eg; a.eu = w.eu; a.ed = w.ed;
-  a.sg = w.sg; a.su = w.su; a.sd = w.sd; a.rlogits = c->m_rlogits; a.ids = c->m_ids; a.gates = c->m_gates;
+  a.n_shared = g.n_shared; a.router = w.router; a.eg = w.eg; a.ed = w.ed;
+  a.sg = w.sg; a.sd = w.sd; a.rlogits = c->m_rlogits; a.ids = c->m_ids; a.gates = c->m_gates;
   a.inject = c->moe_inject ? c->m_inject + (size_t)l * c->lay.R * g.top_k : nullptr;
   a.act = c->act; a.slot_out = c->m_slot_out; a.resid = c->x; a.groups = c->m_groups;
   a.union_out = c->m_union + l; a.dedup = g.moe_dedup;
@@ -350,6 +350,69 @@ ssd_status do_accept(ssd_ctx* c, bool sync, int* a_out, int* nemit_out) {
   return SSD_OK;
 }
 
+// Copies every bf16 GEMM weight into the packed tile layout in the workspace
+// (see device.h) and points the context at the copies; the caller's buffers
+// of these matrices are not read after this.
+hipError_t pack_weights(ssd_ctx* c) {
+  const ssd_cfg& g = c->cfg;
+  const int d = g.d_model, hq = g.n_q_heads, hkv = g.n_kv_heads, hd = g.head_dim;
+  uint16_t* wp = (uint16_t*)at(c, c->lay.wpack);
+  size_t off = 0;
+  hipError_t e = hipSuccess;
+  auto pack = [&](const void* s0, const void* s1, const void* s2, int N, int K, int mode, int pair) {
+    uint16_t* dst = wp + off;
+    off += (size_t)N * K * (pair ? 2 : 1);
+    if (e == hipSuccess) {
+      PackArgs p{};
+      p.src0 = s0; p.src1 = s1; p.src2 = s2; p.dst = dst; p.N = N; p.K = K; p.mode = mode; p.pair = pair;
+      p.hq = hq; p.hkv = hkv; p.hd = hd;
+      e = launch_pack(p, c->stream);
+    }
+    return (const void*)dst;
+  };
+  auto el = [](const void* p, size_t i) { return (const void*)((const uint16_t*)p + i); };
+  for (LayerW& w : c->L) {
+    w.wq = pack(w.wq, w.wk, w.wv, (hq + 2 * hkv) * hd, d, 1, 0);
+    w.wk = w.wv = nullptr;
+    w.wo = pack(w.wo, nullptr, nullptr, d, hq * hd, 0, 0);
+    if (w.moe) {
+      const int E = g.n_experts, fe = g.expert_ffn, S = g.n_shared;
+      w.router = pack(w.router, nullptr, nullptr, E, d, 0, 0);
+      const void* eg = nullptr;
+      for (int x = 0; x < E; ++x) {
+        const void* p = pack(el(w.eg, (size_t)x * fe * d), el(w.eu, (size_t)x * fe * d), nullptr, fe, d, 0, 1);
+        if (!x) eg = p;
+      }
+      const void* ed = nullptr;
+      for (int x = 0; x < E; ++x) {
+        const void* p = pack(el(w.ed, (size_t)x * d * fe), nullptr, nullptr, d, fe, 0, 0);
+        if (!x) ed = p;
+      }
+      const void* sg = nullptr;
+      for (int x = 0; x < S; ++x) {
+        const void* p = pack(el(w.sg, (size_t)x * fe * d), el(w.su, (size_t)x * fe * d), nullptr, fe, d, 0, 1);
+        if (!x) sg = p;
+      }
+      const void* sd = nullptr;
+      for (int x = 0; x < S; ++x) {
+        const void* p = pack(el(w.sd, (size_t)x * d * fe), nullptr, nullptr, d, fe, 0, 0);
+        if (!x) sd = p;
+      }
+      w.eg = eg; w.ed = ed; w.sg = sg; w.sd = sd;
+      w.eu = w.su = nullptr;
+    } else {
+      w.w_gate = pack(w.w_gate, w.w_up, nullptr, w.ffn, d, 0, 1);
+      w.w_up = nullptr;
+      w.w_down = pack(w.w_down, nullptr, nullptr, d, w.ffn, 0, 0);
+    }
+  }
+  c->lm_head = pack(c->lm_head, nullptr, nullptr, g.vocab, d, 0, 0);
+  if (c->fc) c->fc = pack(c->fc, nullptr, nullptr, d, g.n_feat * d, 0, 0);
+  if (e != hipSuccess) return e;
+  if ((int64_t)off != packed_elems(g)) return hipErrorInvalidValue;   // layout and packing disagree
+  return hipStreamSynchronize(c->stream);
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -462,6 +525,13 @@ ssd_status ssd_load(const ssd_cfg* cfg, const ssd_buf* weights, int32_t n_weight
     for (int i = 0; i < EV_N && e == hipSuccess; ++i) e = hipEventCreate(&c->ev[i]);
     if (e != hipSuccess) {
       st = fail(SSD_E_HIP, "load: %s", hipGetErrorString(e));
+      return cleanup(st);
+    }
+  }
+  if (cfg->dtype == SSD_BF16) {
+    const hipError_t e = pack_weights(c);
+    if (e != hipSuccess) {
+      st = fail(SSD_E_HIP, "load (weight packing): %s", hipGetErrorString(e));
       return cleanup(st);
     }
   }

@@ -41,6 +41,24 @@ def test_workload_cfgs_validate_and_weight_table_matches(name):
     assert ssd.workspace_bytes(c) > 0
 
 
+@pytest.mark.parametrize("name", ["tiny", "llama-8b", "qwen3-8b", "dsv2-lite"])
+def test_weight_retention_and_packed_workspace(name):
+    # bf16 models copy every matrix into the workspace at load; only the
+    # embedding and the norm gains stay referenced.  float32 keeps all.
+    cfg = synth.config(name)
+    c = ssd.make_cfg(cfg)
+    specs = synth.weight_specs(cfg)
+    kept = [ssd.lib.ssd_weight_retained(ctypes.byref(c), i) for i in range(len(specs))]
+    if cfg["dtype"] == "f32":
+        assert kept == [1] * len(specs)
+        return
+    expect = [1 if (n == "embed" or n.endswith("norm")) else 0 for n, _, _ in specs]
+    assert kept == expect
+    packed = sum(int(np.prod(s)) for (n, s, _), k in zip(specs, kept) if k == 0) * 2
+    assert ssd.workspace_bytes(c) > packed
+    assert ssd.lib.ssd_weight_retained(ctypes.byref(c), len(specs)) == -1
+
+
 def test_llama8b_weight_bytes():
     # 32 layers x 436.2 MB + embedding and LM head of 1.05 GB each
     assert abs(synth.weight_bytes(synth.config("llama-8b")) / 1e9 - 16.06) < 0.01
