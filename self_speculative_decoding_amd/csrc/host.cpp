@@ -141,7 +141,7 @@ bool compute_layout(const ssd_cfg& c, Layout& L) {
   L.n_part = (c.max_ctx + kAttPT - 1) / kAttPT;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = up256(off + bytes); return o; };
-  const size_t cache = (size_t)c.n_layers * hkv * c.max_ctx * hd * esz;
+  const size_t cache = (size_t)c.n_layers * hkv * ((size_t)L.n_part * kAttPT) * hd * esz;   // rows padded to whole partitions
   L.kc = take(cache);
   L.vc = take(cache);
   L.x = take((size_t)R * d * 4);
@@ -162,7 +162,6 @@ bool compute_layout(const ssd_cfg& c, Layout& L) {
   L.part_o_bytes = (size_t)L.n_part * R * hq * hd * 4;
   L.part_o = take(L.part_o_bytes);
   L.part_ml = take((size_t)L.n_part * R * hq * 2 * 4);
-  L.counters = take((size_t)hkv * (R / 16) * 4);
   L.rope_cos = take((size_t)c.max_ctx * (hd / 2) * 4);
   L.rope_sin = take((size_t)c.max_ctx * (hd / 2) * 4);
   L.block = take(SSD_MAX_BLOCK * 4);

@@ -14,7 +14,7 @@ constexpr int kAttPT = 64;   // attention key partition width (kernels.h: ATT_PT
 // Byte offsets of every workspace buffer (256-byte aligned).
 struct Layout {
   size_t kc = 0, vc = 0, x = 0, xn = 0, ss = 0, q = 0, att = 0, act = 0, logits = 0;
-  size_t part_o = 0, part_ml = 0, counters = 0, rope_cos = 0, rope_sin = 0;
+  size_t part_o = 0, part_ml = 0, rope_cos = 0, rope_sin = 0;
   size_t block = 0, post = 0, toks = 0, state = 0, result = 0, outlog = 0;
   size_t tblock = 0, tpost = 0, tstate = 0, tresult = 0, toutlog = 0;
   size_t tap = 0, feat = 0, amax_v = 0, amax_i = 0, trace = 0, wpack = 0;

@@ -39,12 +39,12 @@ struct GemmArgs {
   // QKV epilogue
   void* q;                    // [M, hq*hd]
   void* kc;                   // this layer's K cache [hkv][max_ctx][hd]
-  void* vc;
-  const float* cos_t;         // [max_ctx][hd/2]
+  void* vc;                   // this layer's V cache, transposed: [hkv][hd][max_ctx]
+  const float* cos_t;         // [positions][hd/2]
   const float* sin_t;
   const int* state;           // state[0] = committed length n
   int pos_off;                // row r sits at position state[0] + pos_off + r
-  int hq, hkv, hd, max_ctx;
+  int hq, hkv, hd, max_ctx;   // max_ctx: positions per cache row (a multiple of 64)
   // LOGITS epilogue: per-tile argmax partials [M][N/16]
   float* amax_v;
   int* amax_i;
@@ -65,13 +65,12 @@ struct GemmArgs {
 struct AttnArgs {
   const void* q;              // [M, hq*hd]
   const void* kc;             // [hkv][max_ctx][hd]
-  const void* vc;
+  const void* vc;             // [hkv][hd][max_ctx]
   void* out;                  // [M, hq*hd]
   float* part_o;              // [n_part][R][hq][hd]
   float* part_ml;             // [n_part][R][hq][2]
-  int* counters;              // [hkv][R/16], zero between launches
   const int* state;
-  int pos_off, M, R, hq, hkv, hd, max_ctx;
+  int pos_off, M, R, hq, hkv, hd, max_ctx;   // max_ctx: positions per cache row (multiple of 64)
   float scale_log2;           // log2(e) / sqrt(hd)
 };
 

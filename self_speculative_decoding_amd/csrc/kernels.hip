@@ -148,10 +148,10 @@ __device__ __forceinline__ void epi_qkv_pair(const GemmArgs& a, int base, int m,
                          : (E*)a.kc + ((size_t)(head - a.hq) * a.max_ctx + pos) * a.hd;
     dst[i] = fromf<E>(o0);
     dst[i + half] = fromf<E>(o1);
-  } else {
-    E* dst = (E*)a.vc + ((size_t)(head - a.hq - a.hkv) * a.max_ctx + pos) * a.hd;
-    dst[i] = fromf<E>(v0);
-    dst[i + half] = fromf<E>(v1);
+  } else {   // V cache: [kv head][dim][position]
+    E* dst = (E*)a.vc + (size_t)(head - a.hq - a.hkv) * a.hd * a.max_ctx + pos;
+    dst[(size_t)i * a.max_ctx] = fromf<E>(v0);
+    dst[(size_t)(i + half) * a.max_ctx] = fromf<E>(v1);
   }
 }
 
@@ -171,7 +171,7 @@ __device__ __forceinline__ void epi_qkv_rot(const GemmArgs& a, int base, int m, 
 template <typename E>
 __device__ __forceinline__ void epi_v_single(const GemmArgs& a, int base, int m, int vh, int dim, float v) {
   const int pos = base + m;
-  ((E*)a.vc)[((size_t)vh * a.max_ctx + pos) * a.hd + dim] = fromf<E>(v);
+  ((E*)a.vc)[((size_t)vh * a.hd + dim) * a.max_ctx + pos] = fromf<E>(v);   // [kv head][dim][position]
 }
 
 // ---------------------------------------------------------------------------
@@ -526,16 +526,17 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 
   if (active) {
     const E* kb = (const E*)a.kc + ((size_t)kvh * a.max_ctx + key0) * HD;
-    const E* vb = (const E*)a.vc + ((size_t)kvh * a.max_ctx + key0) * HD;
     for (int e = tid * VEC; e < PT * HD; e += 256 * VEC) {
       const int key = e / HD;
-      uint4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-      if (key0 + key <= maxpos) {
-        kv = *(const uint4*)(kb + e);
-        vv = *(const uint4*)(vb + e);
-      }
+      uint4 kv = {0u, 0u, 0u, 0u};
+      if (key0 + key <= maxpos) kv = *(const uint4*)(kb + e);
       *(uint4*)(Ks + e) = kv;
-      *(uint4*)(Vs + e) = vv;
+    }
+    // V cache rows are head dims ([dim][position]); Vs is [key][dim]
+    const E* vb = (const E*)a.vc + (size_t)kvh * HD * a.max_ctx + key0;
+    for (int e = tid; e < PT * HD; e += 256) {
+      const int dim = e / PT, key = e % PT;
+      Vs[key * HD + dim] = key0 + key <= maxpos ? vb[(size_t)dim * a.max_ctx + key] : fromf<E>(0.f);
     }
   }
   __syncthreads();
@@ -606,161 +607,140 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 
 }
 
-// bf16 attention partition on MFMA 16x16x32.
+// bf16 attention partition on MFMA 16x16x32, one wave per workgroup.
 //
-// Same partitioning and output as attn_kernel.  Query vectors qi = r*G + g of
-// the row tile form up to four 16-row MFMA tiles (one per wave).  S = Q.K^T
-// takes Q fragments from the q buffer and K fragments straight from the
-// cache rows; the row max and sum of each query are a fixed butterfly over the
-// 16 lanes holding its keys; P is split into bf16 hi + lo parts and
-// O = P_hi.V + P_lo.V reads them and a transposed V tile from LDS.
-// Every output element is produced by the same instruction sequence for any
-// number of rows in the pass.
+// grid (partition p, kv head, tile of 16 query vectors qi = r*G + g: row r,
+// query head g of the kv group).  Keys sit in the MFMA row dimension:
+// S^T = K . Q^T takes K rows (key 16kt + c) and Q as operands straight from
+// the caches, and lane (c, kg) then holds the scores of query c for keys
+// 16kt + 4kg + i.  Those registers are already the B operand of
+// O^T = V^T . P^T when K-step ks takes keys 32ks + 4kg + {0..3} and
+// 32ks + 16 + 4kg + {0..3} in lane group kg; the V cache is stored transposed
+// ([dim][position]) so that A gets the same keys as two 8-byte pieces.  O^T
+// lands as lane (c, kg) holding dims 16dt + 4kg + i of query c.  No LDS, no
+// barrier.  The row max and sum of a query are an in-lane pass in fixed order
+// and a butterfly over its 4 lane groups.  P is split into bf16 hi + lo
+// parts.  Every output element is produced by the same instruction sequence
+// for any number of rows in the pass.
 template <int G>
-__global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
-  constexpr int HD = 128, PT = ATT_PT, PS = PT + 8;
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[HD][PS];
-  __shared__ __attribute__((aligned(16))) uint16_t Ps[4][16][PS];
-  __shared__ __attribute__((aligned(16))) uint16_t Pl[4][16][PS];
-  const int p = blockIdx.x, kvh = blockIdx.y, mt = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int c = lane & 15, kg = lane >> 4;
+__global__ __launch_bounds__(64) void attn_mfma_kernel(AttnArgs a) {
+  constexpr int HD = 128, PT = ATT_PT;
+  const int p = blockIdx.x, kvh = blockIdx.y;
+  const int lane = threadIdx.x, c = lane & 15, kg = lane >> 4;
   const int st0 = a.state[0];   // position load issued first, used late
-  const int row0 = mt * ROW_TILE;
-  const int nrows = min(ROW_TILE, a.M - row0);
   const int key0 = p * PT;
+  const int qi = blockIdx.z * 16 + c;
+  const bool qv = qi < a.M * G;
+  const int qr = qv ? qi / G : 0, qg = qv ? qi % G : 0;
+  const size_t ldc = a.max_ctx;   // positions per cache row (multiple of PT)
 
-  // Every global load of the workgroup is issued up front and unconditionally
-  // (addresses clamped into the cache), before the position is known: the V
-  // tile (into registers, transposed into LDS after S), the Q fragments and
-  // the K fragments.  There is no early exit: a workgroup past every row's
-  // position runs through and stores nothing, so the loads never wait for
-  // the position.  Keys past the last row's position are masked after.
-  const uint16_t* vb = (const uint16_t*)a.vc + (size_t)kvh * a.max_ctx * HD;
-  constexpr int VL = PT * HD / 8 / 256;   // uint4 pieces of V per thread
-  uint4 vv[VL];
-#pragma unroll
-  for (int i = 0; i < VL; ++i) {
-    const int e = tid + 256 * i, key = min(key0 + e / (HD / 8), a.max_ctx - 1), d0 = (e % (HD / 8)) * 8;
-    vv[i] = *(const uint4*)(vb + (size_t)key * HD + d0);
-  }
-  const int QV = nrows * G;
-  const int qi = wave * 16 + c;
-  const bool qv = qi < QV;
-  const int qr = qi / G, qg = qi % G;
-  const uint16_t* qp = (const uint16_t*)a.q + (size_t)(row0 + (qv ? qr : 0)) * a.hq * HD +
-                       (size_t)(kvh * G + (qv ? qg : 0)) * HD + kg * 8;
+  // every load up front: Q (B of S^T), K (A of S^T), V^T (A of O^T)
+  const uint16_t* qp = (const uint16_t*)a.q + (size_t)qr * a.hq * HD + (size_t)(kvh * G + qg) * HD + 8 * kg;
   uint4 qa[4];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) qa[ks] = *(const uint4*)(qp + ks * 32);
-  const uint16_t* kb = (const uint16_t*)a.kc + (size_t)kvh * a.max_ctx * HD + kg * 8;
+  for (int ks = 0; ks < 4; ++ks) qa[ks] = *(const uint4*)(qp + 32 * ks);
+  const uint16_t* kb = (const uint16_t*)a.kc + ((size_t)kvh * ldc + key0 + c) * HD + 8 * kg;
   uint4 kf[4][4];
 #pragma unroll
-  for (int kt = 0; kt < 4; ++kt) {
-    const int key = min(key0 + kt * 16 + c, a.max_ctx - 1);
+  for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) kf[kt][ks] = *(const uint4*)(kb + (size_t)key * HD + ks * 32);
-  }
-  const int base = st0 + a.pos_off;
-  const int maxpos = base + row0 + nrows - 1;
+    for (int ks = 0; ks < 4; ++ks) kf[kt][ks] = *(const uint4*)(kb + (size_t)16 * kt * HD + 32 * ks);
+  const uint16_t* vb = (const uint16_t*)a.vc + ((size_t)kvh * HD + c) * ldc + key0 + 4 * kg;
+  uint2 vf[8][2][2];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    qa[ks].x = qv ? qa[ks].x : 0u;
-    qa[ks].y = qv ? qa[ks].y : 0u;
-    qa[ks].z = qv ? qa[ks].z : 0u;
-    qa[ks].w = qv ? qa[ks].w : 0u;
-  }
+  for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-  for (int i = 0; i < VL; ++i) {
-    const bool keep = key0 + (tid + 256 * i) / (HD / 8) <= maxpos;   // P is 0 past it; keep 0 * V finite
-    vv[i].x = keep ? vv[i].x : 0u;
-    vv[i].y = keep ? vv[i].y : 0u;
-    vv[i].z = keep ? vv[i].z : 0u;
-    vv[i].w = keep ? vv[i].w : 0u;
-  }
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) vf[dt][ks][h] = *(const uint2*)(vb + (size_t)16 * dt * ldc + 32 * ks + 16 * h);
 
-  // S = Q . K^T for this wave's 16 query vectors x 64 keys
+  const int pos = st0 + a.pos_off + qr;   // this lane's query position
   f32x4 s[4];
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt) {
     s[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
-      s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[ks]),
-                                                      __builtin_bit_cast(bf16x8, kf[kt][ks]), s[kt], 0, 0, 0);
+      s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[kt][ks]),
+                                                      __builtin_bit_cast(bf16x8, qa[ks]), s[kt], 0, 0, 0);
   }
-  // lane holds S[query 4*kg+i][key kt*16+c]
-  float mx[4], l[4];
-  int pos_i[4];
-  bool row_ok[4];
+  // softmax over this partition's keys for query c
+  float m = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int q2 = wave * 16 + 4 * kg + i;
-    row_ok[i] = q2 < QV;
-    pos_i[i] = base + row0 + q2 / G;
-    float m = -INFINITY;
+  for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      const bool valid = row_ok[i] && key0 + kt * 16 + c <= pos_i[i];
+    for (int i = 0; i < 4; ++i) {
+      const bool valid = qv && key0 + 16 * kt + 4 * kg + i <= pos;
       m = valid ? fmaxf(m, s[kt][i] * a.scale_log2) : m;
     }
+  m = fmaxf(m, __shfl_xor(m, 16));
+  m = fmaxf(m, __shfl_xor(m, 32));
+  float l = 0.f;
+  uint32_t ph[2][4], pl[2][4];   // P^T hi / lo fragments, bf16 pairs
 #pragma unroll
-    for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
-    mx[i] = m;
-    float sum = 0.f;
+  for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      const bool valid = row_ok[i] && key0 + kt * 16 + c <= pos_i[i];
-      const float pv = valid ? exp2f(s[kt][i] * a.scale_log2 - m) : 0.f;
-      sum += pv;
-      // P = hi + lo, both bf16: the P.V products keep ~16 significant bits
-      const uint16_t hi = f2bf(pv);
-      Ps[wave][4 * kg + i][kt * 16 + c] = hi;
-      Pl[wave][4 * kg + i][kt * 16 + c] = f2bf(pv - bf2f(hi));
+    for (int i = 0; i < 4; i += 2) {
+      float pv[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const bool valid = qv && key0 + 16 * kt + 4 * kg + i + u <= pos;
+        pv[u] = valid ? exp2f(s[kt][i + u] * a.scale_log2 - m) : 0.f;
+        l += pv[u];
+      }
+      const uint16_t h0 = f2bf(pv[0]), h1 = f2bf(pv[1]);
+      const uint16_t l0 = f2bf(pv[0] - bf2f(h0)), l1 = f2bf(pv[1] - bf2f(h1));
+      // K-step kt/2; elements 0..3 from even kt, 4..7 from odd kt
+      ph[kt >> 1][(kt & 1) * 2 + i / 2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+      pl[kt >> 1][(kt & 1) * 2 + i / 2] = (uint32_t)l0 | ((uint32_t)l1 << 16);
     }
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) sum += __shfl_xor(sum, o);
-    l[i] = sum;
-  }
-#pragma unroll
-  for (int i = 0; i < VL; ++i) {
-    const int e = tid + 256 * i, key = e / (HD / 8), d0 = (e % (HD / 8)) * 8;
-    const uint32_t wds[4] = {vv[i].x, vv[i].y, vv[i].z, vv[i].w};
-#pragma unroll
-    for (int j = 0; j < 8; ++j) Vt[d0 + j][key] = (uint16_t)(wds[j >> 1] >> (16 * (j & 1)));
-  }
-  __syncthreads();
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
 
-  // O = P . V
+  // keys past the last row's position: P is 0 there; keep 0 * V finite
+  const int maxpos = st0 + a.pos_off + a.M - 1;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const bool keep = key0 + 32 * ks + 16 * h + 4 * kg + 3 <= maxpos;
+      if (!keep) {
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          const int k = key0 + 32 * ks + 16 * h + 4 * kg;
+          uint2 v = vf[dt][ks][h];
+          // zero the 16-bit entries past maxpos
+          v.x = k > maxpos ? 0u : (k + 1 > maxpos ? (v.x & 0xffffu) : v.x);
+          v.y = k + 2 > maxpos ? 0u : (k + 3 > maxpos ? (v.y & 0xffffu) : v.y);
+          vf[dt][ks][h] = v;
+        }
+      }
+    }
+
   f32x4 o[8];
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int dt = 0; dt < 8; ++dt) {
+    o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    const uint4 pa = *(const uint4*)&Ps[wave][c][ks * 32 + kg * 8];
-    const uint4 pl = *(const uint4*)&Pl[wave][c][ks * 32 + kg * 8];
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const uint4 vf = *(const uint4*)&Vt[dt * 16 + c][ks * 32 + kg * 8];
-      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pa),
-                                                      __builtin_bit_cast(bf16x8, vf), o[dt], 0, 0, 0);
-      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pl),
-                                                      __builtin_bit_cast(bf16x8, vf), o[dt], 0, 0, 0);
+    for (int ks = 0; ks < 2; ++ks) {
+      const uint4 va = {vf[dt][ks][0].x, vf[dt][ks][0].y, vf[dt][ks][1].x, vf[dt][ks][1].y};
+      const uint4 bh = {ph[ks][0], ph[ks][1], ph[ks][2], ph[ks][3]};
+      const uint4 bl = {pl[ks][0], pl[ks][1], pl[ks][2], pl[ks][3]};
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va), __builtin_bit_cast(bf16x8, bh),
+                                                      o[dt], 0, 0, 0);
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va), __builtin_bit_cast(bf16x8, bl),
+                                                      o[dt], 0, 0, 0);
     }
   }
+  if (!qv || key0 > pos) return;
+  const int row = qr, head = kvh * G + qg;
+  const size_t ph_i = ((size_t)p * a.R + row) * a.hq + head;
+  float* po = a.part_o + ph_i * HD + 4 * kg;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if (!row_ok[i] || key0 > pos_i[i]) continue;
-    const int q2 = wave * 16 + 4 * kg + i;
-    const int row = row0 + q2 / G, head = kvh * G + q2 % G;
-    const size_t ph = ((size_t)p * a.R + row) * a.hq + head;
-    float* po = a.part_o + ph * HD;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) po[dt * 16 + c] = o[dt][i];
-    if (c == 0) {
-      a.part_ml[ph * 2] = mx[i];
-      a.part_ml[ph * 2 + 1] = l[i];
-    }
+  for (int dt = 0; dt < 8; ++dt) *(f32x4*)(po + 16 * dt) = o[dt];
+  if (kg == 0) {
+    a.part_ml[ph_i * 2] = m;
+    a.part_ml[ph_i * 2 + 1] = l;
   }
 }
 
@@ -1009,9 +989,10 @@ static hipError_t attn_dispatch(const AttnArgs& a, int n_part, int hd, hipStream
   dim3 grid(n_part, a.hkv, (a.M + ROW_TILE - 1) / ROW_TILE);
   bool done = false;
   if (sizeof(E) == 2 && hd == 128) {
-    if (G == 1) { attn_mfma_kernel<1><<<grid, 256, 0, s>>>(a); done = true; }
-    if (G == 2) { attn_mfma_kernel<2><<<grid, 256, 0, s>>>(a); done = true; }
-    if (G == 4) { attn_mfma_kernel<4><<<grid, 256, 0, s>>>(a); done = true; }
+    const dim3 gq(n_part, a.hkv, (a.M * G + 15) / 16);   // one wave per 16 query vectors
+    if (G == 1) { attn_mfma_kernel<1><<<gq, 64, 0, s>>>(a); done = true; }
+    if (G == 2) { attn_mfma_kernel<2><<<gq, 64, 0, s>>>(a); done = true; }
+    if (G == 4) { attn_mfma_kernel<4><<<gq, 64, 0, s>>>(a); done = true; }
   }
 #define SSD_ATT(HDv, Gv) \
   if (!done && hd == HDv && G == Gv) { attn_kernel<E, HDv, Gv><<<grid, 256, 0, s>>>(a); done = true; }

@@ -82,7 +82,7 @@ struct ssd_ctx {
   float *x, *ss, *logits, *part_o, *part_ml, *cos_t, *sin_t, *amax_v;
   int* amax_i;
   void *xn, *q, *att, *act, *kc, *vc, *tap, *feat;
-  int *counters, *block, *post, *toks, *dstate, *result, *outlog;
+  int *block, *post, *toks, *dstate, *result, *outlog;
   int *tblock, *tpost, *tstate, *tresult, *toutlog;
   float *m_rlogits, *m_gates, *m_slot_out;
   int *m_ids, *m_inject, *m_groups, *m_union;
@@ -94,7 +94,9 @@ constexpr int kCtxBucket = 512;   // positions per graph context bucket (multipl
 
 inline void* at(ssd_ctx* c, size_t off) { return c->ws + off; }
 
-size_t cache_layer_elems(const ssd_cfg& c) { return (size_t)c.n_kv_heads * c.max_ctx * c.head_dim; }
+// positions per KV cache row: max_ctx rounded up to whole attention partitions
+inline int kv_stride(const ssd_cfg& c) { return (c.max_ctx + ATT_PT - 1) / ATT_PT * ATT_PT; }
+size_t cache_layer_elems(const ssd_cfg& c) { return (size_t)c.n_kv_heads * kv_stride(c) * c.head_dim; }
 
 MoeArgs moe_args(ssd_ctx* c, int l, int M) {
   const ssd_cfg& g = c->cfg;
@@ -152,15 +154,15 @@ ssd_status layer_forward(ssd_ctx* c, int l, int M, int pos_off, bool feats, cons
     a.X = c->xn; a.ldx = d; a.W0 = w.wq; a.W1 = w.wk; a.W2 = w.wv;
     a.n0 = hq * hd; a.n1 = hkv * hd; a.M = M; a.N = (hq + 2 * hkv) * hd; a.K = d;
     a.q = c->q; a.kc = kc; a.vc = vc; a.cos_t = c->cos_t; a.sin_t = c->sin_t;
-    a.state = c->dstate; a.pos_off = pos_off; a.hq = hq; a.hkv = hkv; a.hd = hd; a.max_ctx = g.max_ctx;
+    a.state = c->dstate; a.pos_off = pos_off; a.hq = hq; a.hkv = hkv; a.hd = hd; a.max_ctx = kv_stride(g);
     if (fold) fold_in(c, a, 0);
     HIPCHK(launch_gemm(dt, EPI_QKV, a, s));
   }
   {
     AttnArgs a{};
     a.q = c->q; a.kc = kc; a.vc = vc; a.out = c->att; a.part_o = c->part_o; a.part_ml = c->part_ml;
-    a.counters = c->counters; a.state = c->dstate; a.pos_off = pos_off; a.M = M; a.R = c->lay.R;
-    a.hq = hq; a.hkv = hkv; a.hd = hd; a.max_ctx = g.max_ctx;
+    a.state = c->dstate; a.pos_off = pos_off; a.M = M; a.R = c->lay.R;
+    a.hq = hq; a.hkv = hkv; a.hd = hd; a.max_ctx = kv_stride(g);
     a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)hd));
     // a captured pass covers the partitions of its context bucket; workgroups
     // past the last row's position store nothing
@@ -490,7 +492,6 @@ ssd_status ssd_load(const ssd_cfg* cfg, const ssd_buf* weights, int32_t n_weight
   c->amax_v = (float*)at(c, lay.amax_v); c->amax_i = (int*)at(c, lay.amax_i);
   c->trace = (float*)at(c, lay.trace);
   c->part_o = (float*)at(c, lay.part_o); c->part_ml = (float*)at(c, lay.part_ml);
-  c->counters = (int*)at(c, lay.counters);
   c->cos_t = (float*)at(c, lay.rope_cos); c->sin_t = (float*)at(c, lay.rope_sin);
   c->block = (int*)at(c, lay.block); c->post = (int*)at(c, lay.post); c->toks = (int*)at(c, lay.toks);
   c->dstate = (int*)at(c, lay.state); c->result = (int*)at(c, lay.result); c->outlog = (int*)at(c, lay.outlog);
@@ -771,13 +772,21 @@ ssd_status ssd_read_kv(ssd_ctx* c, int32_t layer, int32_t pos0, int32_t n, void*
   const ssd_cfg& g = c->cfg;
   if (layer < 0 || layer >= g.n_layers || pos0 < 0 || n < 1 || pos0 + n > g.max_ctx)
     return fail(SSD_E_ARG, "layer/positions out of range");
-  const size_t hd = g.head_dim, row = hd * c->esz;
+  const size_t hd = g.head_dim, row = hd * c->esz, ld = kv_stride(g), esz = c->esz;
+  // V rows are head dims ([dim][position]): gather [h][dim][n] then transpose
+  std::vector<char> vt((size_t)g.n_kv_heads * hd * n * esz);
   for (int h = 0; h < g.n_kv_heads; ++h) {
-    const size_t off = (((size_t)layer * g.n_kv_heads + h) * g.max_ctx + pos0) * row;
-    HIPCHK(hipMemcpyAsync((char*)k_host + (size_t)h * n * row, (char*)c->kc + off, n * row, hipMemcpyDeviceToHost, c->stream));
-    HIPCHK(hipMemcpyAsync((char*)v_host + (size_t)h * n * row, (char*)c->vc + off, n * row, hipMemcpyDeviceToHost, c->stream));
+    const size_t koff = (((size_t)layer * g.n_kv_heads + h) * ld + pos0) * row;
+    HIPCHK(hipMemcpyAsync((char*)k_host + (size_t)h * n * row, (char*)c->kc + koff, n * row, hipMemcpyDeviceToHost, c->stream));
+    const size_t voff = (((size_t)layer * g.n_kv_heads + h) * hd * ld + pos0) * esz;
+    HIPCHK(hipMemcpy2DAsync(vt.data() + (size_t)h * hd * n * esz, n * esz, (char*)c->vc + voff, ld * esz, n * esz, hd,
+                            hipMemcpyDeviceToHost, c->stream));
   }
   HIPCHK(hipStreamSynchronize(c->stream));
+  for (int h = 0; h < g.n_kv_heads; ++h)
+    for (size_t dd = 0; dd < hd; ++dd)
+      for (int r = 0; r < n; ++r)
+        memcpy((char*)v_host + (((size_t)h * n + r) * hd + dd) * esz, vt.data() + (((size_t)h * hd + dd) * n + r) * esz, esz);
   return SSD_OK;
 }
 
@@ -889,7 +898,7 @@ ssd_status ssd_time_op(ssd_ctx* c, int32_t op, int32_t layer, int32_t m, int32_t
       case 2:
         a.X = c->xn; a.ldx = d; a.W0 = w.wq; a.W1 = w.wk; a.W2 = w.wv; a.n0 = hq * hd; a.n1 = hkv * hd; a.M = m;
         a.N = (hq + 2 * hkv) * hd; a.K = d; a.q = c->q; a.kc = kc; a.vc = vc; a.cos_t = c->cos_t; a.sin_t = c->sin_t;
-        a.state = c->dstate; a.pos_off = 0; a.hq = hq; a.hkv = hkv; a.hd = hd; a.max_ctx = g.max_ctx;
+        a.state = c->dstate; a.pos_off = 0; a.hq = hq; a.hkv = hkv; a.hd = hd; a.max_ctx = kv_stride(g);
         epi = EPI_QKV; break;
       case 3:
         a.X = c->att; a.ldx = hq * hd; a.W0 = w.wo; a.M = m; a.N = d; a.K = hq * hd; a.y = c->x; a.ldy = d;
@@ -913,8 +922,8 @@ ssd_status ssd_time_op(ssd_ctx* c, int32_t op, int32_t layer, int32_t m, int32_t
     } else if (op == 5) {
       AttnArgs at{};
       at.q = c->q; at.kc = kc; at.vc = vc; at.out = c->att; at.part_o = c->part_o; at.part_ml = c->part_ml;
-      at.counters = c->counters; at.state = c->dstate; at.pos_off = 0; at.M = m; at.R = c->lay.R;
-      at.hq = hq; at.hkv = hkv; at.hd = hd; at.max_ctx = g.max_ctx;
+      at.state = c->dstate; at.pos_off = 0; at.M = m; at.R = c->lay.R;
+      at.hq = hq; at.hkv = hkv; at.hd = hd; at.max_ctx = kv_stride(g);
       at.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)hd));
       HIPCHK(launch_attention(dt, at, (c->n + m + ATT_PT - 1) / ATT_PT, s));
     } else {
