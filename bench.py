@@ -76,7 +76,7 @@ def measured_traffic() -> float | None:
     except OSError:
         return None
     csrc = os.path.join(ROOT, "self_speculative_decoding_amd", "csrc")
-    sha = hashlib.sha256(open(os.path.join(csrc, "kernels.hip"), "rb").read() +
+    sha = hashlib.sha256(open(os.path.join(csrc, "gemm.hip"), "rb").read() +
                          open(os.path.join(csrc, "device.h"), "rb").read()).hexdigest()
     rec_sha = nbytes = None
     for line in txt.splitlines():

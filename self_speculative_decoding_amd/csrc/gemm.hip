@@ -1,0 +1,471 @@
+// gfx950 (CDNA4) GEMMs of the greedy self-speculative decode step: the bf16
+// weight-streaming GEMM on MFMA with its fused epilogues (QKV + RoPE + KV
+// append, residual + folded-norm outputs, SwiGLU, logits + argmax partials),
+// the load-time weight packing, and the float32 GEMM of small float32 models.
+//
+// Every reduction has an order fixed by the shape and by the row's own data
+// only, never by the number of rows in the pass (see kernels.hip).
+#include "device.h"
+
+// Build-time tuning of the decode GEMMs: load-batch depth in 64-element
+// chunks (U1 one-matrix, U2 gate/up; the batch depth does not change the
+// accumulation order) and waves per workgroup (gate/up; other
+// GEMMs with fewer than 1024 column tiles; wider GEMMs such as the LM head).
+#ifndef SSD_GEMM_U1
+#define SSD_GEMM_U1 4
+#endif
+#ifndef SSD_GEMM_U2
+#define SSD_GEMM_U2 2
+#endif
+#ifndef SSD_GEMM_U1_LONGK   // one-matrix GEMMs with K >= 8192 (the FFN down projection)
+#define SSD_GEMM_U1_LONGK 2
+#endif
+#ifndef SSD_GEMM_UW         // GEMMs with >= 1024 column tiles (the LM head)
+#define SSD_GEMM_UW 2
+#endif
+#ifndef SSD_KW_SWIGLU
+#define SSD_KW_SWIGLU 8
+#endif
+#ifndef SSD_KW_NARROW
+#define SSD_KW_NARROW 8
+#endif
+#ifndef SSD_KW_WIDE
+#define SSD_KW_WIDE 8
+#endif
+
+namespace ssd {
+
+// ---------------------------------------------------------------------------
+// GEMM epilogues
+// ---------------------------------------------------------------------------
+
+template <typename E>
+__device__ __forceinline__ void epi_single(const GemmArgs& a, int epi, int m, int n, float v) {
+  if (epi == EPI_F32) {
+    a.y[(size_t)m * a.ldy + n] = v;
+  } else if (epi == EPI_LOGITS) {
+    a.y[(size_t)m * a.ldy + n] = v;
+  } else if (epi == EPI_RESID) {
+    const float r = a.y[(size_t)m * a.ldy + n] + v;
+    a.y[(size_t)m * a.ldy + n] = r;
+    if (a.tap) ((E*)a.tap)[(size_t)m * a.ldtap + n] = fromf<E>(r);
+  } else {  // EPI_STORE
+    ((E*)a.out)[(size_t)m * a.ldo + n] = fromf<E>(v);
+  }
+}
+
+template <typename E>
+__device__ __forceinline__ void epi_swiglu(const GemmArgs& a, int m, int n, float g, float u) {
+  const float s = g / (1.0f + expf(-g));
+  ((E*)a.out)[(size_t)m * a.ldo + n] = fromf<E>(s * u);
+}
+
+// (v0, v1) are dims (i, i + hd/2) of output head `head` of [q | k | v]
+template <typename E>
+__device__ __forceinline__ void epi_qkv_pair(const GemmArgs& a, int base, int m, int head, int i, float v0, float v1) {
+  const int half = a.hd >> 1;
+  const int pos = base + m;
+  if (head < a.hq + a.hkv) {
+    const float c = a.cos_t[(size_t)pos * half + i], s = a.sin_t[(size_t)pos * half + i];
+    const float o0 = v0 * c - v1 * s, o1 = v1 * c + v0 * s;
+    E* dst = head < a.hq ? (E*)a.q + (size_t)m * a.hq * a.hd + (size_t)head * a.hd
+                         : (E*)a.kc + ((size_t)(head - a.hq) * a.max_ctx + pos) * a.hd;
+    dst[i] = fromf<E>(o0);
+    dst[i + half] = fromf<E>(o1);
+  } else {   // V cache: [kv head][dim][position]
+    E* dst = (E*)a.vc + (size_t)(head - a.hq - a.hkv) * a.hd * a.max_ctx + pos;
+    dst[(size_t)i * a.max_ctx] = fromf<E>(v0);
+    dst[(size_t)(i + half) * a.max_ctx] = fromf<E>(v1);
+  }
+}
+
+// as epi_qkv_pair for a q or k head, with the rotary cos/sin already loaded
+template <typename E>
+__device__ __forceinline__ void epi_qkv_rot(const GemmArgs& a, int base, int m, int head, int i, float v0, float v1,
+                                            float c, float s) {
+  const int half = a.hd >> 1;
+  const int pos = base + m;
+  const float o0 = v0 * c - v1 * s, o1 = v1 * c + v0 * s;
+  E* dst = head < a.hq ? (E*)a.q + (size_t)m * a.hq * a.hd + (size_t)head * a.hd
+                       : (E*)a.kc + ((size_t)(head - a.hq) * a.max_ctx + pos) * a.hd;
+  dst[i] = fromf<E>(o0);
+  dst[i + half] = fromf<E>(o1);
+}
+
+template <typename E>
+__device__ __forceinline__ void epi_v_single(const GemmArgs& a, int base, int m, int vh, int dim, float v) {
+  const int pos = base + m;
+  ((E*)a.vc)[((size_t)vh * a.hd + dim) * a.max_ctx + pos] = fromf<E>(v);   // [kv head][dim][position]
+}
+
+// ---------------------------------------------------------------------------
+// bf16 skinny GEMM on MFMA 16x16x32 (weight streaming)
+//
+// Y[M,N] = X[M,K] . W[N,K]^T, M padded to 16-row tiles (grid.y).  A workgroup
+// of KW waves owns NW 16-column tiles (NW = 2: the gate and up tiles of the
+// same columns); the waves split K into KW contiguous ranges, each
+// accumulating its MFMA K-steps in order, and the ranges are added in wave
+// order through LDS.  KW and the load-batch depth depend on the shape only,
+// so the per-element arithmetic is a function of (shape, row data).  Weights
+// come from the packed tile layout (device.h): each wave load instruction
+// reads 1 KB contiguous, nontemporal, U 64-element chunks per batch.
+//
+// MFMA 16x16x32 bf16 lane layout: A row = lane%16, B column = lane%16, both
+// with the same 8-element K group lane/16; D: column lane%16, rows
+// 4*(lane/16) .. +3.
+// ---------------------------------------------------------------------------
+
+
+// Row m's sum-of-squares partials (one per 16 columns, nss of them): lane l
+// holds partials 4l..4l+3; partials from 256 on are added after, 64 apart.
+// The order is fixed by nss alone, whatever the pass width.
+__device__ __forceinline__ float4 ss_part(const GemmArgs& a, int m, bool row_ok, int lane) {
+  if (!row_ok || m >= a.M || 4 * lane >= a.nss) return make_float4(0.f, 0.f, 0.f, 0.f);
+  return *(const float4*)(a.ss_in + (size_t)m * a.nss + 4 * lane);
+}
+
+__device__ __forceinline__ float ss_rstd(const GemmArgs& a, int m, bool row_ok, int lane, float4 v) {
+  float s = ((v.x + v.y) + v.z) + v.w;
+  if (row_ok && m < a.M)
+    for (int p = 256 + lane; p < a.nss; p += 64) s += a.ss_in[(size_t)m * a.nss + p];
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) s += __shfl_xor(s, o);
+  return 1.0f / sqrtf(s / (float)a.K + a.eps);
+}
+
+// Output head and head dim of lane c in column tile t of the QKV GEMM.  Its
+// packed weight rows put the RoPE pair (i, i + hd/2) of a q or k head on
+// lanes c and c^8: tile columns 8jj..8jj+7 and hd/2+8jj..+7 of the head.
+__device__ __forceinline__ void qkv_col(const GemmArgs& a, int t, int c, int* head_out, int* dim_out) {
+  const int col0 = t * 16;
+  const int head = col0 / a.hd, jj = (col0 % a.hd) / 16, half = a.hd >> 1;
+  *head_out = head;
+  *dim_out = head < a.hq + a.hkv ? (c < 8 ? 8 * jj + c : half + 8 * jj + (c - 8)) : 16 * jj + c;
+}
+
+template <int EPI, int NW, int KW, int MT, int U>
+__global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = lane & 15, kg = lane >> 4;
+  const int t = blockIdx.x;
+  const uint16_t* xr[MT];
+  bool av_ok[MT];
+#pragma unroll
+  for (int r = 0; r < MT; ++r) {
+    const int am = (blockIdx.y * MT + r) * 16 + c;
+    av_ok[r] = am < a.M;
+    xr[r] = (const uint16_t*)a.X + (size_t)(av_ok[r] ? am : 0) * a.ldx + kg * 16;
+  }
+  const int S = a.K >> 6;   // 64-element chunks
+  // packed weight tiles of this column tile (gate/up interleaved when NW = 2)
+  const uint16_t* wr[NW];
+#pragma unroll
+  for (int j = 0; j < NW; ++j)
+    wr[j] = (const uint16_t*)a.W0 + ((size_t)t * S * NW + j) * PACK_TILE + 8 * lane;
+  int head = 0, dim = 0;
+  if (EPI == EPI_QKV) qkv_col(a, t, c, &head, &dim);
+
+  const int s0 = (S * wave) / KW, s1 = (S * (wave + 1)) / KW;
+
+  // Epilogue inputs fetched before the weight stream so that their latency
+  // hides behind it: the position base (QKV) and, for one-tile launches, the
+  // residual entries wave 0 will update.
+  const int base = EPI == EPI_QKV ? a.state[0] + a.pos_off : 0;
+  float yv[4] = {0.f, 0.f, 0.f, 0.f};
+  if (EPI == EPI_RESID && MT == 1 && wave == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = blockIdx.y * 16 + 4 * kg + i;
+      if (m < a.M) yv[i] = a.y[(size_t)m * a.ldy + t * 16 + c];
+    }
+  }
+
+  // folded RMSNorm: wave w owns tile rows w, w + KW, ...  One-tile launches
+  // load the rows' sum-of-squares partials before the weight stream so the
+  // loads overlap it; multi-tile launches load them afterwards.
+  constexpr int RPW = (16 * MT + KW - 1) / KW;   // rows per wave
+  constexpr int RPRE = MT == 1 ? RPW : 1;
+  const bool fold = a.ss_in != nullptr;
+  float4 ssv[RPRE];
+  if (MT == 1 && fold) {
+#pragma unroll
+    for (int r = 0; r < RPRE; ++r) ssv[r] = ss_part(a, blockIdx.y * 16 + wave + r * KW, r * KW + wave < 16, lane);
+  }
+  f32x4 acc[MT][NW];
+#pragma unroll
+  for (int r = 0; r < MT; ++r)
+#pragma unroll
+    for (int j = 0; j < NW; ++j) acc[r][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // chunks per batch of loads (fewer for the two-matrix gate/up GEMM keeps
+  // its register count, and so the workgroups resident per CU, in check)
+  float rc[4] = {0.f, 0.f, 0.f, 0.f}, rsn[4] = {0.f, 0.f, 0.f, 0.f};   // RoPE cos/sin (QKV)
+  if (MT == 1 && EPI == EPI_QKV) {
+    // first load batch, then the rotary table entries of wave 0's epilogue
+    // (they need the position), then the rest of the K range
+    const int sm = min(s0 + U, s1);
+    mfma_stream<NW, true, U>(xr[0], av_ok[0], wr, s0, sm, acc[0]);
+    if (wave == 0 && head < a.hq + a.hkv && c < 8) {
+      const int half = a.hd >> 1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = blockIdx.y * 16 + 4 * kg + i;
+        if (m < a.M) {
+          rc[i] = a.cos_t[(size_t)(base + m) * half + dim];
+          rsn[i] = a.sin_t[(size_t)(base + m) * half + dim];
+        }
+      }
+    }
+    mfma_stream<NW, true, U>(xr[0], av_ok[0], wr, sm, s1, acc[0]);
+  } else if (MT == 1) {
+    mfma_stream<NW, true, U>(xr[0], av_ok[0], wr, s0, s1, acc[0]);
+  }
+  else mfma_stream_mt<NW, MT>(xr, av_ok, wr, s0, s1, acc);
+
+  __shared__ f32x4 red[KW - 1][MT][NW][64];
+  __shared__ float rs[16 * MT];
+  if (fold) {
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      const int row = r * KW + wave;
+      const int m = blockIdx.y * 16 * MT + row;
+      const float4 v = MT == 1 ? ssv[r < RPRE ? r : 0] : ss_part(a, m, row < 16 * MT, lane);
+      const float f = ss_rstd(a, m, row < 16 * MT, lane, v);
+      if (lane == 0 && row < 16 * MT) rs[row] = f;
+    }
+  }
+  if (wave > 0) {
+#pragma unroll
+    for (int r = 0; r < MT; ++r)
+#pragma unroll
+      for (int j = 0; j < NW; ++j) red[wave - 1][r][j][lane] = acc[r][j];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int w = 0; w < KW - 1; ++w)
+#pragma unroll
+    for (int r = 0; r < MT; ++r)
+#pragma unroll
+      for (int j = 0; j < NW; ++j) acc[r][j] = acc[r][j] + red[w][r][j][lane];
+  if (fold) {
+    // rows of this lane's accumulators: 4*kg + i of each 16-row tile
+#pragma unroll
+    for (int r = 0; r < MT; ++r)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float f = rs[r * 16 + 4 * kg + i];
+#pragma unroll
+        for (int j = 0; j < NW; ++j) acc[r][j][i] *= f;
+      }
+  }
+
+#pragma unroll
+  for (int r = 0; r < MT; ++r) {
+    const int mt = blockIdx.y * MT + r;
+    if (EPI == EPI_QKV) {
+      const bool rot = head < a.hq + a.hkv;
+      float part[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) part[i] = __shfl_xor(acc[r][0][i], 8);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = mt * 16 + 4 * kg + i;
+        if (m >= a.M) continue;
+        if (rot) {
+          if (c < 8 && MT == 1) epi_qkv_rot<uint16_t>(a, base, m, head, dim, acc[r][0][i], part[i], rc[i], rsn[i]);
+          else if (c < 8) epi_qkv_pair<uint16_t>(a, base, m, head, dim, acc[r][0][i], part[i]);
+        } else {
+          epi_v_single<uint16_t>(a, base, m, head - a.hq - a.hkv, dim, acc[r][0][i]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = mt * 16 + 4 * kg + i;
+        const int n = t * 16 + c;
+        if (EPI == EPI_LOGITS) {
+          // (max, lowest index) over this tile's 16 columns, fixed butterfly
+          float bv = acc[r][0][i];
+          int bi = n;
+#pragma unroll
+          for (int o = 1; o < 16; o <<= 1) {
+            const float ov = __shfl_xor(bv, o);
+            const int oi = __shfl_xor(bi, o);
+            if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+          }
+          if (m < a.M && c == 0) {
+            a.amax_v[(size_t)m * gridDim.x + t] = bv;
+            a.amax_i[(size_t)m * gridDim.x + t] = bi;
+          }
+        }
+        if (EPI == EPI_RESID && a.ss_out) {
+          // new residual, its sum of squares over this tile's 16 columns and
+          // bf16(x * gain) for the GEMM that consumes it
+          const float xv = m < a.M ? (MT == 1 ? yv[i] : a.y[(size_t)m * a.ldy + n]) + acc[r][0][i] : 0.f;
+          float sq = xv * xv;
+#pragma unroll
+          for (int o = 1; o < 16; o <<= 1) sq += __shfl_xor(sq, o);
+          if (m < a.M) {
+            a.y[(size_t)m * a.ldy + n] = xv;
+            if (a.tap) ((uint16_t*)a.tap)[(size_t)m * a.ldtap + n] = f2bf(xv);
+            ((uint16_t*)a.xg_out)[(size_t)m * a.ldy + n] = f2bf(xv * bf2f(((const uint16_t*)a.gain_next)[n]));
+            if (c == 0) a.ss_out[(size_t)m * gridDim.x + t] = sq;
+          }
+          continue;
+        }
+        if (m >= a.M) continue;
+        if (EPI == EPI_SWIGLU) epi_swiglu<uint16_t>(a, m, n, acc[r][0][i], acc[r][NW - 1][i]);
+        else if (EPI == EPI_RESID && MT == 1) {
+          const float xv = yv[i] + acc[r][0][i];
+          a.y[(size_t)m * a.ldy + n] = xv;
+          if (a.tap) ((uint16_t*)a.tap)[(size_t)m * a.ldtap + n] = f2bf(xv);
+        } else epi_single<uint16_t>(a, EPI, m, n, acc[r][0][i]);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// weight packing (load time): one workgroup per packed tile, 16 bytes per thread
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(128) void pack_kernel(PackArgs p) {
+  const int t = blockIdx.x, s = blockIdx.y, which = blockIdx.z;
+  const int l = threadIdx.x & 63, h = threadIdx.x >> 6, g = l >> 4, c = l & 15;
+  const uint16_t* src;
+  size_t row;
+  if (p.mode == 1) {
+    const int col0 = t * 16;
+    const int head = col0 / p.hd, jj = (col0 % p.hd) / 16, half = p.hd >> 1;
+    const int dim = head < p.hq + p.hkv ? (c < 8 ? 8 * jj + c : half + 8 * jj + (c - 8)) : 16 * jj + c;
+    if (head < p.hq) { src = (const uint16_t*)p.src0; row = (size_t)head * p.hd + dim; }
+    else if (head < p.hq + p.hkv) { src = (const uint16_t*)p.src1; row = (size_t)(head - p.hq) * p.hd + dim; }
+    else { src = (const uint16_t*)p.src2; row = (size_t)(head - p.hq - p.hkv) * p.hd + dim; }
+  } else {
+    src = (const uint16_t*)(which ? p.src1 : p.src0);
+    row = (size_t)t * 16 + c;
+  }
+  const uint4 v = *(const uint4*)(src + row * p.K + (size_t)s * 64 + 16 * g + 8 * h);
+  const size_t tile = ((size_t)t * (p.K / 64) + s) * (p.pair ? 2 : 1) + which;
+  *(uint4*)((uint16_t*)p.dst + tile * PACK_TILE + h * (PACK_TILE / 2) + 8 * l) = v;
+}
+
+hipError_t launch_pack(const PackArgs& p, hipStream_t s) {
+  if (p.N % 16 || p.K % 64 || p.N <= 0 || p.K <= 0) return hipErrorInvalidValue;
+  pack_kernel<<<dim3(p.N / 16, p.K / 64, p.pair ? 2 : 1), 128, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// float32 GEMM on the vector ALU (small float32 models)
+//
+// One wave owns one output pair: (i, i + hd/2) of a q/k/v head for QKV,
+// (gate i, up i) for SwiGLU, (2i, 2i+1) otherwise.  Lanes stride over K in
+// order and a fixed butterfly adds the lane partials.
+// ---------------------------------------------------------------------------
+
+template <int EPI>
+__global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int pi = blockIdx.x * 4 + wave;
+  int npairs, head = 0, i = 0;
+  const float *w0, *w1;
+  if (EPI == EPI_QKV) {
+    const int half = a.hd >> 1;
+    npairs = (a.hq + 2 * a.hkv) * half;
+    if (pi >= npairs) return;
+    head = pi / half;
+    i = pi % half;
+    const float* W;
+    size_t r;
+    if (head < a.hq) { W = (const float*)a.W0; r = (size_t)head * a.hd + i; }
+    else if (head < a.hq + a.hkv) { W = (const float*)a.W1; r = (size_t)(head - a.hq) * a.hd + i; }
+    else { W = (const float*)a.W2; r = (size_t)(head - a.hq - a.hkv) * a.hd + i; }
+    w0 = W + r * a.K;
+    w1 = W + (r + half) * a.K;
+  } else if (EPI == EPI_SWIGLU) {
+    npairs = a.N;
+    if (pi >= npairs) return;
+    w0 = (const float*)a.W0 + (size_t)pi * a.K;
+    w1 = (const float*)a.W1 + (size_t)pi * a.K;
+  } else {
+    npairs = a.N >> 1;
+    if (pi >= npairs) return;
+    w0 = (const float*)a.W0 + (size_t)(2 * pi) * a.K;
+    w1 = w0 + a.K;
+  }
+  const int m1 = min(a.M, (int)(blockIdx.y + 1) * 16);
+  for (int m = blockIdx.y * 16; m < m1; ++m) {
+    const float* xr = (const float*)a.X + (size_t)m * a.ldx;
+    float s0 = 0.f, s1 = 0.f;
+    for (int k = lane; k < a.K; k += 64) {
+      const float xv = xr[k];
+      s0 = fmaf(xv, w0[k], s0);
+      s1 = fmaf(xv, w1[k], s1);
+    }
+    s0 = wave_sum(s0);
+    s1 = wave_sum(s1);
+    if (lane == 0) {
+      if (EPI == EPI_QKV) epi_qkv_pair<float>(a, a.state[0] + a.pos_off, m, head, i, s0, s1);
+      else if (EPI == EPI_SWIGLU) epi_swiglu<float>(a, m, pi, s0, s1);
+      else {
+        epi_single<float>(a, EPI, m, 2 * pi, s0);
+        epi_single<float>(a, EPI, m, 2 * pi + 1, s1);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launcher
+// ---------------------------------------------------------------------------
+
+hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t s) {
+  const int mt = (a.M + 15) / 16;
+  if (dtype) {
+    int tiles;
+    if (epi == EPI_QKV) tiles = (a.hq + 2 * a.hkv) * a.hd / 16;
+    else tiles = a.N / 16;
+    dim3 grid(tiles, mt);
+    const bool wide = tiles >= 1024;   // a function of N only
+    // decode-loop passes (M <= SSD_MAX_BLOCK rows) always take the one-tile
+    // kernel, so a row's arithmetic never depends on the pass width; longer
+    // passes (prefill chunks) let 4 row tiles share each weight load
+    const bool multi = a.M > 32;
+    const dim3 grid_mt(tiles, (a.M + 63) / 64);
+#define SSD_G(E, NW, KWN, UN)                                                                         \
+  case E:                                                                                             \
+    if (multi) gemm_bf16_kernel<E, NW, 4, 4, 1><<<grid_mt, 256, 0, s>>>(a);                           \
+    else if (wide) gemm_bf16_kernel<E, NW, SSD_KW_WIDE, 1, SSD_GEMM_UW><<<grid, 64 * SSD_KW_WIDE, 0, s>>>(a); \
+    else if (NW == 1 && a.K >= 8192) gemm_bf16_kernel<E, NW, KWN, 1, SSD_GEMM_U1_LONGK><<<grid, 64 * KWN, 0, s>>>(a); \
+    else gemm_bf16_kernel<E, NW, KWN, 1, UN><<<grid, 64 * KWN, 0, s>>>(a);                            \
+    break;
+    switch (epi) {
+      SSD_G(EPI_F32, 1, SSD_KW_NARROW, SSD_GEMM_U1)
+      SSD_G(EPI_LOGITS, 1, SSD_KW_NARROW, SSD_GEMM_U1)
+      SSD_G(EPI_RESID, 1, SSD_KW_NARROW, SSD_GEMM_U1)
+      SSD_G(EPI_SWIGLU, 2, SSD_KW_SWIGLU, SSD_GEMM_U2)
+      SSD_G(EPI_QKV, 1, SSD_KW_NARROW, SSD_GEMM_U1)
+      SSD_G(EPI_STORE, 1, SSD_KW_NARROW, SSD_GEMM_U1)
+      default: return hipErrorInvalidValue;
+    }
+#undef SSD_G
+  } else {
+    int npairs;
+    if (epi == EPI_QKV) npairs = (a.hq + 2 * a.hkv) * (a.hd / 2);
+    else if (epi == EPI_SWIGLU) npairs = a.N;
+    else npairs = a.N / 2;
+    dim3 grid((npairs + 3) / 4, mt);
+    switch (epi) {
+      case EPI_F32: gemm_f32_kernel<EPI_F32><<<grid, 256, 0, s>>>(a); break;
+      case EPI_RESID: gemm_f32_kernel<EPI_RESID><<<grid, 256, 0, s>>>(a); break;
+      case EPI_SWIGLU: gemm_f32_kernel<EPI_SWIGLU><<<grid, 256, 0, s>>>(a); break;
+      case EPI_QKV: gemm_f32_kernel<EPI_QKV><<<grid, 256, 0, s>>>(a); break;
+      case EPI_STORE: gemm_f32_kernel<EPI_STORE><<<grid, 256, 0, s>>>(a); break;
+      default: return hipErrorInvalidValue;
+    }
+  }
+  return hipGetLastError();
+}
+
+}  // namespace ssd

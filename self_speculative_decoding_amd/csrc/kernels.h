@@ -71,6 +71,7 @@ struct AttnArgs {
   float* part_ml;             // [n_part][R][hq][2]
   const int* state;
   int pos_off, M, R, hq, hkv, hd, max_ctx;   // max_ctx: positions per cache row (multiple of 64)
+  int n_part;                 // partitions launched (set by launch_attention)
   float scale_log2;           // log2(e) / sqrt(hd)
 };
 
