@@ -114,7 +114,16 @@ def cpu_baseline(cfg, weights, prompt, budget_s: float) -> dict:
         if el >= budget_s or steps >= 64:
             break
     del m
+    cpu_model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": steps / el, "unit": "tok/s", "cores": int(cores), "kind": "oracle",
+            "host": {"nproc": os.cpu_count(), "cpu": cpu_model},
             "sample": f"{steps} float64 greedy decode steps of the same model after an 8-token prompt "
                       f"(context <= {8 + steps}); weight conversion and prefill excluded"}
 
@@ -315,6 +324,7 @@ def main() -> int:
     # ---- timed region: K self-speculative decodes ----
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    step_tps = []
     dec_ms = ver_ms = dr_ms = 0.0
     vpasses = cycles = acc = drafted = 0
     spec_out = None
@@ -328,23 +338,27 @@ def main() -> int:
         cycles += st["cycles"]
         acc += st["accepted"]
         drafted += st["drafted"]
+        step_tps.append((n_new - 1) / st["t_decode_ms"] * 1e3)
         log(f"step {i + 1}/{args.steps}: {(n_new - 1) / st['t_decode_ms'] * 1e3:.1f} tok/s, "
             f"{st['cycles']} cycles, {st['accepted']}/{st['drafted']} drafts accepted")
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    value = args.steps * (n_new - 1) / (dec_ms / 1e3)
+    value = float(np.median(step_tps))       # median over the timed decodes
+    mean_tps = args.steps * (n_new - 1) / (dec_ms / 1e3)
 
     # ---- plain greedy, back to back ----
     base_ms = base_pass_ms = 0.0
     base_passes = 0
     base_out = None
+    base_steps = []
     for i in range(args.steps):
         out, st = eng.generate(prompt, n_new)
         base_out = out
+        base_steps.append((n_new - 1) / st["t_decode_ms"] * 1e3)
         base_ms += st["t_decode_ms"]
         base_pass_ms += st["t_verify_ms"]
         base_passes += st["verify_passes"]
-    base_tps = args.steps * (n_new - 1) / (base_ms / 1e3)
+    base_tps = float(np.median(base_steps))
     lossless = spec_out == base_out
     log(f"greedy {base_tps:.1f} tok/s; self-spec {value:.1f} tok/s; lossless={lossless}")
 
@@ -371,6 +385,32 @@ def main() -> int:
             "traffic": measured_traffic() if args.workload == "llama-8b" else None,
             "bytes_per_launch": gu_bytes, "avg_us": round(gu_us, 2)}
     log(f"gate/up GEMM m={k + 1}: {gu_us:.1f} us = {roof['achieved']:.0f} GB/s")
+    # achievable HBM bandwidth: a plain streaming read of the 1.05 GB LM head
+    rp_us = min(eng.time_op("read_probe", 0, 4, 3) for _ in range(3))
+    achievable = round(cfg["vocab"] * cfg["d_model"] * 2 / (rp_us * 1e-6) / 1e9, 1)
+
+    # expected-speedup frame: ceiling (all drafts accepted) from byte ratios,
+    # and the prediction from measured step times and the measured acceptance
+    # under geometric acceptance
+    c_d = pass_bytes(cfg, 1, avg_ctx, layers=cfg["n_layers"] - len(skipped)) / bb
+    alpha = acc / max(drafted, 1)
+    e_tok = sum(alpha ** i for i in range(k + 1))
+    t_d = dr_ms / max(drafted, 1)
+    frame = {"draft_byte_ratio": round(c_d, 4),
+             "ceiling_alpha1": round((k + 1) / (k * c_d + 1), 4),
+             "break_even_alpha": None,
+             "alpha": round(alpha, 4),
+             "predicted_speedup": round(e_tok / ((k * t_d + v_ms) / b_ms), 4),
+             "measured_speedup": None}
+    # smallest alpha with (1 - a^(k+1)) / (1 - a) >= k * c_d + 1
+    lo, hi = 0.0, 1.0
+    for _ in range(60):
+        mid = (lo + hi) / 2
+        if sum(mid ** i for i in range(k + 1)) >= k * c_d + 1:
+            hi = mid
+        else:
+            lo = mid
+    frame["break_even_alpha"] = round(hi, 4)
 
     # ---- skip x k sweep (one decode each) ----
     sweep = []
@@ -412,8 +452,10 @@ def main() -> int:
         "decode_pass_m1": {"ms": round(b_ms, 4), "bytes": int(bb), "gbs": round(b_gbs, 1),
                            "frac": round(b_gbs / PEAK_HBM_GBS, 4)},
         "draft_step_ms": round(dr_ms / max(drafted, 1), 4),
-        "roofline": roof, "ops_us": ops, "sweep": sweep, "cpu_baseline": cpu,
+        "roofline": roof, "achievable_gbs": achievable, "speedup_frame": frame,
+        "mean_tok_s": round(mean_tps, 2), "ops_us": ops, "sweep": sweep, "cpu_baseline": cpu,
     }
+    frame["measured_speedup"] = round(value / base_tps, 4)
     print(json.dumps(line), flush=True)
     return 0
 

@@ -479,18 +479,23 @@ __global__ void set_state_kernel(int* state, int idx, int value) { state[idx] = 
 // lane keeps 8 loads in flight; one XOR per workgroup lands in sink.
 __global__ __launch_bounds__(256) void read_probe_kernel(const uint4* __restrict__ src, size_t n16,
                                                          unsigned* __restrict__ sink) {
-  const size_t stride = (size_t)gridDim.x * 256;
+  // the streaming pattern of the GEMMs: each wave reads its own contiguous
+  // range, 1 KB per load instruction, nontemporal, 8 loads per batch
+  const int lane = threadIdx.x & 63;
+  const size_t waves = (size_t)gridDim.x * 4, gw = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const size_t chunks = n16 / 64, per = (chunks + waves - 1) / waves;
+  const size_t c0 = gw * per, c1 = c0 + per < chunks ? c0 + per : chunks;
   unsigned acc = 0;
-  size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-  for (; i + 7 * stride < n16; i += 8 * stride) {
+  size_t c = c0;
+  for (; c + 8 <= c1; c += 8) {
     uint4 v[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = src[i + j * stride];
+    for (int j = 0; j < 8; ++j) v[j] = ld16_nt((const uint16_t*)(src + (c + j) * 64 + lane));
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
   }
-  for (; i < n16; i += stride) {
-    const uint4 v = src[i];
+  for (; c < c1; ++c) {
+    const uint4 v = ld16_nt((const uint16_t*)(src + c * 64 + lane));
     acc ^= v.x ^ v.y ^ v.z ^ v.w;
   }
   acc = __reduce_xor_sync(0xffffffffffffffffull, acc);

@@ -1,0 +1,131 @@
+"""Edge cases of the HIP path through the C ABI (needs an MI355X).
+
+A bf16 model whose KV capacity is not a whole number of 64-key attention
+partitions, filled to the last position; one-token prompts; the largest
+verify block (32 rows); the degenerate skip masks (nothing skipped: the draft
+is the full model, so every draft is accepted; everything skipped: the draft
+is embedding + head); query-head groups of 1 and 2 per KV head.
+Bars as in test_gpu_parity: bf16 |dlogit| <= 3e-2, GPU self-speculation
+bitwise equal to GPU greedy.
+"""
+import numpy as np
+import pytest
+
+import synth
+from oracle import Model
+from _common import engine
+from test_gpu_parity import _gap_ok, _stepwise
+
+pytestmark = pytest.mark.gpu
+
+BOUND = 3e-2
+
+
+def _edge_cfg(**kw):
+    base = dict(n_layers=3, d_model=512, n_q_heads=8, n_kv_heads=2, ffn_dim=1024, vocab=2048,
+                max_ctx=330, prompt_len=100, cid=70)
+    base.update(kw)
+    return synth.config("llama-8b", **base)
+
+
+@pytest.fixture(scope="module")
+def edge():
+    cfg = _edge_cfg()
+    w = synth.make_weights(cfg, seed=5)
+    print("[edge] building engine (max_ctx 330, max_block 32)", flush=True)
+    eng = engine(cfg, w, max_block=32, prefill_chunk=64)
+    yield cfg, w, eng, Model(cfg, w)
+    eng.close()
+
+
+def test_fill_to_the_last_position(edge):
+    """Greedy up to the last position a verify can reach (ragged last partition)
+    matches the oracle; self-speculation filling max_ctx exactly is lossless;
+    one more token is a capacity error."""
+    from self_speculative_decoding_amd import SSDError, skip_mask
+    cfg, w, eng, ora = edge
+    prompt = synth.make_prompt(cfg)
+    P, cap = len(prompt), cfg["max_ctx"]
+    n = cap - P                                       # last verify row at position cap - 2
+    toks, rows = _stepwise(eng, prompt, n)
+    ref = ora.teacher_forced(prompt, toks)
+    err = np.max(np.abs(rows - ref))
+    tail = np.max(np.abs(rows[-8:] - ref[-8:]))
+    print(f"[edge] max |dlogit| = {err:.3e} (last 8 rows {tail:.3e})")
+    assert err <= BOUND
+    assert _gap_ok(toks, ref, BOUND) == []
+    k = 3
+    n_full = cap - P - (k + 1)
+    base, _ = eng.generate(prompt, n_full)
+    spec, _ = eng.generate(prompt, n_full, skip_mask(cfg["n_layers"], 0.34), k)
+    assert spec == base == toks[:n_full]
+    with pytest.raises(SSDError) as e:
+        eng.generate(prompt, n_full + 1, skip_mask(cfg["n_layers"], 0.34), k)
+    assert e.value.status == -3
+
+
+def test_one_token_prompt(edge):
+    cfg, w, eng, ora = edge
+    prompt = synth.make_prompt(cfg)[:1]
+    toks, rows = _stepwise(eng, prompt, 24)
+    ref = ora.teacher_forced(prompt, toks)
+    assert np.max(np.abs(rows - ref)) <= BOUND
+    assert _gap_ok(toks, ref, BOUND) == []
+    mask = np.zeros(cfg["n_layers"], np.uint8)
+    mask[1] = 1
+    spec, _ = eng.generate(prompt, 24, mask, 4)
+    assert spec == toks
+
+
+def test_largest_verify_block_rows_equal_decode_rows(edge):
+    """A 32-row verify (two 16-row MFMA tiles, the block limit) gives the
+    logits of decoding its rows one at a time, bit for bit."""
+    cfg, w, eng, _ = edge
+    prompt = synth.make_prompt(cfg)
+    toks, rows = _stepwise(eng, prompt, 33)
+    eng.reset()
+    eng.prefill(prompt)
+    post = eng.verify(toks[:32])
+    got = eng.read_logits(32)
+    assert np.array_equal(got, rows[1:33])
+    assert post == toks[1:33]
+    a, em = eng.accept()
+    assert a == 31 and em == toks[1:33]
+
+
+def test_degenerate_masks(edge):
+    """No layer skipped: the draft is the full model with the same arithmetic,
+    so every draft is accepted.  Every layer skipped: the draft is embedding +
+    final norm + head; the output is still the greedy sequence."""
+    cfg, w, eng, _ = edge
+    prompt = synth.make_prompt(cfg)
+    base, _ = eng.generate(prompt, 40)
+    for k in (1, 3, 8):
+        out, st = eng.generate(prompt, 40, np.zeros(cfg["n_layers"], np.uint8), k)
+        assert out == base, k
+        assert st["accepted"] == st["drafted"] > 0, (k, st)
+        out, st = eng.generate(prompt, 40, np.ones(cfg["n_layers"], np.uint8), k)
+        assert out == base, k
+
+
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 4)])
+def test_query_groups_of_one_and_two(hq, hkv):
+    """The attention kernel's other head groupings (G = 1, 2) against the oracle."""
+    cfg = _edge_cfg(n_q_heads=hq, n_kv_heads=hkv, max_ctx=200, prompt_len=90, cid=71 + hq // hkv)
+    w = synth.make_weights(cfg, seed=7)
+    print(f"[edge] G = {hq // hkv}", flush=True)
+    eng = engine(cfg, w, max_block=8, prefill_chunk=64)
+    try:
+        prompt = synth.make_prompt(cfg)
+        toks, rows = _stepwise(eng, prompt, 32)
+        ref = Model(cfg, w).teacher_forced(prompt, toks)
+        err = np.max(np.abs(rows - ref))
+        print(f"[edge] G = {hq // hkv}: max |dlogit| = {err:.3e}")
+        assert err <= BOUND
+        assert _gap_ok(toks, ref, BOUND) == []
+        mask = np.zeros(cfg["n_layers"], np.uint8)
+        mask[1] = 1
+        spec, _ = eng.generate(prompt, 32, mask, 3)
+        assert spec == toks
+    finally:
+        eng.close()
