@@ -195,13 +195,17 @@ def bench_verify_blocks(args) -> int:
                     "frac": round(vb / v_ms / 1e6 / PEAK_HBM_GBS, 4),
                     "tok_s": round((float(np.mean(a_list)) + 1) / v_ms * 1e3, 1)})
         log(f"p={p}: {res[-1]}")
+    ops = {}
+    for op in ("gate_up", "down", "qkv", "o", "attention", "lm_head"):
+        for m in (1, B):
+            ops[f"{op}_m{m}"] = round(eng.time_op(op, 0, m, 30), 2)
     eng.close()
     line = {"metric": "verify-pass HBM GB/s (% of peak), 16-token blocks, Qwen3-8B-shaped bf16 + feature tap",
             "value": res[-1]["gbs"], "unit": "GB/s", "n_gpus": 1, "higher_is_better": True, "dtype": "bf16",
             "data": "synthetic", "vs_baseline": None,
             "config": {"workload": f"qwen3-8b-shaped bf16 random-init target, {P}-token prompt, verify blocks of {B} "
                                    f"with geometric correct prefix, feature tap layers {list(cfg['feat_layers'])} + fc"},
-            "by_p": res}
+            "by_p": res, "ops_us": ops}
     print(json.dumps(line), flush=True)
     return 0
 

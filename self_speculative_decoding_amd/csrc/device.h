@@ -61,10 +61,11 @@ constexpr int PACK_TILE = 1024;   // elements per packed tile
 // workgroup at chunk 0 plus 8*lane; consecutive chunks of a tile are NW
 // tiles apart (interleaved pairs).  U chunks of loads are issued before their
 // MFMAs; weights are read with nontemporal loads (read once per pass).
-template <int NW, bool NT, int U>
+// CS: elements between consecutive chunks of one weight stream (NW tiles
+// interleaved: NW * PACK_TILE; independent tiles: PACK_TILE).
+template <int NW, bool NT, int U, int CS = NW * PACK_TILE>
 __device__ __forceinline__ void mfma_stream(const uint16_t* xr, bool xok, const uint16_t* const* wr, int c0, int c1,
                                             f32x4* acc) {
-  constexpr size_t CS = (size_t)NW * PACK_TILE;
   const uint4 zero = {0u, 0u, 0u, 0u};
   auto ldw = [](const uint16_t* p) { return NT ? ld16_nt(p) : ld16(p); };
   int s = c0;
@@ -104,10 +105,9 @@ __device__ __forceinline__ void mfma_stream(const uint16_t* xr, bool xok, const 
 }
 
 // As mfma_stream for MT 16-row tiles sharing every weight fragment.
-template <int NW, int MT>
+template <int NW, int MT, int CS = NW * PACK_TILE>
 __device__ __forceinline__ void mfma_stream_mt(const uint16_t* const* xr, const bool* xok, const uint16_t* const* wr,
                                                int c0, int c1, f32x4 (*acc)[NW]) {
-  constexpr size_t CS = (size_t)NW * PACK_TILE;
   const uint4 zero = {0u, 0u, 0u, 0u};
   for (int s = c0; s < c1; ++s) {
     uint4 wb[NW][2], xa[MT][2];

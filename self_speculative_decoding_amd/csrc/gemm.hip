@@ -143,11 +143,19 @@ __device__ __forceinline__ void qkv_col(const GemmArgs& a, int t, int c, int* he
   *dim_out = head < a.hq + a.hkv ? (c < 8 ? 8 * jj + c : half + 8 * jj + (c - 8)) : 16 * jj + c;
 }
 
-template <int EPI, int NW, int KW, int MT, int U>
+// TPW: independent 16-column tiles per workgroup (one-matrix GEMMs of wide
+// passes), sharing every A fragment.  Each tile's MFMA sequence, K split and
+// reduction order are those of a one-tile workgroup, so TPW never changes a
+// result; it only cuts the A-operand reads from L2.
+template <int EPI, int NW, int KW, int MT, int U, int TPW>
 __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
+  static_assert(TPW == 1 || NW == 1, "tile groups are for one-matrix GEMMs");
+  constexpr int NS = NW * TPW;                               // weight streams
+  constexpr int CS = NW > 1 ? NW * PACK_TILE : PACK_TILE;    // chunk stride of a stream
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane & 15, kg = lane >> 4;
-  const int t = blockIdx.x;
+  const int t0 = blockIdx.x * TPW;                           // first column tile
+  const int ntiles = gridDim.x * TPW;
   const uint16_t* xr[MT];
   bool av_ok[MT];
 #pragma unroll
@@ -157,27 +165,38 @@ __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
     xr[r] = (const uint16_t*)a.X + (size_t)(av_ok[r] ? am : 0) * a.ldx + kg * 16;
   }
   const int S = a.K >> 6;   // 64-element chunks
-  // packed weight tiles of this column tile (gate/up interleaved when NW = 2)
-  const uint16_t* wr[NW];
+  // packed weight tiles: gate/up interleaved when NW = 2, else TPW tiles
+  const uint16_t* wr[NS];
 #pragma unroll
-  for (int j = 0; j < NW; ++j)
-    wr[j] = (const uint16_t*)a.W0 + ((size_t)t * S * NW + j) * PACK_TILE + 8 * lane;
-  int head = 0, dim = 0;
-  if (EPI == EPI_QKV) qkv_col(a, t, c, &head, &dim);
+  for (int j = 0; j < NS; ++j)
+    wr[j] = NW > 1 ? (const uint16_t*)a.W0 + ((size_t)t0 * S * NW + j) * PACK_TILE + 8 * lane
+                   : (const uint16_t*)a.W0 + (size_t)(t0 + j) * S * PACK_TILE + 8 * lane;
+  int head[TPW], dim[TPW];
+#pragma unroll
+  for (int j = 0; j < TPW; ++j) {
+    head[j] = dim[j] = 0;
+    if (EPI == EPI_QKV) qkv_col(a, t0 + j, c, &head[j], &dim[j]);
+  }
 
   const int s0 = (S * wave) / KW, s1 = (S * (wave + 1)) / KW;
 
   // Epilogue inputs fetched before the weight stream so that their latency
-  // hides behind it: the position base (QKV) and, for one-tile launches, the
-  // residual entries wave 0 will update.
+  // hides behind it: the position base (QKV) and, for one-tile-row launches,
+  // the residual entries wave 0 will update.
   const int base = EPI == EPI_QKV ? a.state[0] + a.pos_off : 0;
-  float yv[4] = {0.f, 0.f, 0.f, 0.f};
+  float yv[TPW][4];
+#pragma unroll
+  for (int j = 0; j < TPW; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) yv[j][i] = 0.f;
   if (EPI == EPI_RESID && MT == 1 && wave == 0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = blockIdx.y * 16 + 4 * kg + i;
-      if (m < a.M) yv[i] = a.y[(size_t)m * a.ldy + t * 16 + c];
-    }
+    for (int j = 0; j < TPW; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = blockIdx.y * 16 + 4 * kg + i;
+        if (m < a.M) yv[j][i] = a.y[(size_t)m * a.ldy + (t0 + j) * 16 + c];
+      }
   }
 
   // folded RMSNorm: wave w owns tile rows w, w + KW, ...  One-tile launches
@@ -191,37 +210,43 @@ __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
     for (int r = 0; r < RPRE; ++r) ssv[r] = ss_part(a, blockIdx.y * 16 + wave + r * KW, r * KW + wave < 16, lane);
   }
-  f32x4 acc[MT][NW];
+  f32x4 acc[MT][NS];
 #pragma unroll
   for (int r = 0; r < MT; ++r)
 #pragma unroll
-    for (int j = 0; j < NW; ++j) acc[r][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // chunks per batch of loads (fewer for the two-matrix gate/up GEMM keeps
-  // its register count, and so the workgroups resident per CU, in check)
-  float rc[4] = {0.f, 0.f, 0.f, 0.f}, rsn[4] = {0.f, 0.f, 0.f, 0.f};   // RoPE cos/sin (QKV)
+    for (int j = 0; j < NS; ++j) acc[r][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float rc[TPW][4], rsn[TPW][4];   // RoPE cos/sin (QKV)
+#pragma unroll
+  for (int j = 0; j < TPW; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rc[j][i] = rsn[j][i] = 0.f;
   if (MT == 1 && EPI == EPI_QKV) {
     // first load batch, then the rotary table entries of wave 0's epilogue
     // (they need the position), then the rest of the K range
     const int sm = min(s0 + U, s1);
-    mfma_stream<NW, true, U>(xr[0], av_ok[0], wr, s0, sm, acc[0]);
-    if (wave == 0 && head < a.hq + a.hkv && c < 8) {
+    mfma_stream<NS, true, U, CS>(xr[0], av_ok[0], wr, s0, sm, acc[0]);
+    if (wave == 0 && c < 8) {
       const int half = a.hd >> 1;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = blockIdx.y * 16 + 4 * kg + i;
-        if (m < a.M) {
-          rc[i] = a.cos_t[(size_t)(base + m) * half + dim];
-          rsn[i] = a.sin_t[(size_t)(base + m) * half + dim];
+      for (int j = 0; j < TPW; ++j) {
+        if (head[j] >= a.hq + a.hkv) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = blockIdx.y * 16 + 4 * kg + i;
+          if (m < a.M) {
+            rc[j][i] = a.cos_t[(size_t)(base + m) * half + dim[j]];
+            rsn[j][i] = a.sin_t[(size_t)(base + m) * half + dim[j]];
+          }
         }
       }
     }
-    mfma_stream<NW, true, U>(xr[0], av_ok[0], wr, sm, s1, acc[0]);
+    mfma_stream<NS, true, U, CS>(xr[0], av_ok[0], wr, sm, s1, acc[0]);
   } else if (MT == 1) {
-    mfma_stream<NW, true, U>(xr[0], av_ok[0], wr, s0, s1, acc[0]);
+    mfma_stream<NS, true, U, CS>(xr[0], av_ok[0], wr, s0, s1, acc[0]);
   }
-  else mfma_stream_mt<NW, MT>(xr, av_ok, wr, s0, s1, acc);
+  else mfma_stream_mt<NS, MT, CS>(xr, av_ok, wr, s0, s1, acc);
 
-  __shared__ f32x4 red[KW - 1][MT][NW][64];
+  __shared__ f32x4 red[KW - 1][MT][NS][64];
   __shared__ float rs[16 * MT];
   if (fold) {
 #pragma unroll
@@ -237,7 +262,7 @@ __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
     for (int r = 0; r < MT; ++r)
 #pragma unroll
-      for (int j = 0; j < NW; ++j) red[wave - 1][r][j][lane] = acc[r][j];
+      for (int j = 0; j < NS; ++j) red[wave - 1][r][j][lane] = acc[r][j];
   }
   __syncthreads();
   if (wave != 0) return;
@@ -246,7 +271,7 @@ __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
     for (int r = 0; r < MT; ++r)
 #pragma unroll
-      for (int j = 0; j < NW; ++j) acc[r][j] = acc[r][j] + red[w][r][j][lane];
+      for (int j = 0; j < NS; ++j) acc[r][j] = acc[r][j] + red[w][r][j][lane];
   if (fold) {
     // rows of this lane's accumulators: 4*kg + i of each 16-row tile
 #pragma unroll
@@ -255,37 +280,50 @@ __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
       for (int i = 0; i < 4; ++i) {
         const float f = rs[r * 16 + 4 * kg + i];
 #pragma unroll
-        for (int j = 0; j < NW; ++j) acc[r][j][i] *= f;
+        for (int j = 0; j < NS; ++j) acc[r][j][i] *= f;
       }
   }
 
 #pragma unroll
   for (int r = 0; r < MT; ++r) {
     const int mt = blockIdx.y * MT + r;
-    if (EPI == EPI_QKV) {
-      const bool rot = head < a.hq + a.hkv;
-      float part[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) part[i] = __shfl_xor(acc[r][0][i], 8);
+    if (EPI == EPI_SWIGLU) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int m = mt * 16 + 4 * kg + i;
-        if (m >= a.M) continue;
-        if (rot) {
-          if (c < 8 && MT == 1) epi_qkv_rot<uint16_t>(a, base, m, head, dim, acc[r][0][i], part[i], rc[i], rsn[i]);
-          else if (c < 8) epi_qkv_pair<uint16_t>(a, base, m, head, dim, acc[r][0][i], part[i]);
-        } else {
-          epi_v_single<uint16_t>(a, base, m, head - a.hq - a.hkv, dim, acc[r][0][i]);
-        }
+        if (m < a.M) epi_swiglu<uint16_t>(a, m, t0 * 16 + c, acc[r][0][i], acc[r][NS - 1][i]);
       }
-    } else {
+      continue;
+    }
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+      const int tt = t0 + j;   // column tile
+      if (EPI == EPI_QKV) {
+        const bool rot = head[j] < a.hq + a.hkv;
+        float part[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) part[i] = __shfl_xor(acc[r][j][i], 8);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = mt * 16 + 4 * kg + i;
+          if (m >= a.M) continue;
+          if (rot) {
+            if (c < 8 && MT == 1)
+              epi_qkv_rot<uint16_t>(a, base, m, head[j], dim[j], acc[r][j][i], part[i], rc[j][i], rsn[j][i]);
+            else if (c < 8) epi_qkv_pair<uint16_t>(a, base, m, head[j], dim[j], acc[r][j][i], part[i]);
+          } else {
+            epi_v_single<uint16_t>(a, base, m, head[j] - a.hq - a.hkv, dim[j], acc[r][j][i]);
+          }
+        }
+        continue;
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int m = mt * 16 + 4 * kg + i;
-        const int n = t * 16 + c;
+        const int n = tt * 16 + c;
         if (EPI == EPI_LOGITS) {
           // (max, lowest index) over this tile's 16 columns, fixed butterfly
-          float bv = acc[r][0][i];
+          float bv = acc[r][j][i];
           int bi = n;
 #pragma unroll
           for (int o = 1; o < 16; o <<= 1) {
@@ -294,14 +332,14 @@ __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
             if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
           }
           if (m < a.M && c == 0) {
-            a.amax_v[(size_t)m * gridDim.x + t] = bv;
-            a.amax_i[(size_t)m * gridDim.x + t] = bi;
+            a.amax_v[(size_t)m * ntiles + tt] = bv;
+            a.amax_i[(size_t)m * ntiles + tt] = bi;
           }
         }
         if (EPI == EPI_RESID && a.ss_out) {
           // new residual, its sum of squares over this tile's 16 columns and
           // bf16(x * gain) for the GEMM that consumes it
-          const float xv = m < a.M ? (MT == 1 ? yv[i] : a.y[(size_t)m * a.ldy + n]) + acc[r][0][i] : 0.f;
+          const float xv = m < a.M ? (MT == 1 ? yv[j][i] : a.y[(size_t)m * a.ldy + n]) + acc[r][j][i] : 0.f;
           float sq = xv * xv;
 #pragma unroll
           for (int o = 1; o < 16; o <<= 1) sq += __shfl_xor(sq, o);
@@ -309,17 +347,16 @@ __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
             a.y[(size_t)m * a.ldy + n] = xv;
             if (a.tap) ((uint16_t*)a.tap)[(size_t)m * a.ldtap + n] = f2bf(xv);
             ((uint16_t*)a.xg_out)[(size_t)m * a.ldy + n] = f2bf(xv * bf2f(((const uint16_t*)a.gain_next)[n]));
-            if (c == 0) a.ss_out[(size_t)m * gridDim.x + t] = sq;
+            if (c == 0) a.ss_out[(size_t)m * ntiles + tt] = sq;
           }
           continue;
         }
         if (m >= a.M) continue;
-        if (EPI == EPI_SWIGLU) epi_swiglu<uint16_t>(a, m, n, acc[r][0][i], acc[r][NW - 1][i]);
-        else if (EPI == EPI_RESID && MT == 1) {
-          const float xv = yv[i] + acc[r][0][i];
+        if (EPI == EPI_RESID && MT == 1) {
+          const float xv = yv[j][i] + acc[r][j][i];
           a.y[(size_t)m * a.ldy + n] = xv;
           if (a.tap) ((uint16_t*)a.tap)[(size_t)m * a.ldtap + n] = f2bf(xv);
-        } else epi_single<uint16_t>(a, EPI, m, n, acc[r][0][i]);
+        } else epi_single<uint16_t>(a, EPI, m, n, acc[r][j][i]);
       }
     }
   }
@@ -433,23 +470,40 @@ hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t s) {
     // passes (prefill chunks) let 4 row tiles share each weight load
     const bool multi = a.M > 32;
     const dim3 grid_mt(tiles, (a.M + 63) / 64);
-#define SSD_G(E, NW, KWN, UN)                                                                         \
-  case E:                                                                                             \
-    if (multi) gemm_bf16_kernel<E, NW, 4, 4, 1><<<grid_mt, 256, 0, s>>>(a);                           \
-    else if (wide) gemm_bf16_kernel<E, NW, SSD_KW_WIDE, 1, SSD_GEMM_UW><<<grid, 64 * SSD_KW_WIDE, 0, s>>>(a); \
-    else if (NW == 1 && a.K >= 8192) gemm_bf16_kernel<E, NW, KWN, 1, SSD_GEMM_U1_LONGK><<<grid, 64 * KWN, 0, s>>>(a); \
-    else gemm_bf16_kernel<E, NW, KWN, 1, UN><<<grid, 64 * KWN, 0, s>>>(a);                            \
-    break;
+    // passes wider than 4 rows group 2 or 4 column tiles per workgroup so
+    // the A operand is read once for them (results unchanged, see the kernel),
+    // but only where at least 1024 workgroups remain: spreading the weight
+    // stream over every CU matters more than the A reads (measured)
+    int tpw = 1;
+    if (a.M > 4 && tiles % 4 == 0 && tiles / 4 >= 1024) tpw = 4;
+    else if (a.M > 4 && tiles % 2 == 0 && tiles / 2 >= 1024) tpw = 2;
+#define SSD_G1(E, KWN, UN)                                                                        \
+  if (multi) gemm_bf16_kernel<E, 1, 4, 4, 1, 1><<<grid_mt, 256, 0, s>>>(a);                       \
+  else if (tpw == 4) {                                                                            \
+    const dim3 g4(tiles / 4, mt);                                                                 \
+    if (wide) gemm_bf16_kernel<E, 1, SSD_KW_WIDE, 1, 2, 4><<<g4, 64 * SSD_KW_WIDE, 0, s>>>(a);    \
+    else gemm_bf16_kernel<E, 1, KWN, 1, 2, 4><<<g4, 64 * KWN, 0, s>>>(a);                         \
+  } else if (tpw == 2) {                                                                          \
+    const dim3 g2(tiles / 2, mt);                                                                 \
+    if (wide) gemm_bf16_kernel<E, 1, SSD_KW_WIDE, 1, 2, 2><<<g2, 64 * SSD_KW_WIDE, 0, s>>>(a);    \
+    else gemm_bf16_kernel<E, 1, KWN, 1, 2, 2><<<g2, 64 * KWN, 0, s>>>(a);                         \
+  } else if (wide) gemm_bf16_kernel<E, 1, SSD_KW_WIDE, 1, SSD_GEMM_UW, 1><<<grid, 64 * SSD_KW_WIDE, 0, s>>>(a); \
+  else if (a.K >= 8192) gemm_bf16_kernel<E, 1, KWN, 1, SSD_GEMM_U1_LONGK, 1><<<grid, 64 * KWN, 0, s>>>(a); \
+  else gemm_bf16_kernel<E, 1, KWN, 1, UN, 1><<<grid, 64 * KWN, 0, s>>>(a);
     switch (epi) {
-      SSD_G(EPI_F32, 1, SSD_KW_NARROW, SSD_GEMM_U1)
-      SSD_G(EPI_LOGITS, 1, SSD_KW_NARROW, SSD_GEMM_U1)
-      SSD_G(EPI_RESID, 1, SSD_KW_NARROW, SSD_GEMM_U1)
-      SSD_G(EPI_SWIGLU, 2, SSD_KW_SWIGLU, SSD_GEMM_U2)
-      SSD_G(EPI_QKV, 1, SSD_KW_NARROW, SSD_GEMM_U1)
-      SSD_G(EPI_STORE, 1, SSD_KW_NARROW, SSD_GEMM_U1)
+      case EPI_F32: SSD_G1(EPI_F32, SSD_KW_NARROW, SSD_GEMM_U1) break;
+      case EPI_LOGITS: SSD_G1(EPI_LOGITS, SSD_KW_NARROW, SSD_GEMM_U1) break;
+      case EPI_RESID: SSD_G1(EPI_RESID, SSD_KW_NARROW, SSD_GEMM_U1) break;
+      case EPI_QKV: SSD_G1(EPI_QKV, SSD_KW_NARROW, SSD_GEMM_U1) break;
+      case EPI_STORE: SSD_G1(EPI_STORE, SSD_KW_NARROW, SSD_GEMM_U1) break;
+      case EPI_SWIGLU:
+        if (multi) gemm_bf16_kernel<EPI_SWIGLU, 2, 4, 4, 1, 1><<<grid_mt, 256, 0, s>>>(a);
+        else if (wide) gemm_bf16_kernel<EPI_SWIGLU, 2, SSD_KW_WIDE, 1, SSD_GEMM_U2, 1><<<grid, 64 * SSD_KW_WIDE, 0, s>>>(a);
+        else gemm_bf16_kernel<EPI_SWIGLU, 2, SSD_KW_SWIGLU, 1, SSD_GEMM_U2, 1><<<grid, 64 * SSD_KW_SWIGLU, 0, s>>>(a);
+        break;
       default: return hipErrorInvalidValue;
     }
-#undef SSD_G
+#undef SSD_G1
   } else {
     int npairs;
     if (epi == EPI_QKV) npairs = (a.hq + 2 * a.hkv) * (a.hd / 2);

@@ -341,10 +341,10 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(AttnArgs a) {
 // Combine of the attention partitions: one workgroup per (row, head), one
 // lane per head dim.  Row r at position pos uses partitions 0..pos/PT, added
 // in partition order with weights exp2(m_p - max m).  The partial outputs are
-// loaded (up to 32 at a time) together with the (m, l) pairs.
+// loaded (up to 48 at a time) together with the (m, l) pairs.
 template <typename E>
 __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
-  constexpr int B = 32;
+  constexpr int B = 48;   // partials per load batch (3072 keys)
   __shared__ float sm[128], sl[128];
   const int row = blockIdx.x, head = blockIdx.y, t = threadIdx.x;
   const int st0 = a.state[0];   // position load issued first, used late
