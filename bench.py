@@ -210,6 +210,85 @@ def bench_verify_blocks(args) -> int:
     return 0
 
 
+def bench_kselect(args) -> int:
+    """Draft length from measured step times: fit t_draft, t_verify(k+1) and the
+    per-cycle overhead on the 8B-shaped model, predict k*(alpha) and the rate
+    for geometric acceptance alpha, then measure cycles of real draft passes
+    followed by a verify of a block whose correct prefix is geometric(alpha)
+    (so the acceptance is controlled while every pass runs in full)."""
+    import numpy as np
+    import synth
+    from self_speculative_decoding_amd import Engine, make_cfg, skip_mask, select_k
+    cfg = synth.config("llama-8b")
+    KMAX, V = 8, cfg["vocab"]
+    frac = args.skip if args.skip is not None else cfg["skip_frac"]
+    log("kselect: generating weights")
+    w = synth.make_weights(cfg)
+    prompt = synth.make_prompt(cfg)
+    eng = Engine(make_cfg(cfg, max_block=KMAX + 1, prefill_chunk=256), [w[n] for n, _, _ in synth.weight_specs(cfg)])
+    del w
+    mask = skip_mask(cfg["n_layers"], frac)
+    true, _ = eng.generate(prompt, 40 * (KMAX + 1) + 8)
+    _, st = eng.generate(prompt, 256, mask, 3)          # warm graphs; fit draft step and cycle overhead
+    _, st = eng.generate(prompt, 256, mask, 3)
+    t_draft = st["t_draft_ms"] / st["drafted"]
+    t_cycle = (st["t_decode_ms"] - st["t_draft_ms"] - st["t_verify_ms"]) / st["cycles"]
+    tv = []
+    for k in range(KMAX + 1):
+        ms = []
+        for rep in range(4):
+            eng.reset()
+            eng.prefill(prompt)
+            s0 = eng.stats()
+            eng.verify(true[:k + 1])
+            ms.append(eng.stats()["t_verify_ms"] - s0["t_verify_ms"])
+            eng.accept()
+        tv.append(float(np.median(ms[1:])))
+    log(f"fitted: t_draft {t_draft:.3f} ms, t_cycle {t_cycle:.3f} ms, t_verify {[round(x, 3) for x in tv]}")
+    rows = []
+    for alpha in (0.5, 0.7, 0.8, 0.9, 0.95):
+        k_pred, _ = select_k(tv, t_draft, t_cycle, alpha)
+        meas = []
+        for k in range(KMAX + 1):
+            eng.reset()
+            eng.prefill(prompt)
+            pos, toks, cyc, gpu_ms, stream = 0, 0, 0, 0.0, 0
+            s0 = eng.stats()
+            while pos + k + 2 < len(true) and cyc < 40:
+                if k > 0:
+                    eng.draft(mask, k)                   # the real draft passes; tokens replaced below
+                d, m = synth.make_geometric_block(np.array(true[pos + 1:pos + k + 1], np.int32), V, alpha,
+                                                  k + 1, seed=1, stream=stream) if k > 0 else (np.zeros(0, np.int32), 0)
+                stream += 1
+                eng.verify([true[pos]] + [int(x) for x in d])
+                a, em = eng.accept()
+                if a != m or em != true[pos + 1:pos + a + 2]:
+                    raise RuntimeError(f"accepted {a} of a prefix of {m}")
+                pos += a + 1
+                toks += a + 1
+                cyc += 1
+            s1 = eng.stats()
+            gpu_ms = (s1["t_draft_ms"] - s0["t_draft_ms"]) + (s1["t_verify_ms"] - s0["t_verify_ms"]) + cyc * t_cycle
+            e_k = sum(alpha ** i for i in range(k + 1))
+            meas.append({"k": k, "tokens_per_cycle": round(toks / cyc, 3), "expected": round(e_k, 3),
+                         "measured_tok_s": round(toks / gpu_ms * 1e3, 1),
+                         "predicted_tok_s": round(e_k / (k * t_draft + tv[k] + t_cycle) * 1e3, 1)})
+        k_meas = max(meas, key=lambda r: r["measured_tok_s"])["k"]
+        rows.append({"alpha": alpha, "k_pred": k_pred, "k_measured": k_meas, "by_k": meas})
+        log(f"alpha {alpha}: k* predicted {k_pred}, measured {k_meas}")
+    eng.close()
+    mono = all(rows[i]["k_pred"] <= rows[i + 1]["k_pred"] for i in range(len(rows) - 1))
+    line = {"metric": "draft length k*(alpha) from fitted step times, predicted vs measured, 8B-shaped bf16",
+            "value": sum(r["k_pred"] == r["k_measured"] for r in rows) / len(rows), "unit": "fraction of alphas where k* agrees",
+            "n_gpus": 1, "higher_is_better": True, "dtype": "bf16", "data": "synthetic", "vs_baseline": None,
+            "config": {"workload": f"llama-8b-shaped bf16 random-init, {len(prompt)}-token prompt, middle skip "
+                                   f"{frac:.0%}, k = 0..{KMAX}, verify blocks with geometric(alpha) correct prefix"},
+            "fit": {"t_draft_ms": round(t_draft, 4), "t_cycle_ms": round(t_cycle, 4), "t_verify_ms": [round(x, 4) for x in tv]},
+            "k_pred_monotone": mono, "by_alpha": rows}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def bench_moe(args) -> int:
     """DeepSeek-V2-Lite-shaped MoE verify passes of n = 1..8 tokens with the
     synthetic routing trace: per-slot vs deduplicated expert reads, whole pass
@@ -281,6 +360,8 @@ def main() -> int:
     ap.add_argument("--n-new", type=int, default=None, help="tokens per decode (default: workload's)")
     ap.add_argument("--blocks", type=int, default=40, help="verify blocks per p (qwen3-8b)")
     ap.add_argument("--passes", type=int, default=12, help="verify passes per n and mode (dsv2-lite)")
+    ap.add_argument("--kselect", action="store_true",
+                    help="draft length from fitted step times: predicted vs measured k*(alpha)")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="short fixed kernel sequence for hardware-counter runs (copy probe, read probe, "
                          "gate/up GEMM at m=4 on a 4-layer model of the headline widths)")
@@ -303,6 +384,8 @@ def main() -> int:
         return bench_verify_blocks(args)
     if args.workload == "dsv2-lite":
         return bench_moe(args)
+    if args.kselect:
+        return bench_kselect(args)
     cfg = synth.config(args.workload)
     frac = args.skip if args.skip is not None else cfg.get("skip_frac", 0.5)
     k = args.k if args.k is not None else cfg["k"]

@@ -125,6 +125,20 @@ int64_t ssd_workspace_bytes(const ssd_cfg* cfg);
  * mask[l] = 1 for l in [start, start+n_skip).  mask: host array [n_layers]. */
 ssd_status ssd_skip_mask(int32_t n_layers, double frac, uint8_t* mask);
 
+/* Draft length from measured step times (speculative decoding for MoE models,
+ * abstract: a step costs its bytes over the bandwidth plus a fixed time, so
+ * the best draft length follows from the fitted step times).  Under geometric
+ * acceptance alpha a cycle with k drafts yields E_k = sum_{i=0..k} alpha^i
+ * tokens and costs C_k = k*t_draft + t_verify[k] + t_cycle, where t_verify[k]
+ * is the time of a verify pass over k+1 tokens (k = 0..kmax; k = 0 is plain
+ * decoding) and t_cycle the per-cycle overhead.  *k_best = the smallest k
+ * maximising E_k / C_k; *rate = that maximum (tokens per unit of time).  For
+ * any cost table k_best is non-decreasing in alpha (log E_{k+1}/E_k grows with
+ * alpha).  SSD_E_ARG for NULL pointers, kmax outside [0, 31], alpha outside
+ * [0, 1] or a non-positive time. */
+ssd_status ssd_select_k(const double* t_verify, int32_t kmax, double t_draft, double t_cycle, double alpha,
+                        int32_t* k_best, double* rate);
+
 /* State machine: next state of `op` from `state`, or SSD_E_STATE. */
 ssd_status ssd_check_transition(int32_t state, int32_t op, int32_t* next_state);
 
@@ -169,7 +183,9 @@ ssd_status ssd_draft(ssd_ctx* ctx, const uint8_t* skip_mask, int32_t k, int32_t*
  * m block tokens [t_last, d_1..d_{m-1}] through all layers at positions
  * n..n+m-1, overwriting those KV entries.  block == NULL uses the device-
  * resident block (DRAFTED -> VERIFIED, m must be k+1); a host block [m] is
- * allowed from READY (READY -> VERIFIED; block[0] normally t_last).
+ * allowed from READY or DRAFTED (-> VERIFIED; block[0] normally t_last) and
+ * replaces any drafted tokens: a harness can run the real draft passes and
+ * then verify a block of known agreement with the target.
  * posterior: host [m] or NULL, receives argmax of each row's logits. */
 ssd_status ssd_verify(ssd_ctx* ctx, const int32_t* block, int32_t m, int32_t* posterior);
 

@@ -13,6 +13,8 @@ Contents
               LayerSkip summary, 4.3.2).
 ``model.py``  the decoder, greedy decode, shared-cache self-speculation,
               MoE expert FFN (per-slot and deduplicated), feature tap.
+``kselect.py`` draft length from measured step times under geometric
+              acceptance (speculative decoding for MoE models, abstract).
 
 Every floating-point step runs in float64.  For bf16 workloads values are
 rounded to bf16 (nearest, ties to even) exactly where the GPU stores bf16:
@@ -25,3 +27,4 @@ points are readings, not page facts.
 from .accept import accept, accept_brute
 from .skip import skip_layers, skip_mask
 from .model import Model, bf16_round, decode_weight
+from .kselect import expected_tokens, select_k

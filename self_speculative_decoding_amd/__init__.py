@@ -27,7 +27,7 @@ EXPORTS = ["ssd_validate_cfg", "ssd_n_weights", "ssd_weight_numel", "ssd_weight_
            "ssd_prefill", "ssd_draft", "ssd_verify", "ssd_accept_rollback", "ssd_generate",
            "ssd_get_stats", "ssd_read_logits", "ssd_read_features", "ssd_set_routing",
            "ssd_read_union", "ssd_test_accept", "ssd_time_op", "ssd_set_option", "ssd_read_trace",
-           "ssd_read_kv"]
+           "ssd_read_kv", "ssd_select_k"]
 
 
 class Cfg(ctypes.Structure):
@@ -76,6 +76,7 @@ def _load():
         "ssd_weight_retained": (I32, [pc, I32]),
         "ssd_workspace_bytes": (I64, [pc]),
         "ssd_skip_mask": (I32, [I32, ctypes.c_double, VP]),
+        "ssd_select_k": (I32, [VP, I32, ctypes.c_double, ctypes.c_double, ctypes.c_double, VP, VP]),
         "ssd_check_transition": (I32, [I32, I32, P(I32)]),
         "ssd_strerror": (ctypes.c_char_p, [I32]),
         "ssd_last_error": (ctypes.c_char_p, []),
@@ -158,6 +159,17 @@ def skip_mask(n_layers: int, frac: float) -> np.ndarray:
     m = np.zeros(n_layers, dtype=np.uint8)
     _check(lib.ssd_skip_mask(n_layers, float(frac), _ptr(m)))
     return m
+
+
+def select_k(t_verify, t_draft: float, t_cycle: float, alpha: float) -> tuple[int, float]:
+    """Draft length maximising expected tokens per unit time (ssd_select_k).
+    t_verify[k] = verify-pass time over k+1 tokens, k = 0..len-1."""
+    tv = np.ascontiguousarray(t_verify, dtype=np.float64)
+    k = ctypes.c_int32(-1)
+    r = ctypes.c_double(0.0)
+    _check(lib.ssd_select_k(_ptr(tv), len(tv) - 1, float(t_draft), float(t_cycle), float(alpha),
+                            ctypes.byref(k), ctypes.byref(r)))
+    return k.value, r.value
 
 
 def check_transition(state: int, op: int) -> int:

@@ -201,7 +201,7 @@ ssd_status check_transition(int32_t state, int32_t op, int32_t* next) {
     case SSD_OP_PREFILL: if (state == SSD_ST_LOADED) n = SSD_ST_READY; break;
     case SSD_OP_DRAFT: if (state == SSD_ST_READY) n = SSD_ST_DRAFTED; break;
     case SSD_OP_VERIFY: if (state == SSD_ST_DRAFTED) n = SSD_ST_VERIFIED; break;
-    case SSD_OP_VERIFY_BLOCK: if (state == SSD_ST_READY) n = SSD_ST_VERIFIED; break;
+    case SSD_OP_VERIFY_BLOCK: if (state == SSD_ST_READY || state == SSD_ST_DRAFTED) n = SSD_ST_VERIFIED; break;
     case SSD_OP_ACCEPT: if (state == SSD_ST_VERIFIED) n = SSD_ST_READY; break;
     case SSD_OP_RESET:
       if (state >= SSD_ST_LOADED && state <= SSD_ST_VERIFIED) n = SSD_ST_LOADED;
@@ -270,6 +270,31 @@ int64_t ssd_workspace_bytes(const ssd_cfg* cfg) {
 ssd_status ssd_skip_mask(int32_t n_layers, double frac, uint8_t* mask) {
   ssd::clear_error();
   return ssd::skip_mask(n_layers, frac, mask);
+}
+
+ssd_status ssd_select_k(const double* t_verify, int32_t kmax, double t_draft, double t_cycle, double alpha,
+                        int32_t* k_best, double* rate) {
+  ssd::clear_error();
+  if (!t_verify || !k_best || !rate) return ssd::fail(SSD_E_ARG, "NULL argument");
+  if (kmax < 0 || kmax > SSD_MAX_BLOCK - 1) return ssd::fail(SSD_E_ARG, "kmax=%d outside [0, %d]", kmax, SSD_MAX_BLOCK - 1);
+  if (!(alpha >= 0.0 && alpha <= 1.0)) return ssd::fail(SSD_E_ARG, "alpha must be in [0, 1]");
+  if (!(t_draft > 0.0) || !(t_cycle >= 0.0)) return ssd::fail(SSD_E_ARG, "t_draft must be > 0 and t_cycle >= 0");
+  for (int k = 0; k <= kmax; ++k)
+    if (!(t_verify[k] > 0.0)) return ssd::fail(SSD_E_ARG, "t_verify[%d] must be > 0", k);
+  int best = 0;
+  double best_rate = -1.0, e = 0.0, ak = 1.0;
+  for (int k = 0; k <= kmax; ++k) {
+    e += ak;   // E_k = 1 + alpha + ... + alpha^k
+    ak *= alpha;
+    const double r = e / (k * t_draft + t_verify[k] + t_cycle);
+    if (r > best_rate) {
+      best_rate = r;
+      best = k;
+    }
+  }
+  *k_best = best;
+  *rate = best_rate;
+  return SSD_OK;
 }
 
 ssd_status ssd_check_transition(int32_t state, int32_t op, int32_t* next_state) {

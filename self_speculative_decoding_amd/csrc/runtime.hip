@@ -591,14 +591,15 @@ ssd_status ssd_draft(ssd_ctx* c, const uint8_t* skip_mask, int32_t k, int32_t* d
   SSDCHK(transition(c, SSD_OP_DRAFT));
   if (k < 1 || k + 1 > c->cfg.max_block) return fail(SSD_E_ARG, "k=%d outside [1, max_block-1=%d]", k, c->cfg.max_block - 1);
   if (c->n + k + 1 > c->cfg.max_ctx) return fail(SSD_E_CAPACITY, "n=%d + k+1=%d exceeds max_ctx=%d", c->n, k + 1, c->cfg.max_ctx);
+  HIPCHK(hipEventRecord(c->ev[EV_A], c->stream));
   for (int j = 0; j < k; ++j)
     SSDCHK(decode_pass(c, c->block + j, 1, j, skip_mask, c->block + j + 1, false));
+  HIPCHK(hipEventRecord(c->ev[EV_B], c->stream));
   c->k = k;
-  if (drafts) {
-    HIPCHK(hipMemcpyAsync(c->hbuf, c->block + 1, k * sizeof(int), hipMemcpyDeviceToHost, c->stream));
-    HIPCHK(hipStreamSynchronize(c->stream));
-    memcpy(drafts, c->hbuf, k * sizeof(int));
-  }
+  if (drafts) HIPCHK(hipMemcpyAsync(c->hbuf, c->block + 1, k * sizeof(int), hipMemcpyDeviceToHost, c->stream));
+  HIPCHK(hipStreamSynchronize(c->stream));
+  if (drafts) memcpy(drafts, c->hbuf, k * sizeof(int));
+  c->st.t_draft_ms += elapsed(c->ev[EV_A], c->ev[EV_B]);
   c->st.drafted += k;
   set_state(c, SSD_OP_DRAFT);
   return SSD_OK;

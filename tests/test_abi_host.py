@@ -96,7 +96,7 @@ def test_skip_mask_rejects():
 def test_state_machine():
     L, R, D, V = ssd.ST_LOADED, ssd.ST_READY, ssd.ST_DRAFTED, ssd.ST_VERIFIED
     ok = {(L, ssd.OP_PREFILL): R, (R, ssd.OP_DRAFT): D, (D, ssd.OP_VERIFY): V,
-          (R, ssd.OP_VERIFY_BLOCK): V, (V, ssd.OP_ACCEPT): R}
+          (R, ssd.OP_VERIFY_BLOCK): V, (D, ssd.OP_VERIFY_BLOCK): V, (V, ssd.OP_ACCEPT): R}
     for s in (L, R, D, V):
         assert ssd.check_transition(s, ssd.OP_RESET) == L
         for op in (ssd.OP_PREFILL, ssd.OP_DRAFT, ssd.OP_VERIFY, ssd.OP_VERIFY_BLOCK, ssd.OP_ACCEPT):
@@ -107,3 +107,32 @@ def test_state_machine():
 def test_strerror():
     for s in (0, -1, -2, -3, -4, -5):
         assert ssd.lib.ssd_strerror(s)
+
+
+def test_select_k_matches_oracle_and_is_monotone_in_alpha():
+    from oracle import select_k as ora_select_k
+    rng = np.random.default_rng(11)
+    for trial in range(200):
+        kmax = int(rng.integers(0, 31))
+        tv = np.cumsum(rng.uniform(0.0, 0.2, kmax + 1)) + rng.uniform(0.5, 2.0)
+        if trial % 3 == 0:
+            tv = rng.uniform(0.5, 2.0, kmax + 1)          # any positive table
+        td, tc = float(rng.uniform(0.05, 1.5)), float(rng.uniform(0.0, 0.3))
+        prev = -1
+        for a in np.linspace(0.0, 1.0, 21):
+            k, r = ssd.select_k(tv, td, tc, a)
+            ko, ro = ora_select_k(list(tv), td, tc, a)
+            assert k == ko and abs(r - ro) <= 1e-12 * ro, (trial, a)
+            assert k >= prev, (trial, a)                   # non-decreasing in alpha
+            prev = k
+
+
+def test_select_k_rejects():
+    c = ssd.lib
+    tv = np.ones(4)
+    k, r = ctypes.c_int32(), ctypes.c_double()
+    p = tv.ctypes.data_as(ctypes.c_void_p)
+    assert c.ssd_select_k(p, 3, 0.5, 0.0, 1.5, ctypes.byref(k), ctypes.byref(r)) == -1
+    assert c.ssd_select_k(p, 3, 0.0, 0.0, 0.5, ctypes.byref(k), ctypes.byref(r)) == -1
+    assert c.ssd_select_k(p, 32, 0.5, 0.0, 0.5, ctypes.byref(k), ctypes.byref(r)) == -1
+    assert c.ssd_select_k(None, 3, 0.5, 0.0, 0.5, ctypes.byref(k), ctypes.byref(r)) == -1

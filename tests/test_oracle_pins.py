@@ -463,3 +463,33 @@ def test_geometric_block_prefix():
         d, m = synth.make_geometric_block(true, 1000, 0.7, 16, seed=0, stream=s)
         a, _ = accept(d, list(true) + [0])
         assert a == m
+
+
+# ---------------------------------------------------------------------------
+# draft-length choice (speculative decoding for MoE models, abstract)
+# ---------------------------------------------------------------------------
+
+def test_kselect_hand_worked_example():
+    from oracle import select_k, expected_tokens
+    # flat verify cost 1.0, draft step 0.8, no overhead, alpha 0.9:
+    # r0 = 1/1, r1 = 1.9/1.8 = 1.0556, r2 = 2.71/2.6 = 1.0423, r3 = 3.439/3.4 = 1.0115
+    assert abs(expected_tokens(0.9, 2) - 2.71) < 1e-12
+    k, r = select_k([1.0, 1.0, 1.0, 1.0], 0.8, 0.0, 0.9)
+    assert k == 1 and abs(r - 1.9 / 1.8) < 1e-12
+    # cheaper drafts push k up: t_draft 0.2 -> r3 = 3.439/1.6 beats r2 = 2.71/1.4
+    assert select_k([1.0] * 6, 0.2, 0.0, 0.9)[0] == 5
+
+
+def test_kselect_closed_forms():
+    from oracle import select_k, expected_tokens
+    # geometric sum closed form
+    for a in (0.0, 0.3, 0.95):
+        for k in range(8):
+            cf = (1 - a ** (k + 1)) / (1 - a)
+            assert abs(expected_tokens(a, k) - cf) < 1e-12
+    # alpha = 0: one token per cycle whatever k, so the cheapest cycle wins
+    tv = [1.0, 1.05, 1.1, 1.2]
+    assert select_k(tv, 0.5, 0.1, 0.0) == (0, 1.0 / 1.1)
+    # alpha = 1: E_k = k + 1
+    k, r = select_k([1.0, 1.0, 1.0], 0.5, 0.0, 1.0)
+    assert k == 2 and abs(r - 3 / 2.0) < 1e-12
