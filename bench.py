@@ -289,6 +289,55 @@ def bench_kselect(args) -> int:
     return 0
 
 
+def bench_kvq(args) -> int:
+    """LayerSkip early-exit draft (tail mask: the first E layers + the shared
+    head) with and without exit-state reuse in the verify (SSD_OPT_KVQ), on the
+    8B-shaped model: verify and draft step times, decode tok/s, losslessness;
+    plus the early-exit inference rate (one E-layer pass per token)."""
+    import numpy as np
+    import synth
+    from self_speculative_decoding_amd import Engine, make_cfg
+    cfg = synth.config("llama-8b")
+    L, k = cfg["n_layers"], args.k if args.k is not None else 3
+    n_new = args.n_new or 256
+    log("kvq: generating weights")
+    w = synth.make_weights(cfg)
+    prompt = synth.make_prompt(cfg)
+    eng = Engine(make_cfg(cfg, max_block=k + 1, prefill_chunk=256), [w[n] for n, _, _ in synth.weight_specs(cfg)])
+    del w
+    base, _ = eng.generate(prompt, n_new)
+    _, stb = eng.generate(prompt, n_new)
+    base_tps = (n_new - 1) / stb["t_decode_ms"] * 1e3
+    rows = []
+    for E in (8, 12, 16, 24):
+        mask = np.zeros(L, np.uint8)
+        mask[E:] = 1
+        r = {"E": E}
+        for mode, on in (("full_verify", False), ("kvq_reuse", True)):
+            eng.set_kvq(on)
+            eng.generate(prompt, n_new, mask, k)                 # capture graphs
+            out, st = eng.generate(prompt, n_new, mask, k)
+            r[mode] = {"verify_ms": round(st["t_verify_ms"] / st["verify_passes"], 4),
+                       "draft_step_ms": round(st["t_draft_ms"] / st["drafted"], 4),
+                       "tok_s": round((n_new - 1) / st["t_decode_ms"] * 1e3, 2),
+                       "acceptance": round(st["accepted"] / st["drafted"], 4),
+                       "lossless": out == base}
+        eng.set_kvq(False)
+        r["early_exit_tok_s"] = round(1e3 / r["full_verify"]["draft_step_ms"], 1)
+        r["verify_saving"] = round(1 - r["kvq_reuse"]["verify_ms"] / r["full_verify"]["verify_ms"], 4)
+        rows.append(r)
+        log(f"E={E}: {r}")
+    eng.close()
+    line = {"metric": "early-exit draft: verify ms with vs without exit-state reuse, 8B-shaped bf16",
+            "value": rows[1]["kvq_reuse"]["verify_ms"], "unit": "ms", "n_gpus": 1, "higher_is_better": False,
+            "dtype": "bf16", "data": "synthetic", "vs_baseline": None,
+            "config": {"workload": f"llama-8b-shaped bf16 random-init, {len(prompt)}-token prompt, {n_new} tokens, "
+                                   f"tail masks E in (8, 12, 16, 24), k={k}"},
+            "greedy_tok_s": round(base_tps, 2), "by_E": rows}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def bench_moe(args) -> int:
     """DeepSeek-V2-Lite-shaped MoE verify passes of n = 1..8 tokens with the
     synthetic routing trace: per-slot vs deduplicated expert reads, whole pass
@@ -360,6 +409,8 @@ def main() -> int:
     ap.add_argument("--n-new", type=int, default=None, help="tokens per decode (default: workload's)")
     ap.add_argument("--blocks", type=int, default=40, help="verify blocks per p (qwen3-8b)")
     ap.add_argument("--passes", type=int, default=12, help="verify passes per n and mode (dsv2-lite)")
+    ap.add_argument("--kvq", action="store_true",
+                    help="early-exit draft with vs without exit-state reuse in the verify")
     ap.add_argument("--kselect", action="store_true",
                     help="draft length from fitted step times: predicted vs measured k*(alpha)")
     ap.add_argument("--pmc-probe", action="store_true",
@@ -386,6 +437,8 @@ def main() -> int:
         return bench_moe(args)
     if args.kselect:
         return bench_kselect(args)
+    if args.kvq:
+        return bench_kvq(args)
     cfg = synth.config(args.workload)
     frac = args.skip if args.skip is not None else cfg.get("skip_frac", 0.5)
     k = args.k if args.k is not None else cfg["k"]

@@ -217,7 +217,15 @@ ssd_status ssd_generate(ssd_ctx* ctx, const int32_t* prompt, int32_t n_prompt, i
  * abstract); outputs are bitwise identical.
  * SSD_OPT_TRACE (default 0): decode-loop passes also record the float32
  * residual after every layer (ssd_read_trace); a test hook. */
-enum { SSD_OPT_GRAPHS = 0, SSD_OPT_MOE_DEDUP = 1, SSD_OPT_TRACE = 2 };
+/* SSD_OPT_KVQ (default 0): when a draft's mask is a tail {E..L-1} (the
+ * LayerSkip early-exit draft, 1 <= E < L), the draft saves each row's residual
+ * after layer E-1 and the verify of that draft runs the last drafted token
+ * through layers 0..E-1, then all rows through layers E..L-1 only, reusing
+ * the draft's KV entries of layers < E (LayerSkip summary 4.3.3, the exit
+ * query cache, read as the residual entering layer E).  Posterior and logits
+ * equal the full verify's bit for bit.  The feature tap is not recomputed by
+ * such a verify.  Other masks, and host blocks, verify in full. */
+enum { SSD_OPT_GRAPHS = 0, SSD_OPT_MOE_DEDUP = 1, SSD_OPT_TRACE = 2, SSD_OPT_KVQ = 3 };
 ssd_status ssd_set_option(ssd_ctx* ctx, int32_t option, int32_t value);
 
 /* Statistics accumulated since load/reset (per-phase times from HIP events). */

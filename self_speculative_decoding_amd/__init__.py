@@ -253,6 +253,10 @@ class Engine:
     def set_trace(self, on: bool):
         _check(lib.ssd_set_option(self.ctx, 2, 1 if on else 0))
 
+    def set_kvq(self, on: bool):
+        """Exit-state reuse for tail-mask (early-exit) drafts (SSD_OPT_KVQ)."""
+        _check(lib.ssd_set_option(self.ctx, 3, 1 if on else 0))
+
     def read_trace(self, rows: int) -> np.ndarray:
         out = np.zeros((self.L, rows, self.d), dtype=np.float32)
         _check(lib.ssd_read_trace(self.ctx, _ptr(out), rows))

@@ -158,6 +158,10 @@ bool compute_layout(const ssd_cfg& c, Layout& L) {
   L.logits = take((size_t)c.max_block * c.vocab * 4);
   L.amax_v = take((size_t)c.max_block * (c.vocab / 16 + 1) * 4);
   L.trace = take((size_t)c.n_layers * c.max_block * d * 4);
+  // exit-state cache of an early-exit draft: residual and its sums of squares
+  // per block row after the draft's last layer
+  L.exit_x = take((size_t)c.max_block * d * 4);
+  L.exit_ss = take((size_t)c.max_block * (d / 16) * 4);
   L.amax_i = take((size_t)c.max_block * (c.vocab / 16 + 1) * 4);
   L.part_o_bytes = (size_t)L.n_part * R * hq * hd * 4;
   L.part_o = take(L.part_o_bytes);

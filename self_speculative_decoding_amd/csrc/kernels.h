@@ -93,6 +93,8 @@ hipError_t launch_set_state(int* state, int idx, int value, hipStream_t s);
 hipError_t launch_read_probe(const void* src, size_t bytes, unsigned* sink, int blocks, hipStream_t s);
 hipError_t launch_copy_tokens(const int* src, int* dst, int n, hipStream_t s);
 hipError_t launch_copy_f32(const float* src, float* dst, int n, hipStream_t s);
+// xg[m][n] = bf16(x[m][n] * g[n]) for M rows of d (the folded-norm input)
+hipError_t launch_scale_bf16(const float* x, const void* g, void* xg, int d, int M, hipStream_t s);
 
 // MoE (routed experts + shared experts)
 struct MoeArgs {

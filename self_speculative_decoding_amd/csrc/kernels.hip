@@ -507,6 +507,12 @@ __global__ __launch_bounds__(256) void copy_f32_kernel(const float* __restrict__
   if (i < n) dst[i] = src[i];
 }
 
+__global__ __launch_bounds__(256) void scale_bf16_kernel(const float* __restrict__ x, const uint16_t* __restrict__ g,
+                                                         uint16_t* __restrict__ xg, int d, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) xg[i] = f2bf(x[i] * bf2f(g[i % d]));
+}
+
 __global__ void copy_tokens_kernel(const int* src, int* dst, int n) {
   for (int i = threadIdx.x; i < n; i += blockDim.x) dst[i] = src[i];
 }
@@ -587,6 +593,12 @@ hipError_t launch_set_state(int* state, int idx, int value, hipStream_t s) {
 
 hipError_t launch_copy_f32(const float* src, float* dst, int n, hipStream_t s) {
   copy_f32_kernel<<<(n + 255) / 256, 256, 0, s>>>(src, dst, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_scale_bf16(const float* x, const void* g, void* xg, int d, int M, hipStream_t s) {
+  const int n = d * M;
+  scale_bf16_kernel<<<(n + 255) / 256, 256, 0, s>>>(x, (const uint16_t*)g, (uint16_t*)xg, d, n);
   return hipGetLastError();
 }
 

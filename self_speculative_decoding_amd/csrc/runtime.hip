@@ -78,6 +78,14 @@ struct ssd_ctx {
   int cap_part = 0;        // attention partitions of the pass being captured
   bool trace_on = false;   // record the residual after every layer of decode-loop passes
   float* trace = nullptr;
+  // exit-state reuse of an early-exit draft (SSD_OPT_KVQ): the draft saves
+  // each row's residual and sums of squares after its last layer; a verify
+  // of that draft starts at the exit layer E from them
+  bool kvq_on = false;
+  int kvq_E = -1;                    // exit layer of the current draft, -1: none
+  float *exit_x = nullptr, *exit_ss = nullptr;
+  std::vector<uint8_t> kvq_rest;     // mask running layers E..L-1 only
+  std::vector<uint8_t> kvq_mask;     // the current draft's mask
   // device views
   float *x, *ss, *logits, *part_o, *part_ml, *cos_t, *sin_t, *amax_v;
   int* amax_i;
@@ -201,24 +209,48 @@ ssd_status layer_forward(ssd_ctx* c, int l, int M, int pos_off, bool feats, cons
   return SSD_OK;
 }
 
+// Exit-state handling of a pass: save_row >= 0 copies the residual (and its
+// sums of squares) of rows [0, M) after the pass's last layer to exit-state
+// rows [save_row, save_row + M); load starts the pass from exit-state rows
+// [0, M) instead of the embedding (the first layer's folded-norm input is
+// recomputed from them); head = false skips the final norm and LM head.
+struct PassSpec {
+  int save_row = -1;
+  bool load = false;
+  bool head = true;
+};
+
 // Full pass: M tokens from d_tok at positions state[0]+pos_off+r through the
 // layers with skip[l] == 0 (all when skip is NULL); the head runs on rows
 // [head_row0, head_row0+head_rows) and writes argmax to d_arg.
 ssd_status run_pass(ssd_ctx* c, const int* d_tok, int M, int pos_off, const uint8_t* skip, int head_row0,
-                    int head_rows, int* d_arg, bool feats) {
+                    int head_rows, int* d_arg, bool feats, const PassSpec& ps = PassSpec()) {
   const ssd_cfg& g = c->cfg;
   const int d = g.d_model, dt = g.dtype;
   const bool fold = dt == SSD_BF16;
   hipStream_t s = c->stream;
   if (c->moe_inject && M > c->moe_inject)
     return fail(SSD_E_ARG, "pass of %d rows but routing was injected for %d", M, c->moe_inject);
-  if (fold) HIPCHK(launch_embed_norm(d_tok, c->embed, c->x, d, M, next_gain(c, -1, skip), c->xn, c->ss, s));
-  else HIPCHK(launch_embed(dt, d_tok, c->embed, c->x, d, M, s));
+  if (ps.load) {
+    HIPCHK(launch_copy_f32(c->exit_x, c->x, M * d, s));
+    if (fold) {
+      HIPCHK(launch_copy_f32(c->exit_ss, c->ss, M * (d / 16), s));
+      HIPCHK(launch_scale_bf16(c->x, next_gain(c, -1, skip), c->xn, d, M, s));
+    }
+  } else if (fold) {
+    HIPCHK(launch_embed_norm(d_tok, c->embed, c->x, d, M, next_gain(c, -1, skip), c->xn, c->ss, s));
+  } else {
+    HIPCHK(launch_embed(dt, d_tok, c->embed, c->x, d, M, s));
+  }
   for (int l = 0; l < g.n_layers; ++l) {
     if (skip && skip[l]) continue;
     SSDCHK(layer_forward(c, l, M, pos_off, feats, next_gain(c, l, skip)));
   }
-  if (head_rows > 0) {
+  if (ps.save_row >= 0) {
+    HIPCHK(launch_copy_f32(c->x, c->exit_x + (size_t)ps.save_row * d, M * d, s));
+    if (fold) HIPCHK(launch_copy_f32(c->ss, c->exit_ss + (size_t)ps.save_row * (d / 16), M * (d / 16), s));
+  }
+  if (head_rows > 0 && ps.head) {
     if (!fold)
       HIPCHK(launch_rmsnorm(dt, c->x + (size_t)head_row0 * d, d, c->final_norm, c->xn, d, d, g.rms_eps, head_rows, s));
     GemmArgs a{};
@@ -258,15 +290,17 @@ void destroy_graphs(ssd_ctx* c) {
 // One decode-loop pass (draft step, verify or plain decode step) with its head
 // on all M rows.  Replays a HIP graph captured on first use: every position is
 // read from device state, so one graph serves every context length.
-ssd_status decode_pass(ssd_ctx* c, const int* tok, int M, int pos_off, const uint8_t* skip, int* arg, bool feats) {
-  if (!c->use_graphs) return run_pass(c, tok, M, pos_off, skip, 0, M, arg, feats);
+ssd_status decode_pass(ssd_ctx* c, const int* tok, int M, int pos_off, const uint8_t* skip, int* arg, bool feats,
+                       const PassSpec& ps = PassSpec()) {
+  if (!c->use_graphs) return run_pass(c, tok, M, pos_off, skip, 0, M, arg, feats, ps);
   // Graphs are keyed by the context bucket (kCtxBucket positions) holding
   // the pass's last row: the attention grid covers that bucket, so a replay
   // never launches more than one bucket's worth of idle partitions.
   const int bucket = (c->n + pos_off + M + kCtxBucket - 1) / kCtxBucket;
   std::string key;
   key.reserve(64 + c->cfg.n_layers);
-  const intptr_t parts[6] = {M, pos_off, (intptr_t)tok, (intptr_t)arg, feats ? 1 : 0, bucket};
+  const intptr_t parts[9] = {M, pos_off, (intptr_t)tok, (intptr_t)arg, feats ? 1 : 0, bucket,
+                             ps.save_row, ps.load ? 1 : 0, ps.head ? 1 : 0};
   key.append((const char*)parts, sizeof parts);
   if (skip) key.append((const char*)skip, c->cfg.n_layers);
   auto it = c->graphs.find(key);
@@ -275,7 +309,7 @@ ssd_status decode_pass(ssd_ctx* c, const int* tok, int M, int pos_off, const uin
     c->cap_part = std::min(c->lay.n_part, bucket * kCtxBucket / ATT_PT);
     HIPCHK(hipStreamBeginCapture(c->stream, hipStreamCaptureModeThreadLocal));
     c->capturing = true;
-    const ssd_status st = run_pass(c, tok, M, pos_off, skip, 0, M, arg, feats);
+    const ssd_status st = run_pass(c, tok, M, pos_off, skip, 0, M, arg, feats, ps);
     c->capturing = false;
     const hipError_t ee = hipStreamEndCapture(c->stream, &ge.graph);
     if (st != SSD_OK) {
@@ -291,9 +325,60 @@ ssd_status decode_pass(ssd_ctx* c, const int* tok, int M, int pos_off, const uin
     it = c->graphs.emplace(key, ge).first;
   }
   HIPCHK(hipGraphLaunch(it->second.exec, c->stream));
-  c->head_rows = M;
+  if (ps.head) c->head_rows = M;
   if (feats && c->cfg.n_feat > 0) c->feat_rows = M;
   return SSD_OK;
+}
+
+// Exit layer E of a tail mask (layers E..L-1 skipped, 1 <= E < L), else -1.
+int tail_exit(const ssd_cfg& g, const uint8_t* mask) {
+  if (!mask) return -1;
+  int E = 0;
+  while (E < g.n_layers && !mask[E]) ++E;
+  if (E < 1 || E >= g.n_layers) return -1;
+  for (int l = E; l < g.n_layers; ++l)
+    if (!mask[l]) return -1;
+  return E;
+}
+
+// Starts a draft with mask: remembers it and, with exit-state reuse on and a
+// tail mask, its exit layer.
+void set_kvq(ssd_ctx* c, const uint8_t* mask) {
+  c->kvq_E = c->kvq_on ? tail_exit(c->cfg, mask) : -1;
+  if (mask) c->kvq_mask.assign(mask, mask + c->cfg.n_layers);
+  else c->kvq_mask.clear();
+}
+
+// Draft step j; with exit-state reuse on and a tail mask it also saves the
+// row's state after the exit layer (LayerSkip summary 4.3.3: the exit query
+// cache, read as the residual entering layer E).
+ssd_status draft_step(ssd_ctx* c, int j, const uint8_t* mask) {
+  PassSpec ps;
+  if (c->kvq_E > 0) ps.save_row = j;
+  return decode_pass(c, c->block + j, 1, j, mask, c->block + j + 1, false, ps);
+}
+
+// Verify of the drafted block [t_last, d_1..d_k].  With a saved exit state:
+// d_k (the one row the draft did not run) goes through layers 0..E-1, then
+// all k+1 rows run layers E..L-1 from the saved states; the KV entries of
+// layers < E are the draft's.  Every row gets the arithmetic of the full
+// pass (rows never depend on the pass width), so posterior and logits equal
+// the full verify's bit for bit.
+ssd_status verify_drafted(ssd_ctx* c, const uint8_t* mask, bool feats) {
+  const int k = c->k;
+  if (c->kvq_E > 0 && k > 0) {
+    const int E = c->kvq_E, L = c->cfg.n_layers;
+    PassSpec a;
+    a.save_row = k;
+    a.head = false;
+    SSDCHK(decode_pass(c, c->block + k, 1, k, mask, nullptr, false, a));
+    c->kvq_rest.assign(L, 0);
+    for (int l = 0; l < E; ++l) c->kvq_rest[l] = 1;
+    PassSpec b;
+    b.load = true;
+    return decode_pass(c, c->block, k + 1, 0, c->kvq_rest.data(), c->post, false, b);
+  }
+  return decode_pass(c, c->block, k + 1, 0, nullptr, c->post, feats);
 }
 
 ssd_status check_tokens(const ssd_cfg& g, const int32_t* t, int n) {
@@ -491,6 +576,8 @@ ssd_status ssd_load(const ssd_cfg* cfg, const ssd_buf* weights, int32_t n_weight
   c->act = at(c, lay.act); c->logits = (float*)at(c, lay.logits);
   c->amax_v = (float*)at(c, lay.amax_v); c->amax_i = (int*)at(c, lay.amax_i);
   c->trace = (float*)at(c, lay.trace);
+  c->exit_x = (float*)at(c, lay.exit_x);
+  c->exit_ss = (float*)at(c, lay.exit_ss);
   c->part_o = (float*)at(c, lay.part_o); c->part_ml = (float*)at(c, lay.part_ml);
   c->cos_t = (float*)at(c, lay.rope_cos); c->sin_t = (float*)at(c, lay.rope_sin);
   c->block = (int*)at(c, lay.block); c->post = (int*)at(c, lay.post); c->toks = (int*)at(c, lay.toks);
@@ -560,6 +647,7 @@ ssd_status ssd_reset(ssd_ctx* c) {
   HIPCHK(hipStreamSynchronize(c->stream));
   c->n = 0;
   c->k = 0;
+  c->kvq_E = -1;
   memset(&c->st, 0, sizeof c->st);
   set_state(c, SSD_OP_RESET);
   return SSD_OK;
@@ -591,9 +679,9 @@ ssd_status ssd_draft(ssd_ctx* c, const uint8_t* skip_mask, int32_t k, int32_t* d
   SSDCHK(transition(c, SSD_OP_DRAFT));
   if (k < 1 || k + 1 > c->cfg.max_block) return fail(SSD_E_ARG, "k=%d outside [1, max_block-1=%d]", k, c->cfg.max_block - 1);
   if (c->n + k + 1 > c->cfg.max_ctx) return fail(SSD_E_CAPACITY, "n=%d + k+1=%d exceeds max_ctx=%d", c->n, k + 1, c->cfg.max_ctx);
+  set_kvq(c, skip_mask);
   HIPCHK(hipEventRecord(c->ev[EV_A], c->stream));
-  for (int j = 0; j < k; ++j)
-    SSDCHK(decode_pass(c, c->block + j, 1, j, skip_mask, c->block + j + 1, false));
+  for (int j = 0; j < k; ++j) SSDCHK(draft_step(c, j, skip_mask));
   HIPCHK(hipEventRecord(c->ev[EV_B], c->stream));
   c->k = k;
   if (drafts) HIPCHK(hipMemcpyAsync(c->hbuf, c->block + 1, k * sizeof(int), hipMemcpyDeviceToHost, c->stream));
@@ -621,9 +709,11 @@ ssd_status ssd_verify(ssd_ctx* c, const int32_t* block, int32_t m, int32_t* post
     memcpy(c->hbuf, block, m * sizeof(int));
     HIPCHK(hipMemcpyAsync(c->block, c->hbuf, m * sizeof(int), hipMemcpyHostToDevice, c->stream));
     c->k = m - 1;
+    c->kvq_E = -1;   // the saved exit states belong to the drafted tokens, not to this block
   }
   HIPCHK(hipEventRecord(c->ev[EV_A], c->stream));
-  SSDCHK(decode_pass(c, c->block, m, 0, nullptr, c->post, true));
+  SSDCHK(verify_drafted(c, c->kvq_mask.empty() ? nullptr : c->kvq_mask.data(), true));
+  c->kvq_E = -1;
   HIPCHK(hipEventRecord(c->ev[EV_B], c->stream));
   HIPCHK(hipMemcpyAsync(c->hbuf, c->post, m * sizeof(int), hipMemcpyDeviceToHost, c->stream));
   HIPCHK(hipStreamSynchronize(c->stream));
@@ -689,11 +779,12 @@ ssd_status ssd_generate(ssd_ctx* c, const int32_t* prompt, int32_t n_prompt, int
   } else {
     while (produced < n_new) {
       HIPCHK(hipEventRecord(c->ev[EV_A], s));
-      for (int j = 0; j < k; ++j)
-        SSDCHK(decode_pass(c, c->block + j, 1, j, skip_mask, c->block + j + 1, false));
+      set_kvq(c, skip_mask);
+      for (int j = 0; j < k; ++j) SSDCHK(draft_step(c, j, skip_mask));
       c->k = k;
       HIPCHK(hipEventRecord(c->ev[EV_B], s));
-      SSDCHK(decode_pass(c, c->block, k + 1, 0, nullptr, c->post, true));
+      SSDCHK(verify_drafted(c, skip_mask, true));
+      c->kvq_E = -1;
       HIPCHK(hipEventRecord(c->ev[EV_C], s));
       int a = 0, ne = 0;
       HIPCHK(launch_accept(c->block, c->post, k, c->dstate, c->outlog, c->result, s));
@@ -727,13 +818,14 @@ ssd_status ssd_generate(ssd_ctx* c, const int32_t* prompt, int32_t n_prompt, int
 ssd_status ssd_set_option(ssd_ctx* c, int32_t option, int32_t value) {
   clear_error();
   if (!c) return fail(SSD_E_ARG, "ctx is NULL");
-  if (option != SSD_OPT_GRAPHS && option != SSD_OPT_MOE_DEDUP && option != SSD_OPT_TRACE)
+  if (option != SSD_OPT_GRAPHS && option != SSD_OPT_MOE_DEDUP && option != SSD_OPT_TRACE && option != SSD_OPT_KVQ)
     return fail(SSD_E_ARG, "unknown option %d", option);
   if (option == SSD_OPT_MOE_DEDUP && c->cfg.n_experts == 0) return fail(SSD_E_UNSUPPORTED, "not an MoE model");
   HIPCHK(hipStreamSynchronize(c->stream));
   destroy_graphs(c);
   if (option == SSD_OPT_GRAPHS) c->use_graphs = value != 0;
   else if (option == SSD_OPT_TRACE) c->trace_on = value != 0;
+  else if (option == SSD_OPT_KVQ) c->kvq_on = value != 0;
   else c->cfg.moe_dedup = value != 0;
   return SSD_OK;
 }
