@@ -338,6 +338,65 @@ def bench_kvq(args) -> int:
     return 0
 
 
+def bench_knapsack(args) -> int:
+    """Skip set as a knapsack on the 8B-shaped model: per-layer costs from
+    measured op times, per-layer value 1 - cos(input, output) from a traced
+    16-row verify pass, budgets matching the middle-skip fractions; compares
+    the knapsack mask with the contiguous middle block (acceptance, tok/s)."""
+    import numpy as np
+    import synth
+    from self_speculative_decoding_amd import Engine, make_cfg, skip_mask, knapsack_skip
+    cfg = synth.config("llama-8b")
+    L, k, n_new = cfg["n_layers"], 3, args.n_new or 256
+    log("knapsack: generating weights")
+    w = synth.make_weights(cfg)
+    prompt = synth.make_prompt(cfg)
+    eng = Engine(make_cfg(cfg, max_block=17, prefill_chunk=256), [w[n] for n, _, _ in synth.weight_specs(cfg)])
+    del w
+    true, _ = eng.generate(prompt, 20)
+    eng.set_trace(True)
+    eng.reset()
+    eng.prefill(prompt)
+    eng.verify(true[:16])
+    cos = eng.layer_cosines(16)
+    eng.set_trace(False)
+    eng.reset()
+    eng.prefill(prompt)
+    # per-layer cost (units of 10 ns): attention block + FFN block at M = 1
+    cost = []
+    for l in range(L):
+        us = sum(eng.time_op(op, l, 1, 20) for op in ("qkv", "attention", "o", "gate_up", "down"))
+        cost.append(int(round(us * 100)))
+    base, stb = eng.generate(prompt, n_new)
+    base_tps = (n_new - 1) / stb["t_decode_ms"] * 1e3
+    value = 1.0 - cos
+    rows = []
+    for frac in (0.1, 0.2, 0.3, 0.4, 0.5):
+        mid = skip_mask(L, frac)
+        budget = int(sum(c for c, m in zip(cost, mid) if not m))
+        ks_mask, kept = knapsack_skip(cost, value, budget)
+        r = {"skip_frac": frac, "budget_us": round(budget / 100, 2),
+             "middle": [int(i) for i in np.nonzero(mid)[0]], "knapsack": [int(i) for i in np.nonzero(ks_mask)[0]]}
+        for name, m in (("middle", mid), ("knapsack", ks_mask)):
+            out, st = eng.generate(prompt, n_new, m, k)
+            r[name + "_run"] = {"acceptance": round(st["accepted"] / st["drafted"], 4),
+                                "tok_s": round((n_new - 1) / st["t_decode_ms"] * 1e3, 2),
+                                "draft_step_ms": round(st["t_draft_ms"] / st["drafted"], 4),
+                                "proxy_kept_value": round(float(sum(v for v, mm in zip(value, m) if not mm)), 6),
+                                "lossless": out == base}
+        rows.append(r)
+        log(f"skip {frac}: middle {r['middle_run']} knapsack {r['knapsack_run']} skips {r['knapsack']}")
+    eng.close()
+    line = {"metric": "knapsack skip set vs middle block: draft acceptance at equal layer-time budget, 8B-shaped bf16",
+            "value": rows[1]["knapsack_run"]["acceptance"], "unit": "acceptance (20 % budget)", "n_gpus": 1,
+            "higher_is_better": True, "dtype": "bf16", "data": "synthetic", "vs_baseline": None,
+            "config": {"workload": f"llama-8b-shaped bf16 random-init, {len(prompt)}-token prompt, {n_new} tokens, k={k}"},
+            "greedy_tok_s": round(base_tps, 2), "layer_cos": [round(float(x), 6) for x in cos],
+            "layer_cost_us": [c / 100 for c in cost], "by_budget": rows}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def bench_moe(args) -> int:
     """DeepSeek-V2-Lite-shaped MoE verify passes of n = 1..8 tokens with the
     synthetic routing trace: per-slot vs deduplicated expert reads, whole pass
@@ -409,6 +468,8 @@ def main() -> int:
     ap.add_argument("--n-new", type=int, default=None, help="tokens per decode (default: workload's)")
     ap.add_argument("--blocks", type=int, default=40, help="verify blocks per p (qwen3-8b)")
     ap.add_argument("--passes", type=int, default=12, help="verify passes per n and mode (dsv2-lite)")
+    ap.add_argument("--knapsack", action="store_true",
+                    help="knapsack skip set (cosine proxy, measured layer costs) vs the middle block")
     ap.add_argument("--kvq", action="store_true",
                     help="early-exit draft with vs without exit-state reuse in the verify")
     ap.add_argument("--kselect", action="store_true",
@@ -439,6 +500,8 @@ def main() -> int:
         return bench_kselect(args)
     if args.kvq:
         return bench_kvq(args)
+    if args.knapsack:
+        return bench_knapsack(args)
     cfg = synth.config(args.workload)
     frac = args.skip if args.skip is not None else cfg.get("skip_frac", 0.5)
     k = args.k if args.k is not None else cfg["k"]

@@ -139,6 +139,18 @@ ssd_status ssd_skip_mask(int32_t n_layers, double frac, uint8_t* mask);
 ssd_status ssd_select_k(const double* t_verify, int32_t kmax, double t_draft, double t_cycle, double alpha,
                         int32_t* k_best, double* rate);
 
+/* Skip set as a 0/1 knapsack (MLX layer-skip blog, "Paper -> the idea": choose
+ * the skipped layers to keep the draft accurate within a compute budget, with
+ * hardware-measured per-layer costs and hidden-state cosine similarity as the
+ * acceptance proxy).  Keeps the layer set K maximising sum_{l in K} value[l]
+ * subject to sum_{l in K} cost[l] <= budget (exact dynamic programme over the
+ * integer costs); mask[l] = 1 for skipped layers (host [n_layers]);
+ * *kept_value = the optimum.  Costs are non-negative integers in any unit;
+ * SSD_E_ARG if n_layers * (budget + 1) > 2^26, for NULL pointers or a
+ * negative cost or budget. */
+ssd_status ssd_knapsack_skip(const int32_t* cost, const double* value, int32_t n_layers, int64_t budget,
+                             uint8_t* mask, double* kept_value);
+
 /* State machine: next state of `op` from `state`, or SSD_E_STATE. */
 ssd_status ssd_check_transition(int32_t state, int32_t op, int32_t* next_state);
 
@@ -239,6 +251,12 @@ ssd_status ssd_read_logits(ssd_ctx* ctx, float* host, int32_t rows);
 /* Residual after every layer of the last decode-loop pass (SSD_OPT_TRACE on):
  * host [n_layers * rows * d] float32, layer-major. */
 ssd_status ssd_read_trace(ssd_ctx* ctx, float* host, int32_t rows);
+/* Acceptance proxy of every layer from the last decode-loop pass (SSD_OPT_TRACE
+ * on; the pass must have run every layer): cos[l] = mean over its first rows
+ * rows of cos(input of layer l, output of layer l), the input of layer 0
+ * being the token embedding; computed in double on the host.  A layer that
+ * barely turns the residual (cos near 1) is a good one to skip. */
+ssd_status ssd_layer_cosines(ssd_ctx* ctx, int32_t rows, double* cos);
 /* KV cache entries of one layer, positions [pos0, pos0+n): host k and v,
  * each [n_kv_heads * n * head_dim] in the cfg dtype (bf16 bits or float32). */
 ssd_status ssd_read_kv(ssd_ctx* ctx, int32_t layer, int32_t pos0, int32_t n, void* k_host, void* v_host);

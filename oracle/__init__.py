@@ -15,6 +15,8 @@ Contents
               MoE expert FFN (per-slot and deduplicated), feature tap.
 ``kselect.py`` draft length from measured step times under geometric
               acceptance (speculative decoding for MoE models, abstract).
+``knapsack.py`` skip set as a knapsack over measured layer costs with a
+              cosine-similarity proxy (MLX layer-skip blog, "Paper -> the idea").
 
 Every floating-point step runs in float64.  For bf16 workloads values are
 rounded to bf16 (nearest, ties to even) exactly where the GPU stores bf16:
@@ -28,3 +30,4 @@ from .accept import accept, accept_brute
 from .skip import skip_layers, skip_mask
 from .model import Model, bf16_round, decode_weight
 from .kselect import expected_tokens, select_k
+from .knapsack import knapsack_skip_brute, layer_cosines

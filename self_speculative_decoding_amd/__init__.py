@@ -27,7 +27,7 @@ EXPORTS = ["ssd_validate_cfg", "ssd_n_weights", "ssd_weight_numel", "ssd_weight_
            "ssd_prefill", "ssd_draft", "ssd_verify", "ssd_accept_rollback", "ssd_generate",
            "ssd_get_stats", "ssd_read_logits", "ssd_read_features", "ssd_set_routing",
            "ssd_read_union", "ssd_test_accept", "ssd_time_op", "ssd_set_option", "ssd_read_trace",
-           "ssd_read_kv", "ssd_select_k"]
+           "ssd_read_kv", "ssd_select_k", "ssd_knapsack_skip", "ssd_layer_cosines"]
 
 
 class Cfg(ctypes.Structure):
@@ -77,6 +77,8 @@ def _load():
         "ssd_workspace_bytes": (I64, [pc]),
         "ssd_skip_mask": (I32, [I32, ctypes.c_double, VP]),
         "ssd_select_k": (I32, [VP, I32, ctypes.c_double, ctypes.c_double, ctypes.c_double, VP, VP]),
+        "ssd_knapsack_skip": (I32, [VP, VP, I32, I64, VP, VP]),
+        "ssd_layer_cosines": (I32, [VP, I32, VP]),
         "ssd_check_transition": (I32, [I32, I32, P(I32)]),
         "ssd_strerror": (ctypes.c_char_p, [I32]),
         "ssd_last_error": (ctypes.c_char_p, []),
@@ -172,6 +174,17 @@ def select_k(t_verify, t_draft: float, t_cycle: float, alpha: float) -> tuple[in
     return k.value, r.value
 
 
+def knapsack_skip(cost, value, budget: int) -> tuple[np.ndarray, float]:
+    """Skip mask keeping the layers of largest total value within the cost
+    budget (ssd_knapsack_skip)."""
+    c = np.ascontiguousarray(cost, dtype=np.int32)
+    v = np.ascontiguousarray(value, dtype=np.float64)
+    mask = np.zeros(len(c), dtype=np.uint8)
+    kept = ctypes.c_double(0.0)
+    _check(lib.ssd_knapsack_skip(_ptr(c), _ptr(v), len(c), int(budget), _ptr(mask), ctypes.byref(kept)))
+    return mask, kept.value
+
+
 def check_transition(state: int, op: int) -> int:
     nxt = ctypes.c_int32(-1)
     st = lib.ssd_check_transition(state, op, ctypes.byref(nxt))
@@ -252,6 +265,12 @@ class Engine:
 
     def set_trace(self, on: bool):
         _check(lib.ssd_set_option(self.ctx, 2, 1 if on else 0))
+
+    def layer_cosines(self, rows: int) -> np.ndarray:
+        """Per-layer mean cosine(input, output) of the last full pass (trace on)."""
+        out = np.zeros(self.L, dtype=np.float64)
+        _check(lib.ssd_layer_cosines(self.ctx, rows, _ptr(out)))
+        return out
 
     def set_kvq(self, on: bool):
         """Exit-state reuse for tail-mask (early-exit) drafts (SSD_OPT_KVQ)."""

@@ -3,6 +3,8 @@
 // Nothing here calls HIP, so all of it runs (and is tested) without a GPU.
 #include "host.h"
 
+#include <vector>
+
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -298,6 +300,43 @@ ssd_status ssd_select_k(const double* t_verify, int32_t kmax, double t_draft, do
   }
   *k_best = best;
   *rate = best_rate;
+  return SSD_OK;
+}
+
+ssd_status ssd_knapsack_skip(const int32_t* cost, const double* value, int32_t n, int64_t budget, uint8_t* mask,
+                             double* kept_value) {
+  ssd::clear_error();
+  if (!cost || !value || !mask || !kept_value) return ssd::fail(SSD_E_ARG, "NULL argument");
+  if (n < 1 || budget < 0) return ssd::fail(SSD_E_ARG, "n_layers must be >= 1 and budget >= 0");
+  if ((int64_t)n * (budget + 1) > ((int64_t)1 << 26)) return ssd::fail(SSD_E_ARG, "n_layers * (budget + 1) too large");
+  for (int i = 0; i < n; ++i)
+    if (cost[i] < 0) return ssd::fail(SSD_E_ARG, "cost[%d] < 0", i);
+  const size_t B = (size_t)budget + 1;
+  // best[b]: best value of the layers seen so far with total cost <= b;
+  // take[i*B + b]: layer i kept in that optimum
+  std::vector<double> best(B, 0.0);
+  std::vector<uint8_t> take((size_t)n * B, 0);
+  for (int i = 0; i < n; ++i) {
+    const size_t c = (size_t)cost[i];
+    for (size_t b = B; b-- > 0;) {
+      if (b < c) break;
+      const double v = best[b - c] + value[i];
+      if (v > best[b]) {
+        best[b] = v;
+        take[(size_t)i * B + b] = 1;
+      }
+    }
+  }
+  size_t b = B - 1;
+  for (int i = n - 1; i >= 0; --i) {
+    if (take[(size_t)i * B + b]) {
+      mask[i] = 0;
+      b -= (size_t)cost[i];
+    } else {
+      mask[i] = 1;
+    }
+  }
+  *kept_value = best[B - 1];
   return SSD_OK;
 }
 

@@ -86,6 +86,10 @@ struct ssd_ctx {
   float *exit_x = nullptr, *exit_ss = nullptr;
   std::vector<uint8_t> kvq_rest;     // mask running layers E..L-1 only
   std::vector<uint8_t> kvq_mask;     // the current draft's mask
+  // the last decode-loop pass: its tokens (device), rows, and whether it ran every layer
+  const int* last_tok = nullptr;
+  int last_M = 0;
+  bool last_full = false;
   // device views
   float *x, *ss, *logits, *part_o, *part_ml, *cos_t, *sin_t, *amax_v;
   int* amax_i;
@@ -292,6 +296,11 @@ void destroy_graphs(ssd_ctx* c) {
 // read from device state, so one graph serves every context length.
 ssd_status decode_pass(ssd_ctx* c, const int* tok, int M, int pos_off, const uint8_t* skip, int* arg, bool feats,
                        const PassSpec& ps = PassSpec()) {
+  c->last_tok = tok;
+  c->last_M = M;
+  c->last_full = !ps.load;
+  if (skip)
+    for (int l = 0; l < c->cfg.n_layers; ++l) c->last_full = c->last_full && !skip[l];
   if (!c->use_graphs) return run_pass(c, tok, M, pos_off, skip, 0, M, arg, feats, ps);
   // Graphs are keyed by the context bucket (kCtxBucket positions) holding
   // the pass's last row: the attention grid covers that bucket, so a replay
@@ -856,6 +865,58 @@ ssd_status ssd_read_trace(ssd_ctx* c, float* host, int32_t rows) {
     HIPCHK(hipMemcpyAsync(host + (size_t)l * rows * d, c->trace + (size_t)l * c->cfg.max_block * d,
                           rows * d * 4, hipMemcpyDeviceToHost, c->stream));
   HIPCHK(hipStreamSynchronize(c->stream));
+  return SSD_OK;
+}
+
+ssd_status ssd_layer_cosines(ssd_ctx* c, int32_t rows, double* cos) {
+  clear_error();
+  if (!c || !cos) return fail(SSD_E_ARG, "NULL argument");
+  if (!c->trace_on) return fail(SSD_E_STATE, "residual trace is off (SSD_OPT_TRACE)");
+  if (!c->last_tok || !c->last_full) return fail(SSD_E_STATE, "the last decode-loop pass did not run every layer");
+  if (rows < 1 || rows > c->last_M || rows > c->cfg.max_block)
+    return fail(SSD_E_ARG, "rows=%d but the last pass has %d", rows, c->last_M);
+  const ssd_cfg& g = c->cfg;
+  const size_t d = g.d_model, L = g.n_layers;
+  std::vector<int> tok(rows);
+  std::vector<float> tr(L * rows * d), in((size_t)rows * d);
+  std::vector<char> emb((size_t)rows * d * c->esz);
+  HIPCHK(hipMemcpyAsync(tok.data(), c->last_tok, rows * sizeof(int), hipMemcpyDeviceToHost, c->stream));
+  HIPCHK(hipStreamSynchronize(c->stream));
+  for (int r = 0; r < rows; ++r) {
+    if (tok[r] < 0 || tok[r] >= g.vocab) return fail(SSD_E_HIP, "token buffer holds %d", tok[r]);
+    HIPCHK(hipMemcpyAsync(emb.data() + (size_t)r * d * c->esz, (const char*)c->embed + (size_t)tok[r] * d * c->esz,
+                          d * c->esz, hipMemcpyDeviceToHost, c->stream));
+  }
+  for (size_t l = 0; l < L; ++l)
+    HIPCHK(hipMemcpyAsync(tr.data() + l * rows * d, c->trace + l * g.max_block * d, rows * d * 4,
+                          hipMemcpyDeviceToHost, c->stream));
+  HIPCHK(hipStreamSynchronize(c->stream));
+  for (size_t i = 0; i < (size_t)rows * d; ++i) {
+    if (c->esz == 2) {
+      uint32_t u = (uint32_t)((const uint16_t*)emb.data())[i] << 16;
+      float f;
+      memcpy(&f, &u, 4);
+      in[i] = f;
+    } else {
+      in[i] = ((const float*)emb.data())[i];
+    }
+  }
+  for (size_t l = 0; l < L; ++l) {
+    const float* a = l == 0 ? in.data() : tr.data() + (l - 1) * rows * d;
+    const float* b = tr.data() + l * rows * d;
+    double sum = 0.0;
+    for (int r = 0; r < rows; ++r) {
+      double ab = 0.0, aa = 0.0, bb = 0.0;
+      for (size_t i = 0; i < d; ++i) {
+        const double x = a[(size_t)r * d + i], y = b[(size_t)r * d + i];
+        ab += x * y;
+        aa += x * x;
+        bb += y * y;
+      }
+      sum += ab / std::sqrt(aa * bb);
+    }
+    cos[l] = sum / rows;
+  }
   return SSD_OK;
 }
 

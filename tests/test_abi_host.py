@@ -136,3 +136,35 @@ def test_select_k_rejects():
     assert c.ssd_select_k(p, 3, 0.0, 0.0, 0.5, ctypes.byref(k), ctypes.byref(r)) == -1
     assert c.ssd_select_k(p, 32, 0.5, 0.0, 0.5, ctypes.byref(k), ctypes.byref(r)) == -1
     assert c.ssd_select_k(None, 3, 0.5, 0.0, 0.5, ctypes.byref(k), ctypes.byref(r)) == -1
+
+
+def test_knapsack_skip_matches_brute_force():
+    from oracle import knapsack_skip_brute
+    rng = np.random.default_rng(5)
+    for trial in range(150):
+        n = int(rng.integers(1, 11))
+        cost = rng.integers(0, 9, n)
+        if trial % 4 == 0:
+            cost[:] = 5                                     # uniform costs: top values win
+        value = rng.uniform(0.0, 1.0, n)
+        if trial % 5 == 0:
+            value = np.round(value * 4) / 4                 # ties
+        budget = int(rng.integers(0, int(cost.sum()) + 2))
+        mask, kept = ssd.knapsack_skip(cost, value, budget)
+        best, sets = knapsack_skip_brute(cost.tolist(), value.tolist(), budget)
+        keep = tuple(int(i) for i in np.nonzero(mask == 0)[0])
+        assert abs(kept - best) <= 1e-9, trial
+        assert keep in sets, (trial, keep, sets)            # an optimal, feasible set
+
+
+def test_knapsack_skip_rejects():
+    c = np.ones(4, np.int32)
+    v = np.ones(4)
+    m = np.zeros(4, np.uint8)
+    kv = ctypes.c_double()
+    f = ssd.lib.ssd_knapsack_skip
+    P = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    assert f(P(c), P(v), 4, -1, P(m), ctypes.byref(kv)) == -1
+    assert f(P(c), P(v), 4, 1 << 25, P(m), ctypes.byref(kv)) == -1
+    bad = np.array([1, -1, 1, 1], np.int32)
+    assert f(P(bad), P(v), 4, 3, P(m), ctypes.byref(kv)) == -1

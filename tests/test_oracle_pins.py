@@ -493,3 +493,29 @@ def test_kselect_closed_forms():
     # alpha = 1: E_k = k + 1
     k, r = select_k([1.0, 1.0, 1.0], 0.5, 0.0, 1.0)
     assert k == 2 and abs(r - 3 / 2.0) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# skip set as a knapsack (MLX layer-skip blog, "Paper -> the idea")
+# ---------------------------------------------------------------------------
+
+def test_layer_cosines_closed_forms():
+    from oracle import layer_cosines
+    e = np.array([[1.0, 0.0], [0.0, 2.0]])
+    same = e * 3.0                               # parallel: cos 1
+    orth = np.array([[0.0, 5.0], [-1.0, 0.0]])   # orthogonal to the previous rows: cos 0
+    neg = -orth                                  # opposite: cos -1
+    got = layer_cosines(e, [same, orth, neg])
+    np.testing.assert_allclose(got, [1.0, 0.0, -1.0], atol=1e-15)
+    # 45 degrees
+    np.testing.assert_allclose(layer_cosines(np.array([[1.0, 0.0]]), [np.array([[1.0, 1.0]])]), [2 ** -0.5])
+
+
+def test_knapsack_brute_hand_example():
+    from oracle import knapsack_skip_brute
+    # values 6, 10, 12 with costs 1, 2, 3 and budget 5: keep {1, 2} (22)
+    best, sets = knapsack_skip_brute([1, 2, 3], [6.0, 10.0, 12.0], 5)
+    assert best == 22.0 and sets == [(1, 2)]
+    # budget 0 keeps nothing; a large budget keeps everything
+    assert knapsack_skip_brute([1, 2, 3], [6.0, 10.0, 12.0], 0) == (0.0, [()])
+    assert knapsack_skip_brute([1, 2, 3], [6.0, 10.0, 12.0], 6)[0] == 28.0
