@@ -214,8 +214,23 @@ ssd_status ssd_accept_rollback(ssd_ctx* ctx, int32_t* n_accepted, int32_t* emitt
  * (the first one comes from the prefill).  skip_mask == NULL or k == 0: plain
  * greedy decode (one full pass per token, no host synchronisation per token);
  * otherwise draft/verify/accept cycles with one host synchronisation each.
- * greedy must be 1 (greedy acceptance; other decoding -> SSD_E_UNSUPPORTED).
- * out: host [n_new]; stats: host or NULL.  Leaves the context READY. */
+ * greedy = 1: greedy decoding and greedy acceptance.  greedy = 0: sampling at
+ * the temperature and seed of ssd_set_sampling (SSD_E_STATE if never set):
+ * every token is drawn from softmax(logits / T) and a cycle accepts by
+ * rejection sampling (LayerSkip summary 4.3.2), so the output follows the full
+ * model's sampling distribution; exit-state reuse is not used.  Other values
+ * -> SSD_E_UNSUPPORTED.  out: host [n_new]; stats: host or NULL.  Leaves the
+ * context READY. */
+/* Sampling parameters of ssd_generate(greedy = 0): temperature T > 0 and the
+ * seed of the Philox4x64-10 stream (key (seed, 0), counter (cycle, slot,
+ * purpose, 0): purposes 0 draft token of slot j, 1 accept test of draft i,
+ * 2 final token of a cycle that accepted a drafts; u = top 24 bits / 2^24).
+ * A draft d_i ~ q_i is accepted when u * q_i(d_i) < p_{i-1}(d_i); the first
+ * rejection draws from max(0, p - q) normalised, a full accept from p_k.  A
+ * draw takes the smallest index whose running sum of weights exceeds u times
+ * their total.  SSD_E_ARG for T <= 0 or not finite. */
+ssd_status ssd_set_sampling(ssd_ctx* ctx, float temperature, uint64_t seed);
+
 ssd_status ssd_generate(ssd_ctx* ctx, const int32_t* prompt, int32_t n_prompt, int32_t n_new,
                         int32_t greedy, const uint8_t* skip_mask, int32_t k,
                         int32_t* out, ssd_stats* stats);
@@ -269,6 +284,13 @@ ssd_status ssd_set_routing(ssd_ctx* ctx, const int32_t* ids, int32_t n);
 ssd_status ssd_read_union(ssd_ctx* ctx, int32_t* host);
 /* Runs the accept kernel on host drafts d[k] and predictions p[k+1];
  * *a receives the accepted length.  Does not change the context's state. */
+/* Test hook: `trials` independent sampled cycles on host logits (cycle
+ * cycle0 + t), drafts drawn from the draft rows: target [(k+1) * V] rows
+ * p_0..p_k, draft [k * V] (row i-1 is q for draft i), float32, V <= vocab,
+ * k + 1 <= max_block.  out: host [trials * (k+2)]: a, the a+1 emitted tokens,
+ * -1 padding.  Overwrites the context's logits (read_logits). */
+ssd_status ssd_test_spec_cycle(ssd_ctx* ctx, const float* target, const float* draft, int32_t k, int32_t V,
+                               float temperature, uint64_t seed, uint64_t cycle0, int32_t trials, int32_t* out);
 ssd_status ssd_test_accept(ssd_ctx* ctx, const int32_t* d, const int32_t* p, int32_t k, int32_t* a);
 /* Times `iters` back-to-back launches of one layer operation at m rows on the
  * context's stream with HIP events; *avg_us receives the mean duration.

@@ -17,6 +17,8 @@ Contents
               acceptance (speculative decoding for MoE models, abstract).
 ``knapsack.py`` skip set as a knapsack over measured layer costs with a
               cosine-similarity proxy (MLX layer-skip blog, "Paper -> the idea").
+``sampling.py`` speculative sampling: rejection-sampling accept with a
+              Philox4x64-10 counter-based generator (LayerSkip summary 4.3.2).
 
 Every floating-point step runs in float64.  For bf16 workloads values are
 rounded to bf16 (nearest, ties to even) exactly where the GPU stores bf16:
@@ -31,3 +33,4 @@ from .skip import skip_layers, skip_mask
 from .model import Model, bf16_round, decode_weight
 from .kselect import expected_tokens, select_k
 from .knapsack import knapsack_skip_brute, layer_cosines
+from .sampling import draw, philox4x64_10, probs, spec_cycle, uniform24

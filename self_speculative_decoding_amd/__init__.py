@@ -27,7 +27,8 @@ EXPORTS = ["ssd_validate_cfg", "ssd_n_weights", "ssd_weight_numel", "ssd_weight_
            "ssd_prefill", "ssd_draft", "ssd_verify", "ssd_accept_rollback", "ssd_generate",
            "ssd_get_stats", "ssd_read_logits", "ssd_read_features", "ssd_set_routing",
            "ssd_read_union", "ssd_test_accept", "ssd_time_op", "ssd_set_option", "ssd_read_trace",
-           "ssd_read_kv", "ssd_select_k", "ssd_knapsack_skip", "ssd_layer_cosines"]
+           "ssd_read_kv", "ssd_select_k", "ssd_knapsack_skip", "ssd_layer_cosines",
+           "ssd_set_sampling", "ssd_test_spec_cycle"]
 
 
 class Cfg(ctypes.Structure):
@@ -79,6 +80,8 @@ def _load():
         "ssd_select_k": (I32, [VP, I32, ctypes.c_double, ctypes.c_double, ctypes.c_double, VP, VP]),
         "ssd_knapsack_skip": (I32, [VP, VP, I32, I64, VP, VP]),
         "ssd_layer_cosines": (I32, [VP, I32, VP]),
+        "ssd_set_sampling": (I32, [VP, ctypes.c_float, ctypes.c_uint64]),
+        "ssd_test_spec_cycle": (I32, [VP, VP, VP, I32, I32, ctypes.c_float, ctypes.c_uint64, ctypes.c_uint64, I32, VP]),
         "ssd_check_transition": (I32, [I32, I32, P(I32)]),
         "ssd_strerror": (ctypes.c_char_p, [I32]),
         "ssd_last_error": (ctypes.c_char_p, []),
@@ -270,6 +273,19 @@ class Engine:
         """Per-layer mean cosine(input, output) of the last full pass (trace on)."""
         out = np.zeros(self.L, dtype=np.float64)
         _check(lib.ssd_layer_cosines(self.ctx, rows, _ptr(out)))
+        return out
+
+    def set_sampling(self, temperature: float, seed: int):
+        _check(lib.ssd_set_sampling(self.ctx, float(temperature), int(seed)))
+
+    def test_spec_cycle(self, target, draft, temperature: float, seed: int, cycle0: int, trials: int) -> np.ndarray:
+        """Sampled cycles on host logits: rows [trials, k+2] = a, emitted tokens, -1."""
+        t = np.ascontiguousarray(target, dtype=np.float32)
+        k, V = t.shape[0] - 1, t.shape[1]
+        d = np.ascontiguousarray(draft, dtype=np.float32).reshape(k, V) if k > 0 else np.zeros((1, V), np.float32)
+        out = np.zeros((trials, k + 2), dtype=np.int32)
+        _check(lib.ssd_test_spec_cycle(self.ctx, _ptr(t), _ptr(d), k, V, float(temperature), int(seed), int(cycle0),
+                                       trials, _ptr(out)))
         return out
 
     def set_kvq(self, on: bool):

@@ -164,6 +164,9 @@ bool compute_layout(const ssd_cfg& c, Layout& L) {
   // per block row after the draft's last layer
   L.exit_x = take((size_t)c.max_block * d * 4);
   L.exit_ss = take((size_t)c.max_block * (d / 16) * 4);
+  // speculative sampling: the draft steps' logits rows, test-cycle outputs
+  L.dlog = take((size_t)c.max_block * c.vocab * 4);
+  L.tout = take((size_t)kTestCycles * (SSD_MAX_BLOCK + 2) * 4);
   L.amax_i = take((size_t)c.max_block * (c.vocab / 16 + 1) * 4);
   L.part_o_bytes = (size_t)L.n_part * R * hq * hd * 4;
   L.part_o = take(L.part_o_bytes);

@@ -10,6 +10,7 @@
 namespace ssd {
 
 constexpr int kAttPT = 64;   // attention key partition width (kernels.h: ATT_PT)
+constexpr int kTestCycles = 4096;   // sampling test cycles per launch
 
 // Byte offsets of every workspace buffer (256-byte aligned).
 struct Layout {
@@ -17,7 +18,7 @@ struct Layout {
   size_t part_o = 0, part_ml = 0, rope_cos = 0, rope_sin = 0;
   size_t block = 0, post = 0, toks = 0, state = 0, result = 0, outlog = 0;
   size_t tblock = 0, tpost = 0, tstate = 0, tresult = 0, toutlog = 0;
-  size_t tap = 0, feat = 0, amax_v = 0, amax_i = 0, trace = 0, wpack = 0, exit_x = 0, exit_ss = 0;
+  size_t tap = 0, feat = 0, amax_v = 0, amax_i = 0, trace = 0, wpack = 0, exit_x = 0, exit_ss = 0, dlog = 0, tout = 0;
   size_t m_rlogits = 0, m_ids = 0, m_gates = 0, m_inject = 0, m_slot_out = 0, m_groups = 0, m_union = 0;
   size_t total = 0;
   int R = 0;        // rows per pass (multiple of 16)

@@ -120,6 +120,23 @@ struct MoeArgs {
 };
 hipError_t launch_moe(int dtype, const MoeArgs& a, hipStream_t s);
 
+// Speculative sampling (sampling.hip).  Logits rows are float32, ld apart;
+// T > 0 the temperature; the cycle counter is state[2].
+// One decode-loop cycle: drafts block[1..k], target rows tl[0..k], draft rows
+// dl[0..k-1]; commits a+1 tokens like the greedy accept.
+hipError_t launch_spec_accept(const float* tl, const float* dl, int ld, int V, int k, float T, uint64_t seed,
+                              int* block, int* state, int* outlog, int* result, hipStream_t s);
+// `trials` independent cycles (cycle0 + t) drawing their drafts from dl;
+// out [trials][k+2]: a, the a+1 emitted tokens, -1 padding.
+hipError_t launch_spec_test(const float* tl, const float* dl, int ld, int V, int k, float T, uint64_t seed,
+                            uint64_t cycle0, int trials, int* out, hipStream_t s);
+// draft step `slot`: *tok ~ softmax(l / T); the row is copied to keep
+hipError_t launch_draft_sample(const float* l, int V, float T, uint64_t seed, const int* state, int slot, int* tok,
+                               float* keep, hipStream_t s);
+// first token after a sampled prefill (replaces its argmax in block[0] and the log)
+hipError_t launch_first_sample(const float* l, int V, float T, uint64_t seed, int* block, int* state, int* outlog,
+                               hipStream_t s);
+
 // Packing of a row-major bf16 weight [N, K] into the tile layout the bf16
 // GEMMs stream (see device.h).  mode 0: rows of src0 in order; mode 1: the
 // QKV GEMM's rows gathered from src0 = wq, src1 = wk, src2 = wv; pair: the

@@ -86,6 +86,12 @@ struct ssd_ctx {
   float *exit_x = nullptr, *exit_ss = nullptr;
   std::vector<uint8_t> kvq_rest;     // mask running layers E..L-1 only
   std::vector<uint8_t> kvq_mask;     // the current draft's mask
+  // sampling (ssd_set_sampling)
+  bool smp_set = false;
+  float smp_T = 1.f;
+  uint64_t smp_seed = 0;
+  float* dlog = nullptr;
+  int* tout = nullptr;
   // the last decode-loop pass: its tokens (device), rows, and whether it ran every layer
   const int* last_tok = nullptr;
   int last_M = 0;
@@ -587,6 +593,8 @@ ssd_status ssd_load(const ssd_cfg* cfg, const ssd_buf* weights, int32_t n_weight
   c->trace = (float*)at(c, lay.trace);
   c->exit_x = (float*)at(c, lay.exit_x);
   c->exit_ss = (float*)at(c, lay.exit_ss);
+  c->dlog = (float*)at(c, lay.dlog);
+  c->tout = (int*)at(c, lay.tout);
   c->part_o = (float*)at(c, lay.part_o); c->part_ml = (float*)at(c, lay.part_ml);
   c->cos_t = (float*)at(c, lay.rope_cos); c->sin_t = (float*)at(c, lay.rope_sin);
   c->block = (int*)at(c, lay.block); c->post = (int*)at(c, lay.post); c->toks = (int*)at(c, lay.toks);
@@ -754,7 +762,9 @@ ssd_status ssd_generate(ssd_ctx* c, const int32_t* prompt, int32_t n_prompt, int
                         const uint8_t* skip_mask, int32_t k, int32_t* out, ssd_stats* stats) {
   clear_error();
   if (!c || !prompt || !out) return fail(SSD_E_ARG, "NULL argument");
-  if (greedy != 1) return fail(SSD_E_UNSUPPORTED, "only greedy decoding is supported");
+  if (greedy != 0 && greedy != 1) return fail(SSD_E_UNSUPPORTED, "greedy must be 1 (greedy) or 0 (sampling)");
+  const bool sampled = greedy == 0;
+  if (sampled && !c->smp_set) return fail(SSD_E_STATE, "sampling parameters not set (ssd_set_sampling)");
   if (n_prompt < 1 || n_new < 1) return fail(SSD_E_ARG, "n_prompt and n_new must be positive");
   const bool spec = skip_mask != nullptr && k > 0;
   if (spec && k + 1 > c->cfg.max_block) return fail(SSD_E_ARG, "k=%d exceeds max_block-1", k);
@@ -767,6 +777,9 @@ ssd_status ssd_generate(ssd_ctx* c, const int32_t* prompt, int32_t n_prompt, int
   memset(&c->st, 0, sizeof c->st);
   SSDCHK(ssd_prefill(c, prompt, n_prompt, nullptr));
   hipStream_t s = c->stream;
+  const int V = c->cfg.vocab;
+  if (sampled)
+    HIPCHK(launch_first_sample(c->logits, V, c->smp_T, c->smp_seed, c->block, c->dstate, c->outlog, s));
   auto t0 = std::chrono::steady_clock::now();
   int produced = 1;
   if (!spec) {
@@ -775,7 +788,11 @@ ssd_status ssd_generate(ssd_ctx* c, const int32_t* prompt, int32_t n_prompt, int
     HIPCHK(hipEventRecord(c->ev[EV_A], s));
     for (int i = 1; i < n_new; ++i) {
       SSDCHK(decode_pass(c, c->block, 1, 0, nullptr, c->post, false));
-      SSDCHK(do_accept(c, false, nullptr, nullptr));
+      if (sampled)   // the k = 0 cycle: one token drawn from p_0
+        HIPCHK(launch_spec_accept(c->logits, c->dlog, V, V, 0, c->smp_T, c->smp_seed, c->block, c->dstate, c->outlog,
+                                  c->result, s));
+      else
+        SSDCHK(do_accept(c, false, nullptr, nullptr));
       c->n += 1;
     }
     HIPCHK(hipEventRecord(c->ev[EV_B], s));
@@ -788,15 +805,25 @@ ssd_status ssd_generate(ssd_ctx* c, const int32_t* prompt, int32_t n_prompt, int
   } else {
     while (produced < n_new) {
       HIPCHK(hipEventRecord(c->ev[EV_A], s));
-      set_kvq(c, skip_mask);
-      for (int j = 0; j < k; ++j) SSDCHK(draft_step(c, j, skip_mask));
+      if (sampled) c->kvq_E = -1;
+      else set_kvq(c, skip_mask);
+      for (int j = 0; j < k; ++j) {
+        SSDCHK(draft_step(c, j, skip_mask));
+        if (sampled)   // d_{j+1} ~ q_{j+1}; the draft row is kept for the accept
+          HIPCHK(launch_draft_sample(c->logits, V, c->smp_T, c->smp_seed, c->dstate, j, c->block + j + 1,
+                                     c->dlog + (size_t)j * V, s));
+      }
       c->k = k;
       HIPCHK(hipEventRecord(c->ev[EV_B], s));
       SSDCHK(verify_drafted(c, skip_mask, true));
       c->kvq_E = -1;
       HIPCHK(hipEventRecord(c->ev[EV_C], s));
       int a = 0, ne = 0;
-      HIPCHK(launch_accept(c->block, c->post, k, c->dstate, c->outlog, c->result, s));
+      if (sampled)
+        HIPCHK(launch_spec_accept(c->logits, c->dlog, V, V, k, c->smp_T, c->smp_seed, c->block, c->dstate, c->outlog,
+                                  c->result, s));
+      else
+        HIPCHK(launch_accept(c->block, c->post, k, c->dstate, c->outlog, c->result, s));
       HIPCHK(hipEventRecord(c->ev[EV_D], s));
       HIPCHK(hipMemcpyAsync(c->hbuf, c->result, 2 * sizeof(int), hipMemcpyDeviceToHost, s));
       HIPCHK(hipStreamSynchronize(s));
@@ -836,6 +863,37 @@ ssd_status ssd_set_option(ssd_ctx* c, int32_t option, int32_t value) {
   else if (option == SSD_OPT_TRACE) c->trace_on = value != 0;
   else if (option == SSD_OPT_KVQ) c->kvq_on = value != 0;
   else c->cfg.moe_dedup = value != 0;
+  return SSD_OK;
+}
+
+ssd_status ssd_set_sampling(ssd_ctx* c, float temperature, uint64_t seed) {
+  clear_error();
+  if (!c) return fail(SSD_E_ARG, "ctx is NULL");
+  if (!(temperature > 0.f) || !std::isfinite(temperature)) return fail(SSD_E_ARG, "temperature must be > 0 and finite");
+  c->smp_set = true;
+  c->smp_T = temperature;
+  c->smp_seed = seed;
+  return SSD_OK;
+}
+
+ssd_status ssd_test_spec_cycle(ssd_ctx* c, const float* target, const float* draft, int32_t k, int32_t V,
+                               float temperature, uint64_t seed, uint64_t cycle0, int32_t trials, int32_t* out) {
+  clear_error();
+  if (!c || !target || !out || (k > 0 && !draft)) return fail(SSD_E_ARG, "NULL argument");
+  if (k < 0 || k + 1 > c->cfg.max_block) return fail(SSD_E_ARG, "k=%d outside [0, max_block-1]", k);
+  if (V < 1 || V > c->cfg.vocab) return fail(SSD_E_ARG, "V=%d outside [1, vocab]", V);
+  if (trials < 1) return fail(SSD_E_ARG, "trials < 1");
+  if (!(temperature > 0.f) || !std::isfinite(temperature)) return fail(SSD_E_ARG, "temperature must be > 0 and finite");
+  hipStream_t s = c->stream;
+  HIPCHK(hipMemcpyAsync(c->logits, target, (size_t)(k + 1) * V * 4, hipMemcpyHostToDevice, s));
+  if (k > 0) HIPCHK(hipMemcpyAsync(c->dlog, draft, (size_t)k * V * 4, hipMemcpyHostToDevice, s));
+  for (int t0 = 0; t0 < trials; t0 += kTestCycles) {
+    const int n = std::min(kTestCycles, trials - t0);
+    HIPCHK(launch_spec_test(c->logits, c->dlog, V, V, k, temperature, seed, cycle0 + t0, n, c->tout, s));
+    HIPCHK(hipMemcpyAsync(out + (size_t)t0 * (k + 2), c->tout, (size_t)n * (k + 2) * 4, hipMemcpyDeviceToHost, s));
+    HIPCHK(hipStreamSynchronize(s));
+  }
+  c->head_rows = 0;
   return SSD_OK;
 }
 

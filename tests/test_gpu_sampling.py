@@ -1,0 +1,117 @@
+"""Speculative sampling through the C ABI (needs an MI355X).
+
+The GPU's rejection-sampling cycle against the oracle's on the same Philox
+stream (decisions identical wherever no rounding-level near tie decides
+them), the speculative-sampling theorem on the GPU (emitted tokens follow the
+target distribution whatever the draft), and sampled decoding end to end:
+near-zero temperature reproduces greedy decoding, a draft equal to the target
+is always accepted, the first sampled token follows the oracle's
+distribution.
+"""
+import numpy as np
+import pytest
+
+import synth
+from oracle import Model, probs, spec_cycle
+from _common import engine
+from test_oracle_pins import _chi2_ok
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    cfg = synth.config("tiny")
+    w = synth.make_weights(cfg)
+    eng = engine(cfg, w)
+    yield cfg, w, eng
+    eng.close()
+
+
+def test_cycle_decisions_match_oracle(tiny):
+    """Same Philox stream, same decisions: every cycle whose decisions are all
+    farther than 1e-5 (relative) from their thresholds must be identical; the
+    rest are decided by float32 vs float64 rounding and are only counted."""
+    cfg, w, eng = tiny
+    rng = np.random.default_rng(21)
+    V, k, T, seed, N = 512, 3, 0.9, 1234, 1500
+    tl = rng.normal(0, 2.0, (k + 1, V)).astype(np.float32)
+    dl = (tl[:k] + rng.normal(0, 0.7, (k, V))).astype(np.float32)   # a draft close to the target
+    got = eng.test_spec_cycle(tl, dl, T, seed, 0, N)
+    agree = near = 0
+    for c in range(N):
+        a, em, margin = spec_cycle(tl, dl, T, seed, c)
+        g_a = int(got[c, 0])
+        g_em = [int(x) for x in got[c, 1:g_a + 2]]
+        if margin < 1e-5:
+            near += 1
+            continue
+        assert (g_a, g_em) == (a, em), (c, (g_a, g_em), (a, em), margin)
+        agree += 1
+    print(f"[sampling] {agree} cycles identical to the oracle, {near} near ties skipped")
+    assert near <= N // 20
+
+
+def test_cycle_output_follows_target_distribution(tiny):
+    """Whatever the draft distribution, emitted token i follows p_i; draft 1 is
+    accepted with probability sum_x min(p_0(x), q_1(x))."""
+    cfg, w, eng = tiny
+    rng = np.random.default_rng(8)
+    V, k, T, N = 48, 3, 1.0, 60000
+    tl = rng.normal(0, 1.5, (k + 1, V)).astype(np.float32)
+    dl = rng.normal(0, 1.5, (k, V)).astype(np.float32)
+    out = eng.test_spec_cycle(tl, dl, T, 77, 0, N)
+    a = out[:, 0]
+    for pos in range(2):
+        sel = a >= pos
+        counts = np.bincount(out[sel, 1 + pos], minlength=V)
+        ok, stat, q = _chi2_ok(counts, probs(tl[pos], T))
+        print(f"[sampling] position {pos}: chi2 {stat:.1f} (0.999 quantile {q:.1f}), {int(sel.sum())} tokens")
+        assert ok
+    pa = float(np.sum(np.minimum(probs(tl[0], T), probs(dl[0], T))))
+    assert abs(np.mean(a >= 1) - pa) <= 4 * np.sqrt(pa * (1 - pa) / N)
+    # k = 0: plain sampling from p_0
+    out0 = eng.test_spec_cycle(tl[:1], np.zeros((0, V), np.float32), T, 5, 0, 20000)
+    assert _chi2_ok(np.bincount(out0[:, 1], minlength=V), probs(tl[0], T))[0]
+
+
+def test_near_zero_temperature_is_greedy_and_equal_draft_always_accepted():
+    cfg = synth.config("llama-8b", n_layers=4, d_model=512, n_q_heads=8, n_kv_heads=2, ffn_dim=1024,
+                       vocab=2048, max_ctx=320, prompt_len=150, cid=80)
+    w = synth.make_weights(cfg, seed=9)
+    eng = engine(cfg, w, max_block=17, prefill_chunk=64)
+    try:
+        prompt = synth.make_prompt(cfg)
+        base, _ = eng.generate(prompt, 40)
+        eng.set_sampling(1e-6, 3)
+        plain, _ = eng.generate(prompt, 40, greedy=0)
+        mid = np.array([0, 1, 1, 0], np.uint8)
+        spec, _ = eng.generate(prompt, 40, mid, 3, greedy=0)
+        assert plain == base and spec == base
+        # T = 1: the full-model draft (nothing skipped) has q == p bit for bit
+        eng.set_sampling(1.0, 11)
+        out, st = eng.generate(prompt, 40, np.zeros(4, np.uint8), 3, greedy=0)
+        assert st["accepted"] == st["drafted"] > 0, st
+        assert all(0 <= t < cfg["vocab"] for t in out)
+    finally:
+        eng.close()
+
+
+def test_first_sampled_token_follows_the_model(tiny):
+    from self_speculative_decoding_amd import SSDError
+    cfg, w, eng = tiny
+    prompt = synth.make_prompt(cfg)
+    T = 1.0
+    _, _, last = Model(cfg, w).prefill(prompt)
+    p = probs(last, T)
+    firsts = []
+    for s in range(3000):
+        eng.set_sampling(T, 1000 + s)
+        out, _ = eng.generate(prompt, 1, greedy=0)
+        firsts.append(out[0])
+    ok, stat, q = _chi2_ok(np.bincount(firsts, minlength=cfg["vocab"]), p)
+    print(f"[sampling] first token chi2 {stat:.1f} (0.999 quantile {q:.1f})")
+    assert ok
+    with pytest.raises(SSDError) as e:
+        eng.set_sampling(0.0, 1)
+    assert e.value.status == -1

@@ -519,3 +519,78 @@ def test_knapsack_brute_hand_example():
     # budget 0 keeps nothing; a large budget keeps everything
     assert knapsack_skip_brute([1, 2, 3], [6.0, 10.0, 12.0], 0) == (0.0, [()])
     assert knapsack_skip_brute([1, 2, 3], [6.0, 10.0, 12.0], 6)[0] == 28.0
+
+
+# ---------------------------------------------------------------------------
+# speculative sampling (LayerSkip summary 4.3.2: rejection-sampling accept)
+# ---------------------------------------------------------------------------
+
+def test_philox_matches_numpy_bit_generator():
+    from oracle import philox4x64_10
+    # numpy's Philox (4x64, 10 rounds) advances its counter before each block
+    for ctr, key in (([0, 0, 0, 0], [0, 0]), ([5, 7, 0, 0], [11, 13]), ([2**62 + 5, 3, 9, 1], [2**62, 17])):
+        bg = np.random.Philox(counter=ctr, key=key)
+        got = [int(x) for x in bg.random_raw(4)]
+        nxt = list(ctr)
+        nxt[0] = (nxt[0] + 1) % 2**64
+        if nxt[0] == 0:
+            nxt[1] += 1
+        assert philox4x64_10(nxt, key) == got
+
+
+def test_draw_special_cases():
+    from oracle import draw, uniform24
+    assert draw([0, 0, 3.0, 0], 0.0)[0] == 2 and draw([0, 0, 3.0, 0], 0.99)[0] == 2
+    for u in (0.0, 0.1, 0.5, 0.99):
+        assert draw(np.ones(10), u)[0] == int(u * 10)
+    for s in range(50):
+        u = uniform24(7, s, 1, 2)
+        assert 0.0 <= u < 1.0 and u * 2**24 == int(u * 2**24)
+
+
+def _chi2_ok(counts, p, min_expected=5.0):
+    """Pearson chi-square with bins of small expectation pooled; True unless the
+    statistic exceeds its 0.999 quantile (Wilson-Hilferty approximation)."""
+    counts, p = np.asarray(counts, float), np.asarray(p, float)
+    n = counts.sum()
+    order = np.argsort(p)
+    cs, ps, acc_c, acc_p = [], [], 0.0, 0.0
+    for i in order:
+        acc_c += counts[i]
+        acc_p += p[i]
+        if acc_p * n >= min_expected:
+            cs.append(acc_c); ps.append(acc_p); acc_c = acc_p = 0.0
+    if acc_p > 0:
+        cs[-1] += acc_c; ps[-1] += acc_p
+    cs, ps = np.array(cs), np.array(ps)
+    stat = np.sum((cs - n * ps) ** 2 / (n * ps))
+    df = len(cs) - 1
+    z = 3.090                                              # 0.999 normal quantile
+    q = df * (1 - 2 / (9 * df) + z * np.sqrt(2 / (9 * df))) ** 3
+    return stat <= q, stat, q
+
+
+def test_spec_cycle_output_follows_the_target_distribution():
+    """The speculative-sampling theorem on a small vocabulary: whatever the draft
+    distribution, the first emitted token is distributed as p_0, the second
+    (when emitted) as p_1, and draft 1 is accepted with probability
+    sum_x min(p_0(x), q_1(x))."""
+    from oracle import spec_cycle, probs
+    rng = np.random.default_rng(3)
+    V, k, T, N = 6, 2, 0.8, 12000
+    tl = rng.normal(0, 1.5, (k + 1, V))
+    dl = rng.normal(0, 1.5, (k, V))
+    first, second, acc1 = np.zeros(V), np.zeros(V), 0
+    for c in range(N):
+        a, em, _ = spec_cycle(tl, dl, T, seed=99, cycle=c)
+        first[em[0]] += 1
+        if len(em) > 1:
+            second[em[1]] += 1
+        acc1 += a >= 1
+    assert _chi2_ok(first, probs(tl[0], T))[0]
+    assert _chi2_ok(second, probs(tl[1], T))[0]
+    pa = np.sum(np.minimum(probs(tl[0], T), probs(dl[0], T)))
+    assert abs(acc1 / N - pa) <= 4 * np.sqrt(pa * (1 - pa) / N)
+    # a draft equal to the target is always accepted
+    a, em, _ = spec_cycle(tl, tl[:k], T, seed=1, cycle=0)
+    assert a == k
