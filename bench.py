@@ -338,6 +338,57 @@ def bench_kvq(args) -> int:
     return 0
 
 
+def bench_sampling(args) -> int:
+    """Speculative sampling on the 8B-shaped model: greedy decoding, plain
+    sampling (one pass per token, a Philox draw from softmax(logits / T)) and
+    self-speculative sampling (middle-skip draft sampled from its own
+    distribution, rejection-sampling accept) at T = 1 and 0.6; tok/s, the
+    acceptance rate and the cost per cycle over the greedy cycle."""
+    import numpy as np
+    import synth
+    from self_speculative_decoding_amd import Engine, make_cfg, skip_mask
+    cfg = synth.config("llama-8b")
+    L, k = cfg["n_layers"], args.k if args.k is not None else 3
+    frac = args.skip if args.skip is not None else 0.2
+    n_new = args.n_new or 256
+    log("sampling: generating weights")
+    w = synth.make_weights(cfg)
+    prompt = synth.make_prompt(cfg)
+    eng = Engine(make_cfg(cfg, max_block=k + 1, prefill_chunk=256), [w[n] for n, _, _ in synth.weight_specs(cfg)])
+    del w
+    mask = skip_mask(L, frac)
+
+    def run(*a, **kw):
+        eng.generate(prompt, n_new, *a, **kw)                    # capture graphs
+        out, st = eng.generate(prompt, n_new, *a, **kw)
+        r = {"tok_s": round((n_new - 1) / st["t_decode_ms"] * 1e3, 2)}
+        if st.get("drafted"):
+            r["acceptance"] = round(st["accepted"] / st["drafted"], 4)
+            r["cycle_ms"] = round(st["t_decode_ms"] / st["verify_passes"], 4)
+        return out, r
+
+    _, greedy = run()
+    _, greedy_spec = run(mask, k)
+    rows = {"greedy": greedy, "greedy_selfspec": greedy_spec}
+    for T in (1.0, 0.6):
+        eng.set_sampling(T, 2024)
+        _, plain = run(greedy=0)
+        out, spec = run(mask, k, greedy=0)
+        assert all(0 <= t < cfg["vocab"] for t in out)
+        spec["cycle_overhead_vs_greedy_ms"] = round(spec["cycle_ms"] - greedy_spec["cycle_ms"], 4)
+        rows[f"T={T}"] = {"plain_sampling": plain, "spec_sampling": spec}
+        log(f"T={T}: plain {plain}, spec {spec}")
+    eng.close()
+    line = {"metric": "self-speculative sampling decode throughput, 8B-shaped bf16",
+            "value": rows["T=1.0"]["spec_sampling"]["tok_s"], "unit": "tokens/s", "n_gpus": 1,
+            "higher_is_better": True, "dtype": "bf16", "data": "synthetic", "vs_baseline": None,
+            "config": {"workload": f"llama-8b-shaped bf16 random-init, {len(prompt)}-token prompt, {n_new} tokens, "
+                                   f"middle skip {frac}, k={k}"},
+            "modes": rows}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def bench_knapsack(args) -> int:
     """Skip set as a knapsack on the 8B-shaped model: per-layer costs from
     measured op times, per-layer value 1 - cos(input, output) from a traced
@@ -472,6 +523,8 @@ def main() -> int:
                     help="knapsack skip set (cosine proxy, measured layer costs) vs the middle block")
     ap.add_argument("--kvq", action="store_true",
                     help="early-exit draft with vs without exit-state reuse in the verify")
+    ap.add_argument("--sampling", action="store_true",
+                    help="speculative sampling vs greedy and plain sampling (8B shape)")
     ap.add_argument("--kselect", action="store_true",
                     help="draft length from fitted step times: predicted vs measured k*(alpha)")
     ap.add_argument("--pmc-probe", action="store_true",
@@ -502,6 +555,8 @@ def main() -> int:
         return bench_kvq(args)
     if args.knapsack:
         return bench_knapsack(args)
+    if args.sampling:
+        return bench_sampling(args)
     cfg = synth.config(args.workload)
     frac = args.skip if args.skip is not None else cfg.get("skip_frac", 0.5)
     k = args.k if args.k is not None else cfg["k"]

@@ -284,14 +284,16 @@ ssd_status ssd_set_routing(ssd_ctx* ctx, const int32_t* ids, int32_t n);
 ssd_status ssd_read_union(ssd_ctx* ctx, int32_t* host);
 /* Runs the accept kernel on host drafts d[k] and predictions p[k+1];
  * *a receives the accepted length.  Does not change the context's state. */
-/* Test hook: `trials` independent sampled cycles on host logits (cycle
- * cycle0 + t), drafts drawn from the draft rows: target [(k+1) * V] rows
- * p_0..p_k, draft [k * V] (row i-1 is q for draft i), float32, V <= vocab,
- * k + 1 <= max_block.  out: host [trials * (k+2)]: a, the a+1 emitted tokens,
- * -1 padding.  Overwrites the context's logits (read_logits). */
+ssd_status ssd_test_accept(ssd_ctx* ctx, const int32_t* d, const int32_t* p, int32_t k, int32_t* a);
+/* Test hook: `trials` sampled cycles on host logits with the decode loop's
+ * sampling kernels, cycle numbers cycle0, cycle0 + 1, ... (cycle0 + trials
+ * <= 2^31 - 1, else SSD_E_ARG); each cycle draws its k drafts from the draft
+ * rows, then accepts.  target [(k+1) * V] rows p_0..p_k, draft [k * V] (row
+ * i-1 is q for draft i), float32, V <= vocab, k + 1 <= max_block.  out: host
+ * [trials * (k+2)]: a, the a+1 emitted tokens, -1 padding.  Overwrites the
+ * context's logits (read_logits); the decode state is not touched. */
 ssd_status ssd_test_spec_cycle(ssd_ctx* ctx, const float* target, const float* draft, int32_t k, int32_t V,
                                float temperature, uint64_t seed, uint64_t cycle0, int32_t trials, int32_t* out);
-ssd_status ssd_test_accept(ssd_ctx* ctx, const int32_t* d, const int32_t* p, int32_t k, int32_t* a);
 /* Times `iters` back-to-back launches of one layer operation at m rows on the
  * context's stream with HIP events; *avg_us receives the mean duration.
  * op: 0 = gate/up GEMM (+SwiGLU), 1 = down GEMM, 2 = qkv GEMM (+RoPE/KV),

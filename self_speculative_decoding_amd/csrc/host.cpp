@@ -167,6 +167,10 @@ bool compute_layout(const ssd_cfg& c, Layout& L) {
   // speculative sampling: the draft steps' logits rows, test-cycle outputs
   L.dlog = take((size_t)c.max_block * c.vocab * 4);
   L.tout = take((size_t)kTestCycles * (SSD_MAX_BLOCK + 2) * 4);
+  L.smp_nch = ((size_t)c.vocab + kSmpChunk - 1) / kSmpChunk;   // sampling scratch
+  L.smp_stats = take((size_t)kSmpRows * L.smp_nch * 8);
+  L.smp_csum = take(2 * L.smp_nch * 4);
+  L.smp_ctl = take(kSmpCtlBytes);
   L.amax_i = take((size_t)c.max_block * (c.vocab / 16 + 1) * 4);
   L.part_o_bytes = (size_t)L.n_part * R * hq * hd * 4;
   L.part_o = take(L.part_o_bytes);

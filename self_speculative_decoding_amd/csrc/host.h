@@ -10,7 +10,9 @@
 namespace ssd {
 
 constexpr int kAttPT = 64;   // attention key partition width (kernels.h: ATT_PT)
-constexpr int kTestCycles = 4096;   // sampling test cycles per launch
+constexpr int kTestCycles = 4096;   // sampling test cycles per output copy
+// sampling scratch (kernels.h: SMP_CHUNK, SMP_ROWS, SMP_CTL_BYTES)
+constexpr int kSmpChunk = 2048, kSmpRows = 63, kSmpCtlBytes = 64;
 
 // Byte offsets of every workspace buffer (256-byte aligned).
 struct Layout {
@@ -19,6 +21,7 @@ struct Layout {
   size_t block = 0, post = 0, toks = 0, state = 0, result = 0, outlog = 0;
   size_t tblock = 0, tpost = 0, tstate = 0, tresult = 0, toutlog = 0;
   size_t tap = 0, feat = 0, amax_v = 0, amax_i = 0, trace = 0, wpack = 0, exit_x = 0, exit_ss = 0, dlog = 0, tout = 0;
+  size_t smp_stats = 0, smp_csum = 0, smp_ctl = 0, smp_nch = 0;
   size_t m_rlogits = 0, m_ids = 0, m_gates = 0, m_inject = 0, m_slot_out = 0, m_groups = 0, m_union = 0;
   size_t total = 0;
   int R = 0;        // rows per pass (multiple of 16)

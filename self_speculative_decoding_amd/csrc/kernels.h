@@ -121,21 +121,30 @@ struct MoeArgs {
 hipError_t launch_moe(int dtype, const MoeArgs& a, hipStream_t s);
 
 // Speculative sampling (sampling.hip).  Logits rows are float32, ld apart;
-// T > 0 the temperature; the cycle counter is state[2].
+// T > 0 the temperature; the cycle counter is state[2].  Each call is three
+// launches over chunks of SMP_CHUNK columns; SmpBufs is their scratch:
+// stats [SMP_ROWS][nch_max] float pairs, csum [2 * nch_max], ctl SMP_CTL_BYTES.
+constexpr int SMP_CHUNK = 2048;
+constexpr int SMP_ROWS = 63;       // 2 * 32 - 1: target and draft rows of the largest cycle
+constexpr int SMP_CTL_BYTES = 64;
+struct SmpBufs {
+  void* stats;
+  float* csum;
+  void* ctl;
+  int nch_max;   // chunks of the widest row
+};
 // One decode-loop cycle: drafts block[1..k], target rows tl[0..k], draft rows
-// dl[0..k-1]; commits a+1 tokens like the greedy accept.
+// dl[0..k-1]; commits a+1 tokens like the greedy accept (outlog may be null);
+// trial_out (or null) receives a, the emitted tokens and -1 up to k+2 entries.
 hipError_t launch_spec_accept(const float* tl, const float* dl, int ld, int V, int k, float T, uint64_t seed,
-                              int* block, int* state, int* outlog, int* result, hipStream_t s);
-// `trials` independent cycles (cycle0 + t) drawing their drafts from dl;
-// out [trials][k+2]: a, the a+1 emitted tokens, -1 padding.
-hipError_t launch_spec_test(const float* tl, const float* dl, int ld, int V, int k, float T, uint64_t seed,
-                            uint64_t cycle0, int trials, int* out, hipStream_t s);
-// draft step `slot`: *tok ~ softmax(l / T); the row is copied to keep
-hipError_t launch_draft_sample(const float* l, int V, float T, uint64_t seed, const int* state, int slot, int* tok,
-                               float* keep, hipStream_t s);
+                              int* block, int* state, int* outlog, int* result, int* trial_out, const SmpBufs& b,
+                              hipStream_t s);
+// draft step `slot`: block[slot + 1] ~ softmax(l / T); the row is copied to keep (or not, if null)
+hipError_t launch_draft_sample(const float* l, int V, float T, uint64_t seed, int* block, const int* state, int slot,
+                               float* keep, const SmpBufs& b, hipStream_t s);
 // first token after a sampled prefill (replaces its argmax in block[0] and the log)
 hipError_t launch_first_sample(const float* l, int V, float T, uint64_t seed, int* block, int* state, int* outlog,
-                               hipStream_t s);
+                               const SmpBufs& b, hipStream_t s);
 
 // Packing of a row-major bf16 weight [N, K] into the tile layout the bf16
 // GEMMs stream (see device.h).  mode 0: rows of src0 in order; mode 1: the

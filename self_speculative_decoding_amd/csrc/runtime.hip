@@ -92,6 +92,7 @@ struct ssd_ctx {
   uint64_t smp_seed = 0;
   float* dlog = nullptr;
   int* tout = nullptr;
+  SmpBufs smp{};
   // the last decode-loop pass: its tokens (device), rows, and whether it ran every layer
   const int* last_tok = nullptr;
   int last_M = 0;
@@ -108,6 +109,7 @@ struct ssd_ctx {
 
 namespace {
 
+static_assert(kSmpChunk == SMP_CHUNK && kSmpRows == SMP_ROWS && kSmpCtlBytes == SMP_CTL_BYTES, "sampling scratch");
 constexpr int kCtxBucket = 512;   // positions per graph context bucket (multiple of ATT_PT)
 
 inline void* at(ssd_ctx* c, size_t off) { return c->ws + off; }
@@ -595,6 +597,7 @@ ssd_status ssd_load(const ssd_cfg* cfg, const ssd_buf* weights, int32_t n_weight
   c->exit_ss = (float*)at(c, lay.exit_ss);
   c->dlog = (float*)at(c, lay.dlog);
   c->tout = (int*)at(c, lay.tout);
+  c->smp = SmpBufs{at(c, lay.smp_stats), (float*)at(c, lay.smp_csum), at(c, lay.smp_ctl), (int)lay.smp_nch};
   c->part_o = (float*)at(c, lay.part_o); c->part_ml = (float*)at(c, lay.part_ml);
   c->cos_t = (float*)at(c, lay.rope_cos); c->sin_t = (float*)at(c, lay.rope_sin);
   c->block = (int*)at(c, lay.block); c->post = (int*)at(c, lay.post); c->toks = (int*)at(c, lay.toks);
@@ -779,7 +782,7 @@ ssd_status ssd_generate(ssd_ctx* c, const int32_t* prompt, int32_t n_prompt, int
   hipStream_t s = c->stream;
   const int V = c->cfg.vocab;
   if (sampled)
-    HIPCHK(launch_first_sample(c->logits, V, c->smp_T, c->smp_seed, c->block, c->dstate, c->outlog, s));
+    HIPCHK(launch_first_sample(c->logits, V, c->smp_T, c->smp_seed, c->block, c->dstate, c->outlog, c->smp, s));
   auto t0 = std::chrono::steady_clock::now();
   int produced = 1;
   if (!spec) {
@@ -790,7 +793,7 @@ ssd_status ssd_generate(ssd_ctx* c, const int32_t* prompt, int32_t n_prompt, int
       SSDCHK(decode_pass(c, c->block, 1, 0, nullptr, c->post, false));
       if (sampled)   // the k = 0 cycle: one token drawn from p_0
         HIPCHK(launch_spec_accept(c->logits, c->dlog, V, V, 0, c->smp_T, c->smp_seed, c->block, c->dstate, c->outlog,
-                                  c->result, s));
+                                  c->result, nullptr, c->smp, s));
       else
         SSDCHK(do_accept(c, false, nullptr, nullptr));
       c->n += 1;
@@ -810,8 +813,8 @@ ssd_status ssd_generate(ssd_ctx* c, const int32_t* prompt, int32_t n_prompt, int
       for (int j = 0; j < k; ++j) {
         SSDCHK(draft_step(c, j, skip_mask));
         if (sampled)   // d_{j+1} ~ q_{j+1}; the draft row is kept for the accept
-          HIPCHK(launch_draft_sample(c->logits, V, c->smp_T, c->smp_seed, c->dstate, j, c->block + j + 1,
-                                     c->dlog + (size_t)j * V, s));
+          HIPCHK(launch_draft_sample(c->logits, V, c->smp_T, c->smp_seed, c->block, c->dstate, j,
+                                     c->dlog + (size_t)j * V, c->smp, s));
       }
       c->k = k;
       HIPCHK(hipEventRecord(c->ev[EV_B], s));
@@ -821,7 +824,7 @@ ssd_status ssd_generate(ssd_ctx* c, const int32_t* prompt, int32_t n_prompt, int
       int a = 0, ne = 0;
       if (sampled)
         HIPCHK(launch_spec_accept(c->logits, c->dlog, V, V, k, c->smp_T, c->smp_seed, c->block, c->dstate, c->outlog,
-                                  c->result, s));
+                                  c->result, nullptr, c->smp, s));
       else
         HIPCHK(launch_accept(c->block, c->post, k, c->dstate, c->outlog, c->result, s));
       HIPCHK(hipEventRecord(c->ev[EV_D], s));
@@ -887,9 +890,21 @@ ssd_status ssd_test_spec_cycle(ssd_ctx* c, const float* target, const float* dra
   hipStream_t s = c->stream;
   HIPCHK(hipMemcpyAsync(c->logits, target, (size_t)(k + 1) * V * 4, hipMemcpyHostToDevice, s));
   if (k > 0) HIPCHK(hipMemcpyAsync(c->dlog, draft, (size_t)k * V * 4, hipMemcpyHostToDevice, s));
+  // the decode loop's kernels, one cycle after another on the test state:
+  // cycle counter tstate[2] from cycle0, drafts into tblock[1..k]
+  int st[16] = {0};
+  if (cycle0 + (uint64_t)trials > (uint64_t)INT32_MAX) return fail(SSD_E_ARG, "cycle0 + trials exceeds 2^31 - 1");
+  st[2] = (int)cycle0;
+  HIPCHK(hipMemcpyAsync(c->tstate, st, sizeof st, hipMemcpyHostToDevice, s));
   for (int t0 = 0; t0 < trials; t0 += kTestCycles) {
     const int n = std::min(kTestCycles, trials - t0);
-    HIPCHK(launch_spec_test(c->logits, c->dlog, V, V, k, temperature, seed, cycle0 + t0, n, c->tout, s));
+    for (int t = 0; t < n; ++t) {
+      for (int j = 0; j < k; ++j)
+        HIPCHK(launch_draft_sample(c->dlog + (size_t)j * V, V, temperature, seed, c->tblock, c->tstate, j, nullptr,
+                                   c->smp, s));
+      HIPCHK(launch_spec_accept(c->logits, c->dlog, V, V, k, temperature, seed, c->tblock, c->tstate, nullptr,
+                                c->tresult, c->tout + (size_t)t * (k + 2), c->smp, s));
+    }
     HIPCHK(hipMemcpyAsync(out + (size_t)t0 * (k + 2), c->tout, (size_t)n * (k + 2) * 4, hipMemcpyDeviceToHost, s));
     HIPCHK(hipStreamSynchronize(s));
   }

@@ -17,14 +17,49 @@
 // in device memory (state[2]), so nothing on the host has to follow it.
 //
 // A draw from weights w takes the smallest j whose running sum exceeds u
-// times the total.  Everything runs in one 1024-thread workgroup per row or
-// per cycle, with reductions and scans in a fixed order.
+// times the total.  Rows are split into chunks of SMP_CH columns and every
+// step is three launches, each reading its rows coalesced and reducing in a
+// fixed order:
+//   stats: per (row, chunk) the chunk max m and the sum of exp((l - m) / T);
+//   sums:  every workgroup combines the row stats (same code, same order, so
+//          all agree), takes the cycle's accept decisions and sums the final
+//          distribution's weights over its chunk; workgroup 0 publishes the
+//          decisions;
+//   pick:  one workgroup finds the chunk holding u times the total, scans it
+//          and commits the tokens.
 #include "device.h"
 
 namespace ssd {
 
-constexpr int SMP_T = 1024;    // threads of every sampling workgroup
-constexpr int SMP_MAXB = 32;   // largest block (k + 1) of a cycle
+constexpr int SMP_T = 256;                   // threads of every sampling workgroup
+constexpr int SMP_PER = 8;                   // columns per thread in a chunk
+constexpr int SMP_CH = SMP_T * SMP_PER;      // columns per chunk
+constexpr int SMP_MAXB = 32;                 // largest block (k + 1) of a cycle
+constexpr int SMP_MAXROWS = 2 * SMP_MAXB - 1;
+constexpr int SMP_MAXCH = 128;               // chunks of the widest row (vocabulary <= 262144)
+static_assert(SMP_CH == SMP_CHUNK && SMP_MAXROWS == SMP_ROWS, "scratch layout");
+
+enum { SMP_DRAFT = 0, SMP_CYCLE = 1, SMP_FIRST = 2 };
+
+// the final draw of a step, decided by the sums kernel
+struct SmpCtl {
+  int a;                   // accepted drafts
+  int resid;               // 1: draw from max(0, p - q) of rows (rp, rq); 0: from row rp
+  int rp, rq;
+  float Mp, rZp, Mq, rZq;  // row max and 1 / sum of exp((l - max) / T)
+  float u;                 // uniform of the final draw
+};
+static_assert(sizeof(SmpCtl) <= SMP_CTL_BYTES, "scratch layout");
+
+// target rows tl[0..nt), then draft rows dl[0..)
+struct RowSrc {
+  const float* tl;
+  const float* dl;
+  int ld, nt;
+  __device__ __forceinline__ const float* row(int r) const {
+    return r < nt ? tl + (size_t)r * ld : dl + (size_t)(r - nt) * ld;
+  }
+};
 
 __device__ __forceinline__ uint64_t philox_word0(uint64_t c0, uint64_t c1, uint64_t c2, uint64_t c3, uint64_t k0,
                                                  uint64_t k1) {
@@ -47,56 +82,238 @@ __device__ __forceinline__ float uniform24(uint64_t seed, uint64_t cycle, uint64
   return (float)(philox_word0(cycle, slot, purpose, 0, seed, 0) >> 40) * (1.0f / 16777216.0f);
 }
 
-struct SmpShared {
-  float red[SMP_T / 64];
-  float scan[SMP_T / 64];
-  int pick;
-  int drafts[SMP_MAXB];
-};
-
-// fixed-order block reduction: wave butterfly, then the 16 wave values in order
+// fixed-order workgroup reduction: wave butterfly, then the wave values in order
 template <bool MAX>
-__device__ __forceinline__ float block_reduce(float v, SmpShared& sh) {
+__device__ __forceinline__ float block_reduce(float v, float* red) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     const float w = __shfl_xor(v, o);
     v = MAX ? fmaxf(v, w) : v + w;
   }
-  if (lane == 0) sh.red[wave] = v;
+  if (lane == 0) red[wave] = v;
   __syncthreads();
-  float r = sh.red[0];
+  float r = red[0];
 #pragma unroll
-  for (int w = 1; w < SMP_T / 64; ++w) r = MAX ? fmaxf(r, sh.red[w]) : r + sh.red[w];
+  for (int w = 1; w < SMP_T / 64; ++w) r = MAX ? fmaxf(r, red[w]) : r + red[w];
   __syncthreads();
   return r;
 }
 
-// max and sum of exp((l - max) / T) of one row of V logits
-__device__ __forceinline__ void row_stats(const float* l, int V, float invT, SmpShared& sh, float& M, float& Z) {
-  float m = -INFINITY;
-  for (int j = threadIdx.x; j < V; j += SMP_T) m = fmaxf(m, l[j]);
-  M = block_reduce<true>(m, sh);
-  float z = 0.f;
-  for (int j = threadIdx.x; j < V; j += SMP_T) z += expf((l[j] - M) * invT);
-  Z = block_reduce<false>(z, sh);
+// Weight of column j in the final distribution; the sums and pick kernels
+// evaluate it with this one expression (products rounded separately, no
+// contraction), so both see the same value.  plain: exp((p_j - Mp) / T);
+// residual: max(0, p_j / Zp - q_j / Zq).  *plain: exp((p_j - Mp) / T).
+__device__ __forceinline__ float smp_weight(const SmpCtl& c, const float* p, const float* q, int j, float invT,
+                                            float* plain) {
+  const float ep = expf((p[j] - c.Mp) * invT);
+  *plain = ep;
+  if (!c.resid) return ep;
+  const float eq = expf((q[j] - c.Mq) * invT);
+  return fmaxf(__fmul_rn(ep, c.rZp) - __fmul_rn(eq, c.rZq), 0.f);
 }
 
-// Draw from weights w(0..V-1) with u: thread t owns the contiguous chunk
-// [t*C, t*C + C); chunk sums are scanned in a fixed order, the thread whose
-// range holds u * total walks its chunk.  Falls back to the last index with a
-// positive weight when rounding leaves the target uncovered.
-template <typename W>
-__device__ int draw_block(W w, int V, float u, SmpShared& sh) {
+// grid (chunks, rows): stats[r * nch + c] = (m, sum exp((l - m) / T)) over the
+// chunk's columns; keep (or null) receives a copy of row 0.
+__global__ __launch_bounds__(SMP_T) void smp_stats_kernel(RowSrc src, int V, float invT, float2* stats, int nch,
+                                                          float* keep) {
+  __shared__ float red[SMP_T / 64];
+  const int c = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
+  const float* x = src.row(r);
+  float v[SMP_PER];
+  float m = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < SMP_PER; ++i) {
+    const int j = c * SMP_CH + i * SMP_T + tid;
+    v[i] = j < V ? x[j] : -INFINITY;
+    m = fmaxf(m, v[i]);
+  }
+  if (keep != nullptr && r == 0) {
+#pragma unroll
+    for (int i = 0; i < SMP_PER; ++i) {
+      const int j = c * SMP_CH + i * SMP_T + tid;
+      if (j < V) keep[j] = v[i];
+    }
+  }
+  m = block_reduce<true>(m, red);
+  float s = 0.f;
+  if (m > -INFINITY) {
+#pragma unroll
+    for (int i = 0; i < SMP_PER; ++i) s += expf((v[i] - m) * invT);
+  }
+  s = block_reduce<false>(s, red);
+  if (tid == 0) stats[(size_t)r * nch + c] = make_float2(m, s);
+}
+
+// grid (chunks): row summaries, the step's decisions, and the chunk sums of
+// the final distribution's weights (csum[c]) and of exp((p_rp - Mp) / T)
+// (csum[nch + c], the fallback when a residual has no mass).
+//   SMP_DRAFT: one row (the draft pass's logits), u(cycle, slot, 0).
+//   SMP_CYCLE: rows p_0..p_k then q_1..q_k, drafts block[1..k], cycle state[2].
+//   SMP_FIRST: the k = 0 cycle numbered 0.
+__global__ __launch_bounds__(SMP_T) void smp_sums_kernel(int mode, RowSrc src, int V, int k, float invT,
+                                                         uint64_t seed, const float2* stats, int nch,
+                                                         const int* state, const int* block, int slot, float* csum,
+                                                         SmpCtl* ctl) {
+  __shared__ float red[SMP_T / 64];
+  __shared__ float sM[SMP_MAXROWS], sZ[SMP_MAXROWS];
+  __shared__ float sp_d[SMP_MAXB], sq_d[SMP_MAXB];
+  __shared__ SmpCtl sc;
+  const int tid = threadIdx.x;
+  const int nrows = 2 * k + 1;
+  if (mode != SMP_DRAFT && tid >= 1 && tid <= k) {   // the drafts' logits, fetched in parallel
+    const int tok = min(max(block[tid], 0), V - 1);
+    sp_d[tid] = src.row(tid - 1)[tok];
+    sq_d[tid] = src.row(k + tid)[tok];
+  }
+  // row summaries: 16 lanes per row, lane l takes chunks l, l + 16, ...;
+  // fixed butterflies, so every workgroup gets the same M and Z
+  {
+    const int g = tid >> 4, l = tid & 15;
+    for (int r0 = 0; r0 < nrows; r0 += SMP_T / 16) {
+      const int r = r0 + g;
+      const float2* st = stats + (size_t)min(r, nrows - 1) * nch;
+      float M = -INFINITY;
+#pragma unroll 4
+      for (int c = l; c < nch; c += 16) M = fmaxf(M, st[c].x);
+#pragma unroll
+      for (int o = 8; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+      float Z = 0.f;
+#pragma unroll 4
+      for (int c = l; c < nch; c += 16) Z += st[c].y * expf((st[c].x - M) * invT);
+#pragma unroll
+      for (int o = 8; o > 0; o >>= 1) Z += __shfl_xor(Z, o);
+      if (r < nrows && l == 0) {
+        sM[r] = M;
+        sZ[r] = Z;
+      }
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    const uint64_t cycle = mode == SMP_FIRST ? 0 : (uint64_t)state[2];
+    SmpCtl d;
+    d.resid = 0;
+    d.rq = 0;
+    d.Mq = 0.f;
+    d.rZq = 0.f;
+    if (mode == SMP_DRAFT) {
+      d.a = 0;
+      d.rp = 0;
+      d.u = uniform24(seed, cycle, slot, 0);
+    } else {
+      int a = k;
+      for (int i = 1; i <= k; ++i) {
+        const int rp = i - 1, rq = k + i;
+        const float pd = expf((sp_d[i] - sM[rp]) * invT) / sZ[rp];
+        const float qd = expf((sq_d[i] - sM[rq]) * invT) / sZ[rq];
+        if (uniform24(seed, cycle, i, 1) * qd < pd) continue;
+        a = i - 1;
+        d.resid = 1;
+        d.rq = rq;
+        d.Mq = sM[rq];
+        d.rZq = 1.0f / sZ[rq];
+        break;
+      }
+      d.a = a;
+      d.rp = d.resid ? a : k;
+      d.u = uniform24(seed, cycle, a, 2);
+    }
+    d.Mp = sM[d.rp];
+    d.rZp = 1.0f / sZ[d.rp];
+    sc = d;
+  }
+  __syncthreads();
+  const SmpCtl d = sc;
+  const float* p = src.row(d.rp);
+  const float* q = src.row(d.rq);
+  float s = 0.f, sp = 0.f;
+#pragma unroll
+  for (int i = 0; i < SMP_PER; ++i) {
+    const int j = blockIdx.x * SMP_CH + i * SMP_T + tid;
+    if (j < V) {
+      float e;
+      s += smp_weight(d, p, q, j, invT, &e);
+      sp += e;
+    }
+  }
+  s = block_reduce<false>(s, red);
+  sp = block_reduce<false>(sp, red);
+  if (tid == 0) {
+    csum[blockIdx.x] = s;
+    csum[nch + blockIdx.x] = sp;
+    if (blockIdx.x == 0) *ctl = d;
+  }
+}
+
+// One workgroup: the draw, then the commit.
+//   SMP_DRAFT: block[slot + 1] = token.
+//   SMP_CYCLE: the emitted d_1..d_a + token go to result[2..] and
+//     outlog[state[1]..] (outlog may be null), result[0..1] = a, a+1; the
+//     committed and emitted counts advance by a+1, block[0] = token, the
+//     cycle counter by one; trial_out (or null) gets a, the emitted tokens
+//     and -1 up to k+2 entries.
+//   SMP_FIRST: the token replaces the prefill's argmax in block[0] and the
+//     log; the cycle counter becomes 1.
+__global__ __launch_bounds__(SMP_T) void smp_pick_kernel(int mode, RowSrc src, int V, int k, int slot, float invT,
+                                                         const float* csum, int nch, const SmpCtl* ctl, int* block,
+                                                         int* state, int* outlog, int* result, int* trial_out) {
+  __shared__ float red[SMP_T / 64];
+  __shared__ float scan[SMP_T / 64];
+  __shared__ float scs[2 * SMP_MAXCH];
+  __shared__ SmpCtl sc;
+  __shared__ int s_chunk, s_pick;
+  __shared__ float s_target;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int C = (V + SMP_T - 1) / SMP_T;
-  const int j0 = min(tid * C, V), j1 = min(j0 + C, V);
+  for (int c = tid; c < 2 * nch; c += SMP_T) scs[c] = csum[c];
+  __syncthreads();
+  if (tid == 0) {
+    SmpCtl d = *ctl;
+    const float* cs = scs;
+    float total = 0.f;
+    for (int c = 0; c < nch; ++c) total += cs[c];
+    if (d.resid && !(total > 0.f)) {   // no residual mass: draw from p itself
+      d.resid = 0;
+      cs = scs + nch;
+      total = 0.f;
+      for (int c = 0; c < nch; ++c) total += cs[c];
+    }
+    const float target = d.u * total;
+    int chunk = -1, last = nch - 1;
+    float run = 0.f, before = 0.f;
+    for (int c = 0; c < nch; ++c) {
+      if (cs[c] > 0.f) last = c;
+      if (chunk < 0) {
+        before = run;
+        run += cs[c];
+        if (run > target) chunk = c;
+      }
+    }
+    if (chunk < 0) {   // rounding left the target uncovered: the last positive column
+      chunk = last;
+      s_target = INFINITY;
+    } else {
+      s_target = target - before;
+    }
+    s_chunk = chunk;
+    s_pick = -1;
+    sc = d;
+  }
+  __syncthreads();
+  const SmpCtl d = sc;
+  const float* p = src.row(d.rp);
+  const float* q = src.row(d.rq);
+  // thread t owns the chunk's columns [8t, 8t + 8), scanned in order
+  const int j0 = min(s_chunk * SMP_CH + tid * SMP_PER, V), j1 = min(j0 + SMP_PER, V);
+  float w[SMP_PER];
   float S = 0.f;
   int lastpos = -1;
-  for (int j = j0; j < j1; ++j) {
-    const float x = w(j);
-    S += x;
-    if (x > 0.f) lastpos = j;
+#pragma unroll
+  for (int i = 0; i < SMP_PER; ++i) {
+    float e;
+    w[i] = j0 + i < j1 ? smp_weight(d, p, q, j0 + i, invT, &e) : 0.f;
+    S += w[i];
+    if (w[i] > 0.f) lastpos = j0 + i;
   }
   float incl = S;
 #pragma unroll
@@ -106,175 +323,95 @@ __device__ int draw_block(W w, int V, float u, SmpShared& sh) {
   }
   float excl = __shfl_up(incl, 1);
   if (lane == 0) excl = 0.f;
-  if (lane == 63) sh.scan[wave] = incl;
-  if (tid == 0) sh.pick = -1;
+  if (lane == 63) scan[wave] = incl;
   __syncthreads();
-  float off = 0.f, total = 0.f;
-  for (int v = 0; v < SMP_T / 64; ++v) {
-    if (v < wave) off += sh.scan[v];
-    total += sh.scan[v];
-  }
+  float off = 0.f;
+  for (int v = 0; v < wave; ++v) off += scan[v];
+  // start of thread t == end of thread t-1 bit for bit, so at most one owner
   const float start = off + excl, end = off + incl;
-  const float target = u * total;
+  const float target = s_target;
   if (S > 0.f && start <= target && target < end) {
     float acc = start;
     int pick = lastpos;
-    for (int j = j0; j < j1; ++j) {
-      acc += w(j);
-      if (acc > target) {
-        pick = j;
+#pragma unroll
+    for (int i = 0; i < SMP_PER; ++i) {
+      acc += w[i];
+      if (acc > target && w[i] > 0.f) {
+        pick = j0 + i;
         break;
       }
     }
-    sh.pick = pick;
+    s_pick = pick;
   }
-  const int lp = (int)block_reduce<true>((float)lastpos, sh);   // also orders the pick write
-  const int p = sh.pick;
-  __syncthreads();
-  return p >= 0 ? p : (lp >= 0 ? lp : 0);
-}
-
-// One draft/verify/accept cycle of speculative sampling.  tl: target rows
-// p_0..p_k, dl: draft rows (row i-1 is q for draft i), both ld floats apart.
-// drafts (when !sample_drafts): the k draft tokens.  Leaves the accepted count
-// in *a_out and the emitted tokens d_1..d_a, final in sh.drafts[0..a].
-__device__ void spec_cycle(const float* tl, const float* dl, int ld, int V, int k, float invT, uint64_t seed,
-                           uint64_t cycle, const int* drafts, bool sample_drafts, SmpShared& sh, int* a_out) {
-  float M, Z;
-  if (sample_drafts) {
-    for (int i = 0; i < k; ++i) {
-      const float* q = dl + (size_t)i * ld;
-      row_stats(q, V, invT, sh, M, Z);
-      const float u = uniform24(seed, cycle, i, 0);
-      const int d = draw_block([&](int j) { return expf((q[j] - M) * invT); }, V, u, sh);
-      if (threadIdx.x == 0) sh.drafts[i] = d;
+  const int lp = (int)block_reduce<true>((float)lastpos, red);   // its barrier also orders the pick write
+  const int pk = s_pick;
+  const int tok = pk >= 0 ? pk : (lp >= 0 ? lp : min(s_chunk * SMP_CH, V - 1));
+  if (mode == SMP_DRAFT) {
+    if (tid == 0) block[slot + 1] = tok;
+    return;
+  }
+  if (mode == SMP_FIRST) {
+    if (tid == 0) {
+      block[0] = tok;
+      outlog[state[1] - 1] = tok;
+      state[2] = 1;
     }
-  } else if (threadIdx.x < k) {
-    sh.drafts[threadIdx.x] = drafts[threadIdx.x];
+    return;
   }
-  __syncthreads();
-  int a = k;
-  int fin = -1;
-  for (int i = 1; i <= k; ++i) {
-    const float* p = tl + (size_t)(i - 1) * ld;
-    const float* q = dl + (size_t)(i - 1) * ld;
-    float Mp, Zp, Mq, Zq;
-    row_stats(p, V, invT, sh, Mp, Zp);
-    row_stats(q, V, invT, sh, Mq, Zq);
-    const int d = sh.drafts[i - 1];
-    const float pd = expf((p[d] - Mp) * invT) / Zp, qd = expf((q[d] - Mq) * invT) / Zq;
-    const float u = uniform24(seed, cycle, i, 1);
-    if (u * qd < pd) continue;
-    a = i - 1;
-    const float rp = 1.0f / Zp, rq = 1.0f / Zq;
-    const float ur = uniform24(seed, cycle, i - 1, 2);
-    fin = draw_block([&](int j) { return fmaxf(expf((p[j] - Mp) * invT) * rp - expf((q[j] - Mq) * invT) * rq, 0.f); },
-                     V, ur, sh);
-    break;
-  }
-  if (a == k) {
-    const float* p = tl + (size_t)k * ld;
-    row_stats(p, V, invT, sh, M, Z);
-    fin = draw_block([&](int j) { return expf((p[j] - M) * invT); }, V, uniform24(seed, cycle, k, 2), sh);
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) sh.drafts[a] = fin;
-  __syncthreads();
-  *a_out = a;
-}
-
-// Decode-loop cycle: drafts are block[1..k]; commits like the greedy accept
-// (emitted tokens to result[2..] and the log, committed and emitted counts
-// advance by a+1, the final token becomes t_last) and advances the cycle.
-__global__ __launch_bounds__(SMP_T) void spec_accept_kernel(const float* tl, const float* dl, int ld, int V, int k,
-                                                            float invT, uint64_t seed, int* block, int* state,
-                                                            int* outlog, int* result) {
-  __shared__ SmpShared sh;
-  int a;
-  spec_cycle(tl, dl, ld, V, k, invT, seed, (uint64_t)state[2], block + 1, false, sh, &a);
+  const int a = d.a;
   const int base = state[1];
-  __syncthreads();
-  if (threadIdx.x <= a) {
-    const int tok = sh.drafts[threadIdx.x];
-    result[2 + threadIdx.x] = tok;
-    outlog[base + threadIdx.x] = tok;
+  if (tid <= a) {
+    const int t = tid < a ? block[tid + 1] : tok;
+    result[2 + tid] = t;
+    if (outlog != nullptr) outlog[base + tid] = t;
   }
-  if (threadIdx.x == 0) {
+  if (trial_out != nullptr && tid < k + 2)
+    trial_out[tid] = tid == 0 ? a : (tid - 1 < a ? block[tid] : (tid - 1 == a ? tok : -1));
+  __syncthreads();   // every thread has read state[1] and block[1..a]
+  if (tid == 0) {
     result[0] = a;
     result[1] = a + 1;
     state[0] += a + 1;
     state[1] += a + 1;
     state[2] += 1;
-    block[0] = sh.drafts[a];
+    block[0] = tok;
   }
 }
 
-// Test cycles: workgroup t runs cycle cycle0 + t with drafts drawn from the
-// draft rows; out[t*(k+2)]: a, then the a+1 emitted tokens, then -1.
-__global__ __launch_bounds__(SMP_T) void spec_test_kernel(const float* tl, const float* dl, int ld, int V, int k,
-                                                          float invT, uint64_t seed, uint64_t cycle0, int* out) {
-  __shared__ SmpShared sh;
-  int a;
-  spec_cycle(tl, dl, ld, V, k, invT, seed, cycle0 + blockIdx.x, nullptr, true, sh, &a);
-  int* o = out + (size_t)blockIdx.x * (k + 2);
-  if (threadIdx.x == 0) o[0] = a;
-  if (threadIdx.x < k + 1) o[1 + threadIdx.x] = threadIdx.x <= a ? sh.drafts[threadIdx.x] : -1;
-}
-
-// Draft step `slot` of a sampled cycle: draws d_{slot+1} from the pass's
-// logits row with u(cycle, slot, 0), and keeps the row for the accept.
-__global__ __launch_bounds__(SMP_T) void draft_sample_kernel(const float* l, int V, float invT, uint64_t seed,
-                                                             const int* state, int slot, int* tok, float* keep) {
-  __shared__ SmpShared sh;
-  for (int j = threadIdx.x; j < V; j += SMP_T) keep[j] = l[j];
-  float M, Z;
-  row_stats(l, V, invT, sh, M, Z);
-  const int d = draw_block([&](int j) { return expf((l[j] - M) * invT); }, V,
-                           uniform24(seed, (uint64_t)state[2], slot, 0), sh);
-  if (threadIdx.x == 0) *tok = d;
-}
-
-// First token after a sampled prefill: drawn from the prefill's last-row
-// logits as cycle 0's final token (slot 0); the cycle counter becomes 1.
-__global__ __launch_bounds__(SMP_T) void first_sample_kernel(const float* l, int V, float invT, uint64_t seed,
-                                                             int* block, int* state, int* outlog) {
-  __shared__ SmpShared sh;
-  float M, Z;
-  row_stats(l, V, invT, sh, M, Z);
-  const int d = draw_block([&](int j) { return expf((l[j] - M) * invT); }, V, uniform24(seed, 0, 0, 2), sh);
-  if (threadIdx.x == 0) {
-    block[0] = d;
-    outlog[state[1] - 1] = d;
-    state[2] = 1;
-  }
+static hipError_t smp_run(int mode, RowSrc src, int nrows, int V, int k, int slot, float T, uint64_t seed,
+                          int* block, int* state, int* outlog, int* result, int* trial_out, float* keep,
+                          const SmpBufs& b, hipStream_t s) {
+  const int nch = (V + SMP_CH - 1) / SMP_CH;
+  if (k < 0 || k + 1 > SMP_MAXB || V < 1 || src.ld < V || nch > b.nch_max || nch > SMP_MAXCH || !(T > 0.f))
+    return hipErrorInvalidValue;
+  const float invT = 1.0f / T;
+  float2* stats = (float2*)b.stats;
+  SmpCtl* ctl = (SmpCtl*)b.ctl;
+  smp_stats_kernel<<<dim3(nch, nrows), SMP_T, 0, s>>>(src, V, invT, stats, nch, keep);
+  smp_sums_kernel<<<nch, SMP_T, 0, s>>>(mode, src, V, k, invT, seed, stats, nch, state, block, slot, b.csum, ctl);
+  smp_pick_kernel<<<1, SMP_T, 0, s>>>(mode, src, V, k, slot, invT, b.csum, nch, ctl, block, state, outlog, result,
+                                      trial_out);
+  return hipGetLastError();
 }
 
 hipError_t launch_spec_accept(const float* tl, const float* dl, int ld, int V, int k, float T, uint64_t seed,
-                              int* block, int* state, int* outlog, int* result, hipStream_t s) {
-  if (k < 0 || k + 1 > SMP_MAXB || V < 1 || ld < V || !(T > 0.f)) return hipErrorInvalidValue;
-  spec_accept_kernel<<<1, SMP_T, 0, s>>>(tl, dl, ld, V, k, 1.0f / T, seed, block, state, outlog, result);
-  return hipGetLastError();
+                              int* block, int* state, int* outlog, int* result, int* trial_out, const SmpBufs& b,
+                              hipStream_t s) {
+  return smp_run(SMP_CYCLE, RowSrc{tl, dl, ld, k + 1}, 2 * k + 1, V, k, 0, T, seed, block, state, outlog, result,
+                 trial_out, nullptr, b, s);
 }
 
-hipError_t launch_spec_test(const float* tl, const float* dl, int ld, int V, int k, float T, uint64_t seed,
-                            uint64_t cycle0, int trials, int* out, hipStream_t s) {
-  if (k < 0 || k + 1 > SMP_MAXB || V < 1 || ld < V || trials < 1 || !(T > 0.f)) return hipErrorInvalidValue;
-  spec_test_kernel<<<trials, SMP_T, 0, s>>>(tl, dl, ld, V, k, 1.0f / T, seed, cycle0, out);
-  return hipGetLastError();
-}
-
-hipError_t launch_draft_sample(const float* l, int V, float T, uint64_t seed, const int* state, int slot, int* tok,
-                               float* keep, hipStream_t s) {
-  if (V < 1 || slot < 0 || !(T > 0.f)) return hipErrorInvalidValue;
-  draft_sample_kernel<<<1, SMP_T, 0, s>>>(l, V, 1.0f / T, seed, state, slot, tok, keep);
-  return hipGetLastError();
+hipError_t launch_draft_sample(const float* l, int V, float T, uint64_t seed, int* block, const int* state, int slot,
+                               float* keep, const SmpBufs& b, hipStream_t s) {
+  if (slot < 0 || slot + 2 > SMP_MAXB) return hipErrorInvalidValue;
+  return smp_run(SMP_DRAFT, RowSrc{l, l, V, 1}, 1, V, 0, slot, T, seed, block, (int*)state, nullptr, nullptr,
+                 nullptr, keep, b, s);
 }
 
 hipError_t launch_first_sample(const float* l, int V, float T, uint64_t seed, int* block, int* state, int* outlog,
-                               hipStream_t s) {
-  if (V < 1 || !(T > 0.f)) return hipErrorInvalidValue;
-  first_sample_kernel<<<1, SMP_T, 0, s>>>(l, V, 1.0f / T, seed, block, state, outlog);
-  return hipGetLastError();
+                               const SmpBufs& b, hipStream_t s) {
+  return smp_run(SMP_FIRST, RowSrc{l, l, V, 1}, 1, V, 0, 0, T, seed, block, state, outlog, nullptr, nullptr,
+                 nullptr, b, s);
 }
 
 }  // namespace ssd
