@@ -157,7 +157,10 @@ def test_state_errors_on_gpu(tiny):
         eng.verify([cfg["vocab"]])               # token out of range
     assert e.value.status == -1
     with pytest.raises(SSDError) as e:
-        eng.generate(synth.make_prompt(cfg), 8, greedy=0)
+        eng.generate(synth.make_prompt(cfg), 8, greedy=0)     # sampling never configured
+    assert e.value.status == -2
+    with pytest.raises(SSDError) as e:
+        eng.generate(synth.make_prompt(cfg), 8, greedy=2)
     assert e.value.status == -5
     with pytest.raises(SSDError) as e:
         eng.generate(synth.make_prompt(cfg), cfg["max_ctx"])
