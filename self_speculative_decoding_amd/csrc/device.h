@@ -50,6 +50,10 @@ __device__ __forceinline__ uint4 ld16_nt(const uint16_t* p) {
 // at h*512 + 8l, so each load instruction of a wave reads 1 KB contiguous.
 // The gate and up matrices of a SwiGLU are interleaved tile by tile (gate
 // chunk s, up chunk s, gate chunk s+1, ...) so one wave streams one region.
+// A dense gate/up weight may use narrower tiles of w < 16 rows (element at
+// h*32w + (wg + c)*8 + j, 64w elements per tile) so that its tile count
+// spreads evenly over the compute units (swiglu_tile_width); lanes c >= w
+// then re-read row w-1 and their MFMA output columns are discarded.
 constexpr int PACK_TILE = 1024;   // elements per packed tile
 
 // One wave's share of a 16-row x (NW x 16)-column MFMA tile: K-chunks
@@ -62,8 +66,9 @@ constexpr int PACK_TILE = 1024;   // elements per packed tile
 // tiles apart (interleaved pairs).  U chunks of loads are issued before their
 // MFMAs; weights are read with nontemporal loads (read once per pass).
 // CS: elements between consecutive chunks of one weight stream (NW tiles
-// interleaved: NW * PACK_TILE; independent tiles: PACK_TILE).
-template <int NW, bool NT, int U, int CS = NW * PACK_TILE>
+// interleaved: NW * TE; independent tiles: TE).  TE: elements of one packed
+// tile (PACK_TILE, or 64 * width for the narrow gate/up tiles).
+template <int NW, bool NT, int U, int CS = NW * PACK_TILE, int TE = PACK_TILE>
 __device__ __forceinline__ void mfma_stream(const uint16_t* xr, bool xok, const uint16_t* const* wr, int c0, int c1,
                                             f32x4* acc) {
   const uint4 zero = {0u, 0u, 0u, 0u};
@@ -76,7 +81,7 @@ __device__ __forceinline__ void mfma_stream(const uint16_t* xr, bool xok, const 
 #pragma unroll
       for (int j = 0; j < NW; ++j) {
         wb[j][u][0] = ldw(wr[j] + (size_t)(s + u) * CS);
-        wb[j][u][1] = ldw(wr[j] + (size_t)(s + u) * CS + PACK_TILE / 2);
+        wb[j][u][1] = ldw(wr[j] + (size_t)(s + u) * CS + TE / 2);
       }
       xa[u][0] = xok ? ld16(xr + (size_t)(s + u) * 64) : zero;
       xa[u][1] = xok ? ld16(xr + (size_t)(s + u) * 64 + 8) : zero;
@@ -96,7 +101,7 @@ __device__ __forceinline__ void mfma_stream(const uint16_t* xr, bool xok, const 
       const uint4 xa = xok ? ld16(xr + (size_t)s * 64 + 8 * h) : zero;
 #pragma unroll
       for (int j = 0; j < NW; ++j) {
-        const uint4 wb = ldw(wr[j] + (size_t)s * CS + h * (PACK_TILE / 2));
+        const uint4 wb = ldw(wr[j] + (size_t)s * CS + h * (TE / 2));
         acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa),
                                                          __builtin_bit_cast(bf16x8, wb), acc[j], 0, 0, 0);
       }
@@ -105,7 +110,7 @@ __device__ __forceinline__ void mfma_stream(const uint16_t* xr, bool xok, const 
 }
 
 // As mfma_stream for MT 16-row tiles sharing every weight fragment.
-template <int NW, int MT, int CS = NW * PACK_TILE>
+template <int NW, int MT, int CS = NW * PACK_TILE, int TE = PACK_TILE>
 __device__ __forceinline__ void mfma_stream_mt(const uint16_t* const* xr, const bool* xok, const uint16_t* const* wr,
                                                int c0, int c1, f32x4 (*acc)[NW]) {
   const uint4 zero = {0u, 0u, 0u, 0u};
@@ -114,7 +119,7 @@ __device__ __forceinline__ void mfma_stream_mt(const uint16_t* const* xr, const 
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
 #pragma unroll
-      for (int j = 0; j < NW; ++j) wb[j][h] = ld16(wr[j] + (size_t)s * CS + h * (PACK_TILE / 2));
+      for (int j = 0; j < NW; ++j) wb[j][h] = ld16(wr[j] + (size_t)s * CS + h * (TE / 2));
 #pragma unroll
       for (int r = 0; r < MT; ++r) xa[r][h] = xok[r] ? ld16(xr[r] + (size_t)s * 64 + 8 * h) : zero;
     }

@@ -147,11 +147,17 @@ __device__ __forceinline__ void qkv_col(const GemmArgs& a, int t, int c, int* he
 // passes), sharing every A fragment.  Each tile's MFMA sequence, K split and
 // reduction order are those of a one-tile workgroup, so TPW never changes a
 // result; it only cuts the A-operand reads from L2.
-template <int EPI, int NW, int KW, int MT, int U, int TPW>
+//
+// TW: rows per packed tile (16; 14 for the narrow gate/up tiles, whose lanes
+// c >= TW compute discarded columns).  A column's arithmetic does not depend
+// on TW.
+template <int EPI, int NW, int KW, int MT, int U, int TPW, int TW = 16>
 __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
   static_assert(TPW == 1 || NW == 1, "tile groups are for one-matrix GEMMs");
+  static_assert(TW == 16 || EPI == EPI_SWIGLU, "narrow tiles are for the gate/up GEMM");
   constexpr int NS = NW * TPW;                               // weight streams
-  constexpr int CS = NW > 1 ? NW * PACK_TILE : PACK_TILE;    // chunk stride of a stream
+  constexpr int TE = TW * 64;                                // elements per packed tile
+  constexpr int CS = NW > 1 ? NW * TE : TE;                  // chunk stride of a stream
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane & 15, kg = lane >> 4;
   const int t0 = blockIdx.x * TPW;                           // first column tile
@@ -167,10 +173,11 @@ __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
   const int S = a.K >> 6;   // 64-element chunks
   // packed weight tiles: gate/up interleaved when NW = 2, else TPW tiles
   const uint16_t* wr[NS];
+  const int lo = (TW * kg + min(c, TW - 1)) * 8;             // this lane's 16 bytes in a tile half
 #pragma unroll
   for (int j = 0; j < NS; ++j)
-    wr[j] = NW > 1 ? (const uint16_t*)a.W0 + ((size_t)t0 * S * NW + j) * PACK_TILE + 8 * lane
-                   : (const uint16_t*)a.W0 + (size_t)(t0 + j) * S * PACK_TILE + 8 * lane;
+    wr[j] = NW > 1 ? (const uint16_t*)a.W0 + ((size_t)t0 * S * NW + j) * TE + lo
+                   : (const uint16_t*)a.W0 + (size_t)(t0 + j) * S * TE + lo;
   int head[TPW], dim[TPW];
 #pragma unroll
   for (int j = 0; j < TPW; ++j) {
@@ -224,7 +231,7 @@ __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
     // first load batch, then the rotary table entries of wave 0's epilogue
     // (they need the position), then the rest of the K range
     const int sm = min(s0 + U, s1);
-    mfma_stream<NS, true, U, CS>(xr[0], av_ok[0], wr, s0, sm, acc[0]);
+    mfma_stream<NS, true, U, CS, TE>(xr[0], av_ok[0], wr, s0, sm, acc[0]);
     if (wave == 0 && c < 8) {
       const int half = a.hd >> 1;
 #pragma unroll
@@ -240,11 +247,11 @@ __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
         }
       }
     }
-    mfma_stream<NS, true, U, CS>(xr[0], av_ok[0], wr, sm, s1, acc[0]);
+    mfma_stream<NS, true, U, CS, TE>(xr[0], av_ok[0], wr, sm, s1, acc[0]);
   } else if (MT == 1) {
-    mfma_stream<NS, true, U, CS>(xr[0], av_ok[0], wr, s0, s1, acc[0]);
+    mfma_stream<NS, true, U, CS, TE>(xr[0], av_ok[0], wr, s0, s1, acc[0]);
   }
-  else mfma_stream_mt<NS, MT, CS>(xr, av_ok, wr, s0, s1, acc);
+  else mfma_stream_mt<NS, MT, CS, TE>(xr, av_ok, wr, s0, s1, acc);
 
   __shared__ f32x4 red[KW - 1][MT][NS][64];
   __shared__ float rs[16 * MT];
@@ -291,7 +298,7 @@ __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int m = mt * 16 + 4 * kg + i;
-        if (m < a.M) epi_swiglu<uint16_t>(a, m, t0 * 16 + c, acc[r][0][i], acc[r][NS - 1][i]);
+        if (m < a.M && c < TW) epi_swiglu<uint16_t>(a, m, t0 * TW + c, acc[r][0][i], acc[r][NS - 1][i]);
       }
       continue;
     }
@@ -369,6 +376,7 @@ __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
 __global__ __launch_bounds__(128) void pack_kernel(PackArgs p) {
   const int t = blockIdx.x, s = blockIdx.y, which = blockIdx.z;
   const int l = threadIdx.x & 63, h = threadIdx.x >> 6, g = l >> 4, c = l & 15;
+  const int tw = p.tw ? p.tw : 16;   // rows per tile (16 for mode 1)
   const uint16_t* src;
   size_t row;
   if (p.mode == 1) {
@@ -379,17 +387,20 @@ __global__ __launch_bounds__(128) void pack_kernel(PackArgs p) {
     else if (head < p.hq + p.hkv) { src = (const uint16_t*)p.src1; row = (size_t)(head - p.hq) * p.hd + dim; }
     else { src = (const uint16_t*)p.src2; row = (size_t)(head - p.hq - p.hkv) * p.hd + dim; }
   } else {
+    if (c >= tw) return;
     src = (const uint16_t*)(which ? p.src1 : p.src0);
-    row = (size_t)t * 16 + c;
+    row = (size_t)t * tw + c;
   }
   const uint4 v = *(const uint4*)(src + row * p.K + (size_t)s * 64 + 16 * g + 8 * h);
   const size_t tile = ((size_t)t * (p.K / 64) + s) * (p.pair ? 2 : 1) + which;
-  *(uint4*)((uint16_t*)p.dst + tile * PACK_TILE + h * (PACK_TILE / 2) + 8 * l) = v;
+  *(uint4*)((uint16_t*)p.dst + tile * (64 * tw) + h * (32 * tw) + (tw * g + c) * 8) = v;
 }
 
 hipError_t launch_pack(const PackArgs& p, hipStream_t s) {
-  if (p.N % 16 || p.K % 64 || p.N <= 0 || p.K <= 0) return hipErrorInvalidValue;
-  pack_kernel<<<dim3(p.N / 16, p.K / 64, p.pair ? 2 : 1), 128, 0, s>>>(p);
+  const int tw = p.tw ? p.tw : 16;
+  if (tw < 1 || tw > 16 || (p.mode == 1 && tw != 16)) return hipErrorInvalidValue;
+  if (p.N % tw || p.N % 16 || p.K % 64 || p.N <= 0 || p.K <= 0) return hipErrorInvalidValue;
+  pack_kernel<<<dim3(p.N / tw, p.K / 64, p.pair ? 2 : 1), 128, 0, s>>>(p);
   return hipGetLastError();
 }
 
@@ -461,8 +472,9 @@ hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t s) {
   const int mt = (a.M + 15) / 16;
   if (dtype) {
     int tiles;
+    const int tw = epi == EPI_SWIGLU ? swiglu_tile_width(a.N) : 16;   // as packed
     if (epi == EPI_QKV) tiles = (a.hq + 2 * a.hkv) * a.hd / 16;
-    else tiles = a.N / 16;
+    else tiles = a.N / tw;
     dim3 grid(tiles, mt);
     const bool wide = tiles >= 1024;   // a function of N only
     // decode-loop passes (M <= SSD_MAX_BLOCK rows) always take the one-tile
@@ -497,7 +509,10 @@ hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t s) {
       case EPI_QKV: SSD_G1(EPI_QKV, SSD_KW_NARROW, SSD_GEMM_U1) break;
       case EPI_STORE: SSD_G1(EPI_STORE, SSD_KW_NARROW, SSD_GEMM_U1) break;
       case EPI_SWIGLU:
-        if (multi) gemm_bf16_kernel<EPI_SWIGLU, 2, 4, 4, 1, 1><<<grid_mt, 256, 0, s>>>(a);
+        if (tw == 14) {
+          if (multi) gemm_bf16_kernel<EPI_SWIGLU, 2, 4, 4, 1, 1, 14><<<grid_mt, 256, 0, s>>>(a);
+          else gemm_bf16_kernel<EPI_SWIGLU, 2, SSD_KW_SWIGLU, 1, SSD_GEMM_U2, 1, 14><<<grid, 64 * SSD_KW_SWIGLU, 0, s>>>(a);
+        } else if (multi) gemm_bf16_kernel<EPI_SWIGLU, 2, 4, 4, 1, 1><<<grid_mt, 256, 0, s>>>(a);
         else if (wide) gemm_bf16_kernel<EPI_SWIGLU, 2, SSD_KW_WIDE, 1, SSD_GEMM_U2, 1><<<grid, 64 * SSD_KW_WIDE, 0, s>>>(a);
         else gemm_bf16_kernel<EPI_SWIGLU, 2, SSD_KW_SWIGLU, 1, SSD_GEMM_U2, 1><<<grid, 64 * SSD_KW_SWIGLU, 0, s>>>(a);
         break;

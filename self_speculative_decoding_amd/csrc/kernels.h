@@ -154,7 +154,22 @@ struct PackArgs {
   const void* src0; const void* src1; const void* src2;
   void* dst;
   int N, K, mode, pair, hq, hkv, hd;
+  int tw;   // rows per tile for mode 0 (0: 16); N % tw == 0
 };
+
+// Compute units of one MI355X: the bf16 GEMMs give every workgroup the same
+// weight bytes, so a launch is balanced when its tile count spreads evenly.
+constexpr int NUM_CU = 256;
+// Rows per packed tile of a dense SwiGLU gate/up weight with N output
+// columns: 16, or 14 when that divides N and lowers the largest per-CU share
+// of tile bytes (ceil(tiles / NUM_CU) tiles of w rows each).  A function of N
+// only; the packing and the GEMM launch both call it.
+inline int swiglu_tile_width(int N) {
+  if (N % 14 != 0) return 16;
+  const long w16 = (long)((N / 16 + NUM_CU - 1) / NUM_CU) * 16;
+  const long w14 = (long)((N / 14 + NUM_CU - 1) / NUM_CU) * 14;
+  return w14 < w16 ? 14 : 16;
+}
 hipError_t launch_pack(const PackArgs& p, hipStream_t s);
 
 }  // namespace ssd

@@ -463,12 +463,12 @@ hipError_t pack_weights(ssd_ctx* c) {
   uint16_t* wp = (uint16_t*)at(c, c->lay.wpack);
   size_t off = 0;
   hipError_t e = hipSuccess;
-  auto pack = [&](const void* s0, const void* s1, const void* s2, int N, int K, int mode, int pair) {
+  auto pack = [&](const void* s0, const void* s1, const void* s2, int N, int K, int mode, int pair, int tw = 16) {
     uint16_t* dst = wp + off;
     off += (size_t)N * K * (pair ? 2 : 1);
     if (e == hipSuccess) {
       PackArgs p{};
-      p.src0 = s0; p.src1 = s1; p.src2 = s2; p.dst = dst; p.N = N; p.K = K; p.mode = mode; p.pair = pair;
+      p.src0 = s0; p.src1 = s1; p.src2 = s2; p.dst = dst; p.N = N; p.K = K; p.mode = mode; p.pair = pair; p.tw = tw;
       p.hq = hq; p.hkv = hkv; p.hd = hd;
       e = launch_pack(p, c->stream);
     }
@@ -505,7 +505,7 @@ hipError_t pack_weights(ssd_ctx* c) {
       w.eg = eg; w.ed = ed; w.sg = sg; w.sd = sd;
       w.eu = w.su = nullptr;
     } else {
-      w.w_gate = pack(w.w_gate, w.w_up, nullptr, w.ffn, d, 0, 1);
+      w.w_gate = pack(w.w_gate, w.w_up, nullptr, w.ffn, d, 0, 1, swiglu_tile_width(w.ffn));   // as launch_gemm reads it
       w.w_up = nullptr;
       w.w_down = pack(w.w_down, nullptr, nullptr, d, w.ffn, 0, 0);
     }

@@ -129,3 +129,34 @@ def test_query_groups_of_one_and_two(hq, hkv):
         assert spec == toks
     finally:
         eng.close()
+
+
+def test_narrow_gate_up_tiles():
+    """An FFN width whose gate/up weight is packed in 14-row tiles (3584 = 256
+    tiles of 14 columns, one per compute unit) against the oracle; the narrow
+    tiles keep verify rows bitwise equal to decode rows and self-speculation
+    lossless."""
+    cfg = _edge_cfg(ffn_dim=3584, max_ctx=200, prompt_len=90, cid=74)
+    w = synth.make_weights(cfg, seed=8)
+    print("[edge] ffn 3584 (14-row gate/up tiles)", flush=True)
+    eng = engine(cfg, w, max_block=8, prefill_chunk=64)
+    try:
+        prompt = synth.make_prompt(cfg)
+        toks, rows = _stepwise(eng, prompt, 33)
+        ref = Model(cfg, w).teacher_forced(prompt, toks)
+        err = np.max(np.abs(rows - ref))
+        print(f"[edge] ffn 3584: max |dlogit| = {err:.3e}")
+        assert err <= BOUND
+        assert _gap_ok(toks, ref, BOUND) == []
+        eng.reset()
+        eng.prefill(prompt)
+        post = eng.verify(toks[:8])
+        assert np.array_equal(eng.read_logits(8), rows[1:9])
+        assert post == toks[1:9]
+        eng.accept()
+        mask = np.zeros(cfg["n_layers"], np.uint8)
+        mask[1] = 1
+        spec, _ = eng.generate(prompt, 32, mask, 3)
+        assert spec == toks[:32]
+    finally:
+        eng.close()
