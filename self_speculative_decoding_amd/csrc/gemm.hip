@@ -133,28 +133,18 @@ __device__ __forceinline__ float ss_rstd(const GemmArgs& a, int m, bool row_ok, 
   return 1.0f / sqrtf(s / (float)a.K + a.eps);
 }
 
-// Output head and head dim of lane c in column tile t of the QKV GEMM.  Its
-// packed weight rows put the RoPE pair (i, i + hd/2) of a q or k head on
-// lanes c and c^8: tile columns 8jj..8jj+7 and hd/2+8jj..+7 of the head.
-__device__ __forceinline__ void qkv_col(const GemmArgs& a, int t, int c, int* head_out, int* dim_out) {
-  const int col0 = t * 16;
-  const int head = col0 / a.hd, jj = (col0 % a.hd) / 16, half = a.hd >> 1;
-  *head_out = head;
-  *dim_out = head < a.hq + a.hkv ? (c < 8 ? 8 * jj + c : half + 8 * jj + (c - 8)) : 16 * jj + c;
-}
-
 // TPW: independent 16-column tiles per workgroup (one-matrix GEMMs of wide
 // passes), sharing every A fragment.  Each tile's MFMA sequence, K split and
 // reduction order are those of a one-tile workgroup, so TPW never changes a
 // result; it only cuts the A-operand reads from L2.
 //
-// TW: rows per packed tile (16; 14 for the narrow gate/up tiles, whose lanes
-// c >= TW compute discarded columns).  A column's arithmetic does not depend
-// on TW.
+// TW: rows per packed tile (16; 14 for narrow gate/up tiles, 12 for narrow
+// QKV tiles; lanes c >= TW compute discarded columns).  A column's
+// arithmetic does not depend on TW.
 template <int EPI, int NW, int KW, int MT, int U, int TPW, int TW = 16>
 __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
   static_assert(TPW == 1 || NW == 1, "tile groups are for one-matrix GEMMs");
-  static_assert(TW == 16 || EPI == EPI_SWIGLU, "narrow tiles are for the gate/up GEMM");
+  static_assert(TW == 16 || (EPI == EPI_SWIGLU && TW == 14) || (EPI == EPI_QKV && TW == 12), "tile width");
   constexpr int NS = NW * TPW;                               // weight streams
   constexpr int TE = TW * 64;                                // elements per packed tile
   constexpr int CS = NW > 1 ? NW * TE : TE;                  // chunk stride of a stream
@@ -178,11 +168,17 @@ __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
   for (int j = 0; j < NS; ++j)
     wr[j] = NW > 1 ? (const uint16_t*)a.W0 + ((size_t)t0 * S * NW + j) * TE + lo
                    : (const uint16_t*)a.W0 + (size_t)(t0 + j) * S * TE + lo;
-  int head[TPW], dim[TPW];
+  int head[TPW], dim[TPW], kind[TPW];   // QKV output column of this lane (qkv_col_map)
 #pragma unroll
   for (int j = 0; j < TPW; ++j) {
     head[j] = dim[j] = 0;
-    if (EPI == EPI_QKV) qkv_col(a, t0 + j, c, &head[j], &dim[j]);
+    kind[j] = 1;
+    if (EPI == EPI_QKV) {
+      const QkvCol q = qkv_col_map(TW, t0 + j, c, a.hq, a.hkv, a.hd);
+      head[j] = q.head;
+      dim[j] = q.dim;
+      kind[j] = q.kind;
+    }
   }
 
   const int s0 = (S * wave) / KW, s1 = (S * (wave + 1)) / KW;
@@ -232,11 +228,11 @@ __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
     // (they need the position), then the rest of the K range
     const int sm = min(s0 + U, s1);
     mfma_stream<NS, true, U, CS, TE>(xr[0], av_ok[0], wr, s0, sm, acc[0]);
-    if (wave == 0 && c < 8) {
+    if (wave == 0) {
       const int half = a.hd >> 1;
 #pragma unroll
       for (int j = 0; j < TPW; ++j) {
-        if (head[j] >= a.hq + a.hkv) continue;
+        if (kind[j] != 0) continue;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int m = blockIdx.y * 16 + 4 * kg + i;
@@ -306,19 +302,19 @@ __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
     for (int j = 0; j < TPW; ++j) {
       const int tt = t0 + j;   // column tile
       if (EPI == EPI_QKV) {
-        const bool rot = head[j] < a.hq + a.hkv;
+        // a pair's second element sits TW/2 lanes up (same 16-lane group)
         float part[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) part[i] = __shfl_xor(acc[r][j][i], 8);
+        for (int i = 0; i < 4; ++i) part[i] = __shfl(acc[r][j][i], (lane + TW / 2) & 63);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int m = mt * 16 + 4 * kg + i;
           if (m >= a.M) continue;
-          if (rot) {
-            if (c < 8 && MT == 1)
+          if (kind[j] == 0) {
+            if (MT == 1)
               epi_qkv_rot<uint16_t>(a, base, m, head[j], dim[j], acc[r][j][i], part[i], rc[j][i], rsn[j][i]);
-            else if (c < 8) epi_qkv_pair<uint16_t>(a, base, m, head[j], dim[j], acc[r][j][i], part[i]);
-          } else {
+            else epi_qkv_pair<uint16_t>(a, base, m, head[j], dim[j], acc[r][j][i], part[i]);
+          } else if (kind[j] == 2) {
             epi_v_single<uint16_t>(a, base, m, head[j] - a.hq - a.hkv, dim[j], acc[r][j][i]);
           }
         }
@@ -376,18 +372,17 @@ __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
 __global__ __launch_bounds__(128) void pack_kernel(PackArgs p) {
   const int t = blockIdx.x, s = blockIdx.y, which = blockIdx.z;
   const int l = threadIdx.x & 63, h = threadIdx.x >> 6, g = l >> 4, c = l & 15;
-  const int tw = p.tw ? p.tw : 16;   // rows per tile (16 for mode 1)
+  const int tw = p.tw ? p.tw : 16;   // rows per tile
   const uint16_t* src;
   size_t row;
+  if (c >= tw) return;
   if (p.mode == 1) {
-    const int col0 = t * 16;
-    const int head = col0 / p.hd, jj = (col0 % p.hd) / 16, half = p.hd >> 1;
-    const int dim = head < p.hq + p.hkv ? (c < 8 ? 8 * jj + c : half + 8 * jj + (c - 8)) : 16 * jj + c;
+    const QkvCol q = qkv_col_map(tw, t, c, p.hq, p.hkv, p.hd);
+    const int head = q.head, dim = q.dim;
     if (head < p.hq) { src = (const uint16_t*)p.src0; row = (size_t)head * p.hd + dim; }
     else if (head < p.hq + p.hkv) { src = (const uint16_t*)p.src1; row = (size_t)(head - p.hq) * p.hd + dim; }
     else { src = (const uint16_t*)p.src2; row = (size_t)(head - p.hq - p.hkv) * p.hd + dim; }
   } else {
-    if (c >= tw) return;
     src = (const uint16_t*)(which ? p.src1 : p.src0);
     row = (size_t)t * tw + c;
   }
@@ -398,7 +393,8 @@ __global__ __launch_bounds__(128) void pack_kernel(PackArgs p) {
 
 hipError_t launch_pack(const PackArgs& p, hipStream_t s) {
   const int tw = p.tw ? p.tw : 16;
-  if (tw < 1 || tw > 16 || (p.mode == 1 && tw != 16)) return hipErrorInvalidValue;
+  if (tw < 1 || tw > 16 || (p.mode == 1 && tw != 16 && tw != 12)) return hipErrorInvalidValue;
+  if (p.mode == 1 && (tw == 16 ? p.hd % 16 : p.hd % 2)) return hipErrorInvalidValue;
   if (p.N % tw || p.N % 16 || p.K % 64 || p.N <= 0 || p.K <= 0) return hipErrorInvalidValue;
   pack_kernel<<<dim3(p.N / tw, p.K / 64, p.pair ? 2 : 1), 128, 0, s>>>(p);
   return hipGetLastError();
@@ -472,8 +468,9 @@ hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t s) {
   const int mt = (a.M + 15) / 16;
   if (dtype) {
     int tiles;
-    const int tw = epi == EPI_SWIGLU ? swiglu_tile_width(a.N) : 16;   // as packed
-    if (epi == EPI_QKV) tiles = (a.hq + 2 * a.hkv) * a.hd / 16;
+    const int tw = epi == EPI_SWIGLU ? swiglu_tile_width(a.N)   // as packed
+                   : epi == EPI_QKV ? qkv_tile_width(a.hq, a.hkv, a.hd) : 16;
+    if (epi == EPI_QKV) tiles = (a.hq + 2 * a.hkv) * a.hd / tw;
     else tiles = a.N / tw;
     dim3 grid(tiles, mt);
     const bool wide = tiles >= 1024;   // a function of N only
@@ -489,25 +486,28 @@ hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t s) {
     int tpw = 1;
     if (a.M > 4 && tiles % 4 == 0 && tiles / 4 >= 1024) tpw = 4;
     else if (a.M > 4 && tiles % 2 == 0 && tiles / 2 >= 1024) tpw = 2;
-#define SSD_G1(E, KWN, UN)                                                                        \
-  if (multi) gemm_bf16_kernel<E, 1, 4, 4, 1, 1><<<grid_mt, 256, 0, s>>>(a);                       \
-  else if (tpw == 4) {                                                                            \
-    const dim3 g4(tiles / 4, mt);                                                                 \
-    if (wide) gemm_bf16_kernel<E, 1, SSD_KW_WIDE, 1, 2, 4><<<g4, 64 * SSD_KW_WIDE, 0, s>>>(a);    \
-    else gemm_bf16_kernel<E, 1, KWN, 1, 2, 4><<<g4, 64 * KWN, 0, s>>>(a);                         \
-  } else if (tpw == 2) {                                                                          \
-    const dim3 g2(tiles / 2, mt);                                                                 \
-    if (wide) gemm_bf16_kernel<E, 1, SSD_KW_WIDE, 1, 2, 2><<<g2, 64 * SSD_KW_WIDE, 0, s>>>(a);    \
-    else gemm_bf16_kernel<E, 1, KWN, 1, 2, 2><<<g2, 64 * KWN, 0, s>>>(a);                         \
-  } else if (wide) gemm_bf16_kernel<E, 1, SSD_KW_WIDE, 1, SSD_GEMM_UW, 1><<<grid, 64 * SSD_KW_WIDE, 0, s>>>(a); \
-  else if (a.K >= 8192) gemm_bf16_kernel<E, 1, KWN, 1, SSD_GEMM_U1_LONGK, 1><<<grid, 64 * KWN, 0, s>>>(a); \
-  else gemm_bf16_kernel<E, 1, KWN, 1, UN, 1><<<grid, 64 * KWN, 0, s>>>(a);
+#define SSD_G1(E, KWN, UN, TWV)                                                                         \
+  if (multi) gemm_bf16_kernel<E, 1, 4, 4, 1, 1, TWV><<<grid_mt, 256, 0, s>>>(a);                         \
+  else if (tpw == 4) {                                                                                   \
+    const dim3 g4(tiles / 4, mt);                                                                        \
+    if (wide) gemm_bf16_kernel<E, 1, SSD_KW_WIDE, 1, 2, 4, TWV><<<g4, 64 * SSD_KW_WIDE, 0, s>>>(a);      \
+    else gemm_bf16_kernel<E, 1, KWN, 1, 2, 4, TWV><<<g4, 64 * KWN, 0, s>>>(a);                           \
+  } else if (tpw == 2) {                                                                                 \
+    const dim3 g2(tiles / 2, mt);                                                                        \
+    if (wide) gemm_bf16_kernel<E, 1, SSD_KW_WIDE, 1, 2, 2, TWV><<<g2, 64 * SSD_KW_WIDE, 0, s>>>(a);      \
+    else gemm_bf16_kernel<E, 1, KWN, 1, 2, 2, TWV><<<g2, 64 * KWN, 0, s>>>(a);                           \
+  } else if (wide) gemm_bf16_kernel<E, 1, SSD_KW_WIDE, 1, SSD_GEMM_UW, 1, TWV><<<grid, 64 * SSD_KW_WIDE, 0, s>>>(a); \
+  else if (a.K >= 8192) gemm_bf16_kernel<E, 1, KWN, 1, SSD_GEMM_U1_LONGK, 1, TWV><<<grid, 64 * KWN, 0, s>>>(a); \
+  else gemm_bf16_kernel<E, 1, KWN, 1, UN, 1, TWV><<<grid, 64 * KWN, 0, s>>>(a);
     switch (epi) {
-      case EPI_F32: SSD_G1(EPI_F32, SSD_KW_NARROW, SSD_GEMM_U1) break;
-      case EPI_LOGITS: SSD_G1(EPI_LOGITS, SSD_KW_NARROW, SSD_GEMM_U1) break;
-      case EPI_RESID: SSD_G1(EPI_RESID, SSD_KW_NARROW, SSD_GEMM_U1) break;
-      case EPI_QKV: SSD_G1(EPI_QKV, SSD_KW_NARROW, SSD_GEMM_U1) break;
-      case EPI_STORE: SSD_G1(EPI_STORE, SSD_KW_NARROW, SSD_GEMM_U1) break;
+      case EPI_F32: SSD_G1(EPI_F32, SSD_KW_NARROW, SSD_GEMM_U1, 16) break;
+      case EPI_LOGITS: SSD_G1(EPI_LOGITS, SSD_KW_NARROW, SSD_GEMM_U1, 16) break;
+      case EPI_RESID: SSD_G1(EPI_RESID, SSD_KW_NARROW, SSD_GEMM_U1, 16) break;
+      case EPI_QKV:
+        if (tw == 12) { SSD_G1(EPI_QKV, SSD_KW_NARROW, SSD_GEMM_U1, 12) }
+        else { SSD_G1(EPI_QKV, SSD_KW_NARROW, SSD_GEMM_U1, 16) }
+        break;
+      case EPI_STORE: SSD_G1(EPI_STORE, SSD_KW_NARROW, SSD_GEMM_U1, 16) break;
       case EPI_SWIGLU:
         if (tw == 14) {
           if (multi) gemm_bf16_kernel<EPI_SWIGLU, 2, 4, 4, 1, 1, 14><<<grid_mt, 256, 0, s>>>(a);

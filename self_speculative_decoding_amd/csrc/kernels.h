@@ -154,7 +154,7 @@ struct PackArgs {
   const void* src0; const void* src1; const void* src2;
   void* dst;
   int N, K, mode, pair, hq, hkv, hd;
-  int tw;   // rows per tile for mode 0 (0: 16); N % tw == 0
+  int tw;   // rows per tile (0: 16); mode 0: N % tw == 0; mode 1: 16 or 12 (qkv_col_map)
 };
 
 // Compute units of one MI355X: the bf16 GEMMs give every workgroup the same
@@ -169,6 +169,62 @@ inline int swiglu_tile_width(int N) {
   const long w16 = (long)((N / 16 + NUM_CU - 1) / NUM_CU) * 16;
   const long w14 = (long)((N / 14 + NUM_CU - 1) / NUM_CU) * 14;
   return w14 < w16 ? 14 : 16;
+}
+// Rows per packed tile of the QKV weight ((hq + 2 hkv) x hd output columns):
+// 16, or 12 by the same rule.
+inline int qkv_tile_width(int hq, int hkv, int hd) {
+  const int N = (hq + 2 * hkv) * hd;
+  if (N % 12 != 0) return 16;
+  const long w16 = (long)((N / 16 + NUM_CU - 1) / NUM_CU) * 16;
+  const long w12 = (long)((N / 12 + NUM_CU - 1) / NUM_CU) * 12;
+  return w12 < w16 ? 12 : 16;
+}
+
+// Output column of lane c (c < 16) in column tile t of the packed QKV weight
+// ([q heads | k heads | v heads], hd dims each) with tw = 16 or 12 columns
+// per tile.  kind 0: the first element (dim i < hd/2) of a RoPE pair
+// (i, i + hd/2) of a q or k head, whose second element sits on lane c + tw/2;
+// kind 1: the second element of a pair, or a lane past the tile (c >= tw);
+// kind 2: a V column.  tw = 16 (hd a multiple of 16): dims 8jj..8jj+7 and
+// hd/2 + 8jj..+7 of one head.  tw = 12: six whole pairs, pairs numbered
+// head-major over the q and k heads, then the V columns in order.
+struct QkvCol {
+  int head, dim, kind;
+};
+__host__ __device__ inline QkvCol qkv_col_map(int tw, int t, int c, int hq, int hkv, int hd) {
+  const int half = hd >> 1;
+  QkvCol r{0, 0, 1};
+  if (c >= tw) return r;
+  if (tw == 16) {
+    const int col0 = t * 16, head = col0 / hd, jj = (col0 % hd) / 16;
+    r.head = head;
+    if (head < hq + hkv) {
+      r.dim = c < 8 ? 8 * jj + c : half + 8 * jj + (c - 8);
+      r.kind = c < 8 ? 0 : 1;
+    } else {
+      r.dim = 16 * jj + c;
+      r.kind = 2;
+    }
+    return r;
+  }
+  const int pw = tw / 2;                     // pairs per tile
+  const int np = (hq + hkv) * half;          // RoPE pairs in all
+  const int h = c / pw, q = c % pw;
+  int rot = np - pw * t;                     // pairs in this tile
+  rot = rot < 0 ? 0 : (rot > pw ? pw : rot);
+  if (q < rot) {
+    const int p = pw * t + q;
+    r.head = p / half;
+    r.dim = p % half + h * half;
+    r.kind = h == 0 ? 0 : 1;
+  } else {
+    const int before = tw * t - 2 * (pw * t < np ? pw * t : np);   // V columns in earlier tiles
+    const int v = before + h * (pw - rot) + (q - rot);
+    r.head = hq + hkv + v / hd;
+    r.dim = v % hd;
+    r.kind = 2;
+  }
+  return r;
 }
 hipError_t launch_pack(const PackArgs& p, hipStream_t s);
 

@@ -476,7 +476,7 @@ hipError_t pack_weights(ssd_ctx* c) {
   };
   auto el = [](const void* p, size_t i) { return (const void*)((const uint16_t*)p + i); };
   for (LayerW& w : c->L) {
-    w.wq = pack(w.wq, w.wk, w.wv, (hq + 2 * hkv) * hd, d, 1, 0);
+    w.wq = pack(w.wq, w.wk, w.wv, (hq + 2 * hkv) * hd, d, 1, 0, qkv_tile_width(hq, hkv, hd));
     w.wk = w.wv = nullptr;
     w.wo = pack(w.wo, nullptr, nullptr, d, hq * hd, 0, 0);
     if (w.moe) {
