@@ -339,46 +339,55 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(AttnArgs a) {
 }
 
 // Combine of the attention partitions: one workgroup per (row, head), one
-// lane per head dim.  Row r at position pos uses partitions 0..pos/PT, added
-// in partition order with weights exp2(m_p - max m).  The partial outputs are
-// loaded (up to 48 at a time) together with the (m, l) pairs.
+// lane per head dim.  Row r at position pos uses partitions 0..pos/PT with
+// weights w_p = exp2(m_p - max m): thread p holds partition p's (m, l), the
+// max and sum(w_p l_p) are fixed butterflies over the two waves, and the
+// outputs add w_p o_p in partition order.  The partial outputs are loaded (up
+// to 48 at a time) together with the (m, l) pairs, before the position.
 template <typename E>
 __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
   constexpr int B = 48;   // partials per load batch (3072 keys)
-  __shared__ float sm[128], sl[128];
-  const int row = blockIdx.x, head = blockIdx.y, t = threadIdx.x;
+  __shared__ float sw[128];
+  __shared__ float red[4];
+  const int row = blockIdx.x, head = blockIdx.y, t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int st0 = a.state[0];   // position load issued first, used late
-  const int npmax = a.n_part;   // partitions the attention launch covered
+  const int npmax = a.n_part;   // partitions the attention launch covered (<= 128)
   const size_t stride = (size_t)a.R * a.hq * a.hd;
   const float* po = a.part_o + ((size_t)row * a.hq + head) * a.hd + (t < a.hd ? t : 0);
-  // first loads issued unconditionally (indexes clamped to the launched
-  // partitions) before the position is known
+  // loads issued unconditionally (indexes clamped to the launched partitions)
   float v[B];
 #pragma unroll
   for (int j = 0; j < B; ++j) v[j] = po[(size_t)min(j, npmax - 1) * stride];
   const float* pm = a.part_ml + (((size_t)min(t, npmax - 1) * a.R + row) * a.hq + head) * 2;
-  if (t < npmax) {   // entries past the row's partitions are never read
-    sm[t] = pm[0];
-    sl[t] = pm[1];
-  }
+  const float m_t = pm[0], l_t = pm[1];
   const int pos = st0 + a.pos_off + row;
   const int np = pos / ATT_PT + 1;
+  const bool in = t < np;   // entries past the row's partitions are never used
+  float mx = in ? m_t : -INFINITY;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  if (lane == 0) red[wave] = mx;
   __syncthreads();
-  float M = -INFINITY;
-  for (int pp = 0; pp < np; ++pp) M = fmaxf(M, sm[pp]);
-  float L = 0.f;
-  for (int pp = 0; pp < np; ++pp) L += exp2f(sm[pp] - M) * sl[pp];
+  const float M = fmaxf(red[0], red[1]);
+  const float w = in ? exp2f(m_t - M) : 0.f;
+  sw[t] = w;
+  float lw = in ? w * l_t : 0.f;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) lw += __shfl_xor(lw, o);
+  if (lane == 0) red[2 + wave] = lw;
+  __syncthreads();
+  const float L = red[2] + red[3];
   if (t >= a.hd) return;
   float acc = 0.f;
 #pragma unroll
   for (int j = 0; j < B; ++j)
-    if (j < np) acc += exp2f(sm[j] - M) * v[j];
+    if (j < np) acc += sw[j] * v[j];
   for (int p0 = B; p0 < np; p0 += B) {
 #pragma unroll
     for (int j = 0; j < B; ++j) v[j] = p0 + j < np ? po[(size_t)(p0 + j) * stride] : 0.f;
 #pragma unroll
     for (int j = 0; j < B; ++j)
-      if (p0 + j < np) acc += exp2f(sm[p0 + j] - M) * v[j];
+      if (p0 + j < np) acc += sw[p0 + j] * v[j];
   }
   ((E*)a.out)[(size_t)row * a.hq * a.hd + (size_t)head * a.hd + t] = fromf<E>(acc / L);
 }
