@@ -183,22 +183,29 @@ __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
 
   const int s0 = (S * wave) / KW, s1 = (S * (wave + 1)) / KW;
 
+  // Epilogue split: in one-tile-row launches wave e < 4 finishes accumulator
+  // element e (rows 4kg + e) of every lane, so up to four rows' epilogues run
+  // side by side; other launches finish on wave 0.  ep(i): element i is this
+  // wave's.
+  constexpr bool SPLIT = MT == 1 && KW >= 4;
+  auto ep = [&](int i) { return SPLIT ? i == wave : wave == 0; };
+
   // Epilogue inputs fetched before the weight stream so that their latency
   // hides behind it: the position base (QKV) and, for one-tile-row launches,
-  // the residual entries wave 0 will update.
+  // the residual entries this wave will update.
   const int base = EPI == EPI_QKV ? a.state[0] + a.pos_off : 0;
   float yv[TPW][4];
 #pragma unroll
   for (int j = 0; j < TPW; ++j)
 #pragma unroll
     for (int i = 0; i < 4; ++i) yv[j][i] = 0.f;
-  if (EPI == EPI_RESID && MT == 1 && wave == 0) {
+  if (EPI == EPI_RESID && MT == 1) {
 #pragma unroll
     for (int j = 0; j < TPW; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int m = blockIdx.y * 16 + 4 * kg + i;
-        if (m < a.M) yv[j][i] = a.y[(size_t)m * a.ldy + (t0 + j) * 16 + c];
+        if (ep(i) && m < a.M) yv[j][i] = a.y[(size_t)m * a.ldy + (t0 + j) * 16 + c];
       }
   }
 
@@ -224,11 +231,11 @@ __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) rc[j][i] = rsn[j][i] = 0.f;
   if (MT == 1 && EPI == EPI_QKV) {
-    // first load batch, then the rotary table entries of wave 0's epilogue
-    // (they need the position), then the rest of the K range
+    // first load batch, then the rotary table entries of this wave's
+    // epilogue rows (they need the position), then the rest of the K range
     const int sm = min(s0 + U, s1);
     mfma_stream<NS, true, U, CS, TE>(xr[0], av_ok[0], wr, s0, sm, acc[0]);
-    if (wave == 0) {
+    {
       const int half = a.hd >> 1;
 #pragma unroll
       for (int j = 0; j < TPW; ++j) {
@@ -236,7 +243,7 @@ __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int m = blockIdx.y * 16 + 4 * kg + i;
-          if (m < a.M) {
+          if (ep(i) && m < a.M) {
             rc[j][i] = a.cos_t[(size_t)(base + m) * half + dim[j]];
             rsn[j][i] = a.sin_t[(size_t)(base + m) * half + dim[j]];
           }
@@ -249,7 +256,7 @@ __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
   }
   else mfma_stream_mt<NS, MT, CS, TE>(xr, av_ok, wr, s0, s1, acc);
 
-  __shared__ f32x4 red[KW - 1][MT][NS][64];
+  __shared__ f32x4 red[SPLIT ? KW : KW - 1][MT][NS][64];
   __shared__ float rs[16 * MT];
   if (fold) {
 #pragma unroll
@@ -261,20 +268,41 @@ __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
       if (lane == 0 && row < 16 * MT) rs[row] = f;
     }
   }
-  if (wave > 0) {
+  if (SPLIT) {
+    // every wave's partial sums to LDS; wave e < 4 adds element e of them in
+    // wave order (the order of the unsplit reduction, so the same sums)
 #pragma unroll
     for (int r = 0; r < MT; ++r)
 #pragma unroll
-      for (int j = 0; j < NS; ++j) red[wave - 1][r][j][lane] = acc[r][j];
+      for (int j = 0; j < NS; ++j) red[wave][r][j][lane] = acc[r][j];
+    __syncthreads();
+    if (wave >= 4) return;
+#pragma unroll
+    for (int r = 0; r < MT; ++r)
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        float v = ((const float*)&red[0][r][j][lane])[wave];
+#pragma unroll
+        for (int w = 1; w < KW; ++w) v += ((const float*)&red[w][r][j][lane])[wave];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[r][j][i] = i == wave ? v : acc[r][j][i];
+      }
+  } else {
+    if (wave > 0) {
+#pragma unroll
+      for (int r = 0; r < MT; ++r)
+#pragma unroll
+        for (int j = 0; j < NS; ++j) red[wave - 1][r][j][lane] = acc[r][j];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int w = 0; w < KW - 1; ++w)
+#pragma unroll
+      for (int r = 0; r < MT; ++r)
+#pragma unroll
+        for (int j = 0; j < NS; ++j) acc[r][j] = acc[r][j] + red[w][r][j][lane];
   }
-  __syncthreads();
-  if (wave != 0) return;
-#pragma unroll
-  for (int w = 0; w < KW - 1; ++w)
-#pragma unroll
-    for (int r = 0; r < MT; ++r)
-#pragma unroll
-      for (int j = 0; j < NS; ++j) acc[r][j] = acc[r][j] + red[w][r][j][lane];
   if (fold) {
     // rows of this lane's accumulators: 4*kg + i of each 16-row tile
 #pragma unroll
@@ -293,6 +321,7 @@ __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
     if (EPI == EPI_SWIGLU) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
+        if (!ep(i)) continue;
         const int m = mt * 16 + 4 * kg + i;
         if (m < a.M && c < TW) epi_swiglu<uint16_t>(a, m, t0 * TW + c, acc[r][0][i], acc[r][NS - 1][i]);
       }
@@ -309,7 +338,7 @@ __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int m = mt * 16 + 4 * kg + i;
-          if (m >= a.M) continue;
+          if (!ep(i) || m >= a.M) continue;
           if (kind[j] == 0) {
             if (MT == 1)
               epi_qkv_rot<uint16_t>(a, base, m, head[j], dim[j], acc[r][j][i], part[i], rc[j][i], rsn[j][i]);
@@ -322,6 +351,7 @@ __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
+        if (!ep(i)) continue;
         const int m = mt * 16 + 4 * kg + i;
         const int n = tt * 16 + c;
         if (EPI == EPI_LOGITS) {
