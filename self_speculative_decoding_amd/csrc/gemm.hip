@@ -23,6 +23,9 @@
 #ifndef SSD_GEMM_UW         // GEMMs with >= 1024 column tiles (the LM head)
 #define SSD_GEMM_UW 2
 #endif
+#ifndef SSD_TPW_MIN_M        // tile groups only for passes wider than this
+#define SSD_TPW_MIN_M 4
+#endif
 #ifndef SSD_KW_SWIGLU
 #define SSD_KW_SWIGLU 8
 #endif
@@ -514,8 +517,8 @@ hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t s) {
     // but only where at least 1024 workgroups remain: spreading the weight
     // stream over every CU matters more than the A reads (measured)
     int tpw = 1;
-    if (a.M > 4 && tiles % 4 == 0 && tiles / 4 >= 1024) tpw = 4;
-    else if (a.M > 4 && tiles % 2 == 0 && tiles / 2 >= 1024) tpw = 2;
+    if (a.M > SSD_TPW_MIN_M && tiles % 4 == 0 && tiles / 4 >= 1024) tpw = 4;
+    else if (a.M > SSD_TPW_MIN_M && tiles % 2 == 0 && tiles / 2 >= 1024) tpw = 2;
 #define SSD_G1(E, KWN, UN, TWV)                                                                         \
   if (multi) gemm_bf16_kernel<E, 1, 4, 4, 1, 1, TWV><<<grid_mt, 256, 0, s>>>(a);                         \
   else if (tpw == 4) {                                                                                   \

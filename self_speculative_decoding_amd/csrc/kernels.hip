@@ -203,36 +203,48 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 
 // bf16 attention partition on MFMA 16x16x32, one wave per workgroup.
 //
-// grid (partition p, kv head, tile of 16 query vectors qi = r*G + g: row r,
-// query head g of the kv group).  Keys sit in the MFMA row dimension:
-// S^T = K . Q^T takes K rows (key 16kt + c) and Q as operands straight from
-// the caches, and lane (c, kg) then holds the scores of query c for keys
-// 16kt + 4kg + i.  Those registers are already the B operand of
+// grid (partition p, kv head, group of NT tiles of 16 query vectors
+// qi = r*G + g: row r, query head g of the kv group).  Keys sit in the MFMA
+// row dimension: S^T = K . Q^T takes K rows (key 16kt + c) and Q as operands
+// straight from the caches, and lane (c, kg) then holds the scores of query c
+// for keys 16kt + 4kg + i.  Those registers are already the B operand of
 // O^T = V^T . P^T when K-step ks takes keys 32ks + 4kg + {0..3} and
 // 32ks + 16 + 4kg + {0..3} in lane group kg; the V cache is stored transposed
 // ([dim][position]) so that A gets the same keys as two 8-byte pieces.  O^T
 // lands as lane (c, kg) holding dims 16dt + 4kg + i of query c.  No LDS, no
 // barrier.  The row max and sum of a query are an in-lane pass in fixed order
 // and a butterfly over its 4 lane groups.  P is split into bf16 hi + lo
-// parts.  Every output element is produced by the same instruction sequence
-// for any number of rows in the pass.
-template <int G>
+// parts.  The wave loads the partition's K and V once for its NT query tiles
+// (NT = 2 for passes of two or more tiles); every tile runs the same
+// instruction sequence, so an output element does not depend on the number
+// of rows in the pass or on the tile it shares a wave with.
+template <int G, int NT>
 __global__ __launch_bounds__(64) void attn_mfma_kernel(AttnArgs a) {
   constexpr int HD = 128, PT = ATT_PT;
   const int p = blockIdx.x, kvh = blockIdx.y;
   const int lane = threadIdx.x, c = lane & 15, kg = lane >> 4;
   const int st0 = a.state[0];   // position load issued first, used late
   const int key0 = p * PT;
-  const int qi = blockIdx.z * 16 + c;
-  const bool qv = qi < a.M * G;
-  const int qr = qv ? qi / G : 0, qg = qv ? qi % G : 0;
   const size_t ldc = a.max_ctx;   // positions per cache row (multiple of PT)
+  int qr[NT], qg[NT];
+  bool qv[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int qi = (blockIdx.z * NT + t) * 16 + c;
+    qv[t] = qi < a.M * G;
+    qr[t] = qv[t] ? qi / G : 0;
+    qg[t] = qv[t] ? qi % G : 0;
+  }
 
   // every load up front: Q (B of S^T), K (A of S^T), V^T (A of O^T)
-  const uint16_t* qp = (const uint16_t*)a.q + (size_t)qr * a.hq * HD + (size_t)(kvh * G + qg) * HD + 8 * kg;
-  uint4 qa[4];
+  uint4 qa[NT][4];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) qa[ks] = *(const uint4*)(qp + 32 * ks);
+  for (int t = 0; t < NT; ++t) {
+    const uint16_t* qp =
+        (const uint16_t*)a.q + (size_t)qr[t] * a.hq * HD + (size_t)(kvh * G + qg[t]) * HD + 8 * kg;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qa[t][ks] = *(const uint4*)(qp + 32 * ks);
+  }
   const uint16_t* kb = (const uint16_t*)a.kc + ((size_t)kvh * ldc + key0 + c) * HD + 8 * kg;
   uint4 kf[4][4];
 #pragma unroll
@@ -247,49 +259,6 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(AttnArgs a) {
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int h = 0; h < 2; ++h) vf[dt][ks][h] = *(const uint2*)(vb + (size_t)16 * dt * ldc + 32 * ks + 16 * h);
-
-  const int pos = st0 + a.pos_off + qr;   // this lane's query position
-  f32x4 s[4];
-#pragma unroll
-  for (int kt = 0; kt < 4; ++kt) {
-    s[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[kt][ks]),
-                                                      __builtin_bit_cast(bf16x8, qa[ks]), s[kt], 0, 0, 0);
-  }
-  // softmax over this partition's keys for query c
-  float m = -INFINITY;
-#pragma unroll
-  for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool valid = qv && key0 + 16 * kt + 4 * kg + i <= pos;
-      m = valid ? fmaxf(m, s[kt][i] * a.scale_log2) : m;
-    }
-  m = fmaxf(m, __shfl_xor(m, 16));
-  m = fmaxf(m, __shfl_xor(m, 32));
-  float l = 0.f;
-  uint32_t ph[2][4], pl[2][4];   // P^T hi / lo fragments, bf16 pairs
-#pragma unroll
-  for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-    for (int i = 0; i < 4; i += 2) {
-      float pv[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const bool valid = qv && key0 + 16 * kt + 4 * kg + i + u <= pos;
-        pv[u] = valid ? exp2f(s[kt][i + u] * a.scale_log2 - m) : 0.f;
-        l += pv[u];
-      }
-      const uint16_t h0 = f2bf(pv[0]), h1 = f2bf(pv[1]);
-      const uint16_t l0 = f2bf(pv[0] - bf2f(h0)), l1 = f2bf(pv[1] - bf2f(h1));
-      // K-step kt/2; elements 0..3 from even kt, 4..7 from odd kt
-      ph[kt >> 1][(kt & 1) * 2 + i / 2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-      pl[kt >> 1][(kt & 1) * 2 + i / 2] = (uint32_t)l0 | ((uint32_t)l1 << 16);
-    }
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
 
   // keys past the last row's position: P is 0 there; keep 0 * V finite
   const int maxpos = st0 + a.pos_off + a.M - 1;
@@ -311,30 +280,76 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(AttnArgs a) {
       }
     }
 
-  f32x4 o[8];
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) {
-    o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < NT; ++t) {
+    const int pos = st0 + a.pos_off + qr[t];   // this lane's query position
+    f32x4 sc[4];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const uint4 va = {vf[dt][ks][0].x, vf[dt][ks][0].y, vf[dt][ks][1].x, vf[dt][ks][1].y};
-      const uint4 bh = {ph[ks][0], ph[ks][1], ph[ks][2], ph[ks][3]};
-      const uint4 bl = {pl[ks][0], pl[ks][1], pl[ks][2], pl[ks][3]};
-      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va), __builtin_bit_cast(bf16x8, bh),
-                                                      o[dt], 0, 0, 0);
-      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va), __builtin_bit_cast(bf16x8, bl),
-                                                      o[dt], 0, 0, 0);
+    for (int kt = 0; kt < 4; ++kt) {
+      sc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        sc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[kt][ks]),
+                                                         __builtin_bit_cast(bf16x8, qa[t][ks]), sc[kt], 0, 0, 0);
     }
-  }
-  if (!qv || key0 > pos) return;
-  const int row = qr, head = kvh * G + qg;
-  const size_t ph_i = ((size_t)p * a.R + row) * a.hq + head;
-  float* po = a.part_o + ph_i * HD + 4 * kg;
+    // softmax over this partition's keys for query c
+    float m = -INFINITY;
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) *(f32x4*)(po + 16 * dt) = o[dt];
-  if (kg == 0) {
-    a.part_ml[ph_i * 2] = m;
-    a.part_ml[ph_i * 2 + 1] = l;
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool valid = qv[t] && key0 + 16 * kt + 4 * kg + i <= pos;
+        m = valid ? fmaxf(m, sc[kt][i] * a.scale_log2) : m;
+      }
+    m = fmaxf(m, __shfl_xor(m, 16));
+    m = fmaxf(m, __shfl_xor(m, 32));
+    float l = 0.f;
+    uint32_t ph[2][4], pl[2][4];   // P^T hi / lo fragments, bf16 pairs
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; i += 2) {
+        float pv[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const bool valid = qv[t] && key0 + 16 * kt + 4 * kg + i + u <= pos;
+          pv[u] = valid ? exp2f(sc[kt][i + u] * a.scale_log2 - m) : 0.f;
+          l += pv[u];
+        }
+        const uint16_t h0 = f2bf(pv[0]), h1 = f2bf(pv[1]);
+        const uint16_t l0 = f2bf(pv[0] - bf2f(h0)), l1 = f2bf(pv[1] - bf2f(h1));
+        // K-step kt/2; elements 0..3 from even kt, 4..7 from odd kt
+        ph[kt >> 1][(kt & 1) * 2 + i / 2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+        pl[kt >> 1][(kt & 1) * 2 + i / 2] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+      }
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+
+    f32x4 o[8];
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const uint4 va = {vf[dt][ks][0].x, vf[dt][ks][0].y, vf[dt][ks][1].x, vf[dt][ks][1].y};
+        const uint4 bh = {ph[ks][0], ph[ks][1], ph[ks][2], ph[ks][3]};
+        const uint4 bl = {pl[ks][0], pl[ks][1], pl[ks][2], pl[ks][3]};
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va), __builtin_bit_cast(bf16x8, bh),
+                                                        o[dt], 0, 0, 0);
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va), __builtin_bit_cast(bf16x8, bl),
+                                                        o[dt], 0, 0, 0);
+      }
+    }
+    if (!qv[t] || key0 > pos) continue;
+    const int row = qr[t], head = kvh * G + qg[t];
+    const size_t ph_i = ((size_t)p * a.R + row) * a.hq + head;
+    float* po = a.part_o + ph_i * HD + 4 * kg;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) *(f32x4*)(po + 16 * dt) = o[dt];
+    if (kg == 0) {
+      a.part_ml[ph_i * 2] = m;
+      a.part_ml[ph_i * 2 + 1] = l;
+    }
   }
 }
 
@@ -556,10 +571,18 @@ static hipError_t attn_dispatch(AttnArgs a, int n_part, int hd, hipStream_t s) {
   dim3 grid(n_part, a.hkv, (a.M + ROW_TILE - 1) / ROW_TILE);
   bool done = false;
   if (sizeof(E) == 2 && hd == 128) {
-    const dim3 gq(n_part, a.hkv, (a.M * G + 15) / 16);   // one wave per 16 query vectors
-    if (G == 1) { attn_mfma_kernel<1><<<gq, 64, 0, s>>>(a); done = true; }
-    if (G == 2) { attn_mfma_kernel<2><<<gq, 64, 0, s>>>(a); done = true; }
-    if (G == 4) { attn_mfma_kernel<4><<<gq, 64, 0, s>>>(a); done = true; }
+    // one wave per partition and 16 query vectors, or per 2 x 16 when the
+    // pass has two or more such tiles (the partition's K and V loaded once)
+    const int tiles = (a.M * G + 15) / 16;
+    const dim3 g1(n_part, a.hkv, tiles), g2(n_part, a.hkv, (tiles + 1) / 2);
+#define SSD_ATTM(Gv)                                                              \
+    if (G == Gv) {                                                                \
+      if (tiles >= 2) attn_mfma_kernel<Gv, 2><<<g2, 64, 0, s>>>(a);              \
+      else attn_mfma_kernel<Gv, 1><<<g1, 64, 0, s>>>(a);                         \
+      done = true;                                                                \
+    }
+    SSD_ATTM(1) SSD_ATTM(2) SSD_ATTM(4)
+#undef SSD_ATTM
   }
 #define SSD_ATT(HDv, Gv) \
   if (!done && hd == HDv && G == Gv) { attn_kernel<E, HDv, Gv><<<grid, 256, 0, s>>>(a); done = true; }
