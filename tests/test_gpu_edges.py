@@ -160,3 +160,34 @@ def test_narrow_gate_up_tiles():
         assert spec == toks[:32]
     finally:
         eng.close()
+
+
+def test_long_context_combine_batches():
+    """A 3300-token context: 52 key partitions, so the combine loads its
+    partials in two batches and the passes replay from a high context
+    bucket.  Logits against the oracle; verify rows equal decode rows bit
+    for bit; self-speculation lossless."""
+    cfg = _edge_cfg(n_layers=2, max_ctx=3400, prompt_len=3300, cid=75)
+    w = synth.make_weights(cfg, seed=10)
+    print("[edge] context 3300 (52 partitions)", flush=True)
+    eng = engine(cfg, w, max_block=8, prefill_chunk=256)
+    try:
+        prompt = synth.make_prompt(cfg)
+        toks, rows = _stepwise(eng, prompt, 12)
+        ref = Model(cfg, w).teacher_forced(prompt, toks)
+        err = np.max(np.abs(rows - ref))
+        print(f"[edge] context 3300: max |dlogit| = {err:.3e}")
+        assert err <= BOUND
+        assert _gap_ok(toks, ref, BOUND) == []
+        eng.reset()
+        eng.prefill(prompt)
+        post = eng.verify(toks[:8])
+        assert np.array_equal(eng.read_logits(8), rows[1:9])
+        assert post == toks[1:9]
+        eng.accept()
+        mask = np.zeros(cfg["n_layers"], np.uint8)
+        mask[1] = 1
+        spec, _ = eng.generate(prompt, 12, mask, 3)
+        assert spec == toks
+    finally:
+        eng.close()
