@@ -146,7 +146,7 @@ __device__ __forceinline__ float ss_rstd(const GemmArgs& a, int m, bool row_ok, 
 // arithmetic does not depend on TW.
 template <int EPI, int NW, int KW, int MT, int U, int TPW, int TW = 16>
 __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
-  static_assert(TPW == 1 || NW == 1, "tile groups are for one-matrix GEMMs");
+  static_assert(TPW == 1 || NW == 1 || MT > 1, "gate/up tile groups are for multi-row-tile launches");
   static_assert(TW == 16 || (EPI == EPI_SWIGLU && TW == 14) || (EPI == EPI_QKV && TW == 12), "tile width");
   constexpr int NS = NW * TPW;                               // weight streams
   constexpr int TE = TW * 64;                                // elements per packed tile
@@ -165,11 +165,12 @@ __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
   }
   const int S = a.K >> 6;   // 64-element chunks
   // packed weight tiles: gate/up interleaved when NW = 2, else TPW tiles
+  // stream j: matrix j % NW of column tile t0 + j / NW
   const uint16_t* wr[NS];
   const int lo = (TW * kg + min(c, TW - 1)) * 8;             // this lane's 16 bytes in a tile half
 #pragma unroll
   for (int j = 0; j < NS; ++j)
-    wr[j] = NW > 1 ? (const uint16_t*)a.W0 + ((size_t)t0 * S * NW + j) * TE + lo
+    wr[j] = NW > 1 ? (const uint16_t*)a.W0 + ((size_t)(t0 + j / NW) * S * NW + j % NW) * TE + lo
                    : (const uint16_t*)a.W0 + (size_t)(t0 + j) * S * TE + lo;
   int head[TPW], dim[TPW], kind[TPW];   // QKV output column of this lane (qkv_col_map)
 #pragma unroll
@@ -323,11 +324,14 @@ __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
     const int mt = blockIdx.y * MT + r;
     if (EPI == EPI_SWIGLU) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (!ep(i)) continue;
-        const int m = mt * 16 + 4 * kg + i;
-        if (m < a.M && c < TW) epi_swiglu<uint16_t>(a, m, t0 * TW + c, acc[r][0][i], acc[r][NS - 1][i]);
-      }
+      for (int jt = 0; jt < TPW; ++jt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (!ep(i)) continue;
+          const int m = mt * 16 + 4 * kg + i;
+          if (m < a.M && c < TW)
+            epi_swiglu<uint16_t>(a, m, (t0 + jt) * TW + c, acc[r][jt * NW][i], acc[r][jt * NW + NW - 1][i]);
+        }
       continue;
     }
 #pragma unroll
@@ -511,7 +515,13 @@ hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t s) {
     // kernel, so a row's arithmetic never depends on the pass width; longer
     // passes (prefill chunks) let 4 row tiles share each weight load
     const bool multi = a.M > 32;
-    const dim3 grid_mt(tiles, (a.M + 63) / 64);
+    // long passes group column tiles too, so each workgroup reads its 64 A
+    // rows once for 2 or 4 tiles, while keeping two workgroups per CU
+    const int rb = (a.M + 63) / 64;
+    int tpm = 1;
+    if (multi && tiles % 4 == 0 && (tiles / 4) * rb >= 2 * NUM_CU && epi != EPI_SWIGLU) tpm = 4;
+    else if (multi && tiles % 2 == 0 && (tiles / 2) * rb >= 2 * NUM_CU) tpm = 2;
+    const dim3 grid_mt(tiles / tpm, rb);
     // passes wider than 4 rows group 2 or 4 column tiles per workgroup so
     // the A operand is read once for them (results unchanged, see the kernel),
     // but only where at least 1024 workgroups remain: spreading the weight
@@ -520,7 +530,11 @@ hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t s) {
     if (a.M > SSD_TPW_MIN_M && tiles % 4 == 0 && tiles / 4 >= 1024) tpw = 4;
     else if (a.M > SSD_TPW_MIN_M && tiles % 2 == 0 && tiles / 2 >= 1024) tpw = 2;
 #define SSD_G1(E, KWN, UN, TWV)                                                                         \
-  if (multi) gemm_bf16_kernel<E, 1, 4, 4, 1, 1, TWV><<<grid_mt, 256, 0, s>>>(a);                         \
+  if (multi) {                                                                                           \
+    if (tpm == 4) gemm_bf16_kernel<E, 1, 4, 4, 1, 4, TWV><<<grid_mt, 256, 0, s>>>(a);                    \
+    else if (tpm == 2) gemm_bf16_kernel<E, 1, 4, 4, 1, 2, TWV><<<grid_mt, 256, 0, s>>>(a);               \
+    else gemm_bf16_kernel<E, 1, 4, 4, 1, 1, TWV><<<grid_mt, 256, 0, s>>>(a);                             \
+  }                                                                                                      \
   else if (tpw == 4) {                                                                                   \
     const dim3 g4(tiles / 4, mt);                                                                        \
     if (wide) gemm_bf16_kernel<E, 1, SSD_KW_WIDE, 1, 2, 4, TWV><<<g4, 64 * SSD_KW_WIDE, 0, s>>>(a);      \
@@ -543,9 +557,11 @@ hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t s) {
       case EPI_STORE: SSD_G1(EPI_STORE, SSD_KW_NARROW, SSD_GEMM_U1, 16) break;
       case EPI_SWIGLU:
         if (tw == 14) {
-          if (multi) gemm_bf16_kernel<EPI_SWIGLU, 2, 4, 4, 1, 1, 14><<<grid_mt, 256, 0, s>>>(a);
+          if (multi && tpm == 2) gemm_bf16_kernel<EPI_SWIGLU, 2, 4, 4, 1, 2, 14><<<grid_mt, 256, 0, s>>>(a);
+          else if (multi) gemm_bf16_kernel<EPI_SWIGLU, 2, 4, 4, 1, 1, 14><<<grid_mt, 256, 0, s>>>(a);
           else gemm_bf16_kernel<EPI_SWIGLU, 2, SSD_KW_SWIGLU, 1, SSD_GEMM_U2, 1, 14><<<grid, 64 * SSD_KW_SWIGLU, 0, s>>>(a);
-        } else if (multi) gemm_bf16_kernel<EPI_SWIGLU, 2, 4, 4, 1, 1><<<grid_mt, 256, 0, s>>>(a);
+        } else if (multi && tpm == 2) gemm_bf16_kernel<EPI_SWIGLU, 2, 4, 4, 1, 2><<<grid_mt, 256, 0, s>>>(a);
+        else if (multi) gemm_bf16_kernel<EPI_SWIGLU, 2, 4, 4, 1, 1><<<grid_mt, 256, 0, s>>>(a);
         else if (wide) gemm_bf16_kernel<EPI_SWIGLU, 2, SSD_KW_WIDE, 1, SSD_GEMM_U2, 1><<<grid, 64 * SSD_KW_WIDE, 0, s>>>(a);
         else gemm_bf16_kernel<EPI_SWIGLU, 2, SSD_KW_SWIGLU, 1, SSD_GEMM_U2, 1><<<grid, 64 * SSD_KW_SWIGLU, 0, s>>>(a);
         break;
