@@ -150,6 +150,39 @@ def bench_pmc_probe(args) -> int:
     return 0
 
 
+def bench_moe_pmc_probe(args) -> int:
+    """Kernel sequence for `rocprofv3 --pmc` runs on the MoE expert operation:
+    3 plain copies of 128 MiB (counter calibration), then the expert op of
+    every MoE layer of the DeepSeek-V2-Lite-shaped model twice over at n = 8
+    rows with the synthetic routing trace, per-slot (--moe-dedup 0) or
+    deduplicated (1).  Prints the requested expert bytes per layer op."""
+    import numpy as np
+    import synth
+    from self_speculative_decoding_amd import Engine, make_cfg
+    cfg = dict(synth.config("dsv2-lite"), max_ctx=4096)   # room for a 128 MiB copy in the partial buffer
+    L, E, K, n = cfg["n_layers"], cfg["n_experts"], cfg["top_k"], 8
+    nd = cfg["n_dense_layers"]
+    eb = cfg["expert_ffn"] * cfg["d_model"] * 3 * 2
+    assert (cfg["max_ctx"] // 64) * 256 * cfg["n_q_heads"] * cfg["head_dim"] * 4 >= 128 << 20
+    w = synth.make_weights(cfg)
+    eng = Engine(make_cfg(cfg, max_block=9, prefill_chunk=256), [w[n_] for n_, _, _ in synth.weight_specs(cfg)])
+    del w
+    eng.prefill(synth.make_prompt(cfg)[:64])
+    trace = synth.make_routing_trace(L, n, E, K, seed=0, stream=n)
+    eng.set_moe_dedup(args.moe_dedup)
+    eng.set_routing(trace)
+    unions = [len(set(trace[l].reshape(-1).tolist())) for l in range(nd, L)]
+    res = {"copy_probe_us": eng.time_op("copy_probe", 0, 128, 3),
+           "moe_us": eng.time_op("moe", nd, n, 2 * (L - nd))}
+    eng.close()
+    routed = K * n if args.moe_dedup == 0 else float(np.mean(unions))
+    res.update({"mode": "dedup" if args.moe_dedup else "per_slot", "n": n, "copy_bytes": 128 << 20,
+                "expert_bytes": eb, "requested_bytes_per_layer": (routed + cfg["n_shared"]) * eb,
+                "mean_union": float(np.mean(unions)), "layer_ops": 2 * (L - nd)})
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def bench_verify_blocks(args) -> int:
     """Qwen3-8B-shaped target verifying 16-token blocks at context 2048 with the
     five-layer feature tap + fc on; drafts carry a geometric(p) correct prefix.
@@ -527,6 +560,9 @@ def main() -> int:
                     help="speculative sampling vs greedy and plain sampling (8B shape)")
     ap.add_argument("--kselect", action="store_true",
                     help="draft length from fitted step times: predicted vs measured k*(alpha)")
+    ap.add_argument("--moe-pmc-probe", action="store_true",
+                    help="MoE expert op kernel sequence for rocprofv3 --pmc (with --moe-dedup)")
+    ap.add_argument("--moe-dedup", type=int, default=0, choices=(0, 1))
     ap.add_argument("--pmc-probe", action="store_true",
                     help="short fixed kernel sequence for hardware-counter runs (copy probe, read probe, "
                          "gate/up GEMM at m=4 on a 4-layer model of the headline widths)")
@@ -545,6 +581,8 @@ def main() -> int:
 
     if args.pmc_probe:
         return bench_pmc_probe(args)
+    if args.moe_pmc_probe:
+        return bench_moe_pmc_probe(args)
     if args.workload == "qwen3-8b":
         return bench_verify_blocks(args)
     if args.workload == "dsv2-lite":
