@@ -23,6 +23,12 @@
 #ifndef SSD_GEMM_UW         // GEMMs with >= 1024 column tiles (the LM head)
 #define SSD_GEMM_UW 2
 #endif
+#ifndef SSD_MT_KW            // waves (K ranges) of the multi-row-tile kernel
+#define SSD_MT_KW 4
+#endif
+#ifndef SSD_MT_MT            // 16-row tiles per workgroup of the multi-row-tile kernel
+#define SSD_MT_MT 4
+#endif
 #ifndef SSD_TPW_MIN_M        // tile groups only for passes wider than this
 #define SSD_TPW_MIN_M 4
 #endif
@@ -517,7 +523,7 @@ hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t s) {
     const bool multi = a.M > 32;
     // long passes group column tiles too, so each workgroup reads its 64 A
     // rows once for 2 or 4 tiles, while keeping two workgroups per CU
-    const int rb = (a.M + 63) / 64;
+    const int rb = (a.M + 16 * SSD_MT_MT - 1) / (16 * SSD_MT_MT);
     int tpm = 1;
     if (multi && tiles % 4 == 0 && (tiles / 4) * rb >= 2 * NUM_CU && epi != EPI_SWIGLU) tpm = 4;
     else if (multi && tiles % 2 == 0 && (tiles / 2) * rb >= 2 * NUM_CU) tpm = 2;
@@ -531,9 +537,9 @@ hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t s) {
     else if (a.M > SSD_TPW_MIN_M && tiles % 2 == 0 && tiles / 2 >= 1024) tpw = 2;
 #define SSD_G1(E, KWN, UN, TWV)                                                                         \
   if (multi) {                                                                                           \
-    if (tpm == 4) gemm_bf16_kernel<E, 1, 4, 4, 1, 4, TWV><<<grid_mt, 256, 0, s>>>(a);                    \
-    else if (tpm == 2) gemm_bf16_kernel<E, 1, 4, 4, 1, 2, TWV><<<grid_mt, 256, 0, s>>>(a);               \
-    else gemm_bf16_kernel<E, 1, 4, 4, 1, 1, TWV><<<grid_mt, 256, 0, s>>>(a);                             \
+    if (tpm == 4) gemm_bf16_kernel<E, 1, SSD_MT_KW, SSD_MT_MT, 1, 4, TWV><<<grid_mt, 64 * SSD_MT_KW, 0, s>>>(a); \
+    else if (tpm == 2) gemm_bf16_kernel<E, 1, SSD_MT_KW, SSD_MT_MT, 1, 2, TWV><<<grid_mt, 64 * SSD_MT_KW, 0, s>>>(a); \
+    else gemm_bf16_kernel<E, 1, SSD_MT_KW, SSD_MT_MT, 1, 1, TWV><<<grid_mt, 64 * SSD_MT_KW, 0, s>>>(a);   \
   }                                                                                                      \
   else if (tpw == 4) {                                                                                   \
     const dim3 g4(tiles / 4, mt);                                                                        \
@@ -557,11 +563,11 @@ hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t s) {
       case EPI_STORE: SSD_G1(EPI_STORE, SSD_KW_NARROW, SSD_GEMM_U1, 16) break;
       case EPI_SWIGLU:
         if (tw == 14) {
-          if (multi && tpm == 2) gemm_bf16_kernel<EPI_SWIGLU, 2, 4, 4, 1, 2, 14><<<grid_mt, 256, 0, s>>>(a);
-          else if (multi) gemm_bf16_kernel<EPI_SWIGLU, 2, 4, 4, 1, 1, 14><<<grid_mt, 256, 0, s>>>(a);
+          if (multi && tpm == 2) gemm_bf16_kernel<EPI_SWIGLU, 2, SSD_MT_KW, SSD_MT_MT, 1, 2, 14><<<grid_mt, 64 * SSD_MT_KW, 0, s>>>(a);
+          else if (multi) gemm_bf16_kernel<EPI_SWIGLU, 2, SSD_MT_KW, SSD_MT_MT, 1, 1, 14><<<grid_mt, 64 * SSD_MT_KW, 0, s>>>(a);
           else gemm_bf16_kernel<EPI_SWIGLU, 2, SSD_KW_SWIGLU, 1, SSD_GEMM_U2, 1, 14><<<grid, 64 * SSD_KW_SWIGLU, 0, s>>>(a);
-        } else if (multi && tpm == 2) gemm_bf16_kernel<EPI_SWIGLU, 2, 4, 4, 1, 2><<<grid_mt, 256, 0, s>>>(a);
-        else if (multi) gemm_bf16_kernel<EPI_SWIGLU, 2, 4, 4, 1, 1><<<grid_mt, 256, 0, s>>>(a);
+        } else if (multi && tpm == 2) gemm_bf16_kernel<EPI_SWIGLU, 2, SSD_MT_KW, SSD_MT_MT, 1, 2><<<grid_mt, 64 * SSD_MT_KW, 0, s>>>(a);
+        else if (multi) gemm_bf16_kernel<EPI_SWIGLU, 2, SSD_MT_KW, SSD_MT_MT, 1, 1><<<grid_mt, 64 * SSD_MT_KW, 0, s>>>(a);
         else if (wide) gemm_bf16_kernel<EPI_SWIGLU, 2, SSD_KW_WIDE, 1, SSD_GEMM_U2, 1><<<grid, 64 * SSD_KW_WIDE, 0, s>>>(a);
         else gemm_bf16_kernel<EPI_SWIGLU, 2, SSD_KW_SWIGLU, 1, SSD_GEMM_U2, 1><<<grid, 64 * SSD_KW_SWIGLU, 0, s>>>(a);
         break;
