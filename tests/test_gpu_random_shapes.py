@@ -1,0 +1,68 @@
+"""Seeded random small bf16 shapes through the C ABI (needs an MI355X).
+
+Each case draws a model shape (layers, width, head dim 64 or 128, 1/2/4
+query heads per KV head, FFN widths that take 16- or 14-row gate/up tiles,
+QKV widths that take 16- or 12-row tiles), a prompt length, a verify-block
+limit and a prefill chunk.  Bars as in test_gpu_parity: greedy logits within
+|dlogit| <= 3e-2 of the oracle's teacher-forced logits, tokens equal wherever
+the oracle's top-2 gap exceeds twice that; a verify block's rows equal to the
+decode rows bit for bit; self-speculation equal to greedy for random skip
+masks and draft lengths.
+"""
+import numpy as np
+import pytest
+
+import synth
+from oracle import Model
+from _common import engine
+from test_gpu_parity import _gap_ok, _stepwise
+
+pytestmark = pytest.mark.gpu
+
+BOUND = 3e-2
+
+
+def _shape(seed):
+    r = np.random.default_rng(1000 + seed)
+    hd = int(r.choice([64, 128]))
+    hkv = int(r.choice([1, 2, 4]))
+    hq = hkv * int(r.choice([1, 2, 4]))
+    P = int(r.integers(1, 300))
+    cfg = synth.config("llama-8b", n_layers=int(r.choice([2, 3, 5])), d_model=int(r.choice([256, 512, 768])),
+                       n_q_heads=hq, n_kv_heads=hkv, head_dim=hd,
+                       ffn_dim=int(r.choice([512, 1024, 1792, 3584])), vocab=int(r.choice([1024, 2048, 4096])),
+                       prompt_len=P, max_ctx=P + 80, cid=90 + seed)
+    return cfg, int(r.choice([4, 8, 17])), int(r.choice([16, 64, 256])), r
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_shape(seed):
+    cfg, max_block, chunk, r = _shape(seed)
+    keys = ("n_layers", "d_model", "n_q_heads", "n_kv_heads", "head_dim", "ffn_dim", "vocab", "prompt_len")
+    print(f"[shape {seed}] " + " ".join(f"{k}={cfg[k]}" for k in keys) + f" max_block={max_block} chunk={chunk}",
+          flush=True)
+    w = synth.make_weights(cfg, seed=seed)
+    eng = engine(cfg, w, max_block=max_block, prefill_chunk=chunk)
+    try:
+        prompt = synth.make_prompt(cfg)
+        toks, rows = _stepwise(eng, prompt, 16)
+        ref = Model(cfg, w).teacher_forced(prompt, toks)
+        err = float(np.max(np.abs(rows - ref)))
+        print(f"[shape {seed}] max |dlogit| = {err:.3e}", flush=True)
+        assert err <= BOUND
+        assert _gap_ok(toks, ref, BOUND) == []
+        m = min(max_block, 8)
+        eng.reset()
+        eng.prefill(prompt)
+        post = eng.verify(toks[:m])
+        assert np.array_equal(eng.read_logits(m), rows[1:m + 1])
+        assert post == toks[1:m + 1]
+        eng.accept()
+        L = cfg["n_layers"]
+        for _ in range(2):
+            mask = (r.random(L) < 0.5).astype(np.uint8)
+            k = int(r.integers(1, max_block))
+            spec, _ = eng.generate(prompt, 16, mask, k)
+            assert spec == toks, (mask.tolist(), k)
+    finally:
+        eng.close()
