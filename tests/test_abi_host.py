@@ -125,6 +125,9 @@ def test_select_k_matches_oracle_and_is_monotone_in_alpha():
             assert k == ko and abs(r - ro) <= 1e-12 * ro, (trial, a)
             assert k >= prev, (trial, a)                   # non-decreasing in alpha
             prev = k
+    # exact ties (alpha = 0, k * t_draft + t_verify[k] equal): the smallest k, as in the oracle
+    for tv, want in (([1.0, 0.75, 0.5], 0), ([1.25, 0.75, 0.5], 1)):
+        assert ssd.select_k(tv, 0.25, 0.0, 0.0) == ora_select_k(tv, 0.25, 0.0, 0.0) == (want, 1.0)
 
 
 def test_select_k_rejects():

@@ -493,6 +493,9 @@ def test_kselect_closed_forms():
     # alpha = 1: E_k = k + 1
     k, r = select_k([1.0, 1.0, 1.0], 0.5, 0.0, 1.0)
     assert k == 2 and abs(r - 3 / 2.0) < 1e-12
+    # exact ties (alpha = 0, free drafts, flat verify): the smallest k wins
+    assert select_k([1.0, 1.0, 1.0], 0.0, 0.0, 0.0) == (0, 1.0)
+    assert select_k([2.0, 1.0, 1.0, 1.0], 0.0, 0.0, 0.0) == (1, 1.0)
 
 
 # ---------------------------------------------------------------------------
@@ -509,6 +512,10 @@ def test_layer_cosines_closed_forms():
     np.testing.assert_allclose(got, [1.0, 0.0, -1.0], atol=1e-15)
     # 45 degrees
     np.testing.assert_allclose(layer_cosines(np.array([[1.0, 0.0]]), [np.array([[1.0, 1.0]])]), [2 ** -0.5])
+    # the layer's value averages its rows: cos 1, 1 and 0 over three rows -> 2/3
+    e3 = np.eye(3)
+    out = np.array([[2.0, 0.0, 0.0], [0.0, 3.0, 0.0], [1.0, 0.0, 0.0]])
+    np.testing.assert_allclose(layer_cosines(e3, [out]), [2.0 / 3.0], atol=1e-15)
 
 
 def test_knapsack_brute_hand_example():
@@ -594,3 +601,63 @@ def test_spec_cycle_output_follows_the_target_distribution():
     # a draft equal to the target is always accepted
     a, em, _ = spec_cycle(tl, tl[:k], T, seed=1, cycle=0)
     assert a == k
+
+
+def _np_philox_word0(seed, ctr):
+    """First output word of Philox4x64-10 at counter ctr (ctr[0] >= 1), key
+    (seed, 0), from numpy's own generator (it advances the counter first)."""
+    bg = np.random.Philox(counter=[ctr[0] - 1, ctr[1], ctr[2], ctr[3]], key=[seed, 0])
+    return int(bg.random_raw(1)[0])
+
+
+def test_uniform24_is_the_top_24_bits_of_numpys_philox_word():
+    from oracle import uniform24
+    odd = 0
+    for c in range(1, 300):
+        u = uniform24(17, c, c % 5, c % 3)
+        w = _np_philox_word0(17, [c, c % 5, c % 3, 0])
+        assert u * 2**24 == (w >> 40)
+        odd += (w >> 40) & 1
+    assert odd > 0
+
+
+def test_probs_is_softmax_of_logits_over_temperature():
+    from scipy.special import softmax
+    from oracle import probs
+    rng = np.random.default_rng(4)
+    l = rng.normal(0, 3, 50)
+    for T in (0.25, 0.6, 1.0, 2.5):
+        assert np.allclose(probs(l, T), softmax(l / T), rtol=1e-12, atol=0)
+    assert np.array_equal(probs(np.array([0.0, -np.inf, 0.0]), 1.0), np.array([0.5, 0.0, 0.5]))
+
+
+def test_spec_cycle_decisions_on_constructed_cycles():
+    """Cycles whose every decision follows from one Philox number (numpy's):
+    (A) q_1 puts all mass on token 0 and p_0 half, so d_1 = 0 is accepted iff
+    u(c, 1, accept) < 1/2; accepted, the bonus token comes from p_1 (uniform on
+    {2, 3}) with u(c, 1, final); rejected, the residual is all on token 1.
+    (B) q_1 uniform on {0, 1} and p_0 uniform on {2, 3}: d_1 = 0 iff
+    u(c, 0, draft) < 1/2, always rejected, the final token is 2 iff
+    u(c, 0, final) < 1/2."""
+    from oracle import spec_cycle
+    ninf = -np.inf
+    seed = 5
+    u = lambda c, slot, purpose: (_np_philox_word0(seed, [c, slot, purpose, 0]) >> 40) / 2**24
+    tlA = np.array([[0.0, 0.0, ninf, ninf], [ninf, ninf, 0.0, 0.0]])
+    dlA = np.array([[0.0, ninf, ninf, ninf]])
+    tlB = np.array([[ninf, ninf, 0.0, 0.0], [0.0, 0.0, 0.0, 0.0]])
+    dlB = np.array([[0.0, 0.0, ninf, ninf]])
+    seen = set()
+    for c in range(1, 200):
+        a, em, _ = spec_cycle(tlA, dlA, 1.0, seed, c)
+        if u(c, 1, 1) < 0.5:
+            want = (1, [0, 2 if u(c, 1, 2) < 0.5 else 3])
+        else:
+            want = (0, [1])
+        assert (a, em) == want, c
+        seen.add(tuple(em))
+        a, em, _ = spec_cycle(tlB, dlB, 1.0, seed, c)
+        assert (a, em) == (0, [2 if u(c, 0, 2) < 0.5 else 3]), c
+        d = 0 if u(c, 0, 0) < 0.5 else 1
+        assert spec_cycle(tlB, dlB, 1.0, seed, c, drafts=[d])[:2] == (a, em)
+    assert seen == {(0, 2), (0, 3), (1,)}
