@@ -159,13 +159,26 @@ __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
   constexpr int CS = NW > 1 ? NW * TE : TE;                  // chunk stride of a stream
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane & 15, kg = lane >> 4;
-  const int t0 = blockIdx.x * TPW;                           // first column tile
-  const int ntiles = gridDim.x * TPW;
+  // workgroup -> (column group bx, row block by).  Multi-row-tile launches
+  // may come as one dimension, remapped so that the row blocks sharing a
+  // column group's weights sit on one XCD (workgroups go to the 8 XCDs in
+  // turn) and are dispatched one after another: that XCD's L2 then serves
+  // the weight tiles to all of them.  The mapping never changes what a
+  // workgroup computes.
+  int bx = blockIdx.x, by = blockIdx.y, gxl = gridDim.x;
+  if (MT > 1 && a.remap_gx > 0) {
+    const int L = blockIdx.x, q = L >> 3;
+    by = q % a.remap_rb;
+    bx = (q / a.remap_rb) * 8 + (L & 7);
+    gxl = a.remap_gx;
+  }
+  const int t0 = bx * TPW;                                   // first column tile
+  const int ntiles = gxl * TPW;
   const uint16_t* xr[MT];
   bool av_ok[MT];
 #pragma unroll
   for (int r = 0; r < MT; ++r) {
-    const int am = (blockIdx.y * MT + r) * 16 + c;
+    const int am = (by * MT + r) * 16 + c;
     av_ok[r] = am < a.M;
     xr[r] = (const uint16_t*)a.X + (size_t)(av_ok[r] ? am : 0) * a.ldx + kg * 16;
   }
@@ -214,7 +227,7 @@ __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
     for (int j = 0; j < TPW; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int m = blockIdx.y * 16 + 4 * kg + i;
+        const int m = by * 16 + 4 * kg + i;
         if (ep(i) && m < a.M) yv[j][i] = a.y[(size_t)m * a.ldy + (t0 + j) * 16 + c];
       }
   }
@@ -228,7 +241,7 @@ __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
   float4 ssv[RPRE];
   if (MT == 1 && fold) {
 #pragma unroll
-    for (int r = 0; r < RPRE; ++r) ssv[r] = ss_part(a, blockIdx.y * 16 + wave + r * KW, r * KW + wave < 16, lane);
+    for (int r = 0; r < RPRE; ++r) ssv[r] = ss_part(a, by * 16 + wave + r * KW, r * KW + wave < 16, lane);
   }
   f32x4 acc[MT][NS];
 #pragma unroll
@@ -252,7 +265,7 @@ __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
         if (kind[j] != 0) continue;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int m = blockIdx.y * 16 + 4 * kg + i;
+          const int m = by * 16 + 4 * kg + i;
           if (ep(i) && m < a.M) {
             rc[j][i] = a.cos_t[(size_t)(base + m) * half + dim[j]];
             rsn[j][i] = a.sin_t[(size_t)(base + m) * half + dim[j]];
@@ -272,7 +285,7 @@ __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
       const int row = r * KW + wave;
-      const int m = blockIdx.y * 16 * MT + row;
+      const int m = by * 16 * MT + row;
       const float4 v = MT == 1 ? ssv[r < RPRE ? r : 0] : ss_part(a, m, row < 16 * MT, lane);
       const float f = ss_rstd(a, m, row < 16 * MT, lane, v);
       if (lane == 0 && row < 16 * MT) rs[row] = f;
@@ -327,7 +340,7 @@ __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
 
 #pragma unroll
   for (int r = 0; r < MT; ++r) {
-    const int mt = blockIdx.y * MT + r;
+    const int mt = by * MT + r;
     if (EPI == EPI_SWIGLU) {
 #pragma unroll
       for (int jt = 0; jt < TPW; ++jt)
@@ -527,7 +540,14 @@ hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t s) {
     int tpm = 1;
     if (multi && tiles % 4 == 0 && (tiles / 4) * rb >= 2 * NUM_CU && epi != EPI_SWIGLU) tpm = 4;
     else if (multi && tiles % 2 == 0 && (tiles / 2) * rb >= 2 * NUM_CU) tpm = 2;
-    const dim3 grid_mt(tiles / tpm, rb);
+    dim3 grid_mt(tiles / tpm, rb);
+    GemmArgs am = a;
+    am.remap_gx = am.remap_rb = 0;
+    if (multi && (tiles / tpm) % 8 == 0 && rb > 1) {   // XCD-aware 1-D launch (see the kernel)
+      am.remap_gx = tiles / tpm;
+      am.remap_rb = rb;
+      grid_mt = dim3((tiles / tpm) * rb, 1);
+    }
     // passes wider than 4 rows group 2 or 4 column tiles per workgroup so
     // the A operand is read once for them (results unchanged, see the kernel),
     // but only where at least 1024 workgroups remain: spreading the weight
@@ -537,9 +557,9 @@ hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t s) {
     else if (a.M > SSD_TPW_MIN_M && tiles % 2 == 0 && tiles / 2 >= 1024) tpw = 2;
 #define SSD_G1(E, KWN, UN, TWV)                                                                         \
   if (multi) {                                                                                           \
-    if (tpm == 4) gemm_bf16_kernel<E, 1, SSD_MT_KW, SSD_MT_MT, 1, 4, TWV><<<grid_mt, 64 * SSD_MT_KW, 0, s>>>(a); \
-    else if (tpm == 2) gemm_bf16_kernel<E, 1, SSD_MT_KW, SSD_MT_MT, 1, 2, TWV><<<grid_mt, 64 * SSD_MT_KW, 0, s>>>(a); \
-    else gemm_bf16_kernel<E, 1, SSD_MT_KW, SSD_MT_MT, 1, 1, TWV><<<grid_mt, 64 * SSD_MT_KW, 0, s>>>(a);   \
+    if (tpm == 4) gemm_bf16_kernel<E, 1, SSD_MT_KW, SSD_MT_MT, 1, 4, TWV><<<grid_mt, 64 * SSD_MT_KW, 0, s>>>(am); \
+    else if (tpm == 2) gemm_bf16_kernel<E, 1, SSD_MT_KW, SSD_MT_MT, 1, 2, TWV><<<grid_mt, 64 * SSD_MT_KW, 0, s>>>(am); \
+    else gemm_bf16_kernel<E, 1, SSD_MT_KW, SSD_MT_MT, 1, 1, TWV><<<grid_mt, 64 * SSD_MT_KW, 0, s>>>(am);   \
   }                                                                                                      \
   else if (tpw == 4) {                                                                                   \
     const dim3 g4(tiles / 4, mt);                                                                        \
@@ -563,11 +583,11 @@ hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t s) {
       case EPI_STORE: SSD_G1(EPI_STORE, SSD_KW_NARROW, SSD_GEMM_U1, 16) break;
       case EPI_SWIGLU:
         if (tw == 14) {
-          if (multi && tpm == 2) gemm_bf16_kernel<EPI_SWIGLU, 2, SSD_MT_KW, SSD_MT_MT, 1, 2, 14><<<grid_mt, 64 * SSD_MT_KW, 0, s>>>(a);
-          else if (multi) gemm_bf16_kernel<EPI_SWIGLU, 2, SSD_MT_KW, SSD_MT_MT, 1, 1, 14><<<grid_mt, 64 * SSD_MT_KW, 0, s>>>(a);
+          if (multi && tpm == 2) gemm_bf16_kernel<EPI_SWIGLU, 2, SSD_MT_KW, SSD_MT_MT, 1, 2, 14><<<grid_mt, 64 * SSD_MT_KW, 0, s>>>(am);
+          else if (multi) gemm_bf16_kernel<EPI_SWIGLU, 2, SSD_MT_KW, SSD_MT_MT, 1, 1, 14><<<grid_mt, 64 * SSD_MT_KW, 0, s>>>(am);
           else gemm_bf16_kernel<EPI_SWIGLU, 2, SSD_KW_SWIGLU, 1, SSD_GEMM_U2, 1, 14><<<grid, 64 * SSD_KW_SWIGLU, 0, s>>>(a);
-        } else if (multi && tpm == 2) gemm_bf16_kernel<EPI_SWIGLU, 2, SSD_MT_KW, SSD_MT_MT, 1, 2><<<grid_mt, 64 * SSD_MT_KW, 0, s>>>(a);
-        else if (multi) gemm_bf16_kernel<EPI_SWIGLU, 2, SSD_MT_KW, SSD_MT_MT, 1, 1><<<grid_mt, 64 * SSD_MT_KW, 0, s>>>(a);
+        } else if (multi && tpm == 2) gemm_bf16_kernel<EPI_SWIGLU, 2, SSD_MT_KW, SSD_MT_MT, 1, 2><<<grid_mt, 64 * SSD_MT_KW, 0, s>>>(am);
+        else if (multi) gemm_bf16_kernel<EPI_SWIGLU, 2, SSD_MT_KW, SSD_MT_MT, 1, 1><<<grid_mt, 64 * SSD_MT_KW, 0, s>>>(am);
         else if (wide) gemm_bf16_kernel<EPI_SWIGLU, 2, SSD_KW_WIDE, 1, SSD_GEMM_U2, 1><<<grid, 64 * SSD_KW_WIDE, 0, s>>>(a);
         else gemm_bf16_kernel<EPI_SWIGLU, 2, SSD_KW_SWIGLU, 1, SSD_GEMM_U2, 1><<<grid, 64 * SSD_KW_SWIGLU, 0, s>>>(a);
         break;

@@ -60,6 +60,9 @@ struct GemmArgs {
   float* ss_out;
   void* xg_out;
   const void* gain_next;
+  // set by the launcher only: a 1-D launch of remap_gx x remap_rb workgroups
+  // of the multi-row-tile kernel mapped XCD-aware (see gemm.hip); 0 otherwise
+  int remap_gx, remap_rb;
 };
 
 struct AttnArgs {
