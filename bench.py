@@ -150,6 +150,41 @@ def bench_pmc_probe(args) -> int:
     return 0
 
 
+def bench_prefill(args) -> int:
+    """Prefill (time to the first token) of the 1024-token prompt on the
+    8B-shaped model (--prefill-layers of its 32 layers) in 64- and 256-row
+    chunks: best of --steps prefills each, wall time including the first
+    token's read-back.  Outside the decode rate; also the kernel sequence
+    for counter runs of the prefill GEMMs."""
+    import numpy as np
+    import synth
+    from self_speculative_decoding_amd import Engine, make_cfg
+    cfg = synth.config("llama-8b", n_layers=args.prefill_layers)
+    w = synth.make_weights(cfg)
+    prompt = synth.make_prompt(cfg)
+    rows = {}
+    for chunk in (64, 256):
+        eng = Engine(make_cfg(cfg, max_block=4, prefill_chunk=chunk), [w[n] for n, _, _ in synth.weight_specs(cfg)])
+        ts = []
+        for _ in range(max(1, args.steps)):
+            eng.reset()
+            t = time.perf_counter()
+            eng.prefill(prompt)
+            ts.append(time.perf_counter() - t)
+        eng.close()
+        rows[f"chunk_{chunk}_ms"] = round(min(ts) * 1e3, 2)
+        log(f"prefill chunk {chunk}: {rows[f'chunk_{chunk}_ms']} ms")
+    flops = 2.0 * len(prompt) * sum(int(np.prod(sh)) for n, sh, kind in synth.weight_specs(cfg)
+                                    if kind == "mat" and n not in ("embed", "lm_head"))
+    line = {"metric": "prefill ms (time to first token), 8B-shaped bf16", "value": rows["chunk_256_ms"], "unit": "ms",
+            "n_gpus": 1, "higher_is_better": False, "dtype": "bf16", "data": "synthetic", "vs_baseline": None,
+            "config": {"workload": f"llama-8b-shaped bf16 random-init, {cfg['n_layers']} layers, "
+                                   f"{len(prompt)}-token prompt, 64- and 256-row chunks"},
+            "by_chunk": rows, "gemm_tflops_at_256": round(flops / (rows["chunk_256_ms"] * 1e-3) / 1e12, 1)}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def bench_moe_pmc_probe(args) -> int:
     """Kernel sequence for `rocprofv3 --pmc` runs on the MoE expert operation:
     3 plain copies of 128 MiB (counter calibration), then the expert op of
@@ -560,6 +595,8 @@ def main() -> int:
                     help="speculative sampling vs greedy and plain sampling (8B shape)")
     ap.add_argument("--kselect", action="store_true",
                     help="draft length from fitted step times: predicted vs measured k*(alpha)")
+    ap.add_argument("--prefill", action="store_true", help="prefill time of the 1024-token prompt (8B shape)")
+    ap.add_argument("--prefill-layers", type=int, default=32)
     ap.add_argument("--moe-pmc-probe", action="store_true",
                     help="MoE expert op kernel sequence for rocprofv3 --pmc (with --moe-dedup)")
     ap.add_argument("--moe-dedup", type=int, default=0, choices=(0, 1))
@@ -583,6 +620,8 @@ def main() -> int:
         return bench_pmc_probe(args)
     if args.moe_pmc_probe:
         return bench_moe_pmc_probe(args)
+    if args.prefill:
+        return bench_prefill(args)
     if args.workload == "qwen3-8b":
         return bench_verify_blocks(args)
     if args.workload == "dsv2-lite":
