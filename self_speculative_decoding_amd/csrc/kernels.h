@@ -70,11 +70,12 @@ struct AttnArgs {
   const void* kc;             // [hkv][max_ctx][hd]
   const void* vc;             // [hkv][hd][max_ctx]
   void* out;                  // [M, hq*hd]
-  float* part_o;              // [n_part][R][hq][hd]
-  float* part_ml;             // [n_part][R][hq][2]
+  float* part_o;              // [R][hq][pstride][hd]: one row-head's partitions contiguous
+  float* part_ml;             // [R][hq][pstride][2]
   const int* state;
   int pos_off, M, R, hq, hkv, hd, max_ctx;   // max_ctx: positions per cache row (multiple of 64)
   int n_part;                 // partitions launched (set by launch_attention)
+  int pstride;                // partition slots per (row, head) in part_o / part_ml (>= n_part)
   float scale_log2;           // log2(e) / sqrt(hd)
 };
 

@@ -189,11 +189,11 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int d = 0; d < SL; ++d) o[d] += valid ? pv * tof(vr[d]) : 0.f;
     }
-    float* po = a.part_o + (((size_t)p * a.R + row) * a.hq + head) * HD + sub * SL;
+    float* po = a.part_o + (((size_t)row * a.hq + head) * a.pstride + p) * HD + sub * SL;
 #pragma unroll
     for (int d = 0; d < SL; ++d) po[d] = o[d];
     if (sub == 0) {
-      float* pm = a.part_ml + (((size_t)p * a.R + row) * a.hq + head) * 2;
+      float* pm = a.part_ml + (((size_t)row * a.hq + head) * a.pstride + p) * 2;
       pm[0] = mx;
       pm[1] = l;
     }
@@ -342,7 +342,7 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(AttnArgs a) {
     }
     if (!qv[t] || key0 > pos) continue;
     const int row = qr[t], head = kvh * G + qg[t];
-    const size_t ph_i = ((size_t)p * a.R + row) * a.hq + head;
+    const size_t ph_i = ((size_t)row * a.hq + head) * a.pstride + p;
     float* po = a.part_o + ph_i * HD + 4 * kg;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) *(f32x4*)(po + 16 * dt) = o[dt];
@@ -367,13 +367,13 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
   const int row = blockIdx.x, head = blockIdx.y, t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int st0 = a.state[0];   // position load issued first, used late
   const int npmax = a.n_part;   // partitions the attention launch covered (<= 128)
-  const size_t stride = (size_t)a.R * a.hq * a.hd;
-  const float* po = a.part_o + ((size_t)row * a.hq + head) * a.hd + (t < a.hd ? t : 0);
+  const size_t stride = a.hd;   // partitions of one (row, head) are contiguous
+  const float* po = a.part_o + ((size_t)row * a.hq + head) * a.pstride * a.hd + (t < a.hd ? t : 0);
   // loads issued unconditionally (indexes clamped to the launched partitions)
   float v[B];
 #pragma unroll
   for (int j = 0; j < B; ++j) v[j] = po[(size_t)min(j, npmax - 1) * stride];
-  const float* pm = a.part_ml + (((size_t)min(t, npmax - 1) * a.R + row) * a.hq + head) * 2;
+  const float* pm = a.part_ml + (((size_t)row * a.hq + head) * a.pstride + min(t, npmax - 1)) * 2;
   const float m_t = pm[0], l_t = pm[1];
   const int pos = st0 + a.pos_off + row;
   const int np = pos / ATT_PT + 1;
@@ -566,6 +566,7 @@ hipError_t launch_rmsnorm(int dtype, const float* x, int ldx, const void* g, voi
 
 template <typename E>
 static hipError_t attn_dispatch(AttnArgs a, int n_part, int hd, hipStream_t s) {
+  if (n_part < 1 || n_part > a.pstride) return hipErrorInvalidValue;
   a.n_part = n_part;
   const int G = a.hq / a.hkv;
   dim3 grid(n_part, a.hkv, (a.M + ROW_TILE - 1) / ROW_TILE);

@@ -180,7 +180,7 @@ ssd_status layer_forward(ssd_ctx* c, int l, int M, int pos_off, bool feats, cons
   }
   {
     AttnArgs a{};
-    a.q = c->q; a.kc = kc; a.vc = vc; a.out = c->att; a.part_o = c->part_o; a.part_ml = c->part_ml;
+    a.q = c->q; a.kc = kc; a.vc = vc; a.out = c->att; a.part_o = c->part_o; a.part_ml = c->part_ml; a.pstride = c->lay.n_part;
     a.state = c->dstate; a.pos_off = pos_off; a.M = M; a.R = c->lay.R;
     a.hq = hq; a.hkv = hkv; a.hd = hd; a.max_ctx = kv_stride(g);
     a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)hd));
@@ -1148,7 +1148,7 @@ ssd_status ssd_time_op(ssd_ctx* c, int32_t op, int32_t layer, int32_t m, int32_t
       HIPCHK(launch_moe(dt, moe_args(c, l, m), s));
     } else if (op == 5) {
       AttnArgs at{};
-      at.q = c->q; at.kc = kc; at.vc = vc; at.out = c->att; at.part_o = c->part_o; at.part_ml = c->part_ml;
+      at.q = c->q; at.kc = kc; at.vc = vc; at.out = c->att; at.part_o = c->part_o; at.part_ml = c->part_ml; at.pstride = c->lay.n_part;
       at.state = c->dstate; at.pos_off = 0; at.M = m; at.R = c->lay.R;
       at.hq = hq; at.hkv = hkv; at.hd = hd; at.max_ctx = kv_stride(g);
       at.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)hd));
