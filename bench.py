@@ -66,6 +66,10 @@ def pass_bytes(cfg: dict, M: int, ctx: float, layers: int | None = None, head: b
     return b
 
 
+def _weights_progress(frac: float) -> None:
+    log(f"weights {frac:.0%} generated")
+
+
 def measured_traffic() -> float | None:
     """HBM bytes per launch of the gate/up GEMM from the committed hardware-
     counter summary, or None when the kernel sources changed since."""
@@ -136,7 +140,7 @@ def bench_pmc_probe(args) -> int:
     import synth
     from self_speculative_decoding_amd import Engine, make_cfg
     cfg = synth.config("llama-8b", n_layers=4)
-    w = synth.make_weights(cfg)
+    w = synth.make_weights(cfg, progress=_weights_progress)
     eng = Engine(make_cfg(cfg, max_block=6, prefill_chunk=256), [w[n] for n, _, _ in synth.weight_specs(cfg)])
     eng.prefill(synth.make_prompt(cfg)[:64])
     res = {"copy_probe_us": eng.time_op("copy_probe", 0, 128, 3),
@@ -160,7 +164,7 @@ def bench_prefill(args) -> int:
     import synth
     from self_speculative_decoding_amd import Engine, make_cfg
     cfg = synth.config("llama-8b", n_layers=args.prefill_layers)
-    w = synth.make_weights(cfg)
+    w = synth.make_weights(cfg, progress=_weights_progress)
     prompt = synth.make_prompt(cfg)
     rows = {}
     for chunk in (64, 256):
@@ -199,7 +203,7 @@ def bench_moe_pmc_probe(args) -> int:
     nd = cfg["n_dense_layers"]
     eb = cfg["expert_ffn"] * cfg["d_model"] * 3 * 2
     assert (cfg["max_ctx"] // 64) * 256 * cfg["n_q_heads"] * cfg["head_dim"] * 4 >= 128 << 20
-    w = synth.make_weights(cfg)
+    w = synth.make_weights(cfg, progress=_weights_progress)
     eng = Engine(make_cfg(cfg, max_block=9, prefill_chunk=256), [w[n_] for n_, _, _ in synth.weight_specs(cfg)])
     del w
     eng.prefill(synth.make_prompt(cfg)[:64])
@@ -228,7 +232,7 @@ def bench_verify_blocks(args) -> int:
     cfg = synth.config("qwen3-8b")
     B, P = cfg["block"], cfg["prompt_len"]
     log("qwen3-8b: generating weights")
-    w = synth.make_weights(cfg)
+    w = synth.make_weights(cfg, progress=_weights_progress)
     prompt = synth.make_prompt(cfg)
     eng = Engine(make_cfg(cfg, max_block=B, prefill_chunk=256), [w[n] for n, _, _ in synth.weight_specs(cfg)])
     n_cont = 400
@@ -291,7 +295,7 @@ def bench_kselect(args) -> int:
     KMAX, V = 8, cfg["vocab"]
     frac = args.skip if args.skip is not None else cfg["skip_frac"]
     log("kselect: generating weights")
-    w = synth.make_weights(cfg)
+    w = synth.make_weights(cfg, progress=_weights_progress)
     prompt = synth.make_prompt(cfg)
     eng = Engine(make_cfg(cfg, max_block=KMAX + 1, prefill_chunk=256), [w[n] for n, _, _ in synth.weight_specs(cfg)])
     del w
@@ -369,7 +373,7 @@ def bench_kvq(args) -> int:
     L, k = cfg["n_layers"], args.k if args.k is not None else 3
     n_new = args.n_new or 256
     log("kvq: generating weights")
-    w = synth.make_weights(cfg)
+    w = synth.make_weights(cfg, progress=_weights_progress)
     prompt = synth.make_prompt(cfg)
     eng = Engine(make_cfg(cfg, max_block=k + 1, prefill_chunk=256), [w[n] for n, _, _ in synth.weight_specs(cfg)])
     del w
@@ -420,7 +424,7 @@ def bench_sampling(args) -> int:
     frac = args.skip if args.skip is not None else 0.2
     n_new = args.n_new or 256
     log("sampling: generating weights")
-    w = synth.make_weights(cfg)
+    w = synth.make_weights(cfg, progress=_weights_progress)
     prompt = synth.make_prompt(cfg)
     eng = Engine(make_cfg(cfg, max_block=k + 1, prefill_chunk=256), [w[n] for n, _, _ in synth.weight_specs(cfg)])
     del w
@@ -468,7 +472,7 @@ def bench_knapsack(args) -> int:
     cfg = synth.config("llama-8b")
     L, k, n_new = cfg["n_layers"], 3, args.n_new or 256
     log("knapsack: generating weights")
-    w = synth.make_weights(cfg)
+    w = synth.make_weights(cfg, progress=_weights_progress)
     prompt = synth.make_prompt(cfg)
     eng = Engine(make_cfg(cfg, max_block=17, prefill_chunk=256), [w[n] for n, _, _ in synth.weight_specs(cfg)])
     del w
@@ -527,7 +531,7 @@ def bench_moe(args) -> int:
     L, E, K = cfg["n_layers"], cfg["n_experts"], cfg["top_k"]
     eb = cfg["expert_ffn"] * cfg["d_model"] * 3 * 2             # one expert's gate/up/down bytes
     log("dsv2-lite: generating weights")
-    w = synth.make_weights(cfg)
+    w = synth.make_weights(cfg, progress=_weights_progress)
     prompt = synth.make_prompt(cfg)
     eng = Engine(make_cfg(cfg, max_block=9, prefill_chunk=256), [w[n] for n, _, _ in synth.weight_specs(cfg)])
     rows = []
@@ -642,7 +646,7 @@ def main() -> int:
     n_new, P = args.n_new or cfg["n_new"], cfg["prompt_len"]
     log(f"workload {args.workload}: generating weights")
     t = time.perf_counter()
-    weights = synth.make_weights(cfg)
+    weights = synth.make_weights(cfg, progress=_weights_progress)
     prompt = synth.make_prompt(cfg)
     log(f"weights ready in {time.perf_counter() - t:.1f}s; uploading")
     eng = Engine(make_cfg(cfg, max_block=max(ks + [k]) + 1, prefill_chunk=256),

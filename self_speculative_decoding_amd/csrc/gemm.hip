@@ -38,6 +38,9 @@
 #ifndef SSD_KW_NARROW
 #define SSD_KW_NARROW 8
 #endif
+#ifndef SSD_KW_LONGK_NARROW  // waves (one 64-element chunk per load batch) of K >= 8192 GEMMs in narrow tiles
+#define SSD_KW_LONGK_NARROW 16
+#endif
 #ifndef SSD_KW_WIDE
 #define SSD_KW_WIDE 8
 #endif
@@ -153,7 +156,9 @@ __device__ __forceinline__ float ss_rstd(const GemmArgs& a, int m, bool row_ok, 
 template <int EPI, int NW, int KW, int MT, int U, int TPW, int TW = 16>
 __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
   static_assert(TPW == 1 || NW == 1 || MT > 1, "gate/up tile groups are for multi-row-tile launches");
-  static_assert(TW == 16 || (EPI == EPI_SWIGLU && TW == 14) || (EPI == EPI_QKV && TW == 12), "tile width");
+  static_assert(TW == 16 || (EPI == EPI_SWIGLU && TW == 14) || (EPI == EPI_QKV && TW == 12) ||
+                    (EPI == EPI_RESID && (TW == 10 || TW == 8)),
+                "tile width");
   constexpr int NS = NW * TPW;                               // weight streams
   constexpr int TE = TW * 64;                                // elements per packed tile
   constexpr int CS = NW > 1 ? NW * TE : TE;                  // chunk stride of a stream
@@ -228,7 +233,7 @@ __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int m = by * 16 + 4 * kg + i;
-        if (ep(i) && m < a.M) yv[j][i] = a.y[(size_t)m * a.ldy + (t0 + j) * 16 + c];
+        if (ep(i) && m < a.M && c < TW) yv[j][i] = a.y[(size_t)m * a.ldy + (t0 + j) * TW + c];
       }
   }
 
@@ -379,7 +384,7 @@ __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
       for (int i = 0; i < 4; ++i) {
         if (!ep(i)) continue;
         const int m = mt * 16 + 4 * kg + i;
-        const int n = tt * 16 + c;
+        const int n = tt * TW + c;   // lanes c >= TW (narrow residual tiles) write nothing
         if (EPI == EPI_LOGITS) {
           // (max, lowest index) over this tile's 16 columns, fixed butterfly
           float bv = acc[r][j][i];
@@ -398,11 +403,12 @@ __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
         if (EPI == EPI_RESID && a.ss_out) {
           // new residual, its sum of squares over this tile's 16 columns and
           // bf16(x * gain) for the GEMM that consumes it
-          const float xv = m < a.M ? (MT == 1 ? yv[j][i] : a.y[(size_t)m * a.ldy + n]) + acc[r][j][i] : 0.f;
+          const bool col = c < TW;
+          const float xv = m < a.M && col ? (MT == 1 ? yv[j][i] : a.y[(size_t)m * a.ldy + n]) + acc[r][j][i] : 0.f;
           float sq = xv * xv;
 #pragma unroll
           for (int o = 1; o < 16; o <<= 1) sq += __shfl_xor(sq, o);
-          if (m < a.M) {
+          if (m < a.M && col) {
             a.y[(size_t)m * a.ldy + n] = xv;
             if (a.tap) ((uint16_t*)a.tap)[(size_t)m * a.ldtap + n] = f2bf(xv);
             ((uint16_t*)a.xg_out)[(size_t)m * a.ldy + n] = f2bf(xv * bf2f(((const uint16_t*)a.gain_next)[n]));
@@ -410,7 +416,7 @@ __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
           }
           continue;
         }
-        if (m >= a.M) continue;
+        if (m >= a.M || c >= TW) continue;
         if (EPI == EPI_RESID && MT == 1) {
           const float xv = yv[j][i] + acc[r][j][i];
           a.y[(size_t)m * a.ldy + n] = xv;
@@ -525,7 +531,11 @@ hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t s) {
   if (dtype) {
     int tiles;
     const int tw = epi == EPI_SWIGLU ? swiglu_tile_width(a.N)   // as packed
-                   : epi == EPI_QKV ? qkv_tile_width(a.hq, a.hkv, a.hd) : 16;
+                   : epi == EPI_QKV   ? qkv_tile_width(a.hq, a.hkv, a.hd)
+                   : epi == EPI_RESID ? resid_tile_width(a.N)
+                                      : 16;
+    // the folded norm's partials come one per residual tile
+    if (epi == EPI_RESID && a.ss_out && a.N % tw != 0) return hipErrorInvalidValue;
     if (epi == EPI_QKV) tiles = (a.hq + 2 * a.hkv) * a.hd / tw;
     else tiles = a.N / tw;
     dim3 grid(tiles, mt);
@@ -552,9 +562,12 @@ hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t s) {
     // the A operand is read once for them (results unchanged, see the kernel),
     // but only where at least 1024 workgroups remain: spreading the weight
     // stream over every CU matters more than the A reads (measured)
+    // (never for long-K narrow tiles: their one-tile kernel splits K over
+    // more waves, and a row's K split must not depend on the pass width)
     int tpw = 1;
-    if (a.M > SSD_TPW_MIN_M && tiles % 4 == 0 && tiles / 4 >= 1024) tpw = 4;
-    else if (a.M > SSD_TPW_MIN_M && tiles % 2 == 0 && tiles / 2 >= 1024) tpw = 2;
+    const bool tpw_ok = a.M > SSD_TPW_MIN_M && !(a.K >= 8192 && tw < 16);
+    if (tpw_ok && tiles % 4 == 0 && tiles / 4 >= 1024) tpw = 4;
+    else if (tpw_ok && tiles % 2 == 0 && tiles / 2 >= 1024) tpw = 2;
 #define SSD_G1(E, KWN, UN, TWV)                                                                         \
   if (multi) {                                                                                           \
     if (tpm == 4) gemm_bf16_kernel<E, 1, SSD_MT_KW, SSD_MT_MT, 1, 4, TWV><<<grid_mt, 64 * SSD_MT_KW, 0, s>>>(am); \
@@ -570,12 +583,20 @@ hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t s) {
     if (wide) gemm_bf16_kernel<E, 1, SSD_KW_WIDE, 1, 2, 2, TWV><<<g2, 64 * SSD_KW_WIDE, 0, s>>>(a);      \
     else gemm_bf16_kernel<E, 1, KWN, 1, 2, 2, TWV><<<g2, 64 * KWN, 0, s>>>(a);                           \
   } else if (wide) gemm_bf16_kernel<E, 1, SSD_KW_WIDE, 1, SSD_GEMM_UW, 1, TWV><<<grid, 64 * SSD_KW_WIDE, 0, s>>>(a); \
-  else if (a.K >= 8192) gemm_bf16_kernel<E, 1, KWN, 1, SSD_GEMM_U1_LONGK, 1, TWV><<<grid, 64 * KWN, 0, s>>>(a); \
+  else if (a.K >= 8192) {                                                                               \
+    if constexpr (TWV < 16)                                                                              \
+      gemm_bf16_kernel<E, 1, SSD_KW_LONGK_NARROW, 1, 1, 1, TWV><<<grid, 64 * SSD_KW_LONGK_NARROW, 0, s>>>(a); \
+    else gemm_bf16_kernel<E, 1, KWN, 1, SSD_GEMM_U1_LONGK, 1, TWV><<<grid, 64 * KWN, 0, s>>>(a);          \
+  }                                                                                                      \
   else gemm_bf16_kernel<E, 1, KWN, 1, UN, 1, TWV><<<grid, 64 * KWN, 0, s>>>(a);
     switch (epi) {
       case EPI_F32: SSD_G1(EPI_F32, SSD_KW_NARROW, SSD_GEMM_U1, 16) break;
       case EPI_LOGITS: SSD_G1(EPI_LOGITS, SSD_KW_NARROW, SSD_GEMM_U1, 16) break;
-      case EPI_RESID: SSD_G1(EPI_RESID, SSD_KW_NARROW, SSD_GEMM_U1, 16) break;
+      case EPI_RESID:
+        if (tw == 10) { SSD_G1(EPI_RESID, SSD_KW_NARROW, SSD_GEMM_U1, 10) }
+        else if (tw == 8) { SSD_G1(EPI_RESID, SSD_KW_NARROW, SSD_GEMM_U1, 8) }
+        else { SSD_G1(EPI_RESID, SSD_KW_NARROW, SSD_GEMM_U1, 16) }
+        break;
       case EPI_QKV:
         if (tw == 12) { SSD_G1(EPI_QKV, SSD_KW_NARROW, SSD_GEMM_U1, 12) }
         else { SSD_G1(EPI_QKV, SSD_KW_NARROW, SSD_GEMM_U1, 16) }

@@ -148,7 +148,7 @@ bool compute_layout(const ssd_cfg& c, Layout& L) {
   L.vc = take(cache);
   L.x = take((size_t)R * d * 4);
   L.xn = take((size_t)R * d * esz);
-  L.ss = take((size_t)R * (d / 16) * 4);   // folded-norm partial sums of squares
+  L.ss = take((size_t)R * (d / 8) * 4);   // folded-norm partial sums of squares (tiles of >= 8 columns)
   L.q = take((size_t)R * hq * hd * esz);
   L.att = take((size_t)R * hq * hd * esz);
   size_t fact = (size_t)layer_ffn(c);
@@ -163,7 +163,7 @@ bool compute_layout(const ssd_cfg& c, Layout& L) {
   // exit-state cache of an early-exit draft: residual and its sums of squares
   // per block row after the draft's last layer
   L.exit_x = take((size_t)c.max_block * d * 4);
-  L.exit_ss = take((size_t)c.max_block * (d / 16) * 4);
+  L.exit_ss = take((size_t)c.max_block * (d / 8) * 4);
   // speculative sampling: the draft steps' logits rows, test-cycle outputs
   L.dlog = take((size_t)c.max_block * c.vocab * 4);
   L.tout = take((size_t)kTestCycles * (SSD_MAX_BLOCK + 2) * 4);

@@ -50,10 +50,11 @@ struct GemmArgs {
   int* amax_i;
   // RMSNorm folded into the GEMMs (bf16 models).  A consumer GEMM (QKV,
   // gate/up, LM head) reads X = bf16(x * gain) and scales its float
-  // accumulator by rstd = 1/sqrt(mean(x^2) + eps), summing the per-16-column
-  // partial sums of squares ss_in [M][nss] the producer left.  The producer
-  // (residual epilogue) writes those partials (ss_out [M][N/16]) and the next
-  // consumer's input xg_out = bf16(x_new * gain_next) [M][N].
+  // accumulator by rstd = 1/sqrt(mean(x^2) + eps), summing the partial sums
+  // of squares ss_in [M][nss] (nss a multiple of 4) the producer left.  The
+  // producer (residual epilogue) writes one partial per column tile (ss_out
+  // [M][N/TW]) and the next consumer's input xg_out = bf16(x_new * gain_next)
+  // [M][N].
   const float* ss_in;
   int nss;
   float eps;
@@ -82,9 +83,9 @@ struct AttnArgs {
 // dtype: 0 = f32, 1 = bf16 (uint16 bit patterns)
 hipError_t launch_embed(int dtype, const int* tok, const void* E, float* x, int d, int M, hipStream_t s);
 // bf16 embedding that also leaves the folded-RMSNorm inputs of the first layer:
-// xg = bf16(x * gain) and per-16-column sums of squares ss [M][d/16]
+// xg = bf16(x * gain) and sums of squares over runs of ssw columns, ss [M][d/ssw]
 hipError_t launch_embed_norm(const int* tok, const void* E, float* x, int d, int M, const void* gain, void* xg,
-                             float* ss, hipStream_t s);
+                             float* ss, int ssw, hipStream_t s);
 hipError_t launch_rmsnorm(int dtype, const float* x, int ldx, const void* g, void* y, int ldy, int d,
                           float eps, int M, hipStream_t s);
 hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t s);
@@ -118,7 +119,8 @@ struct MoeArgs {
   int* union_out;             // [1] union size of this pass
   int dedup;
   // folded RMSNorm of the next GEMM (see GemmArgs): written when ss_out != 0
-  float* ss_out;              // [M, d/16]
+  float* ss_out;              // [M, d/ssw]: sums of squares over runs of ssw columns
+  int ssw;                    // columns per combine run (>= 1, divides d; launch_moe checks)
   void* xg_out;               // [M, d] bf16(x * gain_next)
   const void* gain_next;      // [d]
 };
@@ -182,6 +184,27 @@ inline int qkv_tile_width(int hq, int hkv, int hd) {
   const long w16 = (long)((N / 16 + NUM_CU - 1) / NUM_CU) * 16;
   const long w12 = (long)((N / 12 + NUM_CU - 1) / NUM_CU) * 12;
   return w12 < w16 ? 12 : 16;
+}
+
+// Rows per packed tile of the weights whose GEMM adds into the residual
+// stream (o projection and down, N = d): 16, 10 or 8, whichever divides N
+// into a multiple of 4 tiles with the smallest largest per-CU share (ties to
+// the wider tile).  d = 2560 gives 256 tiles of 10 rows instead of 160 of
+// 16, so no CU idles.  The folded norm's sums of squares come one per tile
+// of these GEMMs: every producer of them writes d / resid_tile_width(d)
+// partials per row, each over that many consecutive columns.
+inline int resid_tile_width(int N) {
+  int best = 16;
+  long best_share = (long)((N / 16 + NUM_CU - 1) / NUM_CU) * 16;
+  for (int w : {10, 8}) {
+    if (N % w != 0 || (N / w) % 4 != 0) continue;
+    const long share = (long)((N / w + NUM_CU - 1) / NUM_CU) * w;
+    if (share < best_share) {
+      best = w;
+      best_share = share;
+    }
+  }
+  return best;
 }
 
 // Output column of lane c (c < 16) in column tile t of the packed QKV weight

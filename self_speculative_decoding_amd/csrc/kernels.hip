@@ -24,18 +24,18 @@ __global__ __launch_bounds__(256) void embed_kernel(const int* __restrict__ tok,
 
 __global__ __launch_bounds__(256) void embed_norm_kernel(const int* __restrict__ tok, const uint16_t* __restrict__ emb,
                                                          float* __restrict__ x, int d, const uint16_t* __restrict__ g,
-                                                         uint16_t* __restrict__ xg, float* __restrict__ ss) {
+                                                         uint16_t* __restrict__ xg, float* __restrict__ ss, int ssw) {
   const int m = blockIdx.x;
   const uint16_t* row = emb + (size_t)tok[m] * d;
-  for (int c0 = threadIdx.x * 16; c0 < d; c0 += 256 * 16) {
+  for (int c0 = threadIdx.x * ssw; c0 < d; c0 += 256 * ssw) {
     float q = 0.f;
-    for (int j = 0; j < 16; ++j) {
+    for (int j = 0; j < ssw; ++j) {
       const float v = bf2f(row[c0 + j]);
       x[(size_t)m * d + c0 + j] = v;
       xg[(size_t)m * d + c0 + j] = f2bf(v * bf2f(g[c0 + j]));
       q = fmaf(v, v, q);
     }
-    ss[(size_t)m * (d / 16) + c0 / 16] = q;
+    ss[(size_t)m * (d / ssw) + c0 / ssw] = q;
   }
 }
 
@@ -552,8 +552,9 @@ hipError_t launch_embed(int dtype, const int* tok, const void* E, float* x, int 
 }
 
 hipError_t launch_embed_norm(const int* tok, const void* E, float* x, int d, int M, const void* gain, void* xg,
-                             float* ss, hipStream_t s) {
-  embed_norm_kernel<<<M, 256, 0, s>>>(tok, (const uint16_t*)E, x, d, (const uint16_t*)gain, (uint16_t*)xg, ss);
+                             float* ss, int ssw, hipStream_t s) {
+  if (ssw < 1 || d % ssw != 0) return hipErrorInvalidValue;
+  embed_norm_kernel<<<M, 256, 0, s>>>(tok, (const uint16_t*)E, x, d, (const uint16_t*)gain, (uint16_t*)xg, ss, ssw);
   return hipGetLastError();
 }
 

@@ -128,6 +128,7 @@ MoeArgs moe_args(ssd_ctx* c, int l, int M) {
   a.inject = c->moe_inject ? c->m_inject + (size_t)l * c->lay.R * g.top_k : nullptr;
   a.act = c->act; a.slot_out = c->m_slot_out; a.resid = c->x; a.groups = c->m_groups;
   a.union_out = c->m_union + l; a.dedup = g.moe_dedup;
+  a.ssw = resid_tile_width(g.d_model);   // the combine's column runs, also without ss_out
   return a;
 }
 
@@ -136,10 +137,14 @@ MoeArgs moe_args(ssd_ctx* c, int l, int M) {
 // per-16-column sums of squares in ss, and the GEMM scales its product by
 // 1/rms.  The MoE feed-forward keeps a standalone norm (router and experts
 // share its output).
+// Sums-of-squares partials per row: one per column tile of the residual
+// GEMMs (resid_tile_width), as every producer writes them.
+inline int n_ss(const ssd_cfg& g) { return g.d_model / resid_tile_width(g.d_model); }
+
 void fold_in(ssd_ctx* c, GemmArgs& a, int row0) {
-  const int d = c->cfg.d_model;
-  a.ss_in = c->ss + (size_t)row0 * (d / 16);
-  a.nss = d / 16;
+  const int nss = n_ss(c->cfg);
+  a.ss_in = c->ss + (size_t)row0 * nss;
+  a.nss = nss;
   a.eps = c->cfg.rms_eps;
 }
 
@@ -246,11 +251,11 @@ ssd_status run_pass(ssd_ctx* c, const int* d_tok, int M, int pos_off, const uint
   if (ps.load) {
     HIPCHK(launch_copy_f32(c->exit_x, c->x, M * d, s));
     if (fold) {
-      HIPCHK(launch_copy_f32(c->exit_ss, c->ss, M * (d / 16), s));
+      HIPCHK(launch_copy_f32(c->exit_ss, c->ss, M * n_ss(g), s));
       HIPCHK(launch_scale_bf16(c->x, next_gain(c, -1, skip), c->xn, d, M, s));
     }
   } else if (fold) {
-    HIPCHK(launch_embed_norm(d_tok, c->embed, c->x, d, M, next_gain(c, -1, skip), c->xn, c->ss, s));
+    HIPCHK(launch_embed_norm(d_tok, c->embed, c->x, d, M, next_gain(c, -1, skip), c->xn, c->ss, resid_tile_width(d), s));
   } else {
     HIPCHK(launch_embed(dt, d_tok, c->embed, c->x, d, M, s));
   }
@@ -260,7 +265,7 @@ ssd_status run_pass(ssd_ctx* c, const int* d_tok, int M, int pos_off, const uint
   }
   if (ps.save_row >= 0) {
     HIPCHK(launch_copy_f32(c->x, c->exit_x + (size_t)ps.save_row * d, M * d, s));
-    if (fold) HIPCHK(launch_copy_f32(c->ss, c->exit_ss + (size_t)ps.save_row * (d / 16), M * (d / 16), s));
+    if (fold) HIPCHK(launch_copy_f32(c->ss, c->exit_ss + (size_t)ps.save_row * n_ss(g), M * n_ss(g), s));
   }
   if (head_rows > 0 && ps.head) {
     if (!fold)
@@ -478,7 +483,7 @@ hipError_t pack_weights(ssd_ctx* c) {
   for (LayerW& w : c->L) {
     w.wq = pack(w.wq, w.wk, w.wv, (hq + 2 * hkv) * hd, d, 1, 0, qkv_tile_width(hq, hkv, hd));
     w.wk = w.wv = nullptr;
-    w.wo = pack(w.wo, nullptr, nullptr, d, hq * hd, 0, 0);
+    w.wo = pack(w.wo, nullptr, nullptr, d, hq * hd, 0, 0, resid_tile_width(d));   // as launch_gemm reads it
     if (w.moe) {
       const int E = g.n_experts, fe = g.expert_ffn, S = g.n_shared;
       w.router = pack(w.router, nullptr, nullptr, E, d, 0, 0);
@@ -507,7 +512,7 @@ hipError_t pack_weights(ssd_ctx* c) {
     } else {
       w.w_gate = pack(w.w_gate, w.w_up, nullptr, w.ffn, d, 0, 1, swiglu_tile_width(w.ffn));   // as launch_gemm reads it
       w.w_up = nullptr;
-      w.w_down = pack(w.w_down, nullptr, nullptr, d, w.ffn, 0, 0);
+      w.w_down = pack(w.w_down, nullptr, nullptr, d, w.ffn, 0, 0, resid_tile_width(d));
     }
   }
   c->lm_head = pack(c->lm_head, nullptr, nullptr, g.vocab, d, 0, 0);

@@ -159,13 +159,14 @@ def _fill_chunk(flat: np.ndarray, seed: int, tid: int, chunk: int, bf16: bool, s
     flat[c0:c1] = _f32_to_bf16_bits(v) if bf16 else v
 
 
-def make_weights(cfg: dict, seed: int = 0, threads: int | None = None) -> dict[str, np.ndarray]:
+def make_weights(cfg: dict, seed: int = 0, threads: int | None = None, progress=None) -> dict[str, np.ndarray]:
     """All weights of ``cfg``: name -> float32 array (f32 configs) or uint16 bf16 bits.
 
     Matrices are uniform on (-0.02*sqrt(3), 0.02*sqrt(3)) (standard deviation
     0.02), drawn in independently seeded chunks of 2^24 elements; norm gains
     are 1.  Layers listed in cfg["out_scale"] have both residual-writing
-    matrices (wo and w_down) scaled by the given factor.
+    matrices (wo and w_down) scaled by the given factor.  ``progress``, if
+    given, is called with the finished fraction about every tenth of the work.
     """
     bf16 = cfg["dtype"] == "bf16"
     one = np.uint16(0x3F80) if bf16 else np.float32(1.0)
@@ -184,8 +185,11 @@ def make_weights(cfg: dict, seed: int = 0, threads: int | None = None) -> dict[s
         for chunk in range((flat.size + _CHUNK - 1) // _CHUNK):
             jobs.append((flat, tid, chunk, scale))
     threads = threads or min(16, os.cpu_count() or 1)
+    step = max(1, len(jobs) // 10)
     with ThreadPoolExecutor(threads) as ex:
-        list(ex.map(lambda j: _fill_chunk(j[0], seed, j[1], j[2], bf16, j[3]), jobs))
+        for i, _ in enumerate(ex.map(lambda j: _fill_chunk(j[0], seed, j[1], j[2], bf16, j[3]), jobs), 1):
+            if progress is not None and (i % step == 0 or i == len(jobs)):
+                progress(i / len(jobs))
     return out
 
 

@@ -162,6 +162,37 @@ def test_narrow_gate_up_tiles():
         eng.close()
 
 
+def test_narrow_residual_tiles():
+    """d = 2560 (the Qwen3-4B width): the o-projection and down weights are
+    packed in 10-row tiles (256 tiles, one per compute unit) and the folded
+    norm's sums of squares come one per 10 columns from every producer
+    (embedding, both residual GEMMs).  Against the oracle, verify rows bitwise
+    equal to decode rows, self-speculation lossless."""
+    cfg = _edge_cfg(n_layers=2, d_model=2560, n_q_heads=16, n_kv_heads=4, max_ctx=200, prompt_len=70, cid=75)
+    w = synth.make_weights(cfg, seed=12)
+    print("[edge] d 2560 (10-row residual tiles)", flush=True)
+    eng = engine(cfg, w, max_block=8, prefill_chunk=64)
+    try:
+        prompt = synth.make_prompt(cfg)
+        toks, rows = _stepwise(eng, prompt, 25)
+        ref = Model(cfg, w).teacher_forced(prompt, toks)
+        err = np.max(np.abs(rows - ref))
+        print(f"[edge] d 2560: max |dlogit| = {err:.3e}")
+        assert err <= BOUND
+        assert _gap_ok(toks, ref, BOUND) == []
+        eng.reset()
+        eng.prefill(prompt)
+        post = eng.verify(toks[:8])
+        assert np.array_equal(eng.read_logits(8), rows[1:9])
+        assert post == toks[1:9]
+        eng.accept()
+        mask = np.array([0, 1], np.uint8)
+        spec, _ = eng.generate(prompt, 24, mask, 3)
+        assert spec == toks[:24]
+    finally:
+        eng.close()
+
+
 def test_long_context_combine_batches():
     """A 3300-token context: 52 key partitions, so the combine loads its
     partials in two batches and the passes replay from a high context

@@ -102,3 +102,23 @@ def test_moe_router_choice_matches_oracle_logits(moe):
     got = ps.read_logits(1)[0]
     _, _, last = ora.prefill(prompt)
     assert np.max(np.abs(got - last)) <= 3e-2
+
+
+def test_measurement_hooks_run_every_op(moe):
+    """ssd_time_op on every operation of an MoE model (the bench's timing
+    hook): each returns a positive time and leaves the engine usable; the MoE
+    op runs the same kernels as a pass, its combine included."""
+    cfg, w, ps, dd, ora = moe
+    prompt = synth.make_prompt(cfg)
+    for eng in (ps, dd):
+        eng.reset()
+        eng.prefill(prompt)
+        moe_layer = cfg["n_dense_layers"]
+        for op, layer in (("moe", moe_layer), ("qkv", moe_layer), ("o", moe_layer), ("attention", moe_layer),
+                          ("gate_up", 0), ("down", 0), ("lm_head", 0)):
+            for m in (1, 4):
+                us = eng.time_op(op, layer, m, 3)
+                print(f"[moe] time_op {op} layer {layer} m={m}: {us:.2f} us", flush=True)
+                assert us > 0.0
+        base, _ = eng.generate(prompt, 8)
+        assert len(base) == 8
