@@ -83,7 +83,7 @@ struct AttnArgs {
 // dtype: 0 = f32, 1 = bf16 (uint16 bit patterns)
 hipError_t launch_embed(int dtype, const int* tok, const void* E, float* x, int d, int M, hipStream_t s);
 // bf16 embedding that also leaves the folded-RMSNorm inputs of the first layer:
-// xg = bf16(x * gain) and sums of squares over runs of ssw columns, ss [M][d/ssw]
+// xg = bf16(x * gain) and sums of squares over runs of ssw columns (16, 10 or 8), ss [M][d/ssw]
 hipError_t launch_embed_norm(const int* tok, const void* E, float* x, int d, int M, const void* gain, void* xg,
                              float* ss, int ssw, hipStream_t s);
 hipError_t launch_rmsnorm(int dtype, const float* x, int ldx, const void* g, void* y, int ldy, int d,
@@ -120,7 +120,7 @@ struct MoeArgs {
   int dedup;
   // folded RMSNorm of the next GEMM (see GemmArgs): written when ss_out != 0
   float* ss_out;              // [M, d/ssw]: sums of squares over runs of ssw columns
-  int ssw;                    // columns per combine run (>= 1, divides d; launch_moe checks)
+  int ssw;                    // columns per combine run: 16, 10 or 8, dividing d (launch_moe checks)
   void* xg_out;               // [M, d] bf16(x * gain_next)
   const void* gain_next;      // [d]
 };

@@ -22,20 +22,22 @@ __global__ __launch_bounds__(256) void embed_kernel(const int* __restrict__ tok,
   for (int i = threadIdx.x; i < d; i += 256) x[(size_t)m * d + i] = tof(row[i]);
 }
 
+template <int SSW>
 __global__ __launch_bounds__(256) void embed_norm_kernel(const int* __restrict__ tok, const uint16_t* __restrict__ emb,
                                                          float* __restrict__ x, int d, const uint16_t* __restrict__ g,
-                                                         uint16_t* __restrict__ xg, float* __restrict__ ss, int ssw) {
+                                                         uint16_t* __restrict__ xg, float* __restrict__ ss) {
   const int m = blockIdx.x;
   const uint16_t* row = emb + (size_t)tok[m] * d;
-  for (int c0 = threadIdx.x * ssw; c0 < d; c0 += 256 * ssw) {
+  for (int c0 = threadIdx.x * SSW; c0 < d; c0 += 256 * SSW) {
     float q = 0.f;
-    for (int j = 0; j < ssw; ++j) {
+#pragma unroll
+    for (int j = 0; j < SSW; ++j) {
       const float v = bf2f(row[c0 + j]);
       x[(size_t)m * d + c0 + j] = v;
       xg[(size_t)m * d + c0 + j] = f2bf(v * bf2f(g[c0 + j]));
       q = fmaf(v, v, q);
     }
-    ss[(size_t)m * (d / ssw) + c0 / ssw] = q;
+    ss[(size_t)m * (d / SSW) + c0 / SSW] = q;
   }
 }
 
@@ -553,8 +555,14 @@ hipError_t launch_embed(int dtype, const int* tok, const void* E, float* x, int 
 
 hipError_t launch_embed_norm(const int* tok, const void* E, float* x, int d, int M, const void* gain, void* xg,
                              float* ss, int ssw, hipStream_t s) {
-  if (ssw < 1 || d % ssw != 0) return hipErrorInvalidValue;
-  embed_norm_kernel<<<M, 256, 0, s>>>(tok, (const uint16_t*)E, x, d, (const uint16_t*)gain, (uint16_t*)xg, ss, ssw);
+  if (d % ssw != 0) return hipErrorInvalidValue;
+  const uint16_t *e16 = (const uint16_t*)E, *g16 = (const uint16_t*)gain;
+  switch (ssw) {   // the residual tile widths (resid_tile_width)
+    case 16: embed_norm_kernel<16><<<M, 256, 0, s>>>(tok, e16, x, d, g16, (uint16_t*)xg, ss); break;
+    case 10: embed_norm_kernel<10><<<M, 256, 0, s>>>(tok, e16, x, d, g16, (uint16_t*)xg, ss); break;
+    case 8: embed_norm_kernel<8><<<M, 256, 0, s>>>(tok, e16, x, d, g16, (uint16_t*)xg, ss); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

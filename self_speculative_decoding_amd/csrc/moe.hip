@@ -198,13 +198,15 @@ __global__ __launch_bounds__(256) void moe_gemm_kernel(MoeArgs a) {
 // x[m] += sum_j gate[m][j] * y[m][j] + sum_s y[m][top_k + s], in slot order.
 // A thread owns ssw consecutive columns; with ss_out set it also leaves their
 // sum of squares and bf16(x * gain_next) for the next layer's folded norm.
+template <int SSW>
 __global__ __launch_bounds__(256) void moe_combine_kernel(MoeArgs a) {
   const int m = blockIdx.x;
   const int slots = a.top_k + a.n_shared;
   const float* y = a.slot_out + (size_t)m * slots * a.d;
-  for (int c0 = threadIdx.x * a.ssw; c0 < a.d; c0 += 256 * a.ssw) {
+  for (int c0 = threadIdx.x * SSW; c0 < a.d; c0 += 256 * SSW) {
     float q = 0.f;
-    for (int i = c0; i < c0 + a.ssw; ++i) {
+#pragma unroll
+    for (int i = c0; i < c0 + SSW; ++i) {
       float acc = 0.f;
       for (int j = 0; j < a.top_k; ++j) acc += a.gates[(size_t)m * a.top_k + j] * y[(size_t)j * a.d + i];
       for (int s = 0; s < a.n_shared; ++s) acc += y[(size_t)(a.top_k + s) * a.d + i];
@@ -215,14 +217,14 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(MoeArgs a) {
         ((uint16_t*)a.xg_out)[(size_t)m * a.d + i] = f2bf(xv * bf2f(((const uint16_t*)a.gain_next)[i]));
       }
     }
-    if (a.ss_out) a.ss_out[(size_t)m * (a.d / a.ssw) + c0 / a.ssw] = q;
+    if (a.ss_out) a.ss_out[(size_t)m * (a.d / SSW) + c0 / SSW] = q;
   }
 }
 
 hipError_t launch_moe(int dtype, const MoeArgs& a, hipStream_t s) {
   if (dtype != 1) return hipErrorNotSupported;
-  // the combine walks each row in runs of ssw columns
-  if (a.ssw < 1 || a.d % a.ssw != 0) return hipErrorInvalidValue;
+  // the combine walks each row in runs of ssw columns (a residual tile width)
+  if ((a.ssw != 16 && a.ssw != 10 && a.ssw != 8) || a.d % a.ssw != 0) return hipErrorInvalidValue;
   GemmArgs r{};
   r.X = a.X; r.ldx = a.d; r.W0 = a.router; r.M = a.M; r.N = a.E; r.K = a.d; r.y = a.rlogits; r.ldy = a.E;
   hipError_t e = launch_gemm(1, EPI_F32, r, s);
@@ -232,7 +234,9 @@ hipError_t launch_moe(int dtype, const MoeArgs& a, hipStream_t s) {
   const int max_units = a.M * a.top_k + ((a.M + 15) / 16) * a.n_shared;
   moe_gemm_kernel<0><<<dim3(a.fe / 16, max_units), 256, 0, s>>>(a);
   moe_gemm_kernel<1><<<dim3(a.d / 16, max_units), 256, 0, s>>>(a);
-  moe_combine_kernel<<<a.M, 256, 0, s>>>(a);
+  if (a.ssw == 16) moe_combine_kernel<16><<<a.M, 256, 0, s>>>(a);
+  else if (a.ssw == 10) moe_combine_kernel<10><<<a.M, 256, 0, s>>>(a);
+  else moe_combine_kernel<8><<<a.M, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 
