@@ -41,6 +41,15 @@
 #ifndef SSD_KW_LONGK_NARROW  // waves (one 64-element chunk per load batch) of K >= 8192 GEMMs in narrow tiles
 #define SSD_KW_LONGK_NARROW 16
 #endif
+#ifndef SSD_TILE_WG_MIN      // long-pass tile kernel: fewest workgroups a wider column group may leave
+#define SSD_TILE_WG_MIN 512
+#endif
+#ifndef SSD_TILE_P1          // long-pass tile kernel: chunks in flight per wave x weight streams
+#define SSD_TILE_P1 8
+#endif
+#ifndef SSD_TILE_WPE         // long-pass tile kernel: waves per SIMD the register allocation aims at
+#define SSD_TILE_WPE 2
+#endif
 #ifndef SSD_KW_WIDE
 #define SSD_KW_WIDE 8
 #endif
@@ -108,6 +117,24 @@ template <typename E>
 __device__ __forceinline__ void epi_v_single(const GemmArgs& a, int base, int m, int vh, int dim, float v) {
   const int pos = base + m;
   ((E*)a.vc)[((size_t)vh * a.hd + dim) * a.max_ctx + pos] = fromf<E>(v);   // [kv head][dim][position]
+}
+
+// New residual value xv of row m, column n of column tile tt (xv = 0 where
+// ok is false: rows past M, lanes past a narrow tile): stores it, its bf16
+// tap and the next GEMM's input bf16(xv * gain), and the tile's sum of
+// squares (a butterfly over the 16 lanes of the tile; every lane of the wave
+// must call this, lane c == 0 writes).
+__device__ __forceinline__ void epi_resid_fold(const GemmArgs& a, int m, int n, int tt, int ntiles, int c, bool ok,
+                                               float xv) {
+  float sq = xv * xv;
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) sq += __shfl_xor(sq, o);
+  if (ok) {
+    a.y[(size_t)m * a.ldy + n] = xv;
+    if (a.tap) ((uint16_t*)a.tap)[(size_t)m * a.ldtap + n] = f2bf(xv);
+    ((uint16_t*)a.xg_out)[(size_t)m * a.ldy + n] = f2bf(xv * bf2f(((const uint16_t*)a.gain_next)[n]));
+    if (c == 0) a.ss_out[(size_t)m * ntiles + tt] = sq;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -403,17 +430,9 @@ __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
         if (EPI == EPI_RESID && a.ss_out) {
           // new residual, its sum of squares over this tile's 16 columns and
           // bf16(x * gain) for the GEMM that consumes it
-          const bool col = c < TW;
-          const float xv = m < a.M && col ? (MT == 1 ? yv[j][i] : a.y[(size_t)m * a.ldy + n]) + acc[r][j][i] : 0.f;
-          float sq = xv * xv;
-#pragma unroll
-          for (int o = 1; o < 16; o <<= 1) sq += __shfl_xor(sq, o);
-          if (m < a.M && col) {
-            a.y[(size_t)m * a.ldy + n] = xv;
-            if (a.tap) ((uint16_t*)a.tap)[(size_t)m * a.ldtap + n] = f2bf(xv);
-            ((uint16_t*)a.xg_out)[(size_t)m * a.ldy + n] = f2bf(xv * bf2f(((const uint16_t*)a.gain_next)[n]));
-            if (c == 0) a.ss_out[(size_t)m * ntiles + tt] = sq;
-          }
+          const bool ok = m < a.M && c < TW;
+          const float xv = ok ? (MT == 1 ? yv[j][i] : a.y[(size_t)m * a.ldy + n]) + acc[r][j][i] : 0.f;
+          epi_resid_fold(a, m, n, tt, ntiles, c, ok, xv);
           continue;
         }
         if (m >= a.M || c >= TW) continue;
@@ -425,6 +444,163 @@ __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
       }
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// gate/up GEMM + SwiGLU of long passes (prefill chunks, M > 32) on MFMA
+// 16x16x32 with the A operand staged through LDS.
+//
+// A workgroup of 4 waves owns 64 rows (4 row tiles) and 4 * NTW column tiles;
+// wave w owns tiles t0 + w*NTW .. t0 + w*NTW + NTW - 1 (gate and up streams
+// of each) for all 64 rows.  Every output element accumulates its MFMA
+// K-steps in K order over the whole K range: no K split, no cross-wave
+// reduction, and nothing depends on M or on the grouping.  Per 64-element K
+// chunk the workgroup copies the 64 x 64 A block into one of two LDS buffers
+// (one barrier per chunk) while each wave keeps the A pieces and weight
+// fragments of the next P - 1 chunks in flight in registers (P = 8 / streams,
+// at least 2); a wave reads its A fragments from LDS once per chunk for all
+// its column tiles and reuses each weight fragment for the 4 row tiles.
+// Measured at 256 rows (8B shape): 209 -> 131 us against the multi-row-tile
+// kernel; the one-matrix GEMMs (QKV, o, down: fewer column tiles, down with
+// 224 chunks per wave) ran no faster this way and keep that kernel.
+// ---------------------------------------------------------------------------
+constexpr int TILE_WAVES = 4;
+constexpr int TILE_MT = 4;
+constexpr int TILE_LDA = 64 + 8;   // LDS row stride of the A block (elements): rows 144 B apart
+
+template <int TW, int NTW>
+__global__ __launch_bounds__(64 * TILE_WAVES) __attribute__((amdgpu_waves_per_eu(SSD_TILE_WPE)))
+void gemm_swiglu_tile_kernel(GemmArgs a) {
+  constexpr int NW = 2, MT = TILE_MT, NS = NW * NTW, TE = TW * 64, CS = NW * TE;
+  constexpr int P = NS >= 4 ? 2 : SSD_TILE_P1 / NS;   // chunks in flight per wave
+  static_assert(P >= 2 && P % 2 == 0, "the LDS buffer of chunk s is s & 1");
+  constexpr int ROWS = 16 * MT;
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][ROWS * TILE_LDA];
+  __shared__ float rs[ROWS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = lane & 15, kg = lane >> 4;
+  // workgroup -> (column group bx, row block by), optionally as the XCD-aware
+  // 1-D launch of gemm_bf16_kernel
+  int bx = blockIdx.x, by = blockIdx.y;
+  if (a.remap_gx > 0) {
+    const int L = blockIdx.x, q = L >> 3;
+    by = q % a.remap_rb;
+    bx = (q / a.remap_rb) * 8 + (L & 7);
+  }
+  const int t0 = (bx * TILE_WAVES + wave) * NTW;   // this wave's first column tile
+  const int row0 = by * ROWS;
+  const int S = a.K >> 6;
+
+  // weight streams: stream j = matrix j % 2 (gate, up) of column tile t0 + j / 2
+  const uint16_t* wr[NS];
+  const int lo = (TW * kg + min(c, TW - 1)) * 8;
+#pragma unroll
+  for (int j = 0; j < NS; ++j)
+    wr[j] = (const uint16_t*)a.W0 + ((size_t)(t0 + j / NW) * S * NW + j % NW) * TE + lo;
+
+  // A block copy: 64 rows x 64 elements = 512 pieces of 16 bytes, two per
+  // thread (piece p: row p / 8, elements 8 * (p % 8) ..)
+  const uint16_t* ag[2];
+  bool aok[2];
+  int aoff[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int p = tid + 64 * TILE_WAVES * i, r = p >> 3, cc = p & 7;
+    aok[i] = row0 + r < a.M;
+    ag[i] = (const uint16_t*)a.X + (size_t)(aok[i] ? row0 + r : 0) * a.ldx + cc * 8;
+    aoff[i] = r * TILE_LDA + cc * 8;
+  }
+  const uint4 zero = {0u, 0u, 0u, 0u};
+  uint4 areg[P][2];
+  uint4 wb[P][NS][2];
+  f32x4 acc[MT][NS];
+#pragma unroll
+  for (int r = 0; r < MT; ++r)
+#pragma unroll
+    for (int j = 0; j < NS; ++j) acc[r][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto load_a = [&](uint4 (&ar)[2], int s) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) ar[i] = aok[i] ? ld16(ag[i] + (size_t)s * 64) : zero;
+  };
+  auto store_a = [&](int buf, const uint4 (&ar)[2]) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) *(uint4*)(&As[buf][aoff[i]]) = ar[i];
+  };
+  auto load_w = [&](uint4 (&w)[NS][2], int s) {   // cached loads: the row blocks share the tiles
+#pragma unroll
+    for (int j = 0; j < NS; ++j)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) w[j][h] = ld16(wr[j] + (size_t)s * CS + h * (TE / 2));
+  };
+  // lane (c, kg) of row tile r reads row 16r + c, elements 16kg + 8h .. + 7
+  // of the chunk: the MFMA A fragment of K-step h
+  auto compute = [&](int buf, const uint4 (&w)[NS][2]) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint4 af[MT];
+#pragma unroll
+      for (int r = 0; r < MT; ++r) af[r] = *(const uint4*)(&As[buf][(16 * r + c) * TILE_LDA + 16 * kg + 8 * h]);
+#pragma unroll
+      for (int r = 0; r < MT; ++r)
+#pragma unroll
+        for (int j = 0; j < NS; ++j)
+          acc[r][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af[r]),
+                                                              __builtin_bit_cast(bf16x8, w[j][h]), acc[r][j], 0, 0, 0);
+    }
+  };
+
+  // chunk s: A pieces areg[s % P] -> LDS buffer s & 1, weights wb[s % P].
+  // Iteration s issues the loads of chunk s + P - 1, computes chunk s and
+  // moves chunk s + 1's A pieces into the other LDS buffer (whose chunk s - 1
+  // every wave finished before the previous barrier).  Unrolled by P so that
+  // every register index is static.
+#pragma unroll
+  for (int u = 0; u < P - 1; ++u)
+    if (u < S) {
+      load_a(areg[u], u);
+      load_w(wb[u], u);
+    }
+  store_a(0, areg[0]);
+  __syncthreads();
+  for (int s0 = 0; s0 < S; s0 += P) {
+#pragma unroll
+    for (int u = 0; u < P; ++u) {
+      const int s = s0 + u;
+      if (s >= S) break;
+      if (s + P - 1 < S) {
+        load_a(areg[(u + P - 1) % P], s + P - 1);
+        load_w(wb[(u + P - 1) % P], s + P - 1);
+      }
+      compute(u & 1, wb[u]);
+      if (s + 1 < S) store_a((u + 1) & 1, areg[(u + 1) % P]);
+      __syncthreads();
+    }
+  }
+
+  // folded RMSNorm: wave w finds rstd of rows w, w + 4, ...
+  const bool fold = a.ss_in != nullptr;
+  if (fold) {
+#pragma unroll 1
+    for (int r = 0; r < ROWS / TILE_WAVES; ++r) {
+      const int row = r * TILE_WAVES + wave, m = row0 + row;
+      const float f = ss_rstd(a, m, true, lane, ss_part(a, m, true, lane));
+      if (lane == 0) rs[row] = f;
+    }
+  }
+  __syncthreads();
+  // epilogue: each wave finishes its own column tiles for all 64 rows
+#pragma unroll
+  for (int r = 0; r < MT; ++r)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = row0 + 16 * r + 4 * kg + i;
+      const float f = fold ? rs[16 * r + 4 * kg + i] : 1.f;
+#pragma unroll
+      for (int j = 0; j < NTW; ++j)
+        if (m < a.M && c < TW)
+          epi_swiglu<uint16_t>(a, m, (t0 + j) * TW + c, acc[r][j * NW][i] * f, acc[r][j * NW + 1][i] * f);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -540,6 +716,31 @@ hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t s) {
     else tiles = a.N / tw;
     dim3 grid(tiles, mt);
     const bool wide = tiles >= 1024;   // a function of N only
+    // gate/up of long passes (prefill chunks): the LDS-staged tile kernel,
+    // 64 rows x 4*ntw column tiles per workgroup, ntw = 2 where that still
+    // leaves SSD_TILE_WG_MIN workgroups (the grouping never changes a result)
+    if (a.M > 32 && epi == EPI_SWIGLU && tiles % TILE_WAVES == 0) {
+      const int rbt = (a.M + 16 * TILE_MT - 1) / (16 * TILE_MT);
+      const int ntw = tiles % (TILE_WAVES * 2) == 0 && (tiles / (TILE_WAVES * 2)) * rbt >= SSD_TILE_WG_MIN ? 2 : 1;
+      const int gx = tiles / (TILE_WAVES * ntw);
+      GemmArgs at = a;
+      at.remap_gx = at.remap_rb = 0;
+      dim3 g(gx, rbt);
+      if (gx % 8 == 0 && rbt > 1) {   // XCD-aware 1-D launch (see gemm_bf16_kernel)
+        at.remap_gx = gx;
+        at.remap_rb = rbt;
+        g = dim3(gx * rbt, 1);
+      }
+      const dim3 blk(64 * TILE_WAVES);
+      if (tw == 14) {
+        if (ntw == 2) gemm_swiglu_tile_kernel<14, 2><<<g, blk, 0, s>>>(at);
+        else gemm_swiglu_tile_kernel<14, 1><<<g, blk, 0, s>>>(at);
+      } else {
+        if (ntw == 2) gemm_swiglu_tile_kernel<16, 2><<<g, blk, 0, s>>>(at);
+        else gemm_swiglu_tile_kernel<16, 1><<<g, blk, 0, s>>>(at);
+      }
+      return hipGetLastError();
+    }
     // decode-loop passes (M <= SSD_MAX_BLOCK rows) always take the one-tile
     // kernel, so a row's arithmetic never depends on the pass width; longer
     // passes (prefill chunks) let 4 row tiles share each weight load

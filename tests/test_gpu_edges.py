@@ -225,12 +225,13 @@ def test_long_context_combine_batches():
 
 
 def test_prefill_column_groups_bitwise_across_chunkings():
-    """Long prefill chunks group column tiles per workgroup (256-row chunks
-    here: QKV and gate/up tiles in pairs); 64-row chunks do not.
-    Both take the multi-row-tile kernel, whose per-row arithmetic does not
-    depend on the grouping or the chunk, so the last-row logits and the KV
-    cache agree bit for bit; the logits match the oracle."""
-    cfg = _edge_cfg(n_layers=2, d_model=1024, n_q_heads=16, n_kv_heads=4, ffn_dim=4096,
+    """Long prefill chunks group column tiles per workgroup; 64-row chunks do
+    not (256-row chunks here: QKV tiles in pairs in the multi-row-tile kernel,
+    and the gate/up tile kernel, 14-row tiles of FFN 14336, takes two column
+    tiles per wave).  The per-row arithmetic of both kernels depends neither
+    on the grouping nor on the chunk, so the last-row logits and the KV cache
+    agree bit for bit; the logits match the oracle."""
+    cfg = _edge_cfg(n_layers=2, d_model=1024, n_q_heads=16, n_kv_heads=4, ffn_dim=14336,
                     max_ctx=700, prompt_len=640, cid=76)
     w = synth.make_weights(cfg, seed=12)
     prompt = synth.make_prompt(cfg)
