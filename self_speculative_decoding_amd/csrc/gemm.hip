@@ -47,6 +47,15 @@
 #ifndef SSD_TILE_P1          // long-pass tile kernel: chunks in flight per wave x weight streams
 #define SSD_TILE_P1 8
 #endif
+#ifndef SSD_TILE_PA          // long-pass tile kernel: A chunks in flight per thread
+#define SSD_TILE_PA 4
+#endif
+#ifndef SSD_TILE_MT          // long-pass tile kernel: 16-row tiles per workgroup (even)
+#define SSD_TILE_MT 4
+#endif
+#ifndef SSD_TILE_PB4         // long-pass tile kernel: weight chunks in flight with 4 streams per wave
+#define SSD_TILE_PB4 2
+#endif
 #ifndef SSD_TILE_WPE         // long-pass tile kernel: waves per SIMD the register allocation aims at
 #define SSD_TILE_WPE 2
 #endif
@@ -456,24 +465,43 @@ __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
 // K-steps in K order over the whole K range: no K split, no cross-wave
 // reduction, and nothing depends on M or on the grouping.  Per 64-element K
 // chunk the workgroup copies the 64 x 64 A block into one of two LDS buffers
-// (one barrier per chunk) while each wave keeps the A pieces and weight
-// fragments of the next P - 1 chunks in flight in registers (P = 8 / streams,
-// at least 2); a wave reads its A fragments from LDS once per chunk for all
-// its column tiles and reuses each weight fragment for the 4 row tiles.
+// (one barrier per chunk) while each thread keeps the A pieces of the next
+// PA - 1 chunks and each wave the weight fragments of the next PB - 1 chunks
+// in flight in registers (PB = 8 / streams, at least 2); a wave reads its A
+// fragments from LDS once per chunk for all its column tiles and reuses each
+// weight fragment for the 4 row tiles.
 // Measured at 256 rows (8B shape): 209 -> 131 us against the multi-row-tile
 // kernel; the one-matrix GEMMs (QKV, o, down: fewer column tiles, down with
 // 224 chunks per wave) ran no faster this way and keep that kernel.
 // ---------------------------------------------------------------------------
 constexpr int TILE_WAVES = 4;
-constexpr int TILE_MT = 4;
-constexpr int TILE_LDA = 64 + 8;   // LDS row stride of the A block (elements): rows 144 B apart
+constexpr int TILE_MT = SSD_TILE_MT;   // row tiles per workgroup
+constexpr int TILE_LDA = 64 + 8;       // LDS row stride of the A block (elements): rows 144 B apart
+
+constexpr int tile_lcm(int x, int y) {
+  int a = x, b = y;
+  while (b) {
+    const int t = a % b;
+    a = b;
+    b = t;
+  }
+  return x / a * y;
+}
+// ring depths of a wave with ns weight streams, and the unroll that makes
+// every ring index static (the K chunks must be a multiple of it)
+constexpr int tile_pb(int ns) { return ns >= 4 ? SSD_TILE_PB4 : SSD_TILE_P1 / ns; }
+constexpr int tile_unroll(int ns) { return tile_lcm(tile_lcm(SSD_TILE_PA, tile_pb(ns)), 2); }
 
 template <int TW, int NTW>
 __global__ __launch_bounds__(64 * TILE_WAVES) __attribute__((amdgpu_waves_per_eu(SSD_TILE_WPE)))
 void gemm_swiglu_tile_kernel(GemmArgs a) {
   constexpr int NW = 2, MT = TILE_MT, NS = NW * NTW, TE = TW * 64, CS = NW * TE;
-  constexpr int P = NS >= 4 ? 2 : SSD_TILE_P1 / NS;   // chunks in flight per wave
-  static_assert(P >= 2 && P % 2 == 0, "the LDS buffer of chunk s is s & 1");
+  constexpr int NA = MT / 2;                           // 16-byte A pieces per thread and chunk
+  static_assert(MT % 2 == 0, "A block copy");
+  constexpr int PB = tile_pb(NS);      // weight chunks in flight per wave
+  constexpr int PA = SSD_TILE_PA;      // A chunks in flight (4 * NA registers each)
+  constexpr int U = tile_unroll(NS);
+  static_assert(PB >= 2 && PA >= 2, "ring depths");
   constexpr int ROWS = 16 * MT;
   __shared__ __attribute__((aligned(16))) uint16_t As[2][ROWS * TILE_LDA];
   __shared__ float rs[ROWS];
@@ -498,34 +526,43 @@ void gemm_swiglu_tile_kernel(GemmArgs a) {
   for (int j = 0; j < NS; ++j)
     wr[j] = (const uint16_t*)a.W0 + ((size_t)(t0 + j / NW) * S * NW + j % NW) * TE + lo;
 
-  // A block copy: 64 rows x 64 elements = 512 pieces of 16 bytes, two per
-  // thread (piece p: row p / 8, elements 8 * (p % 8) ..)
-  const uint16_t* ag[2];
-  bool aok[2];
-  int aoff[2];
+  // A block copy: 16*MT rows x 64 elements = 128*MT pieces of 16 bytes, NA
+  // per thread (piece p: row p / 8, elements 8 * (p % 8) ..)
+  const uint16_t* ag[NA];
+  bool aok[NA];
+  int aoff[NA];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < NA; ++i) {
     const int p = tid + 64 * TILE_WAVES * i, r = p >> 3, cc = p & 7;
     aok[i] = row0 + r < a.M;
     ag[i] = (const uint16_t*)a.X + (size_t)(aok[i] ? row0 + r : 0) * a.ldx + cc * 8;
     aoff[i] = r * TILE_LDA + cc * 8;
   }
   const uint4 zero = {0u, 0u, 0u, 0u};
-  uint4 areg[P][2];
-  uint4 wb[P][NS][2];
+  uint4 areg[PA][NA];
+  uint4 wb[PB][NS][2];
   f32x4 acc[MT][NS];
 #pragma unroll
   for (int r = 0; r < MT; ++r)
 #pragma unroll
     for (int j = 0; j < NS; ++j) acc[r][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto load_a = [&](uint4 (&ar)[2], int s) {
+  // every load below is unconditional (rows past M read row 0 and are
+  // masked to zero, chunk indexes past the end are clamped): branches in the
+  // loop would make the compiler drain all loads in flight at each chunk
+  unsigned amask[NA];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) ar[i] = aok[i] ? ld16(ag[i] + (size_t)s * 64) : zero;
+  for (int i = 0; i < NA; ++i) amask[i] = aok[i] ? ~0u : 0u;
+  auto load_a = [&](uint4 (&ar)[NA], int s) {
+#pragma unroll
+    for (int i = 0; i < NA; ++i) ar[i] = ld16(ag[i] + (size_t)s * 64);
   };
-  auto store_a = [&](int buf, const uint4 (&ar)[2]) {
+  auto store_a = [&](int buf, const uint4 (&ar)[NA]) {   // masked here, where the data is due anyway
 #pragma unroll
-    for (int i = 0; i < 2; ++i) *(uint4*)(&As[buf][aoff[i]]) = ar[i];
+    for (int i = 0; i < NA; ++i) {
+      const uint4 v = ar[i];
+      *(uint4*)(&As[buf][aoff[i]]) = uint4{v.x & amask[i], v.y & amask[i], v.z & amask[i], v.w & amask[i]};
+    }
   };
   auto load_w = [&](uint4 (&w)[NS][2], int s) {   // cached loads: the row blocks share the tiles
 #pragma unroll
@@ -550,30 +587,30 @@ void gemm_swiglu_tile_kernel(GemmArgs a) {
     }
   };
 
-  // chunk s: A pieces areg[s % P] -> LDS buffer s & 1, weights wb[s % P].
-  // Iteration s issues the loads of chunk s + P - 1, computes chunk s and
+  // chunk s: A pieces areg[s % PA] -> LDS buffer s & 1, weights wb[s % PB].
+  // Iteration s issues the A loads of chunk s + PA - 1 and the weight loads
+  // of chunk s + PB - 1 (clamped to the last chunk), computes chunk s and
   // moves chunk s + 1's A pieces into the other LDS buffer (whose chunk s - 1
-  // every wave finished before the previous barrier).  Unrolled by P so that
-  // every register index is static.
+  // every wave finished before the previous barrier).  The launcher
+  // guarantees S % U == 0.
+  const int last = S - 1;
 #pragma unroll
-  for (int u = 0; u < P - 1; ++u)
-    if (u < S) {
-      load_a(areg[u], u);
-      load_w(wb[u], u);
-    }
+  for (int u = 0; u < PA - 1; ++u) load_a(areg[u], min(u, last));
+#pragma unroll
+  for (int u = 0; u < PB - 1; ++u) load_w(wb[u], min(u, last));
   store_a(0, areg[0]);
   __syncthreads();
-  for (int s0 = 0; s0 < S; s0 += P) {
+  for (int s0 = 0; s0 < S; s0 += U) {
 #pragma unroll
-    for (int u = 0; u < P; ++u) {
+    for (int u = 0; u < U; ++u) {
       const int s = s0 + u;
-      if (s >= S) break;
-      if (s + P - 1 < S) {
-        load_a(areg[(u + P - 1) % P], s + P - 1);
-        load_w(wb[(u + P - 1) % P], s + P - 1);
-      }
-      compute(u & 1, wb[u]);
-      if (s + 1 < S) store_a((u + 1) & 1, areg[(u + 1) % P]);
+      load_a(areg[(u + PA - 1) % PA], min(s + PA - 1, last));
+      load_w(wb[(u + PB - 1) % PB], min(s + PB - 1, last));
+      // keep the prefetch loads ahead of this chunk's MFMAs (the scheduler
+      // would otherwise sink them towards their uses and wait on them)
+      __builtin_amdgcn_sched_barrier(0);
+      compute(u & 1, wb[u % PB]);
+      store_a((u + 1) & 1, areg[(u + 1) % PA]);
       __syncthreads();
     }
   }
@@ -719,7 +756,8 @@ hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t s) {
     // gate/up of long passes (prefill chunks): the LDS-staged tile kernel,
     // 64 rows x 4*ntw column tiles per workgroup, ntw = 2 where that still
     // leaves SSD_TILE_WG_MIN workgroups (the grouping never changes a result)
-    if (a.M > 32 && epi == EPI_SWIGLU && tiles % TILE_WAVES == 0) {
+    constexpr int tile_u = tile_lcm(tile_unroll(2), tile_unroll(4));   // either grouping
+    if (a.M > 32 && epi == EPI_SWIGLU && tiles % TILE_WAVES == 0 && (a.K / 64) % tile_u == 0) {
       const int rbt = (a.M + 16 * TILE_MT - 1) / (16 * TILE_MT);
       const int ntw = tiles % (TILE_WAVES * 2) == 0 && (tiles / (TILE_WAVES * 2)) * rbt >= SSD_TILE_WG_MIN ? 2 : 1;
       const int gx = tiles / (TILE_WAVES * ntw);
