@@ -456,23 +456,23 @@ __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// gate/up GEMM + SwiGLU of long passes (prefill chunks, M > 32) on MFMA
-// 16x16x32 with the A operand staged through LDS.
+// Layer GEMMs of long passes (prefill chunks, M > 32: QKV + RoPE + KV append,
+// gate/up + SwiGLU, o and down + residual) on MFMA 16x16x32 with the A
+// operand staged through LDS.
 //
-// A workgroup of 4 waves owns 64 rows (4 row tiles) and 4 * NTW column tiles;
-// wave w owns tiles t0 + w*NTW .. t0 + w*NTW + NTW - 1 (gate and up streams
-// of each) for all 64 rows.  Every output element accumulates its MFMA
-// K-steps in K order over the whole K range: no K split, no cross-wave
-// reduction, and nothing depends on M or on the grouping.  Per 64-element K
-// chunk the workgroup copies the 64 x 64 A block into one of two LDS buffers
-// (one barrier per chunk) while each thread keeps the A pieces of the next
-// PA - 1 chunks and each wave the weight fragments of the next PB - 1 chunks
-// in flight in registers (PB = 8 / streams, at least 2); a wave reads its A
-// fragments from LDS once per chunk for all its column tiles and reuses each
-// weight fragment for the 4 row tiles.
-// Measured at 256 rows (8B shape): 209 -> 131 us against the multi-row-tile
-// kernel; the one-matrix GEMMs (QKV, o, down: fewer column tiles, down with
-// 224 chunks per wave) ran no faster this way and keep that kernel.
+// A workgroup of 4 waves owns 16*MT rows and 4 * NTW column tiles; wave w
+// owns tiles t0 + w*NTW .. t0 + w*NTW + NTW - 1 (both gate/up streams of
+// each) for all the rows.  Every output element accumulates its MFMA K-steps
+// in K order over the whole K range: no K split, no cross-wave reduction,
+// and nothing depends on M or on the grouping.  Per 64-element K chunk the
+// workgroup copies the A block into one of two LDS buffers (one barrier per
+// chunk) while each thread keeps the A pieces of the next PA - 1 chunks and
+// each wave the weight fragments of the next PB - 1 chunks in flight in
+// registers (PB = 8 / streams, at least 2); a wave reads its A fragments from
+// LDS once per chunk for all its column tiles and reuses each weight fragment
+// for every row tile.  Measured at 256 rows (8B shape) against the
+// multi-row-tile kernel: gate/up 209 -> 99 us, down 144 -> 74, QKV 66 -> 46,
+// o 51 -> 29.
 // ---------------------------------------------------------------------------
 constexpr int TILE_WAVES = 4;
 constexpr int TILE_MT = SSD_TILE_MT;   // row tiles per workgroup
@@ -492,10 +492,12 @@ constexpr int tile_lcm(int x, int y) {
 constexpr int tile_pb(int ns) { return ns >= 4 ? SSD_TILE_PB4 : SSD_TILE_P1 / ns; }
 constexpr int tile_unroll(int ns) { return tile_lcm(tile_lcm(SSD_TILE_PA, tile_pb(ns)), 2); }
 
-template <int TW, int NTW>
+template <int EPI, int TW, int NTW>
 __global__ __launch_bounds__(64 * TILE_WAVES) __attribute__((amdgpu_waves_per_eu(SSD_TILE_WPE)))
-void gemm_swiglu_tile_kernel(GemmArgs a) {
-  constexpr int NW = 2, MT = TILE_MT, NS = NW * NTW, TE = TW * 64, CS = NW * TE;
+void gemm_tile_kernel(GemmArgs a) {
+  static_assert(EPI == EPI_QKV || EPI == EPI_SWIGLU || EPI == EPI_RESID, "layer GEMM epilogues");
+  constexpr int NW = EPI == EPI_SWIGLU ? 2 : 1;   // gate/up: two interleaved streams per tile
+  constexpr int MT = TILE_MT, NS = NW * NTW, TE = TW * 64, CS = NW * TE;
   constexpr int NA = MT / 2;                           // 16-byte A pieces per thread and chunk
   static_assert(MT % 2 == 0, "A block copy");
   constexpr int PB = tile_pb(NS);      // weight chunks in flight per wave
@@ -519,7 +521,7 @@ void gemm_swiglu_tile_kernel(GemmArgs a) {
   const int row0 = by * ROWS;
   const int S = a.K >> 6;
 
-  // weight streams: stream j = matrix j % 2 (gate, up) of column tile t0 + j / 2
+  // weight streams: stream j = matrix j % NW (gate, up) of column tile t0 + j / NW
   const uint16_t* wr[NS];
   const int lo = (TW * kg + min(c, TW - 1)) * 8;
 #pragma unroll
@@ -626,17 +628,68 @@ void gemm_swiglu_tile_kernel(GemmArgs a) {
     }
   }
   __syncthreads();
-  // epilogue: each wave finishes its own column tiles for all 64 rows
+  if (fold) {
+#pragma unroll
+    for (int r = 0; r < MT; ++r)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float f = rs[16 * r + 4 * kg + i];
+#pragma unroll
+        for (int j = 0; j < NS; ++j) acc[r][j][i] *= f;
+      }
+  }
+  // epilogue: each wave finishes its own column tiles for all its rows
+  int head[NTW], dim[NTW], kind[NTW];   // QKV output column of this lane (qkv_col_map)
+#pragma unroll
+  for (int j = 0; j < NTW; ++j) {
+    head[j] = dim[j] = 0;
+    kind[j] = 1;
+    if (EPI == EPI_QKV) {
+      const QkvCol q = qkv_col_map(TW, t0 + j, c, a.hq, a.hkv, a.hd);
+      head[j] = q.head;
+      dim[j] = q.dim;
+      kind[j] = q.kind;
+    }
+  }
+  const int base = EPI == EPI_QKV ? a.state[0] + a.pos_off : 0;
+  const int ntiles = (a.remap_gx > 0 ? a.remap_gx : gridDim.x) * TILE_WAVES * NTW;
 #pragma unroll
   for (int r = 0; r < MT; ++r)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = row0 + 16 * r + 4 * kg + i;
-      const float f = fold ? rs[16 * r + 4 * kg + i] : 1.f;
+    for (int j = 0; j < NTW; ++j) {
+      const int tt = t0 + j;
+      if (EPI == EPI_SWIGLU) {
 #pragma unroll
-      for (int j = 0; j < NTW; ++j)
-        if (m < a.M && c < TW)
-          epi_swiglu<uint16_t>(a, m, (t0 + j) * TW + c, acc[r][j * NW][i] * f, acc[r][j * NW + 1][i] * f);
+        for (int i = 0; i < 4; ++i) {
+          const int m = row0 + 16 * r + 4 * kg + i;
+          if (m < a.M && c < TW) epi_swiglu<uint16_t>(a, m, tt * TW + c, acc[r][j * NW][i], acc[r][j * NW + 1][i]);
+        }
+      } else if (EPI == EPI_QKV) {
+        // a pair's second element sits TW/2 lanes up (same 16-lane group)
+        float part[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) part[i] = __shfl(acc[r][j][i], (lane + TW / 2) & 63);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = row0 + 16 * r + 4 * kg + i;
+          if (m >= a.M) continue;
+          if (kind[j] == 0) epi_qkv_pair<uint16_t>(a, base, m, head[j], dim[j], acc[r][j][i], part[i]);
+          else if (kind[j] == 2) epi_v_single<uint16_t>(a, base, m, head[j] - a.hq - a.hkv, dim[j], acc[r][j][i]);
+        }
+      } else {   // EPI_RESID
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = row0 + 16 * r + 4 * kg + i;
+          const int n = tt * TW + c;
+          const bool ok = m < a.M && c < TW;
+          if (a.ss_out) {
+            const float xv = ok ? a.y[(size_t)m * a.ldy + n] + acc[r][j][i] : 0.f;
+            epi_resid_fold(a, m, n, tt, ntiles, c, ok, xv);
+          } else if (ok) {
+            epi_single<uint16_t>(a, EPI_RESID, m, n, acc[r][j][i]);
+          }
+        }
+      }
     }
 }
 
@@ -756,10 +809,18 @@ hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t s) {
     // gate/up of long passes (prefill chunks): the LDS-staged tile kernel,
     // 64 rows x 4*ntw column tiles per workgroup, ntw = 2 where that still
     // leaves SSD_TILE_WG_MIN workgroups (the grouping never changes a result)
-    constexpr int tile_u = tile_lcm(tile_unroll(2), tile_unroll(4));   // either grouping
-    if (a.M > 32 && epi == EPI_SWIGLU && tiles % TILE_WAVES == 0 && (a.K / 64) % tile_u == 0) {
+    // streams per wave: 1, 2 or 4 (gate/up: 2 or 4), any of which the
+    // grouping may pick, so the K chunks must suit every ring unroll
+    constexpr int tile_u = tile_lcm(tile_lcm(tile_unroll(1), tile_unroll(2)), tile_unroll(4));
+    const bool tile_epi = epi == EPI_QKV || epi == EPI_SWIGLU || epi == EPI_RESID;
+    if (a.M > 32 && tile_epi && tiles % TILE_WAVES == 0 && (a.K / 64) % tile_u == 0) {
       const int rbt = (a.M + 16 * TILE_MT - 1) / (16 * TILE_MT);
-      const int ntw = tiles % (TILE_WAVES * 2) == 0 && (tiles / (TILE_WAVES * 2)) * rbt >= SSD_TILE_WG_MIN ? 2 : 1;
+      int ntw = 1;
+      for (int v = epi == EPI_SWIGLU ? 2 : 4; v > 1; v >>= 1)
+        if (tiles % (TILE_WAVES * v) == 0 && (tiles / (TILE_WAVES * v)) * rbt >= SSD_TILE_WG_MIN) {
+          ntw = v;
+          break;
+        }
       const int gx = tiles / (TILE_WAVES * ntw);
       GemmArgs at = a;
       at.remap_gx = at.remap_rb = 0;
@@ -770,13 +831,20 @@ hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t s) {
         g = dim3(gx * rbt, 1);
       }
       const dim3 blk(64 * TILE_WAVES);
-      if (tw == 14) {
-        if (ntw == 2) gemm_swiglu_tile_kernel<14, 2><<<g, blk, 0, s>>>(at);
-        else gemm_swiglu_tile_kernel<14, 1><<<g, blk, 0, s>>>(at);
+#define SSD_T(E, TWV)                                                                 \
+  {                                                                                   \
+    if (ntw == 4) gemm_tile_kernel<E, TWV, E == EPI_SWIGLU ? 2 : 4><<<g, blk, 0, s>>>(at); \
+    else if (ntw == 2) gemm_tile_kernel<E, TWV, 2><<<g, blk, 0, s>>>(at);             \
+    else gemm_tile_kernel<E, TWV, 1><<<g, blk, 0, s>>>(at);                           \
+  }
+      if (epi == EPI_SWIGLU) {
+        if (tw == 14) SSD_T(EPI_SWIGLU, 14) else SSD_T(EPI_SWIGLU, 16)
+      } else if (epi == EPI_QKV) {
+        if (tw == 12) SSD_T(EPI_QKV, 12) else SSD_T(EPI_QKV, 16)
       } else {
-        if (ntw == 2) gemm_swiglu_tile_kernel<16, 2><<<g, blk, 0, s>>>(at);
-        else gemm_swiglu_tile_kernel<16, 1><<<g, blk, 0, s>>>(at);
+        if (tw == 10) SSD_T(EPI_RESID, 10) else if (tw == 8) SSD_T(EPI_RESID, 8) else SSD_T(EPI_RESID, 16)
       }
+#undef SSD_T
       return hipGetLastError();
     }
     // decode-loop passes (M <= SSD_MAX_BLOCK rows) always take the one-tile
