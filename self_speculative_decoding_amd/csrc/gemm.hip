@@ -146,6 +146,24 @@ __device__ __forceinline__ void epi_resid_fold(const GemmArgs& a, int m, int n, 
   }
 }
 
+// Workgroup -> (column group bx, row block by, column groups gx) of a GEMM
+// launch.  A 1-D launch of remap_gx x remap_rb workgroups (set by the
+// launcher) maps the row blocks sharing a column group's weights to one XCD
+// (workgroups go to the 8 XCDs in turn), dispatched one after another, so
+// that XCD's L2 serves the weight tiles to all of them; the mapping never
+// changes what a workgroup computes.
+struct BlockPos {
+  int bx, by, gx;
+};
+template <bool MAY_REMAP>   // false: launches that never come as the 1-D launch
+__device__ __forceinline__ BlockPos block_pos(const GemmArgs& a) {
+  if (MAY_REMAP && a.remap_gx > 0) {
+    const int L = blockIdx.x, q = L >> 3;
+    return BlockPos{(q / a.remap_rb) * 8 + (L & 7), q % a.remap_rb, a.remap_gx};
+  }
+  return BlockPos{(int)blockIdx.x, (int)blockIdx.y, (int)gridDim.x};
+}
+
 // ---------------------------------------------------------------------------
 // bf16 skinny GEMM on MFMA 16x16x32 (weight streaming)
 //
@@ -200,21 +218,12 @@ __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
   constexpr int CS = NW > 1 ? NW * TE : TE;                  // chunk stride of a stream
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane & 15, kg = lane >> 4;
-  // workgroup -> (column group bx, row block by).  Multi-row-tile launches
-  // may come as one dimension, remapped so that the row blocks sharing a
-  // column group's weights sit on one XCD (workgroups go to the 8 XCDs in
-  // turn) and are dispatched one after another: that XCD's L2 then serves
-  // the weight tiles to all of them.  The mapping never changes what a
-  // workgroup computes.
-  int bx = blockIdx.x, by = blockIdx.y, gxl = gridDim.x;
-  if (MT > 1 && a.remap_gx > 0) {
-    const int L = blockIdx.x, q = L >> 3;
-    by = q % a.remap_rb;
-    bx = (q / a.remap_rb) * 8 + (L & 7);
-    gxl = a.remap_gx;
-  }
+  // workgroup -> (column group bx, row block by); multi-row-tile launches may
+  // come as the XCD-aware 1-D launch (block_pos)
+  const BlockPos bp = block_pos<(MT > 1)>(a);
+  const int bx = bp.bx, by = bp.by;
   const int t0 = bx * TPW;                                   // first column tile
-  const int ntiles = gxl * TPW;
+  const int ntiles = bp.gx * TPW;
   const uint16_t* xr[MT];
   bool av_ok[MT];
 #pragma unroll
@@ -509,16 +518,9 @@ void gemm_tile_kernel(GemmArgs a) {
   __shared__ float rs[ROWS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 15, kg = lane >> 4;
-  // workgroup -> (column group bx, row block by), optionally as the XCD-aware
-  // 1-D launch of gemm_bf16_kernel
-  int bx = blockIdx.x, by = blockIdx.y;
-  if (a.remap_gx > 0) {
-    const int L = blockIdx.x, q = L >> 3;
-    by = q % a.remap_rb;
-    bx = (q / a.remap_rb) * 8 + (L & 7);
-  }
-  const int t0 = (bx * TILE_WAVES + wave) * NTW;   // this wave's first column tile
-  const int row0 = by * ROWS;
+  const BlockPos bp = block_pos<true>(a);           // column group, row block (XCD-aware order)
+  const int t0 = (bp.bx * TILE_WAVES + wave) * NTW;   // this wave's first column tile
+  const int row0 = bp.by * ROWS;
   const int S = a.K >> 6;
 
   // weight streams: stream j = matrix j % NW (gate, up) of column tile t0 + j / NW
@@ -652,7 +654,7 @@ void gemm_tile_kernel(GemmArgs a) {
     }
   }
   const int base = EPI == EPI_QKV ? a.state[0] + a.pos_off : 0;
-  const int ntiles = (a.remap_gx > 0 ? a.remap_gx : gridDim.x) * TILE_WAVES * NTW;
+  const int ntiles = bp.gx * TILE_WAVES * NTW;
 #pragma unroll
   for (int r = 0; r < MT; ++r)
 #pragma unroll

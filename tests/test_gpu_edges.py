@@ -193,6 +193,30 @@ def test_narrow_residual_tiles():
         eng.close()
 
 
+def test_prefill_fallback_kernel_for_odd_k():
+    """d = 576 and FFN 1600 give 9 and 25 K chunks, not a multiple of the
+    tile kernel's ring unroll, so the long prefill chunks run the layer
+    GEMMs on the multi-row-tile kernel instead; against the oracle, and
+    self-speculation still equals greedy."""
+    cfg = _edge_cfg(n_layers=2, d_model=576, n_q_heads=9, n_kv_heads=9, head_dim=64, ffn_dim=1600,
+                    max_ctx=240, prompt_len=150, cid=77)
+    w = synth.make_weights(cfg, seed=13)
+    print("[edge] d 576, ffn 1600 (prefill fallback kernel)", flush=True)
+    eng = engine(cfg, w, max_block=8, prefill_chunk=64)
+    try:
+        prompt = synth.make_prompt(cfg)
+        toks, rows = _stepwise(eng, prompt, 25)
+        ref = Model(cfg, w).teacher_forced(prompt, toks)
+        err = np.max(np.abs(rows - ref))
+        print(f"[edge] d 576: max |dlogit| = {err:.3e}")
+        assert err <= BOUND
+        assert _gap_ok(toks, ref, BOUND) == []
+        spec, _ = eng.generate(prompt, 24, np.array([1, 0], np.uint8), 3)
+        assert spec == toks[:24]
+    finally:
+        eng.close()
+
+
 def test_long_context_combine_batches():
     """A 3300-token context: 52 key partitions, so the combine loads its
     partials in two batches and the passes replay from a high context
