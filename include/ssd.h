@@ -252,7 +252,12 @@ ssd_status ssd_generate(ssd_ctx* ctx, const int32_t* prompt, int32_t n_prompt, i
  * query cache, read as the residual entering layer E).  Posterior and logits
  * equal the full verify's bit for bit.  The feature tap is not recomputed by
  * such a verify.  Other masks, and host blocks, verify in full. */
-enum { SSD_OPT_GRAPHS = 0, SSD_OPT_MOE_DEDUP = 1, SSD_OPT_TRACE = 2, SSD_OPT_KVQ = 3 };
+/* SSD_OPT_TILE_GROUPS (default 0 = 512): passes wider than 32 rows run the
+ * layer GEMMs on workgroups of 64 rows x 4 * ntw column tiles, ntw = 4, 2 or
+ * 1 (gate/up: 2 or 1), the widest that leaves at least this many
+ * workgroups.  The grouping never changes a result; a test and measurement
+ * hook (a small value forces the widest grouping).  value >= 0. */
+enum { SSD_OPT_GRAPHS = 0, SSD_OPT_MOE_DEDUP = 1, SSD_OPT_TRACE = 2, SSD_OPT_KVQ = 3, SSD_OPT_TILE_GROUPS = 4 };
 ssd_status ssd_set_option(ssd_ctx* ctx, int32_t option, int32_t value);
 
 /* Statistics accumulated since load/reset (per-phase times from HIP events). */

@@ -292,6 +292,10 @@ class Engine:
         """Exit-state reuse for tail-mask (early-exit) drafts (SSD_OPT_KVQ)."""
         _check(lib.ssd_set_option(self.ctx, 3, 1 if on else 0))
 
+    def set_tile_groups(self, min_workgroups: int):
+        """Long-pass GEMM grouping threshold (SSD_OPT_TILE_GROUPS; 0 = default)."""
+        _check(lib.ssd_set_option(self.ctx, 4, int(min_workgroups)))
+
     def read_trace(self, rows: int) -> np.ndarray:
         out = np.zeros((self.L, rows, self.d), dtype=np.float32)
         _check(lib.ssd_read_trace(self.ctx, _ptr(out), rows))

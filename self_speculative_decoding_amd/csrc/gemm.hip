@@ -817,9 +817,10 @@ hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t s) {
     const bool tile_epi = epi == EPI_QKV || epi == EPI_SWIGLU || epi == EPI_RESID;
     if (a.M > 32 && tile_epi && tiles % TILE_WAVES == 0 && (a.K / 64) % tile_u == 0) {
       const int rbt = (a.M + 16 * TILE_MT - 1) / (16 * TILE_MT);
+      const int wg_min = a.tile_wg_min > 0 ? a.tile_wg_min : SSD_TILE_WG_MIN;
       int ntw = 1;
       for (int v = epi == EPI_SWIGLU ? 2 : 4; v > 1; v >>= 1)
-        if (tiles % (TILE_WAVES * v) == 0 && (tiles / (TILE_WAVES * v)) * rbt >= SSD_TILE_WG_MIN) {
+        if (tiles % (TILE_WAVES * v) == 0 && (tiles / (TILE_WAVES * v)) * rbt >= wg_min) {
           ntw = v;
           break;
         }

@@ -64,6 +64,9 @@ struct GemmArgs {
   // set by the launcher only: a 1-D launch of remap_gx x remap_rb workgroups
   // of the multi-row-tile kernel mapped XCD-aware (see gemm.hip); 0 otherwise
   int remap_gx, remap_rb;
+  // long passes: fewest workgroups a wider column group may leave (0: the
+  // built-in SSD_TILE_WG_MIN); never changes a result
+  int tile_wg_min;
 };
 
 struct AttnArgs {

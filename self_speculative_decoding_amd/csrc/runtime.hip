@@ -82,6 +82,7 @@ struct ssd_ctx {
   // each row's residual and sums of squares after its last layer; a verify
   // of that draft starts at the exit layer E from them
   bool kvq_on = false;
+  int tile_wg_min = 0;               // SSD_OPT_TILE_GROUPS
   int kvq_E = -1;                    // exit layer of the current draft, -1: none
   float *exit_x = nullptr, *exit_ss = nullptr;
   std::vector<uint8_t> kvq_rest;     // mask running layers E..L-1 only
@@ -130,6 +131,13 @@ MoeArgs moe_args(ssd_ctx* c, int l, int M) {
   a.union_out = c->m_union + l; a.dedup = g.moe_dedup;
   a.ssw = resid_tile_width(g.d_model);   // the combine's column runs, also without ss_out
   return a;
+}
+
+// A GEMM of the pass on the context's stream, with the context's grouping
+// option for long passes.
+hipError_t run_gemm(ssd_ctx* c, int epi, GemmArgs a) {
+  a.tile_wg_min = c->tile_wg_min;
+  return launch_gemm(c->cfg.dtype, epi, a, c->stream);
 }
 
 // bf16 models fold every RMSNorm that feeds a dense GEMM (QKV, gate/up, LM
@@ -181,7 +189,7 @@ ssd_status layer_forward(ssd_ctx* c, int l, int M, int pos_off, bool feats, cons
     a.q = c->q; a.kc = kc; a.vc = vc; a.cos_t = c->cos_t; a.sin_t = c->sin_t;
     a.state = c->dstate; a.pos_off = pos_off; a.hq = hq; a.hkv = hkv; a.hd = hd; a.max_ctx = kv_stride(g);
     if (fold) fold_in(c, a, 0);
-    HIPCHK(launch_gemm(dt, EPI_QKV, a, s));
+    HIPCHK(run_gemm(c, EPI_QKV, a));
   }
   {
     AttnArgs a{};
@@ -198,7 +206,7 @@ ssd_status layer_forward(ssd_ctx* c, int l, int M, int pos_off, bool feats, cons
     GemmArgs a{};
     a.X = c->att; a.ldx = hq * hd; a.W0 = w.wo; a.M = M; a.N = d; a.K = hq * hd; a.y = c->x; a.ldy = d;
     if (fold && !w.moe) fold_out(c, a, w.ffn_norm);
-    HIPCHK(launch_gemm(dt, EPI_RESID, a, s));
+    HIPCHK(run_gemm(c, EPI_RESID, a));
   }
   if (w.moe) {
     HIPCHK(launch_rmsnorm(dt, c->x, d, w.ffn_norm, c->xn, d, d, g.rms_eps, M, s));
@@ -211,7 +219,7 @@ ssd_status layer_forward(ssd_ctx* c, int l, int M, int pos_off, bool feats, cons
     a.X = c->xn; a.ldx = d; a.W0 = w.w_gate; a.W1 = w.w_up; a.M = M; a.N = w.ffn; a.K = d;
     a.out = c->act; a.ldo = w.ffn;
     if (fold) fold_in(c, a, 0);
-    HIPCHK(launch_gemm(dt, EPI_SWIGLU, a, s));
+    HIPCHK(run_gemm(c, EPI_SWIGLU, a));
     GemmArgs b{};
     b.X = c->act; b.ldx = w.ffn; b.W0 = w.w_down; b.M = M; b.N = d; b.K = w.ffn; b.y = c->x; b.ldy = d;
     if (feats && w.feat_slot >= 0) {
@@ -219,7 +227,7 @@ ssd_status layer_forward(ssd_ctx* c, int l, int M, int pos_off, bool feats, cons
       b.ldtap = g.n_feat * d;
     }
     if (fold) fold_out(c, b, gain_next);
-    HIPCHK(launch_gemm(dt, EPI_RESID, b, s));
+    HIPCHK(run_gemm(c, EPI_RESID, b));
   }
   if (c->trace_on && M <= g.max_block)
     HIPCHK(launch_copy_f32(c->x, c->trace + (size_t)l * g.max_block * d, M * d, s));
@@ -278,10 +286,10 @@ ssd_status run_pass(ssd_ctx* c, const int* d_tok, int M, int pos_off, const uint
       // the LM head epilogue leaves (max, index) per 16 columns; reduce those
       fold_in(c, a, head_row0);
       a.amax_v = c->amax_v; a.amax_i = c->amax_i;
-      HIPCHK(launch_gemm(dt, EPI_LOGITS, a, s));
+      HIPCHK(run_gemm(c, EPI_LOGITS, a));
       HIPCHK(launch_argmax_tiles(c->amax_v, c->amax_i, g.vocab / 16, d_arg, head_rows, s));
     } else {
-      HIPCHK(launch_gemm(dt, EPI_F32, a, s));
+      HIPCHK(run_gemm(c, EPI_F32, a));
       HIPCHK(launch_argmax(c->logits, g.vocab, g.vocab, d_arg, head_rows, s));
     }
     c->head_rows = head_rows;
@@ -290,7 +298,7 @@ ssd_status run_pass(ssd_ctx* c, const int* d_tok, int M, int pos_off, const uint
     GemmArgs a{};
     a.X = c->tap; a.ldx = g.n_feat * d; a.W0 = c->fc; a.M = M; a.N = d; a.K = g.n_feat * d;
     a.out = c->feat; a.ldo = d;
-    HIPCHK(launch_gemm(dt, EPI_STORE, a, s));
+    HIPCHK(run_gemm(c, EPI_STORE, a));
     c->feat_rows = M;
   }
   return SSD_OK;
@@ -862,14 +870,17 @@ ssd_status ssd_generate(ssd_ctx* c, const int32_t* prompt, int32_t n_prompt, int
 ssd_status ssd_set_option(ssd_ctx* c, int32_t option, int32_t value) {
   clear_error();
   if (!c) return fail(SSD_E_ARG, "ctx is NULL");
-  if (option != SSD_OPT_GRAPHS && option != SSD_OPT_MOE_DEDUP && option != SSD_OPT_TRACE && option != SSD_OPT_KVQ)
+  if (option != SSD_OPT_GRAPHS && option != SSD_OPT_MOE_DEDUP && option != SSD_OPT_TRACE && option != SSD_OPT_KVQ &&
+      option != SSD_OPT_TILE_GROUPS)
     return fail(SSD_E_ARG, "unknown option %d", option);
+  if (option == SSD_OPT_TILE_GROUPS && value < 0) return fail(SSD_E_ARG, "tile groups threshold must be >= 0");
   if (option == SSD_OPT_MOE_DEDUP && c->cfg.n_experts == 0) return fail(SSD_E_UNSUPPORTED, "not an MoE model");
   HIPCHK(hipStreamSynchronize(c->stream));
   destroy_graphs(c);
   if (option == SSD_OPT_GRAPHS) c->use_graphs = value != 0;
   else if (option == SSD_OPT_TRACE) c->trace_on = value != 0;
   else if (option == SSD_OPT_KVQ) c->kvq_on = value != 0;
+  else if (option == SSD_OPT_TILE_GROUPS) c->tile_wg_min = value;
   else c->cfg.moe_dedup = value != 0;
   return SSD_OK;
 }
@@ -1162,7 +1173,7 @@ ssd_status ssd_time_op(ssd_ctx* c, int32_t op, int32_t layer, int32_t m, int32_t
       // bf16 GEMMs carry their folded-norm work as in a pass
       if (dt == SSD_BF16 && (op == 0 || op == 2 || op == 4)) fold_in(c, a, 0);
       if (dt == SSD_BF16 && (op == 1 || op == 3)) fold_out(c, a, w.ffn_norm);
-      HIPCHK(launch_gemm(dt, epi, a, s));
+      HIPCHK(run_gemm(c, epi, a));
     }
   }
   HIPCHK(hipEventRecord(c->ev[EV_B], s));

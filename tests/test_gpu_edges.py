@@ -193,6 +193,33 @@ def test_narrow_residual_tiles():
         eng.close()
 
 
+def test_prefill_widest_column_groups_bitwise():
+    """SSD_OPT_TILE_GROUPS = 1 forces the widest grouping of the prefill tile
+    kernel (four column tiles per wave for QKV, o and down, two for gate/up),
+    which the default threshold only picks at very long chunks; the last-row
+    logits and the KV cache equal the default grouping's bit for bit."""
+    cfg = _edge_cfg(n_layers=2, d_model=1024, n_q_heads=16, n_kv_heads=4, ffn_dim=14336,
+                    max_ctx=400, prompt_len=300, cid=78)
+    w = synth.make_weights(cfg, seed=14)
+    prompt = synth.make_prompt(cfg)
+    out = []
+    for groups in (0, 1):
+        print(f"[edge] prefill tile groups threshold {groups}", flush=True)
+        eng = engine(cfg, w, max_block=4, prefill_chunk=256)
+        try:
+            eng.set_tile_groups(groups)
+            t = eng.prefill(prompt)
+            out.append((t, eng.read_logits(1)[0], [eng.read_kv(l, 0, len(prompt)) for l in range(cfg["n_layers"])]))
+        finally:
+            eng.close()
+    assert out[0][0] == out[1][0]
+    assert np.array_equal(out[0][1], out[1][1])
+    for (k0, v0), (k1, v1) in zip(out[0][2], out[1][2]):
+        assert np.array_equal(k0, k1) and np.array_equal(v0, v1)
+    _, _, last = Model(cfg, w).prefill(prompt)
+    assert np.max(np.abs(out[1][1] - last)) <= BOUND
+
+
 def test_prefill_fallback_kernel_for_odd_k():
     """d = 576 and FFN 1600 give 9 and 25 K chunks, not a multiple of the
     tile kernel's ring unroll, so the long prefill chunks run the layer
