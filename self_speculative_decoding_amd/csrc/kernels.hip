@@ -253,6 +253,9 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(AttnArgs a) {
   for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) kf[kt][ks] = *(const uint4*)(kb + (size_t)16 * kt * HD + 32 * ks);
+  // Q and K issue before V: the waits count loads in issue order, so S^T and
+  // the softmax can run while V is still arriving
+  __builtin_amdgcn_sched_barrier(0);
   const uint16_t* vb = (const uint16_t*)a.vc + ((size_t)kvh * HD + c) * ldc + key0 + 4 * kg;
   uint2 vf[8][2][2];
 #pragma unroll
@@ -261,26 +264,9 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(AttnArgs a) {
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int h = 0; h < 2; ++h) vf[dt][ks][h] = *(const uint2*)(vb + (size_t)16 * dt * ldc + 32 * ks + 16 * h);
-
-  // keys past the last row's position: P is 0 there; keep 0 * V finite
-  const int maxpos = st0 + a.pos_off + a.M - 1;
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const bool keep = key0 + 32 * ks + 16 * h + 4 * kg + 3 <= maxpos;
-      if (!keep) {
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-          const int k = key0 + 32 * ks + 16 * h + 4 * kg;
-          uint2 v = vf[dt][ks][h];
-          // zero the 16-bit entries past maxpos
-          v.x = k > maxpos ? 0u : (k + 1 > maxpos ? (v.x & 0xffffu) : v.x);
-          v.y = k + 2 > maxpos ? 0u : (k + 3 > maxpos ? (v.y & 0xffffu) : v.y);
-          vf[dt][ks][h] = v;
-        }
-      }
-    }
+  // and all of them issue here, not next to their first use
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
 
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
@@ -327,6 +313,27 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(AttnArgs a) {
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
 
+    if (t == 0) {
+      // keys past the last row's position: P is 0 there; keep 0 * V finite
+      const int maxpos = st0 + a.pos_off + a.M - 1;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const bool keep = key0 + 32 * ks + 16 * h + 4 * kg + 3 <= maxpos;
+          if (!keep) {
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+              const int k = key0 + 32 * ks + 16 * h + 4 * kg;
+              uint2 v = vf[dt][ks][h];
+              // zero the 16-bit entries past maxpos
+              v.x = k > maxpos ? 0u : (k + 1 > maxpos ? (v.x & 0xffffu) : v.x);
+              v.y = k + 2 > maxpos ? 0u : (k + 3 > maxpos ? (v.y & 0xffffu) : v.y);
+              vf[dt][ks][h] = v;
+            }
+          }
+        }
+    }
     f32x4 o[8];
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
