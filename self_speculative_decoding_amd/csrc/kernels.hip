@@ -362,10 +362,39 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(AttnArgs a) {
   }
 }
 
+// Wave-wide sum and max on DPP lane moves (VALU, no LDS round trip):
+// quad swaps, half-row and row mirrors, then the row 15 / row 31 broadcasts
+// carry the partial results up to lane 63, which readlane returns to every
+// lane.  Lanes a step does not write keep `old`: 0 for sums, the lane's own
+// value for maxima.  A fixed order, the same for every call.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_move(float v, float old) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), CTRL, ROW_MASK, 0xf, false));
+}
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += dpp_move<0xb1, 0xf>(v, 0.f);    // quad_perm [1,0,3,2]
+  v += dpp_move<0x4e, 0xf>(v, 0.f);    // quad_perm [2,3,0,1]
+  v += dpp_move<0x141, 0xf>(v, 0.f);   // row_half_mirror
+  v += dpp_move<0x140, 0xf>(v, 0.f);   // row_mirror
+  v += dpp_move<0x142, 0xa>(v, 0.f);   // row_bcast15 into rows 1 and 3
+  v += dpp_move<0x143, 0xc>(v, 0.f);   // row_bcast31 into rows 2 and 3
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = fmaxf(v, dpp_move<0xb1, 0xf>(v, v));
+  v = fmaxf(v, dpp_move<0x4e, 0xf>(v, v));
+  v = fmaxf(v, dpp_move<0x141, 0xf>(v, v));
+  v = fmaxf(v, dpp_move<0x140, 0xf>(v, v));
+  v = fmaxf(v, dpp_move<0x142, 0xa>(v, v));
+  v = fmaxf(v, dpp_move<0x143, 0xc>(v, v));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
 // Combine of the attention partitions: one workgroup per (row, head), one
 // lane per head dim.  Row r at position pos uses partitions 0..pos/PT with
 // weights w_p = exp2(m_p - max m): thread p holds partition p's (m, l), the
-// max and sum(w_p l_p) are fixed butterflies over the two waves, and the
+// max and sum(w_p l_p) are fixed DPP reductions over each wave, then the two
+// waves' results added through LDS, and the
 // outputs add w_p o_p in partition order.  The partial outputs are loaded (up
 // to 48 at a time) together with the (m, l) pairs, before the position.
 template <typename E>
@@ -387,17 +416,13 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
   const int pos = st0 + a.pos_off + row;
   const int np = pos / ATT_PT + 1;
   const bool in = t < np;   // entries past the row's partitions are never used
-  float mx = in ? m_t : -INFINITY;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  const float mx = wave_max_dpp(in ? m_t : -INFINITY);
   if (lane == 0) red[wave] = mx;
   __syncthreads();
   const float M = fmaxf(red[0], red[1]);
   const float w = in ? exp2f(m_t - M) : 0.f;
   sw[t] = w;
-  float lw = in ? w * l_t : 0.f;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) lw += __shfl_xor(lw, o);
+  const float lw = wave_sum_dpp(in ? w * l_t : 0.f);
   if (lane == 0) red[2 + wave] = lw;
   __syncthreads();
   const float L = red[2] + red[3];
