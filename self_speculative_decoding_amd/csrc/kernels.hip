@@ -220,6 +220,17 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 // (NT = 2 for passes of two or more tiles); every tile runs the same
 // instruction sequence, so an output element does not depend on the number
 // of rows in the pass or on the tile it shares a wave with.
+// The value of lane ^ 16 and lane ^ 32 on the gfx950 permlane swaps (VALU,
+// no LDS): the same partners, so the same results, as __shfl_xor(v, 16 / 32).
+__device__ __forceinline__ float lane_xor16(float v, int lane) {
+  const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float((lane & 16) ? s[0] : s[1]);
+}
+__device__ __forceinline__ float lane_xor32(float v, int lane) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float((lane & 32) ? s[0] : s[1]);
+}
+
 template <int G, int NT>
 __global__ __launch_bounds__(64) void attn_mfma_kernel(AttnArgs a) {
   constexpr int HD = 128, PT = ATT_PT;
@@ -289,8 +300,8 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(AttnArgs a) {
         const bool valid = qv[t] && key0 + 16 * kt + 4 * kg + i <= pos;
         m = valid ? fmaxf(m, sc[kt][i] * a.scale_log2) : m;
       }
-    m = fmaxf(m, __shfl_xor(m, 16));
-    m = fmaxf(m, __shfl_xor(m, 32));
+    m = fmaxf(m, lane_xor16(m, lane));
+    m = fmaxf(m, lane_xor32(m, lane));
     float l = 0.f;
     uint32_t ph[2][4], pl[2][4];   // P^T hi / lo fragments, bf16 pairs
 #pragma unroll
@@ -310,8 +321,8 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(AttnArgs a) {
         ph[kt >> 1][(kt & 1) * 2 + i / 2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
         pl[kt >> 1][(kt & 1) * 2 + i / 2] = (uint32_t)l0 | ((uint32_t)l1 << 16);
       }
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    l += lane_xor16(l, lane);
+    l += lane_xor32(l, lane);
 
     if (t == 0) {
       // keys past the last row's position: P is 0 there; keep 0 * V finite
