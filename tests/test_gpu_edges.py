@@ -4,7 +4,8 @@ A bf16 model whose KV capacity is not a whole number of 64-key attention
 partitions, filled to the last position; one-token prompts; the largest
 verify block (32 rows); the degenerate skip masks (nothing skipped: the draft
 is the full model, so every draft is accepted; everything skipped: the draft
-is embedding + head); query-head groups of 1 and 2 per KV head.
+is embedding + head); query-head groups of 1 and 2 per KV head; the largest
+KV capacity the boundary accepts (8192 keys, 128 attention partitions).
 Bars as in test_gpu_parity: bf16 |dlogit| <= 3e-2, GPU self-speculation
 bitwise equal to GPU greedy.
 """
@@ -271,6 +272,44 @@ def test_long_context_combine_batches():
         mask[1] = 1
         spec, _ = eng.generate(prompt, 12, mask, 3)
         assert spec == toks
+    finally:
+        eng.close()
+
+
+def test_maximum_context():
+    """The largest KV capacity the boundary accepts, 8192 keys = 128 attention
+    partitions: every lane of the combine holds a partition and its partials
+    load in three batches.  Greedy filled to the last position a verify can
+    reach against the oracle; an 8-row verify block ending there equals the
+    decode rows bit for bit; self-speculation filling the cache is lossless."""
+    from self_speculative_decoding_amd import skip_mask
+    cap = 128 * 64
+    cfg = _edge_cfg(n_layers=2, max_ctx=cap, prompt_len=cap - 16, cid=79)
+    w = synth.make_weights(cfg, seed=11)
+    print("[edge] context 8192 (128 partitions)", flush=True)
+    eng = engine(cfg, w, max_block=8, prefill_chunk=256)
+    try:
+        prompt = synth.make_prompt(cfg)
+        P = len(prompt)
+        toks, rows = _stepwise(eng, prompt, cap - P)      # last row at position cap - 2
+        ref = Model(cfg, w).teacher_forced(prompt, toks)
+        err = np.max(np.abs(rows - ref))
+        print(f"[edge] context 8192: max |dlogit| = {err:.3e}", flush=True)
+        assert err <= BOUND
+        assert _gap_ok(toks, ref, BOUND) == []
+        eng.reset()
+        eng.prefill(prompt)
+        for t in toks[:7]:                                 # one-row steps to position P + 6
+            eng.verify([t])
+            eng.accept()
+        post = eng.verify(toks[7:15])                      # rows at P + 7 .. cap - 2
+        assert np.array_equal(eng.read_logits(8), rows[8:16])
+        assert post == toks[8:16]
+        eng.accept()
+        k = 3
+        n_full = cap - P - (k + 1)
+        spec, _ = eng.generate(prompt, n_full, skip_mask(cfg["n_layers"], 0.5), k)
+        assert spec == toks[:n_full]
     finally:
         eng.close()
 
