@@ -136,7 +136,9 @@ def bench_pmc_probe(args) -> int:
     """Kernel sequence for `rocprofv3 --pmc` runs: 3 plain copies of 128 MiB
     (counter calibration), then 24 gate/up GEMM launches at m = 4 over the
     layers of a 4-layer model with the headline widths (940 MB of weights, more
-    than the on-die caches hold), then 3 read probes of the 1.05 GB LM head."""
+    than the on-die caches hold), 3 read probes of the 1.05 GB LM head, and 24
+    launches each of the QKV, o and down GEMMs at m = 4 (the other decode
+    GEMMs, cycling over the same layers)."""
     import synth
     from self_speculative_decoding_amd import Engine, make_cfg
     cfg = synth.config("llama-8b", n_layers=4)
@@ -146,6 +148,8 @@ def bench_pmc_probe(args) -> int:
     res = {"copy_probe_us": eng.time_op("copy_probe", 0, 128, 3),
            "gate_up_m4_us": eng.time_op("gate_up", 0, 4, 24),
            "read_probe_us": eng.time_op("read_probe", 0, 4, 3)}
+    for op in ("qkv", "o", "down"):
+        res[op + "_m4_us"] = eng.time_op(op, 0, 4, 24)
     eng.close()
     res["copy_bytes"] = 128 << 20
     res["gate_up_bytes"] = 2 * cfg["ffn_dim"] * cfg["d_model"] * 2
