@@ -155,16 +155,23 @@ class Model:
         v = self.rn(v)
         cache.K[l][:, pos0:pos0 + M] = k.transpose(1, 0, 2)
         cache.V[l][:, pos0:pos0 + M] = v.transpose(1, 0, 2)
-        Kc, Vc = cache.K[l][:, :pos0 + M], cache.V[l][:, :pos0 + M]
+        out = self.attend(q, cache.K[l][:, :pos0 + M], cache.V[l][:, :pos0 + M], pos)
+        att = self.rn(out.reshape(M, self.hq * self.hd))
+        return x + self.lin(att, w[p + "wo"])
+
+    def attend(self, q: np.ndarray, Kc: np.ndarray, Vc: np.ndarray, pos: np.ndarray) -> np.ndarray:
+        """Causal grouped-query attention of queries q [M, Hq, hd] at positions
+        pos over the cache entries Kc, Vc [Hkv, ctx, hd]: softmax(q.k / sqrt(hd))
+        over the keys at positions <= the query's own."""
+        M, ctx = q.shape[0], Kc.shape[1]
         out = np.zeros((M, self.hq, self.hd))
         scale = 1.0 / np.sqrt(self.hd)
         for h in range(self.hq):
             g = (h * self.hkv) // self.hq
             s = (q[:, h, :] @ Kc[g].T) * scale                     # [M, ctx]
-            s = np.where(np.arange(pos0 + M)[None, :] <= pos[:, None], s, -np.inf)
+            s = np.where(np.arange(ctx)[None, :] <= pos[:, None], s, -np.inf)
             out[:, h, :] = softmax(s) @ Vc[g]
-        att = self.rn(out.reshape(M, self.hq * self.hd))
-        return x + self.lin(att, w[p + "wo"])
+        return out
 
     def dense_ffn(self, l: int, h: np.ndarray) -> np.ndarray:
         """SwiGLU feed-forward of the normed residual h (ffn_norm folded in)."""

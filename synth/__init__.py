@@ -5,9 +5,9 @@ weights, prompts, the synthetic MoE routing trace and the random parts of the
 geometric-prefix verify blocks.  It contains none of the decoding method's
 arithmetic, and it imports neither the oracle nor the HIP binding.
 
-Weight matrices are uniform with standard deviation 0.02, drawn per tensor
-chunk from ``numpy.random.Generator(PCG64(SeedSequence([seed, tensor_id,
-chunk])))`` (norm gains are 1).  bf16 configurations draw float32 and store the
+Weight matrices are normal N(0, 0.02), drawn per tensor chunk from
+``numpy.random.Generator(PCG64(SeedSequence([seed, tensor_id, chunk])))``
+(norm gains are 1).  bf16 configurations draw float32 and store the
 round-to-nearest-even bf16 bit pattern (uint16); float32 configurations
 store float32.  Prompts are uniform over the vocabulary.
 """
@@ -146,26 +146,25 @@ def _f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
     return r.astype(np.uint16)
 
 
-_UNIFORM_HALF_WIDTH = 0.02 * 3.0 ** 0.5   # U(-a, a) has standard deviation 0.02
+_STD = 0.02
 
 
 def _fill_chunk(flat: np.ndarray, seed: int, tid: int, chunk: int, bf16: bool, scale: float) -> None:
     c0 = chunk * _CHUNK
     c1 = min(flat.size, c0 + _CHUNK)
     g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, tid, chunk])))
-    v = g.random(c1 - c0, dtype=np.float32)
-    v *= np.float32(2.0 * _UNIFORM_HALF_WIDTH * scale)
-    v -= np.float32(_UNIFORM_HALF_WIDTH * scale)
+    v = g.standard_normal(c1 - c0, dtype=np.float32)
+    v *= np.float32(_STD * scale)
     flat[c0:c1] = _f32_to_bf16_bits(v) if bf16 else v
 
 
 def make_weights(cfg: dict, seed: int = 0, threads: int | None = None, progress=None) -> dict[str, np.ndarray]:
     """All weights of ``cfg``: name -> float32 array (f32 configs) or uint16 bf16 bits.
 
-    Matrices are uniform on (-0.02*sqrt(3), 0.02*sqrt(3)) (standard deviation
-    0.02), drawn in independently seeded chunks of 2^24 elements; norm gains
-    are 1.  Layers listed in cfg["out_scale"] have both residual-writing
-    matrices (wo and w_down) scaled by the given factor.  ``progress``, if
+    Matrices are normal with mean 0 and standard deviation 0.02, drawn in
+    independently seeded chunks of 2^24 elements; norm gains are 1.  Layers
+    listed in cfg["out_scale"] have both residual-writing matrices (wo and
+    w_down) scaled by the given factor.  ``progress``, if
     given, is called with the finished fraction about every tenth of the work.
     """
     bf16 = cfg["dtype"] == "bf16"
