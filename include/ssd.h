@@ -115,9 +115,16 @@ int64_t ssd_weight_numel(const ssd_cfg* cfg, int32_t i);
  * in the tile order their GEMMs stream; float32 models keep every buffer. */
 int32_t ssd_weight_retained(const ssd_cfg* cfg, int32_t i);
 
-/* Device workspace size in bytes (KV cache, activations, partial results,
- * rotary tables, token buffers and, for bf16 models, the packed copy of the
- * weight matrices) for cfg; -1 if cfg is invalid. */
+/* Device workspace size in bytes for cfg; -1 if cfg is invalid.  It holds the
+ * one KV cache that draft and verify share (LayerSkip summary 4.3.3; mlx-dflash
+ * README, "Apple Silicon Optimizations": the cache is kept across steps and
+ * cropped on rejection, so it is allocated once at its full capacity max_ctx),
+ * the activations and partial results of one pass of up to
+ * max(max_block, prefill_chunk) rows, the rotary tables, the device-resident
+ * block and committed-length state (mlx-dflash README, "Apple Silicon
+ * Optimizations": verify ids assembled on the GPU) and, for bf16 models, the
+ * packed copy of the weight matrices.  The caller allocates it (host code of
+ * this library never allocates device memory). */
 int64_t ssd_workspace_bytes(const ssd_cfg* cfg);
 
 /* Skip mask of the naive layer-skip draft (MLX layer-skip blog, "Code"):
@@ -161,9 +168,13 @@ const char* ssd_last_error(void);
 
 typedef struct ssd_ctx ssd_ctx;
 
-/* Binds weights (device buffers, canonical order, n_weights of them, sizes
- * checked) and a device workspace of at least ssd_workspace_bytes(cfg) bytes,
- * 256-byte aligned.  hip_stream: a hipStream_t (NULL = the null stream).
+/* Binds one model's weights for both the draft and the verify passes: the
+ * draft is the same network run on a subset of its layers, so there is one
+ * weight table (LayerSkip summary 4.3.1, self-drafting with the model's own
+ * early layers; MLX layer-skip blog, "Code": the draft shares the full model's
+ * layer objects).  weights: device buffers, canonical order, n_weights of them,
+ * sizes checked; a device workspace of at least ssd_workspace_bytes(cfg)
+ * bytes, 256-byte aligned.  hip_stream: a hipStream_t (NULL = the null stream).
  * Clears the KV cache; for bf16 models packs the weight matrices into the
  * workspace (synchronously) after which the buffers ssd_weight_retained
  * reports as 0 are no longer read.  *out receives the context (free with
@@ -178,10 +189,14 @@ int32_t ssd_state(const ssd_ctx* ctx);
 /* Committed KV length n (positions [0, n) hold full-model entries). */
 int32_t ssd_context_length(const ssd_ctx* ctx);
 
-/* Runs the prompt tokens[0..n) (host, ids in [0,V)) at positions 0..n-1 through
- * all layers in passes of prefill_chunk rows; *next_tok (host, may be NULL)
- * receives argmax of the last row's logits (lowest index on ties), which
- * becomes the pending token t_last at position n.  LOADED -> READY. */
+/* Prefill (mlx-dflash README, "Architecture": the target's prefill fills the
+ * KV cache before the decode loop; LayerSkip summary 4.3: the cache of the
+ * verified tokens is what draft and verify read): runs the prompt
+ * tokens[0..n) (host, ids in [0,V)) at positions 0..n-1 through all layers in
+ * passes of prefill_chunk rows; *next_tok (host, may be NULL) receives argmax
+ * of the last row's logits (lowest index on ties), which becomes the pending
+ * token t_last at position n.  LOADED -> READY.  SSD_E_ARG for n < 1 or a
+ * token outside [0, V); SSD_E_CAPACITY for n + 1 > max_ctx. */
 ssd_status ssd_prefill(ssd_ctx* ctx, const int32_t* tokens, int32_t n, int32_t* next_tok);
 
 /* Draft (LayerSkip summary 4.3.1): k tokens, each through the layers with
@@ -283,7 +298,10 @@ ssd_status ssd_read_kv(ssd_ctx* ctx, int32_t layer, int32_t pos0, int32_t n, voi
 /* Feature-tap output of the last verify pass: host [rows * d] bf16 bits. */
 ssd_status ssd_read_features(ssd_ctx* ctx, uint16_t* host, int32_t rows);
 /* Injects expert ids for the next passes: host [n_layers][n][top_k] (entries for
- * dense layers ignored); n == 0 returns to the router's own choice. */
+ * dense layers ignored); n == 0 returns to the router's own choice.  Passes
+ * are then limited to n rows (SSD_E_ARG otherwise).  Switching between
+ * injected and router-chosen ids drops the captured pass graphs (they are
+ * captured again on next use); the injected ids are read at every replay. */
 ssd_status ssd_set_routing(ssd_ctx* ctx, const int32_t* ids, int32_t n);
 /* Routed-expert union size per layer of the last MoE pass: host [n_layers]. */
 ssd_status ssd_read_union(ssd_ctx* ctx, int32_t* host);

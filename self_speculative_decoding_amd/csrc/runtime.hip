@@ -317,6 +317,9 @@ void destroy_graphs(ssd_ctx* c) {
 // read from device state, so one graph serves every context length.
 ssd_status decode_pass(ssd_ctx* c, const int* tok, int M, int pos_off, const uint8_t* skip, int* arg, bool feats,
                        const PassSpec& ps = PassSpec()) {
+  // checked here as well as in run_pass: a replayed graph never re-runs run_pass
+  if (c->moe_inject && M > c->moe_inject)
+    return fail(SSD_E_ARG, "pass of %d rows but routing was injected for %d", M, c->moe_inject);
   c->last_tok = tok;
   c->last_M = M;
   c->last_full = !ps.load;
@@ -1048,8 +1051,15 @@ ssd_status ssd_set_routing(ssd_ctx* c, const int32_t* ids, int32_t n) {
   clear_error();
   if (!c) return fail(SSD_E_ARG, "ctx is NULL");
   if (c->cfg.n_experts == 0) return fail(SSD_E_UNSUPPORTED, "not an MoE model");
+  if (n != 0 && (!ids || n < 0 || n > c->lay.R)) return fail(SSD_E_ARG, "n=%d outside [0, %d]", n, c->lay.R);
+  // Captured passes bake in where the expert ids come from (the router's
+  // choice or the injected buffer): switching between the two drops them.
+  // The injected ids themselves are read from device memory at replay.
+  if ((n == 0) != (c->moe_inject == 0)) {
+    HIPCHK(hipStreamSynchronize(c->stream));
+    destroy_graphs(c);
+  }
   if (n == 0) { c->moe_inject = 0; return SSD_OK; }
-  if (!ids || n < 0 || n > c->lay.R) return fail(SSD_E_ARG, "n=%d outside [0, %d]", n, c->lay.R);
   const ssd_cfg& g = c->cfg;
   std::vector<int32_t> buf((size_t)g.n_layers * c->lay.R * g.top_k, 0);
   for (int l = 0; l < g.n_layers; ++l)

@@ -80,6 +80,50 @@ def test_moe_per_slot_equals_dedup_router_choice(moe, n):
     assert np.array_equal(out[0][1], out[1][1])
 
 
+def test_routing_switch_drops_captured_passes(moe):
+    """A verify pass captured with injected expert ids, then the same shape
+    with the router's own choice: the second pass must use the router (equal
+    to an eager, graphs-off router-choice verify), not replay the injected
+    graph; and an injection for fewer rows than a captured pass is refused."""
+    cfg, w, ps, dd, _ = moe
+    from self_speculative_decoding_amd import SSDError
+    prompt = synth.make_prompt(cfg)
+    block = list(synth.make_tokens(cfg["vocab"], 6, seed=8, stream=9))
+    trace = synth.make_routing_trace(cfg["n_layers"], 6, cfg["n_experts"], cfg["top_k"], seed=8)
+
+    def run(eng, ids):
+        eng.set_routing(None)          # the prompt runs on the router's choice
+        eng.reset()
+        eng.prefill(prompt)
+        eng.set_routing(ids)
+        post = eng.verify(block)
+        lg = eng.read_logits(len(block))
+        eng.accept()
+        return post, lg
+
+    for eng in (ps, dd):
+        injected = run(eng, trace)
+        router = run(eng, None)
+        eng.set_graphs(False)
+        eager = run(eng, None)
+        eng.set_graphs(True)
+        assert router[0] == eager[0]
+        assert np.array_equal(router[1], eager[1])
+        assert not np.array_equal(router[1], injected[1])
+        # a captured 6-row pass with injected ids, then ids for 4 rows only
+        # (same mode, so the graph stays): the 6-row pass is refused, not replayed
+        eng.set_routing(None)
+        eng.reset()
+        eng.prefill(prompt)
+        eng.set_routing(trace)
+        eng.verify(block)
+        eng.accept()
+        eng.set_routing(trace[:, :4])
+        with pytest.raises(SSDError):
+            eng.verify(block)
+        eng.set_routing(None)
+
+
 def test_moe_self_spec_lossless(moe):
     cfg, w, ps, dd, _ = moe
     from self_speculative_decoding_amd import skip_mask
