@@ -112,7 +112,7 @@ def test_tiny_self_spec_matches_greedy_and_oracle(tiny):
     assert out == ref
     print(f"[tiny] cycles gpu {st['cycles']} oracle {ost['cycles']}, accepted {st['accepted']} / {ost['accepted']}")
     assert st["accepted"] > 0
-    assert abs(st["cycles"] - ost["cycles"]) <= 2
+    # the cycle-by-cycle history against the oracle: test_gpu_draft_parity.py
 
 
 def test_tiny_every_mask_and_k_is_lossless(tiny):
