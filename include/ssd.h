@@ -308,6 +308,20 @@ ssd_status ssd_read_union(ssd_ctx* ctx, int32_t* host);
 /* Runs the accept kernel on host drafts d[k] and predictions p[k+1];
  * *a receives the accepted length.  Does not change the context's state. */
 ssd_status ssd_test_accept(ssd_ctx* ctx, const int32_t* d, const int32_t* p, int32_t k, int32_t* a);
+/* Allocation-free form of ssd_test_accept, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  No context: the accept kernel's staging (block and
+ * predictions), its counters and its outputs live in a static device array of
+ * SSD_NOALLOC_SCRATCH_BYTES per GPU, which each GPU keeps until the process
+ * ends; its address is looked up once per device, on the first call made with
+ * that device current.  Same inputs and result as ssd_test_accept: d[k] and
+ * p[k+1] host arrays, *a = accepted length; SSD_E_ARG for k outside
+ * [0, SSD_MAX_BLOCK - 1] or NULL pointers.  Runs on hip_stream (NULL = the
+ * null stream) and synchronises it.  Calls no allocator.  Every call on a GPU
+ * shares that GPU's array: calls that overlap on one GPU (other threads or
+ * streams) race. */
+#define SSD_NOALLOC_SCRATCH_BYTES 1024
+ssd_status ssd_test_accept_noalloc(const int32_t* d, const int32_t* p, int32_t k, void* hip_stream, int32_t* a);
 /* Test hook: `trials` sampled cycles on host logits with the decode loop's
  * sampling kernels, cycle numbers cycle0, cycle0 + 1, ... (cycle0 + trials
  * <= 2^31 - 1, else SSD_E_ARG); each cycle draws its k drafts from the draft

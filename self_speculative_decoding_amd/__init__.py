@@ -28,7 +28,7 @@ EXPORTS = ["ssd_validate_cfg", "ssd_n_weights", "ssd_weight_numel", "ssd_weight_
            "ssd_get_stats", "ssd_read_logits", "ssd_read_features", "ssd_set_routing",
            "ssd_read_union", "ssd_test_accept", "ssd_time_op", "ssd_set_option", "ssd_read_trace",
            "ssd_read_kv", "ssd_select_k", "ssd_knapsack_skip", "ssd_layer_cosines",
-           "ssd_set_sampling", "ssd_test_spec_cycle"]
+           "ssd_set_sampling", "ssd_test_spec_cycle", "ssd_test_accept_noalloc"]
 
 
 class Cfg(ctypes.Structure):
@@ -101,6 +101,7 @@ def _load():
         "ssd_set_routing": (I32, [VP, VP, I32]),
         "ssd_read_union": (I32, [VP, VP]),
         "ssd_test_accept": (I32, [VP, VP, VP, I32, P(I32)]),
+        "ssd_test_accept_noalloc": (I32, [VP, VP, I32, VP, P(I32)]),
         "ssd_time_op": (I32, [VP, I32, I32, I32, I32, P(ctypes.c_float)]),
         "ssd_set_option": (I32, [VP, I32, I32]),
         "ssd_read_trace": (I32, [VP, VP, I32]),
@@ -186,6 +187,17 @@ def knapsack_skip(cost, value, budget: int) -> tuple[np.ndarray, float]:
     kept = ctypes.c_double(0.0)
     _check(lib.ssd_knapsack_skip(_ptr(c), _ptr(v), len(c), int(budget), _ptr(mask), ctypes.byref(kept)))
     return mask, kept.value
+
+
+def test_accept_noalloc(d, p, stream=None) -> int:
+    """The accept kernel on host drafts and predictions with no context and no
+    device allocation (ssd_test_accept_noalloc); stream: a torch stream or None."""
+    dd = np.ascontiguousarray(d, dtype=np.int32)
+    pp = np.ascontiguousarray(p, dtype=np.int32)
+    a = ctypes.c_int32()
+    s = None if stream is None else ctypes.c_void_p(stream.cuda_stream)
+    _check(lib.ssd_test_accept_noalloc(_ptr(dd) if len(dd) else None, _ptr(pp), len(dd), s, ctypes.byref(a)))
+    return a.value
 
 
 def check_transition(state: int, op: int) -> int:

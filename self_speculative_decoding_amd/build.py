@@ -14,7 +14,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libssd.so")
 BUILD = os.path.join(PKG, "_build")
 
-SOURCES = ["kernels.hip", "gemm.hip", "moe.hip", "sampling.hip", "runtime.hip", "host.cpp"]
+SOURCES = ["kernels.hip", "gemm.hip", "moe.hip", "sampling.hip", "runtime.hip", "noalloc.hip", "host.cpp"]
 # Packed-FP32 instructions are switched off for all device code.
 DEVICE_FLAGS = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-fPIC", "-std=c++17", "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-function"]

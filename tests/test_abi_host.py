@@ -171,3 +171,16 @@ def test_knapsack_skip_rejects():
     assert f(P(c), P(v), 4, 1 << 25, P(m), ctypes.byref(kv)) == -1
     bad = np.array([1, -1, 1, 1], np.int32)
     assert f(P(bad), P(v), 4, 3, P(m), ctypes.byref(kv)) == -1
+
+
+def test_noalloc_accept_rejects_bad_arguments_before_any_hip_call():
+    """Argument checks of the allocation-free accept run on the host: an
+    out-of-range k or a NULL pointer returns SSD_E_ARG without a HIP call."""
+    a = ctypes.c_int32(-7)
+    p = np.zeros(40, np.int32)
+    for k in (-1, ssd.SSD_MAX_BLOCK, 40):
+        st = ssd.lib.ssd_test_accept_noalloc(p.ctypes.data_as(ctypes.c_void_p), p.ctypes.data_as(ctypes.c_void_p),
+                                             k, None, ctypes.byref(a))
+        assert st == -1 and a.value == -7
+    assert ssd.lib.ssd_test_accept_noalloc(None, p.ctypes.data_as(ctypes.c_void_p), 3, None, ctypes.byref(a)) == -1
+    assert ssd.lib.ssd_test_accept_noalloc(p.ctypes.data_as(ctypes.c_void_p), None, 3, None, ctypes.byref(a)) == -1
