@@ -92,8 +92,10 @@ def measured_traffic() -> float | None:
 
 
 def cpu_baseline(cfg, weights, prompt, budget_s: float) -> dict:
-    """The oracle (float64 CPU decoder) timed on this host: greedy decode steps
-    after a short prompt, until about budget_s seconds of decode work."""
+    """The oracle (float64 CPU decoder) timed on this host at the workload's
+    own context: it prefills the workload's prompt itself (not timed), then
+    greedy decode steps at context len(prompt), len(prompt)+1, ... are timed
+    until about budget_s seconds of decode work (a bounded sample)."""
     import numpy as np
     from oracle import Model
     try:
@@ -103,8 +105,11 @@ def cpu_baseline(cfg, weights, prompt, budget_s: float) -> dict:
         cores = os.cpu_count() or 1
     log("cpu baseline: building the oracle model")
     m = Model(cfg, weights)
-    short = prompt[:8]
-    cache, n, last = m.prefill(short)
+    P = len(prompt)
+    t0 = time.perf_counter()
+    cache, n, last = m.prefill(prompt)
+    t_pre = time.perf_counter() - t0
+    log(f"cpu baseline: oracle prefill of {P} tokens took {t_pre:.1f}s")
     tok = int(np.argmax(last))
     t0 = time.perf_counter()
     steps = 0
@@ -117,7 +122,7 @@ def cpu_baseline(cfg, weights, prompt, budget_s: float) -> dict:
         log(f"cpu baseline: decode step {steps} at {el:.1f}s")
         if el >= budget_s or steps >= 64:
             break
-    del m
+    del m, cache
     cpu_model = ""
     try:
         for line in open("/proc/cpuinfo"):
@@ -128,8 +133,10 @@ def cpu_baseline(cfg, weights, prompt, budget_s: float) -> dict:
         pass
     return {"value": steps / el, "unit": "tok/s", "cores": int(cores), "kind": "oracle",
             "host": {"nproc": os.cpu_count(), "cpu": cpu_model},
-            "sample": f"{steps} float64 greedy decode steps of the same model after an 8-token prompt "
-                      f"(context <= {8 + steps}); weight conversion and prefill excluded"}
+            "sample": f"{steps} float64 greedy decode steps at context {P}-{P + steps - 1}, after the oracle's "
+                      f"own prefill of the workload's {P}-token prompt ({t_pre:.0f} s, not timed); the sample "
+                      f"is bounded to about {budget_s:.0f} s of decode work, so it holds fewer steps than a "
+                      f"full 16-step sample would"}
 
 
 def bench_pmc_probe(args) -> int:

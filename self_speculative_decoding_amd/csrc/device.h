@@ -56,11 +56,12 @@ __device__ __forceinline__ uint4 ld16_nt(const uint16_t* p) {
 // then re-read row w-1 and their MFMA output columns are discarded.
 constexpr int PACK_TILE = 1024;   // elements per packed tile
 
-// One wave's share of a 16-row x (NW x 16)-column MFMA tile: K-chunks
-// [c0, c1) of 64 elements, accumulated in order.  In each chunk lane group g
-// (lane/16) reads 32 contiguous bytes (elements 16g..16g+15) of its A row;
-// the chunk is two MFMA K-steps, the first over elements 16g..16g+7 of every
-// group, the second over 16g+8..16g+15 (A and B permuted alike).
+// One wave's share of a 16-row x (NW x 16)-column MFMA tile: the K-chunks
+// c0, c0 + step, c0 + 2 step, ... below c1, 64 elements each, accumulated in
+// that order.  In each chunk lane group g (lane/16) reads 32 contiguous bytes
+// (elements 16g..16g+15) of its A row; the chunk is two MFMA K-steps, the
+// first over elements 16g..16g+7 of every group, the second over
+// 16g+8..16g+15 (A and B permuted alike).
 // xr: this lane's A row at element 16g; wr[j]: packed tile j of this
 // workgroup at chunk 0 plus 8*lane; consecutive chunks of a tile are NW
 // tiles apart (interleaved pairs).  U chunks of loads are issued before their
@@ -70,21 +71,23 @@ constexpr int PACK_TILE = 1024;   // elements per packed tile
 // tile (PACK_TILE, or 64 * width for the narrow gate/up tiles).
 template <int NW, bool NT, int U, int CS = NW * PACK_TILE, int TE = PACK_TILE>
 __device__ __forceinline__ void mfma_stream(const uint16_t* xr, bool xok, const uint16_t* const* wr, int c0, int c1,
-                                            f32x4* acc) {
+                                            f32x4* acc, int step = 1) {
   const uint4 zero = {0u, 0u, 0u, 0u};
   auto ldw = [](const uint16_t* p) { return NT ? ld16_nt(p) : ld16(p); };
-  int s = c0;
-  for (; s + U <= c1; s += U) {
+  const int n = c1 > c0 ? (c1 - c0 + step - 1) / step : 0;
+  int i = 0;
+  for (; i + U <= n; i += U) {
     uint4 xa[U][2], wb[NW][U][2];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
+      const size_t s = (size_t)c0 + (size_t)(i + u) * step;
 #pragma unroll
       for (int j = 0; j < NW; ++j) {
-        wb[j][u][0] = ldw(wr[j] + (size_t)(s + u) * CS);
-        wb[j][u][1] = ldw(wr[j] + (size_t)(s + u) * CS + TE / 2);
+        wb[j][u][0] = ldw(wr[j] + s * CS);
+        wb[j][u][1] = ldw(wr[j] + s * CS + TE / 2);
       }
-      xa[u][0] = xok ? ld16(xr + (size_t)(s + u) * 64) : zero;
-      xa[u][1] = xok ? ld16(xr + (size_t)(s + u) * 64 + 8) : zero;
+      xa[u][0] = xok ? ld16(xr + s * 64) : zero;
+      xa[u][1] = xok ? ld16(xr + s * 64 + 8) : zero;
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
@@ -95,13 +98,14 @@ __device__ __forceinline__ void mfma_stream(const uint16_t* xr, bool xok, const 
           acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa[u][h]),
                                                            __builtin_bit_cast(bf16x8, wb[j][u][h]), acc[j], 0, 0, 0);
   }
-  for (; s < c1; ++s) {
+  for (; i < n; ++i) {
+    const size_t s = (size_t)c0 + (size_t)i * step;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const uint4 xa = xok ? ld16(xr + (size_t)s * 64 + 8 * h) : zero;
+      const uint4 xa = xok ? ld16(xr + s * 64 + 8 * h) : zero;
 #pragma unroll
       for (int j = 0; j < NW; ++j) {
-        const uint4 wb = ldw(wr[j] + (size_t)s * CS + h * (TE / 2));
+        const uint4 wb = ldw(wr[j] + s * CS + h * (TE / 2));
         acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa),
                                                          __builtin_bit_cast(bf16x8, wb), acc[j], 0, 0, 0);
       }

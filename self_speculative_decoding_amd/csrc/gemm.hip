@@ -30,7 +30,7 @@
 #define SSD_MT_MT 4
 #endif
 #ifndef SSD_TPW_MIN_M        // tile groups only for passes wider than this
-#define SSD_TPW_MIN_M 4
+#define SSD_TPW_MIN_M 8
 #endif
 #ifndef SSD_KW_SWIGLU
 #define SSD_KW_SWIGLU 8
@@ -62,6 +62,7 @@
 #ifndef SSD_KW_WIDE
 #define SSD_KW_WIDE 8
 #endif
+
 
 namespace ssd {
 
@@ -254,7 +255,15 @@ __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
     }
   }
 
-  const int s0 = (S * wave) / KW, s1 = (S * (wave + 1)) / KW;
+  // K split over the waves: in the LM head and the o projection (one-tile
+  // launches) wave w takes chunks w, w + KW, ..., so the waves of a
+  // workgroup read adjacent chunks at each step (measured faster there:
+  // LM head at 16 rows 188 -> 181 us, o at 6 rows 8.5 -> 8.1 us); elsewhere
+  // each wave takes the contiguous range [s0, s1).  The choice depends on
+  // the epilogue and K only, never on the pass width.
+  const bool kil = MT == 1 && (EPI == EPI_LOGITS || (EPI == EPI_RESID && a.K < 8192));
+  const int s0 = kil ? wave : (S * wave) / KW, s1 = kil ? S : (S * (wave + 1)) / KW;
+  const int kst = kil ? KW : 1;
 
   // Epilogue split: in one-tile-row launches wave e < 4 finishes accumulator
   // element e (rows 4kg + e) of every lane, so up to four rows' epilogues run
@@ -306,8 +315,8 @@ __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
   if (MT == 1 && EPI == EPI_QKV) {
     // first load batch, then the rotary table entries of this wave's
     // epilogue rows (they need the position), then the rest of the K range
-    const int sm = min(s0 + U, s1);
-    mfma_stream<NS, true, U, CS, TE>(xr[0], av_ok[0], wr, s0, sm, acc[0]);
+    const int sm = min(s0 + U * kst, s1);
+    mfma_stream<NS, true, U, CS, TE>(xr[0], av_ok[0], wr, s0, sm, acc[0], kst);
     {
       const int half = a.hd >> 1;
 #pragma unroll
@@ -323,9 +332,9 @@ __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
         }
       }
     }
-    mfma_stream<NS, true, U, CS, TE>(xr[0], av_ok[0], wr, sm, s1, acc[0]);
+    mfma_stream<NS, true, U, CS, TE>(xr[0], av_ok[0], wr, sm, s1, acc[0], kst);
   } else if (MT == 1) {
-    mfma_stream<NS, true, U, CS, TE>(xr[0], av_ok[0], wr, s0, s1, acc[0]);
+    mfma_stream<NS, true, U, CS, TE>(xr[0], av_ok[0], wr, s0, s1, acc[0], kst);
   }
   else mfma_stream_mt<NS, MT, CS, TE>(xr, av_ok, wr, s0, s1, acc);
 
@@ -868,7 +877,7 @@ hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t s) {
       am.remap_rb = rb;
       grid_mt = dim3((tiles / tpm) * rb, 1);
     }
-    // passes wider than 4 rows group 2 or 4 column tiles per workgroup so
+    // passes wider than 8 rows group 2 or 4 column tiles per workgroup so
     // the A operand is read once for them (results unchanged, see the kernel),
     // but only where at least 1024 workgroups remain: spreading the weight
     // stream over every CU matters more than the A reads (measured)
