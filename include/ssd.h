@@ -286,6 +286,19 @@ ssd_status ssd_read_logits(ssd_ctx* ctx, float* host, int32_t rows);
 /* Residual after every layer of the last decode-loop pass (SSD_OPT_TRACE on):
  * host [n_layers * rows * d] float32, layer-major. */
 ssd_status ssd_read_trace(ssd_ctx* ctx, float* host, int32_t rows);
+/* Stored operands of one layer of the last decode-loop pass (SSD_OPT_TRACE on;
+ * rows <= min(rows of that pass, max_block)), the values later kernels read:
+ * point 0 the QKV GEMM input (bf16(x * attn_norm) for bf16 models, the normed
+ * row for float32 models) [rows][d], 1 q after the rotary embedding
+ * [rows][n_q_heads * head_dim], 2 the attention output [rows][n_q_heads *
+ * head_dim], 3 the residual after the attention block, float32 [rows][d],
+ * 4 the gate/up GEMM input [rows][d] (MoE layers: the normed row router and
+ * experts share), 5 the SwiGLU activation [rows][F] (MoE layers: [rows]
+ * [top_k + n_shared][expert_ffn], routed slots then shared experts); cfg
+ * dtype except point 3.  layer == n_layers with
+ * point 0: the LM head's input of rows [0, rows).  Layers a draft skipped keep
+ * an earlier pass's values.  host: caller-owned, rows x the row size. */
+ssd_status ssd_read_trace_point(ssd_ctx* ctx, int32_t layer, int32_t point, int32_t rows, void* host);
 /* Acceptance proxy of every layer from the last decode-loop pass (SSD_OPT_TRACE
  * on; the pass must have run every layer): cos[l] = mean over its first rows
  * rows of cos(input of layer l, output of layer l), the input of layer 0

@@ -28,7 +28,7 @@ EXPORTS = ["ssd_validate_cfg", "ssd_n_weights", "ssd_weight_numel", "ssd_weight_
            "ssd_get_stats", "ssd_read_logits", "ssd_read_features", "ssd_set_routing",
            "ssd_read_union", "ssd_test_accept", "ssd_time_op", "ssd_set_option", "ssd_read_trace",
            "ssd_read_kv", "ssd_select_k", "ssd_knapsack_skip", "ssd_layer_cosines",
-           "ssd_set_sampling", "ssd_test_spec_cycle", "ssd_test_accept_noalloc"]
+           "ssd_set_sampling", "ssd_test_spec_cycle", "ssd_test_accept_noalloc", "ssd_read_trace_point"]
 
 
 class Cfg(ctypes.Structure):
@@ -105,6 +105,7 @@ def _load():
         "ssd_time_op": (I32, [VP, I32, I32, I32, I32, P(ctypes.c_float)]),
         "ssd_set_option": (I32, [VP, I32, I32]),
         "ssd_read_trace": (I32, [VP, VP, I32]),
+        "ssd_read_trace_point": (I32, [VP, I32, I32, I32, VP]),
         "ssd_read_kv": (I32, [VP, I32, I32, I32, VP, VP]),
     }
     for name, (res, args) in sig.items():
@@ -311,6 +312,19 @@ class Engine:
     def read_trace(self, rows: int) -> np.ndarray:
         out = np.zeros((self.L, rows, self.d), dtype=np.float32)
         _check(lib.ssd_read_trace(self.ctx, _ptr(out), rows))
+        return out
+
+    def read_trace_point(self, layer: int, point: int, rows: int) -> np.ndarray:
+        """A stored operand of one layer of the last traced pass
+        (ssd_read_trace_point): bf16 bits (uint16) or float32, [rows, width]."""
+        c = self.cfg
+        qo = c.n_q_heads * c.head_dim
+        moe = c.n_experts > 0 and c.n_dense_layers <= layer < c.n_layers
+        ffn = (c.top_k + c.n_shared) * c.expert_ffn if moe else (c.dense_ffn if c.n_experts > 0 else c.ffn_dim)
+        width = {0: c.d_model, 1: qo, 2: qo, 3: c.d_model, 4: c.d_model, 5: ffn}[point]
+        dt = np.float32 if point == 3 or c.dtype == 0 else np.uint16
+        out = np.zeros((rows, width), dtype=dt)
+        _check(lib.ssd_read_trace_point(self.ctx, layer, point, rows, _ptr(out)))
         return out
 
     def read_kv(self, layer: int, pos0: int, n: int):

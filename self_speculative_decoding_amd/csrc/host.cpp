@@ -133,6 +133,23 @@ ssd_status validate(const ssd_cfg* cp) {
 
 static size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+TracePoints trace_points(const ssd_cfg& c) {
+  TracePoints t;
+  const size_t esz = c.dtype == SSD_BF16 ? 2 : 4, d = c.d_model, qo = (size_t)c.n_q_heads * c.head_dim;
+  size_t f = (size_t)layer_ffn(c);   // dense activation, or the MoE layers' [slot][expert_ffn]
+  if (c.n_experts > 0 && (size_t)(c.top_k + c.n_shared) * c.expert_ffn > f) f = (size_t)(c.top_k + c.n_shared) * c.expert_ffn;
+  const size_t rows[6] = {d * esz, qo * esz, qo * esz, d * 4, d * esz, f * esz};
+  size_t off = 0;
+  for (int i = 0; i < 6; ++i) {
+    t.off[i] = off;
+    t.row[i] = rows[i];
+    off = up256(off + rows[i] * c.max_block);
+  }
+  t.layer = off;
+  t.total = (size_t)c.n_layers * t.layer + up256(d * esz * c.max_block);
+  return t;
+}
+
 bool compute_layout(const ssd_cfg& c, Layout& L) {
   if (validate(&c) != SSD_OK) return false;
   const size_t esz = c.dtype == SSD_BF16 ? 2 : 4;
@@ -160,6 +177,7 @@ bool compute_layout(const ssd_cfg& c, Layout& L) {
   L.logits = take((size_t)c.max_block * c.vocab * 4);
   L.amax_v = take((size_t)c.max_block * (c.vocab / 16 + 1) * 4);
   L.trace = take((size_t)c.n_layers * c.max_block * d * 4);
+  L.trace_pts = take(trace_points(c).total);
   // exit-state cache of an early-exit draft: residual and its sums of squares
   // per block row after the draft's last layer
   L.exit_x = take((size_t)c.max_block * d * 4);

@@ -20,7 +20,7 @@ struct Layout {
   size_t part_o = 0, part_ml = 0, rope_cos = 0, rope_sin = 0;
   size_t block = 0, post = 0, toks = 0, state = 0, result = 0, outlog = 0;
   size_t tblock = 0, tpost = 0, tstate = 0, tresult = 0, toutlog = 0;
-  size_t tap = 0, feat = 0, amax_v = 0, amax_i = 0, trace = 0, wpack = 0, exit_x = 0, exit_ss = 0, dlog = 0, tout = 0;
+  size_t tap = 0, feat = 0, amax_v = 0, amax_i = 0, trace = 0, trace_pts = 0, wpack = 0, exit_x = 0, exit_ss = 0, dlog = 0, tout = 0;
   size_t smp_stats = 0, smp_csum = 0, smp_ctl = 0, smp_nch = 0;
   size_t m_rlogits = 0, m_ids = 0, m_gates = 0, m_inject = 0, m_slot_out = 0, m_groups = 0, m_union = 0;
   size_t total = 0;
@@ -28,6 +28,18 @@ struct Layout {
   int n_part = 0;   // attention partitions covering max_ctx
   size_t part_o_bytes = 0;
 };
+
+// Stored operands of every layer of a traced pass (SSD_OPT_TRACE): per layer
+// six points of up to max_block rows each: the QKV input, q after RoPE, the
+// attention output, the residual after the attention block (float32), the
+// gate/up input and the SwiGLU activation; then the LM head's input.
+struct TracePoints {
+  size_t off[6] = {};     // byte offset of each point inside a layer record
+  size_t row[6] = {};     // bytes per row of each point
+  size_t layer = 0;       // bytes per layer record
+  size_t total = 0;       // all layers + the head input
+};
+TracePoints trace_points(const ssd_cfg& c);
 
 ssd_status fail(ssd_status s, const char* fmt, ...);
 const char* last_error();

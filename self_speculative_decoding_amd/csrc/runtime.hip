@@ -78,6 +78,8 @@ struct ssd_ctx {
   int cap_part = 0;        // attention partitions of the pass being captured
   bool trace_on = false;   // record the residual after every layer of decode-loop passes
   float* trace = nullptr;
+  char* trace_pts = nullptr;   // and the stored operands of every layer (TracePoints)
+  TracePoints tp;
   // exit-state reuse of an early-exit draft (SSD_OPT_KVQ): the draft saves
   // each row's residual and sums of squares after its last layer; a verify
   // of that draft starts at the exit layer E from them
@@ -170,6 +172,14 @@ const void* next_gain(ssd_ctx* c, int l, const uint8_t* skip) {
   return c->final_norm;
 }
 
+// Copies rows [0, M) of a pass buffer (rows of `row` bytes) into trace
+// point `pt` of layer l (the head input when l == n_layers).
+hipError_t trace_point(ssd_ctx* c, int l, int pt, const void* src, int M) {
+  const size_t off = (size_t)l * c->tp.layer + (l < c->cfg.n_layers ? c->tp.off[pt] : 0);
+  const size_t row = l < c->cfg.n_layers ? c->tp.row[pt] : c->tp.row[0];
+  return launch_copy_f32((const float*)src, (float*)(c->trace_pts + off), (int)(M * row / 4), c->stream);
+}
+
 // One decoder layer over M rows at positions state[0] + pos_off + r.
 ssd_status layer_forward(ssd_ctx* c, int l, int M, int pos_off, bool feats, const void* gain_next) {
   const ssd_cfg& g = c->cfg;
@@ -182,6 +192,8 @@ ssd_status layer_forward(ssd_ctx* c, int l, int M, int pos_off, bool feats, cons
   void* vc = (char*)c->vc + (size_t)l * cache_layer_elems(g) * c->esz;
 
   if (!fold) HIPCHK(launch_rmsnorm(dt, c->x, d, w.attn_norm, c->xn, d, d, g.rms_eps, M, s));
+  const bool tr = c->trace_on && M <= g.max_block;
+  if (tr) HIPCHK(trace_point(c, l, 0, c->xn, M));
   {
     GemmArgs a{};
     a.X = c->xn; a.ldx = d; a.W0 = w.wq; a.W1 = w.wk; a.W2 = w.wv;
@@ -191,6 +203,7 @@ ssd_status layer_forward(ssd_ctx* c, int l, int M, int pos_off, bool feats, cons
     if (fold) fold_in(c, a, 0);
     HIPCHK(run_gemm(c, EPI_QKV, a));
   }
+  if (tr) HIPCHK(trace_point(c, l, 1, c->q, M));
   {
     AttnArgs a{};
     a.q = c->q; a.kc = kc; a.vc = vc; a.out = c->att; a.part_o = c->part_o; a.part_ml = c->part_ml; a.pstride = c->lay.n_part;
@@ -202,24 +215,31 @@ ssd_status layer_forward(ssd_ctx* c, int l, int M, int pos_off, bool feats, cons
     const int n_part = c->capturing ? c->cap_part : (c->n + pos_off + M + ATT_PT - 1) / ATT_PT;
     HIPCHK(launch_attention(dt, a, n_part, s));
   }
+  if (tr) HIPCHK(trace_point(c, l, 2, c->att, M));
   {
     GemmArgs a{};
     a.X = c->att; a.ldx = hq * hd; a.W0 = w.wo; a.M = M; a.N = d; a.K = hq * hd; a.y = c->x; a.ldy = d;
     if (fold && !w.moe) fold_out(c, a, w.ffn_norm);
     HIPCHK(run_gemm(c, EPI_RESID, a));
   }
+  if (tr) HIPCHK(trace_point(c, l, 3, c->x, M));
   if (w.moe) {
     HIPCHK(launch_rmsnorm(dt, c->x, d, w.ffn_norm, c->xn, d, d, g.rms_eps, M, s));
+    if (tr) HIPCHK(trace_point(c, l, 4, c->xn, M));
     MoeArgs a = moe_args(c, l, M);
     a.ss_out = c->ss; a.xg_out = c->xn; a.gain_next = gain_next;
     HIPCHK(launch_moe(dt, a, s));
+    if (tr) HIPCHK(launch_copy_f32((const float*)c->act, (float*)(c->trace_pts + (size_t)l * c->tp.layer + c->tp.off[5]),
+                                   (int)((size_t)M * (g.top_k + g.n_shared) * g.expert_ffn * c->esz / 4), s));
   } else {
     if (!fold) HIPCHK(launch_rmsnorm(dt, c->x, d, w.ffn_norm, c->xn, d, d, g.rms_eps, M, s));
+    if (tr) HIPCHK(trace_point(c, l, 4, c->xn, M));
     GemmArgs a{};
     a.X = c->xn; a.ldx = d; a.W0 = w.w_gate; a.W1 = w.w_up; a.M = M; a.N = w.ffn; a.K = d;
     a.out = c->act; a.ldo = w.ffn;
     if (fold) fold_in(c, a, 0);
     HIPCHK(run_gemm(c, EPI_SWIGLU, a));
+    if (tr) HIPCHK(trace_point(c, l, 5, c->act, M));
     GemmArgs b{};
     b.X = c->act; b.ldx = w.ffn; b.W0 = w.w_down; b.M = M; b.N = d; b.K = w.ffn; b.y = c->x; b.ldy = d;
     if (feats && w.feat_slot >= 0) {
@@ -278,6 +298,7 @@ ssd_status run_pass(ssd_ctx* c, const int* d_tok, int M, int pos_off, const uint
   if (head_rows > 0 && ps.head) {
     if (!fold)
       HIPCHK(launch_rmsnorm(dt, c->x + (size_t)head_row0 * d, d, c->final_norm, c->xn, d, d, g.rms_eps, head_rows, s));
+    if (c->trace_on && head_row0 == 0 && head_rows <= g.max_block) HIPCHK(trace_point(c, g.n_layers, 0, c->xn, head_rows));
     GemmArgs a{};
     a.X = fold ? (const void*)((const uint16_t*)c->xn + (size_t)head_row0 * d) : c->xn;
     a.ldx = d; a.W0 = c->lm_head; a.M = head_rows; a.N = g.vocab; a.K = d;
@@ -609,6 +630,8 @@ ssd_status ssd_load(const ssd_cfg* cfg, const ssd_buf* weights, int32_t n_weight
   c->act = at(c, lay.act); c->logits = (float*)at(c, lay.logits);
   c->amax_v = (float*)at(c, lay.amax_v); c->amax_i = (int*)at(c, lay.amax_i);
   c->trace = (float*)at(c, lay.trace);
+  c->trace_pts = (char*)at(c, lay.trace_pts);
+  c->tp = trace_points(*cfg);
   c->exit_x = (float*)at(c, lay.exit_x);
   c->exit_ss = (float*)at(c, lay.exit_ss);
   c->dlog = (float*)at(c, lay.dlog);
@@ -956,6 +979,24 @@ ssd_status ssd_read_trace(ssd_ctx* c, float* host, int32_t rows) {
   for (int l = 0; l < c->cfg.n_layers; ++l)
     HIPCHK(hipMemcpyAsync(host + (size_t)l * rows * d, c->trace + (size_t)l * c->cfg.max_block * d,
                           rows * d * 4, hipMemcpyDeviceToHost, c->stream));
+  HIPCHK(hipStreamSynchronize(c->stream));
+  return SSD_OK;
+}
+
+ssd_status ssd_read_trace_point(ssd_ctx* c, int32_t layer, int32_t point, int32_t rows, void* host) {
+  clear_error();
+  if (!c || !host) return fail(SSD_E_ARG, "NULL argument");
+  if (!c->trace_on) return fail(SSD_E_STATE, "residual trace is off (SSD_OPT_TRACE)");
+  const ssd_cfg& g = c->cfg;
+  if (layer < 0 || layer > g.n_layers || point < 0 || point > 5 || (layer == g.n_layers && point != 0))
+    return fail(SSD_E_ARG, "no trace point %d of layer %d", point, layer);
+  if (rows < 1 || rows > c->last_M || rows > g.max_block)
+    return fail(SSD_E_ARG, "rows=%d but the last pass has %d", rows, c->last_M);
+  const size_t off = (size_t)layer * c->tp.layer + (layer < g.n_layers ? c->tp.off[point] : 0);
+  size_t row = layer < g.n_layers ? c->tp.row[point] : c->tp.row[0];
+  if (layer < g.n_layers && point == 5)   // the layer's own activation width
+    row = (c->L[layer].moe ? (size_t)(g.top_k + g.n_shared) * g.expert_ffn : (size_t)c->L[layer].ffn) * c->esz;
+  HIPCHK(hipMemcpyAsync(host, c->trace_pts + off, rows * row, hipMemcpyDeviceToHost, c->stream));
   HIPCHK(hipStreamSynchronize(c->stream));
   return SSD_OK;
 }

@@ -2,14 +2,17 @@
 
 Properties at the full size: self-speculation emits exactly plain greedy over
 the 1024-token prompt and 512 generated tokens; a verify block at context
-1024+ reproduces the decode rows bitwise.  Oracle parity on the same full
-model over a short sequence (the float64 oracle finishes it in seconds).
+1024+ reproduces the decode rows bitwise.  Oracle parity at context 1024 for
+a 4-row verify pass and a draft step, all layers end to end, with every bf16
+storage decision checked against the oracle's (tests/_matched.py); and the
+whole greedy run's tokens against the plain oracle teacher-forced on them.
 """
 import numpy as np
 import pytest
 
 import synth
 from _common import engine
+from _matched import check_matched
 
 pytestmark = pytest.mark.gpu
 
@@ -55,89 +58,75 @@ def test_fullsize_verify_rows_equal_decode_rows(big):
     eng.accept()
 
 
-def _layerwise(cfg, w, eng, prompt, block):
-    """Each layer of one verify pass recomputed by the oracle from the GPU's
-    own input residual and KV prefix: returns per-layer max |dx| / rms(x),
-    the fraction of new K/V entries that round to a different bf16 value
-    (each such entry is checked to be one ulp away), and the head's |dlogit|."""
-    from oracle import Model
-    from oracle.model import Cache
-    from _common import bf16_bits_to_f32
+def test_fullsize_verify_pass_matches_oracle_decision_by_decision(big):
+    """4-row verify pass at context 1024 (the workload's prompt), all 32
+    layers, checked end to end from the embedding against the oracle."""
+    cfg, w, eng = big
+    prompt = synth.make_prompt(cfg)
     eng.reset()
-    print("[llama-8b] layer-local check", flush=True)
     eng.set_trace(True)
     try:
-        eng.prefill(prompt)
-        n, M = len(prompt), len(block)
+        t = eng.prefill(prompt)
+        block = [t] + [int(x) for x in synth.make_tokens(cfg["vocab"], 3, seed=1, stream=77)]
         eng.verify(block)
-        trace = eng.read_trace(M).astype(np.float64)
-        logits = eng.read_logits(M)
-        kv = [eng.read_kv(l, 0, n + M) for l in range(cfg["n_layers"])]
+        logits = eng.read_logits(4)
+        check_matched("llama-8b verify", cfg, w, eng, block, len(prompt), list(range(cfg["n_layers"])), logits)
         eng.accept()
     finally:
         eng.set_trace(False)
-    ora = Model(cfg, w)
-    x = ora.embed(block)
-    rel, kvdiff = [], []
-    for l in range(cfg["n_layers"]):
-        cache = Cache(cfg)
-        k, v = (bf16_bits_to_f32(a).astype(np.float64) for a in kv[l])
-        cache.K[l][:, :n] = k[:, :n]
-        cache.V[l][:, :n] = v[:, :n]
-        y = ora.layer(l, x, n, cache)
-        rel.append(float(np.max(np.abs(y - trace[l])) / np.sqrt(np.mean(trace[l] ** 2))))
-        for ref_, got_ in ((cache.K[l][:, n:n + M], k[:, n:]), (cache.V[l][:, n:n + M], v[:, n:])):
-            # an entry may round to a neighbouring bf16 value: one ulp at its
-            # magnitude plus the pre-rounding difference a few RMSNorm-output
-            # flips leave (|W| <= 0.035 times one bf16 ulp of |n| <= 8, x3)
-            tol = 2.0 ** -7 * np.maximum(np.abs(ref_), np.abs(got_)) + 3 * 0.035 * 2.0 ** -8 * 8
-            worst = float(np.max(np.abs(ref_ - got_) - tol))
-            assert worst <= 0, (l, worst, float(np.max(np.abs(ref_ - got_))))
-        kvdiff.append(float(np.mean(cache.K[l][:, n:n + M] != k[:, n:]) + np.mean(cache.V[l][:, n:n + M] != v[:, n:])) / 2)
-        x = trace[l]                                   # next layer starts from the GPU's residual
-    head = float(np.max(np.abs(ora.head(trace[-1]) - logits)))
-    return rel, kvdiff, head
 
 
-def test_fullsize_each_layer_matches_oracle(big):
-    """Full-size layer-local parity: no cross-layer amplification of rounding flips."""
+def test_fullsize_draft_step_matches_oracle_decision_by_decision(big):
+    """One draft step (20 % middle skip: layers 13-18 skipped) at context
+    1025, checked the same way through the kept layers."""
+    from self_speculative_decoding_amd import skip_mask
     cfg, w, eng = big
-    prompt = synth.make_prompt(cfg)[:200]
-    block = [int(t) for t in synth.make_tokens(cfg["vocab"], 4, seed=1, stream=77)]
-    rel, kvdiff, head = _layerwise(cfg, w, eng, prompt, block)
-    print(f"[llama-8b] per-layer max|dx|/rms(x): max {max(rel):.2e} median {np.median(rel):.2e}; "
-          f"new K/V entries differing: max {max(kvdiff):.2e}; head |dlogit| {head:.2e}", flush=True)
-    assert max(rel) <= 1e-2
-    assert max(kvdiff) <= 0.05
-    assert head <= 3e-2
+    prompt = synth.make_prompt(cfg)
+    mask = skip_mask(cfg["n_layers"], 0.2)
+    kept = [l for l in range(cfg["n_layers"]) if not mask[l]]
+    eng.reset()
+    eng.set_trace(True)
+    try:
+        t = eng.prefill(prompt)
+        eng.verify([t])
+        t2 = eng.accept()[1][0]
+        n = eng.context_length
+        d = eng.draft(mask, 1)
+        logits = eng.read_logits(1)
+        check_matched("llama-8b draft", cfg, w, eng, [t2], n, kept, logits)
+        assert d[0] == int(np.argmax(logits[0]))
+        eng.verify(None, 2)
+        eng.accept()
+    finally:
+        eng.set_trace(False)
 
 
-def test_fullsize_end_to_end_logits_short_sequence(big):
-    """End to end through all 32 layers the logits of a float32 path drift
-    from the float64 oracle by the model's own sensitivity: bf16 storage
-    points turn float32-level differences into one-ulp flips that
-    attention spreads to later rows.  Bound: three times the oracle's own
-    drift when only its residual is rounded to float32 after each layer."""
+def test_fullsize_greedy_tokens_match_teacher_forced_oracle(big):
+    """The workload end to end: GPU greedy over the 1024-token prompt and 512
+    tokens against the plain oracle teacher-forced on the GPU's tokens.  The
+    tokens must equal the oracle's argmax wherever its top-1/top-2 gap exceeds
+    6e-2.  The logits themselves drift by the compounding of float32-vs-float64
+    rounding decisions at the bf16 storage points (about 0.1 over 32 layers);
+    the decision-matched tests above show that this is the whole of the
+    difference (1e-6 once the decisions agree)."""
     from oracle import Model
     cfg, w, eng = big
-    prompt = synth.make_prompt(cfg)[:24]
+    prompt, N = synth.make_prompt(cfg), cfg["n_new"]
     eng.reset()
     t = eng.prefill(prompt)
     toks, rows = [t], [eng.read_logits(1)[0]]
-    for _ in range(4):
+    while len(toks) < N:
         eng.verify([toks[-1]])
         rows.append(eng.read_logits(1)[0])
         toks.append(eng.accept()[1][0])
-    ora = Model(cfg, w)
-    ref = ora.teacher_forced(prompt, toks)
-    base_layer = Model.layer
-    ora.layer = lambda l, x, p, c, d=False: base_layer(ora, l, x, p, c, d).astype(np.float32).astype(np.float64)
-    ref32 = ora.teacher_forced(prompt, toks)
-    spread = float(np.max(np.abs(ref32 - ref)))
-    err = float(np.max(np.abs(np.stack(rows) - ref)))
-    print(f"[llama-8b] end-to-end max |dlogit| {err:.3e}; oracle float32-residual drift {spread:.3e}", flush=True)
-    assert err <= max(3e-2, 3 * spread)
-    for i, r in enumerate(ref):
-        top = np.sort(r)[-2:]
-        if top[1] - top[0] > 2 * max(3e-2, 3 * spread):
-            assert int(np.argmax(r)) == toks[i]
+    assert eng.generate(prompt, N)[0] == toks
+    print("[llama-8b] oracle teacher-forced over 1536 positions", flush=True)
+    ref = Model(cfg, w).teacher_forced(prompt, toks)
+    per = np.max(np.abs(np.stack(rows) - ref), axis=1)
+    gaps = np.array([float(np.diff(np.sort(r)[-2:])[0]) for r in ref])
+    wrong = np.array([int(np.argmax(r)) != tk for r, tk in zip(ref, toks)])
+    print(f"[llama-8b] teacher-forced: max |dlogit| {per.max():.4f} (median per position {np.median(per):.4f}); "
+          f"{int((gaps > 6e-2).sum())} of {N} positions with gap > 6e-2, token differs at "
+          f"{int((wrong & (gaps > 6e-2)).sum())} of them; largest gap where a token differs "
+          f"{float(gaps[wrong].max()) if wrong.any() else 0.0:.4f}", flush=True)
+    assert not (wrong & (gaps > 6e-2)).any()

@@ -5,81 +5,40 @@ reads) bf16 models with every layer and the full vocabulary.
 
 Properties at the full size: self-speculation emits exactly plain greedy; a
 verify block reproduces the decode rows bit for bit (per-slot and dedup MoE
-verify blocks agree bit for bit).  Oracle parity layer by layer: sampled
-layers of one verify pass recomputed by the float64 oracle from the GPU's
-own input residual and KV prefix, the head from the GPU's last residual, and
-the fc features from the GPU's tapped residuals.  The oracle only converts
-the weights of the layers it recomputes.
+verify blocks agree bit for bit).  Oracle parity: one verify block after the
+workload's full prompt (512, 2048 and 256 tokens), every layer, checked
+against the oracle decision by decision at every bf16 storage point (with the
+fc features of the tap and the MoE expert activations), end to end from the
+embedding to the logits (tests/_matched.py).
 """
-import re
-
 import numpy as np
 import pytest
 
 import synth
-from _common import bf16_bits_to_f32, engine
+from _common import engine
 
 pytestmark = pytest.mark.gpu
 
-BOUND = 3e-2
-# Layer-local bound on max |dx| / rms(x): layer 0's residual is embedding-scale
-# (rms ~ 0.02), so a few one-ulp flips of its bf16 intermediates (attention
-# output, SwiGLU activation, K/V entries) reach about 1e-2 of it at the
-# maximum over a 16-row block; deeper layers sit near 1e-3.
-LAYER_BOUND = 2e-2
 
-
-def _sampled_oracle(cfg, w, layers):
-    from oracle import Model
-    keep = {}
-    for n, a in w.items():
-        m = re.match(r"l(\d+)\.", n)   # layer weights: "l<index>.<name>"
-        if m is None or int(m.group(1)) in layers:
-            keep[n] = a
-    return Model(cfg, keep, keep_f32=True)
-
-
-def _layer_local(cfg, w, eng, prompt, block, layers, routing=None):
-    """Per sampled layer: max |dx| / rms(x) of the GPU residual against the
-    oracle's layer from the GPU's input residual and KV prefix; the head's
-    |dlogit|; the fc features' max |d| / rms (if the model taps features)."""
-    from oracle.model import Cache
+def _matched_verify(tag, cfg, w, eng, prompt, block, routing=None, dedup=False):
+    """A verify block after the workload's full prompt, all layers, checked
+    against the oracle decision by decision (tests/_matched.py)."""
+    from _matched import check_matched
     eng.reset()
     eng.set_trace(True)
     try:
         eng.prefill(prompt)
         if routing is not None:
             eng.set_routing(routing)
-        n, M = len(prompt), len(block)
         eng.verify(block)
-        trace = eng.read_trace(M).astype(np.float64)
-        logits = eng.read_logits(M)
-        feats = bf16_bits_to_f32(eng.read_features(M)).astype(np.float64) if cfg["feat_layers"] else None
-        kv = {l: eng.read_kv(l, 0, n + M) for l in layers}
+        logits = eng.read_logits(len(block))
+        check_matched(tag, cfg, w, eng, block, len(prompt), list(range(cfg["n_layers"])), logits,
+                      routing=routing, dedup=dedup)
         eng.accept()
     finally:
         if routing is not None:
             eng.set_routing(None)
         eng.set_trace(False)
-    ora = _sampled_oracle(cfg, w, set(layers))
-    if routing is not None:
-        ora.routing = {l: routing[l] for l in range(cfg["n_layers"])}
-    rel = {}
-    for l in layers:
-        x = ora.embed(block) if l == 0 else trace[l - 1]
-        cache = Cache(cfg)
-        k, v = (bf16_bits_to_f32(a).astype(np.float64) for a in kv[l])
-        cache.K[l][:, :n] = k[:, :n]
-        cache.V[l][:, :n] = v[:, :n]
-        y = ora.layer(l, x, n, cache)
-        rel[l] = float(np.max(np.abs(y - trace[l])) / np.sqrt(np.mean(trace[l] ** 2)))
-    head = float(np.max(np.abs(ora.head(trace[-1]) - logits)))
-    frel = None
-    if feats is not None:
-        cat = ora.rn(np.concatenate([trace[l] for l in cfg["feat_layers"]], axis=-1))
-        ref = ora.rn(ora.lin(cat, ora.w["fc"]))
-        frel = float(np.max(np.abs(ref - feats)) / np.sqrt(np.mean(ref ** 2)))
-    return rel, head, frel
 
 
 def _verify_rows_equal_decode_rows(eng, prompt, m):
@@ -122,12 +81,8 @@ def test_qwen3_4b_fullsize(qwen4b):
     prompt = synth.make_prompt(cfg)
     _lossless(cfg, eng, prompt, 40, cfg["skip_frac"], cfg["k"])
     _verify_rows_equal_decode_rows(eng, prompt, 6)
-    L = cfg["n_layers"]
     block = [int(t) for t in synth.make_tokens(cfg["vocab"], 4, seed=2, stream=78)]
-    rel, head, _ = _layer_local(cfg, w, eng, prompt[:200], block, [0, L // 2, L - 1])
-    print(f"[qwen3-4b] sampled layers max|dx|/rms(x) {rel}; head |dlogit| {head:.2e}", flush=True)
-    assert max(rel.values()) <= LAYER_BOUND
-    assert head <= BOUND
+    _matched_verify("qwen3-4b verify", cfg, w, eng, prompt, block)
 
 
 @pytest.fixture(scope="module")
@@ -147,13 +102,7 @@ def test_qwen3_8b_fullsize_feature_tap(qwen8b):
     _lossless(cfg, eng, prompt[:600], 32, 0.2, 3)
     _verify_rows_equal_decode_rows(eng, prompt[:600], 16)
     block = [int(t) for t in synth.make_tokens(cfg["vocab"], cfg["block"], seed=3, stream=79)]
-    L = cfg["n_layers"]
-    rel, head, frel = _layer_local(cfg, w, eng, prompt[:300], block, [0, 17, L - 1])
-    print(f"[qwen3-8b] 16-row verify: sampled layers max|dx|/rms(x) {rel}; head |dlogit| {head:.2e}; "
-          f"fc features max|d|/rms {frel:.2e}", flush=True)
-    assert max(rel.values()) <= LAYER_BOUND
-    assert head <= BOUND
-    assert frel <= 2e-2   # bf16 output rounding (2^-8 relative) on top of the tap's bf16 inputs
+    _matched_verify("qwen3-8b 16-row verify", cfg, w, eng, prompt, block)
 
 
 @pytest.fixture(scope="module")
@@ -183,11 +132,8 @@ def test_dsv2_lite_fullsize_moe(dsv2):
         res.append(eng.read_logits(8))
         eng.accept()
     assert np.array_equal(res[0], res[1])
-    # layer-local parity with an injected routing trace (dense layer 0, the
-    # first MoE layer, the last layer)
+    # oracle parity of an 8-row verify with an injected routing trace (dense
+    # layer 0 and the 26 MoE layers, expert activations included)
     L = cfg["n_layers"]
     trace = synth.make_routing_trace(L, 8, cfg["n_experts"], cfg["top_k"], seed=4, stream=81)
-    rel, head, _ = _layer_local(cfg, w, dd, prompt[:128], block, [0, 1, L - 1], routing=trace)
-    print(f"[dsv2-lite] sampled layers max|dx|/rms(x) {rel}; head |dlogit| {head:.2e}", flush=True)
-    assert max(rel.values()) <= LAYER_BOUND
-    assert head <= BOUND
+    _matched_verify("dsv2-lite verify", cfg, w, dd, prompt, block, routing=trace, dedup=True)
