@@ -101,6 +101,7 @@ ssd_status validate(const ssd_cfg* cp) {
     if (c.n_experts % 16) return fail(SSD_E_UNSUPPORTED, "n_experts must be a multiple of 16");
     if (c.top_k < 1 || c.top_k > c.n_experts || c.top_k > 8) return fail(SSD_E_ARG, "top_k must be in [1, min(8, n_experts)]");
     if (c.expert_ffn < 1) return fail(SSD_E_ARG, "expert_ffn must be positive");
+    if (c.n_shared > 8) return fail(SSD_E_UNSUPPORTED, "at most 8 shared experts");
     if (c.n_dense_layers > c.n_layers) return fail(SSD_E_ARG, "n_dense_layers > n_layers");
     if (c.n_dense_layers > 0 && c.dense_ffn < 1) return fail(SSD_E_ARG, "dense_ffn must be positive");
   } else if (c.ffn_dim < 1) {
