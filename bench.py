@@ -165,6 +165,50 @@ def bench_pmc_probe(args) -> int:
     return 0
 
 
+def bench_trace_verify(args) -> int:
+    """Kernel sequence for `rocprofv3 --kernel-trace`: the workload's model
+    after its full prompt, then groups of 12 verify passes (host blocks of
+    random tokens, each followed by the accept): llama-8b 4, 6 and 1 rows (the
+    k = 3 and k = 5 cycles and plain decoding), qwen3-4b 4 and 1, qwen3-8b 16
+    and 1, dsv2-lite 8 and 1 rows per-slot then deduplicated (synthetic
+    routing).  Prints the mean verify time per group."""
+    import numpy as np
+    import synth
+    from self_speculative_decoding_amd import Engine, make_cfg
+    widths = {"llama-8b": (4, 6, 1), "qwen3-4b": (4, 1), "qwen3-8b": (16, 1), "dsv2-lite": (8, 1)}[args.workload]
+    cfg = synth.config(args.workload)
+    w = synth.make_weights(cfg, progress=_weights_progress)
+    eng = Engine(make_cfg(cfg, max_block=17, prefill_chunk=256), [w[n] for n, _, _ in synth.weight_specs(cfg)])
+    del w
+    moe = cfg["n_experts"] > 0
+    prompt = synth.make_prompt(cfg)
+    toks = synth.make_tokens(cfg["vocab"], 400, seed=1, stream=5)
+    res, i = {}, 0
+    for mode in ((0, 1) if moe else (None,)):
+        if moe:
+            eng.set_moe_dedup(mode)
+            eng.set_routing(None)
+        eng.reset()
+        eng.prefill(prompt)
+        for m in widths:
+            if moe:
+                eng.set_routing(synth.make_routing_trace(cfg["n_layers"], m, cfg["n_experts"], cfg["top_k"], seed=0,
+                                                         stream=m))
+            ms = []
+            for _ in range(12):
+                st0 = eng.stats()
+                eng.verify([int(t) for t in toks[i:i + m]])
+                ms.append(eng.stats()["t_verify_ms"] - st0["t_verify_ms"])
+                eng.accept()
+                i = (i + m) % 380
+            key = f"verify_m{m}_ms" + ("" if not moe else ("_dedup" if mode else "_per_slot"))
+            res[key] = round(float(np.mean(ms[1:])), 4)
+            log(f"{key}: {res[key]} ms, context {eng.context_length}")
+    eng.close()
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def bench_prefill(args) -> int:
     """Prefill (time to the first token) of the 1024-token prompt on the
     8B-shaped model (--prefill-layers of its 32 layers) in 64- and 256-row
@@ -615,6 +659,9 @@ def main() -> int:
     ap.add_argument("--moe-pmc-probe", action="store_true",
                     help="MoE expert op kernel sequence for rocprofv3 --pmc (with --moe-dedup)")
     ap.add_argument("--moe-dedup", type=int, default=0, choices=(0, 1))
+    ap.add_argument("--trace-verify", action="store_true",
+                    help="kernel sequence for rocprofv3 --kernel-trace: groups of replayed verify graphs after "
+                         "the workload's prompt (see bench_trace_verify)")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="short fixed kernel sequence for hardware-counter runs (copy probe, read probe, "
                          "gate/up GEMM at m=4 on a 4-layer model of the headline widths)")
@@ -631,6 +678,8 @@ def main() -> int:
     import synth
     from self_speculative_decoding_amd import Engine, make_cfg, skip_mask
 
+    if args.trace_verify:
+        return bench_trace_verify(args)
     if args.pmc_probe:
         return bench_pmc_probe(args)
     if args.moe_pmc_probe:
