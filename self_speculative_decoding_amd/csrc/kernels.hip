@@ -279,31 +279,44 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(AttnArgs a) {
   __asm__ volatile("" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
 
+  // The tiles' phases run side by side (both S^T, both softmaxes, both
+  // O^T), so one tile's MFMA chains overlap the other's; each tile's own
+  // instruction sequence is unchanged.
+  int pos[NT];
+  f32x4 sc[NT][4];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    const int pos = st0 + a.pos_off + qr[t];   // this lane's query position
-    f32x4 sc[4];
+    pos[t] = st0 + a.pos_off + qr[t];   // this lane's query position
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
-      sc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      sc[t][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
-        sc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[kt][ks]),
-                                                         __builtin_bit_cast(bf16x8, qa[t][ks]), sc[kt], 0, 0, 0);
+        sc[t][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[kt][ks]),
+                                                            __builtin_bit_cast(bf16x8, qa[t][ks]), sc[t][kt], 0, 0, 0);
     }
-    // softmax over this partition's keys for query c
-    float m = -INFINITY;
+  }
+  // softmax over this partition's keys for query c
+  float m[NT], l[NT];
+  uint32_t ph[NT][2][4], pl[NT][2][4];   // P^T hi / lo fragments, bf16 pairs
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    m[t] = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const bool valid = qv[t] && key0 + 16 * kt + 4 * kg + i <= pos;
-        m = valid ? fmaxf(m, sc[kt][i] * a.scale_log2) : m;
+        const bool valid = qv[t] && key0 + 16 * kt + 4 * kg + i <= pos[t];
+        m[t] = valid ? fmaxf(m[t], sc[t][kt][i] * a.scale_log2) : m[t];
       }
-    m = fmaxf(m, lane_xor16(m, lane));
-    m = fmaxf(m, lane_xor32(m, lane));
-    float l = 0.f;
-    uint32_t ph[2][4], pl[2][4];   // P^T hi / lo fragments, bf16 pairs
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) m[t] = fmaxf(m[t], lane_xor16(m[t], lane));
+#pragma unroll
+  for (int t = 0; t < NT; ++t) m[t] = fmaxf(m[t], lane_xor32(m[t], lane));
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    l[t] = 0.f;
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
@@ -311,64 +324,69 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(AttnArgs a) {
         float pv[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          const bool valid = qv[t] && key0 + 16 * kt + 4 * kg + i + u <= pos;
-          pv[u] = valid ? exp2f(sc[kt][i + u] * a.scale_log2 - m) : 0.f;
-          l += pv[u];
+          const bool valid = qv[t] && key0 + 16 * kt + 4 * kg + i + u <= pos[t];
+          pv[u] = valid ? exp2f(sc[t][kt][i + u] * a.scale_log2 - m[t]) : 0.f;
+          l[t] += pv[u];
         }
         const uint16_t h0 = f2bf(pv[0]), h1 = f2bf(pv[1]);
         const uint16_t l0 = f2bf(pv[0] - bf2f(h0)), l1 = f2bf(pv[1] - bf2f(h1));
         // K-step kt/2; elements 0..3 from even kt, 4..7 from odd kt
-        ph[kt >> 1][(kt & 1) * 2 + i / 2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-        pl[kt >> 1][(kt & 1) * 2 + i / 2] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+        ph[t][kt >> 1][(kt & 1) * 2 + i / 2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+        pl[t][kt >> 1][(kt & 1) * 2 + i / 2] = (uint32_t)l0 | ((uint32_t)l1 << 16);
       }
-    l += lane_xor16(l, lane);
-    l += lane_xor32(l, lane);
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) l[t] += lane_xor16(l[t], lane);
+#pragma unroll
+  for (int t = 0; t < NT; ++t) l[t] += lane_xor32(l[t], lane);
 
-    if (t == 0) {
-      // keys past the last row's position: P is 0 there; keep 0 * V finite
-      const int maxpos = st0 + a.pos_off + a.M - 1;
+  // keys past the last row's position: P is 0 there; keep 0 * V finite
+  // (selects only: entries at or below the position pass unchanged)
+  {
+    const int maxpos = st0 + a.pos_off + a.M - 1;
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const bool keep = key0 + 32 * ks + 16 * h + 4 * kg + 3 <= maxpos;
-          if (!keep) {
+      for (int h = 0; h < 2; ++h) {
+        const int k = key0 + 32 * ks + 16 * h + 4 * kg;
 #pragma unroll
-            for (int dt = 0; dt < 8; ++dt) {
-              const int k = key0 + 32 * ks + 16 * h + 4 * kg;
-              uint2 v = vf[dt][ks][h];
-              // zero the 16-bit entries past maxpos
-              v.x = k > maxpos ? 0u : (k + 1 > maxpos ? (v.x & 0xffffu) : v.x);
-              v.y = k + 2 > maxpos ? 0u : (k + 3 > maxpos ? (v.y & 0xffffu) : v.y);
-              vf[dt][ks][h] = v;
-            }
-          }
+        for (int dt = 0; dt < 8; ++dt) {
+          uint2 v = vf[dt][ks][h];
+          // zero the 16-bit entries past maxpos
+          v.x = k > maxpos ? 0u : (k + 1 > maxpos ? (v.x & 0xffffu) : v.x);
+          v.y = k + 2 > maxpos ? 0u : (k + 3 > maxpos ? (v.y & 0xffffu) : v.y);
+          vf[dt][ks][h] = v;
         }
-    }
-    f32x4 o[8];
+      }
+  }
+  f32x4 o[NT][8];
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      o[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const uint4 va = {vf[dt][ks][0].x, vf[dt][ks][0].y, vf[dt][ks][1].x, vf[dt][ks][1].y};
-        const uint4 bh = {ph[ks][0], ph[ks][1], ph[ks][2], ph[ks][3]};
-        const uint4 bl = {pl[ks][0], pl[ks][1], pl[ks][2], pl[ks][3]};
-        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va), __builtin_bit_cast(bf16x8, bh),
-                                                        o[dt], 0, 0, 0);
-        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va), __builtin_bit_cast(bf16x8, bl),
-                                                        o[dt], 0, 0, 0);
+        const uint4 bh = {ph[t][ks][0], ph[t][ks][1], ph[t][ks][2], ph[t][ks][3]};
+        const uint4 bl = {pl[t][ks][0], pl[t][ks][1], pl[t][ks][2], pl[t][ks][3]};
+        o[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va),
+                                                           __builtin_bit_cast(bf16x8, bh), o[t][dt], 0, 0, 0);
+        o[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va),
+                                                           __builtin_bit_cast(bf16x8, bl), o[t][dt], 0, 0, 0);
       }
     }
-    if (!qv[t] || key0 > pos) continue;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    if (!qv[t] || key0 > pos[t]) continue;
     const int row = qr[t], head = kvh * G + qg[t];
     const size_t ph_i = ((size_t)row * a.hq + head) * a.pstride + p;
     float* po = a.part_o + ph_i * HD + 4 * kg;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) *(f32x4*)(po + 16 * dt) = o[dt];
+    for (int dt = 0; dt < 8; ++dt) *(f32x4*)(po + 16 * dt) = o[t][dt];
     if (kg == 0) {
-      a.part_ml[ph_i * 2] = m;
-      a.part_ml[ph_i * 2 + 1] = l;
+      a.part_ml[ph_i * 2] = m[t];
+      a.part_ml[ph_i * 2 + 1] = l[t];
     }
   }
 }
