@@ -56,14 +56,28 @@ __device__ __forceinline__ uint4 ld16_nt(const uint16_t* p) {
 // then re-read row w-1 and their MFMA output columns are discarded.
 constexpr int PACK_TILE = 1024;   // elements per packed tile
 
+// Fragment order of a GEMM input (bf16 [rows, K]): the packed tile layout
+// above with the 16 rows of each row tile in the place of a weight tile's 16
+// columns: element (m, k) of chunk k/64 of row tile m/16 at the slot where
+// lane 16g + m%16 reads it for K-step h (k%64 = 16g + 8h + j).  A GEMM then
+// reads each chunk of its A tile as two 1 KB loads, 8 whole cache lines each,
+// where the row-major A touches 16 lines per load instruction.  Producers in
+// passes of several rows write this copy next to the row-major one.
+__device__ __forceinline__ size_t frag_index(int m, int k, int K) {
+  const int q = k & 63;
+  return (((size_t)(m >> 4) * (size_t)(K >> 6) + (size_t)(k >> 6)) << 10) + (((q >> 3) & 1) << 9) +
+         ((((q >> 4) << 4) + (m & 15)) << 3) + (q & 7);
+}
+
 // One wave's share of a 16-row x (NW x 16)-column MFMA tile: the K-chunks
 // c0, c0 + step, c0 + 2 step, ... below c1, 64 elements each, accumulated in
 // that order.  In each chunk lane group g (lane/16) reads 32 contiguous bytes
 // (elements 16g..16g+15) of its A row; the chunk is two MFMA K-steps, the
 // first over elements 16g..16g+7 of every group, the second over
 // 16g+8..16g+15 (A and B permuted alike).
-// xr: this lane's A row at element 16g; wr[j]: packed tile j of this
-// workgroup at chunk 0 plus 8*lane; consecutive chunks of a tile are NW
+// xr: this lane's A row at element 16g (xs = 64, xh = 8), or, for an A tile
+// in fragment order, at 8*lane (xs = 1024, xh = 512); wr[j]: packed tile j of
+// this workgroup at chunk 0 plus 8*lane; consecutive chunks of a tile are NW
 // tiles apart (interleaved pairs).  U chunks of loads are issued before their
 // MFMAs; weights are read with nontemporal loads (read once per pass).
 // CS: elements between consecutive chunks of one weight stream (NW tiles
@@ -71,7 +85,7 @@ constexpr int PACK_TILE = 1024;   // elements per packed tile
 // tile (PACK_TILE, or 64 * width for the narrow gate/up tiles).
 template <int NW, bool NT, int U, int CS = NW * PACK_TILE, int TE = PACK_TILE>
 __device__ __forceinline__ void mfma_stream(const uint16_t* xr, bool xok, const uint16_t* const* wr, int c0, int c1,
-                                            f32x4* acc, int step = 1) {
+                                            f32x4* acc, int step = 1, int xs = 64, int xh = 8) {
   const uint4 zero = {0u, 0u, 0u, 0u};
   auto ldw = [](const uint16_t* p) { return NT ? ld16_nt(p) : ld16(p); };
   const int n = c1 > c0 ? (c1 - c0 + step - 1) / step : 0;
@@ -86,8 +100,8 @@ __device__ __forceinline__ void mfma_stream(const uint16_t* xr, bool xok, const 
         wb[j][u][0] = ldw(wr[j] + s * CS);
         wb[j][u][1] = ldw(wr[j] + s * CS + TE / 2);
       }
-      xa[u][0] = xok ? ld16(xr + s * 64) : zero;
-      xa[u][1] = xok ? ld16(xr + s * 64 + 8) : zero;
+      xa[u][0] = xok ? ld16(xr + s * xs) : zero;
+      xa[u][1] = xok ? ld16(xr + s * xs + xh) : zero;
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
@@ -102,7 +116,7 @@ __device__ __forceinline__ void mfma_stream(const uint16_t* xr, bool xok, const 
     const size_t s = (size_t)c0 + (size_t)i * step;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const uint4 xa = xok ? ld16(xr + s * 64 + 8 * h) : zero;
+      const uint4 xa = xok ? ld16(xr + s * xs + xh * h) : zero;
 #pragma unroll
       for (int j = 0; j < NW; ++j) {
         const uint4 wb = ldw(wr[j] + s * CS + h * (TE / 2));

@@ -88,7 +88,9 @@ __device__ __forceinline__ void epi_single(const GemmArgs& a, int epi, int m, in
 template <typename E>
 __device__ __forceinline__ void epi_swiglu(const GemmArgs& a, int m, int n, float g, float u) {
   const float s = g / (1.0f + expf(-g));
-  ((E*)a.out)[(size_t)m * a.ldo + n] = fromf<E>(s * u);
+  const E v = fromf<E>(s * u);
+  ((E*)a.out)[(size_t)m * a.ldo + n] = v;
+  if (sizeof(E) == 2 && a.out_p) ((E*)a.out_p)[frag_index(m, n, a.N)] = v;
 }
 
 // (v0, v1) are dims (i, i + hd/2) of output head `head` of [q | k | v]
@@ -142,7 +144,10 @@ __device__ __forceinline__ void epi_resid_fold(const GemmArgs& a, int m, int n, 
   if (ok) {
     a.y[(size_t)m * a.ldy + n] = xv;
     if (a.tap) ((uint16_t*)a.tap)[(size_t)m * a.ldtap + n] = f2bf(xv);
-    ((uint16_t*)a.xg_out)[(size_t)m * a.ldy + n] = f2bf(xv * bf2f(((const uint16_t*)a.gain_next)[n]));
+    if (a.tap_p) ((uint16_t*)a.tap_p)[frag_index(m, a.tap_col + n, a.ldtap)] = f2bf(xv);
+    const uint16_t xg = f2bf(xv * bf2f(((const uint16_t*)a.gain_next)[n]));
+    ((uint16_t*)a.xg_out)[(size_t)m * a.ldy + n] = xg;
+    if (a.xg_out_p) ((uint16_t*)a.xg_out_p)[frag_index(m, n, a.N)] = xg;
     if (c == 0) a.ss_out[(size_t)m * ntiles + tt] = sq;
   }
 }
@@ -234,6 +239,11 @@ __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
     xr[r] = (const uint16_t*)a.X + (size_t)(av_ok[r] ? am : 0) * a.ldx + kg * 16;
   }
   const int S = a.K >> 6;   // 64-element chunks
+  // an A tile in fragment order (decode passes of several rows): each chunk
+  // is two 1 KB loads (the same values, so the same results)
+  const bool xfrag = MT == 1 && a.Xp != nullptr;
+  if (xfrag) xr[0] = (const uint16_t*)a.Xp + ((size_t)by * S << 10) + 8 * lane;
+  const int xs = xfrag ? 1024 : 64, xh = xfrag ? 512 : 8;
   // packed weight tiles: gate/up interleaved when NW = 2, else TPW tiles
   // stream j: matrix j % NW of column tile t0 + j / NW
   const uint16_t* wr[NS];
@@ -316,7 +326,7 @@ __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
     // first load batch, then the rotary table entries of this wave's
     // epilogue rows (they need the position), then the rest of the K range
     const int sm = min(s0 + U * kst, s1);
-    mfma_stream<NS, true, U, CS, TE>(xr[0], av_ok[0], wr, s0, sm, acc[0], kst);
+    mfma_stream<NS, true, U, CS, TE>(xr[0], av_ok[0], wr, s0, sm, acc[0], kst, xs, xh);
     {
       const int half = a.hd >> 1;
 #pragma unroll
@@ -332,9 +342,9 @@ __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
         }
       }
     }
-    mfma_stream<NS, true, U, CS, TE>(xr[0], av_ok[0], wr, sm, s1, acc[0], kst);
+    mfma_stream<NS, true, U, CS, TE>(xr[0], av_ok[0], wr, sm, s1, acc[0], kst, xs, xh);
   } else if (MT == 1) {
-    mfma_stream<NS, true, U, CS, TE>(xr[0], av_ok[0], wr, s0, s1, acc[0], kst);
+    mfma_stream<NS, true, U, CS, TE>(xr[0], av_ok[0], wr, s0, s1, acc[0], kst, xs, xh);
   }
   else mfma_stream_mt<NS, MT, CS, TE>(xr, av_ok, wr, s0, s1, acc);
 
@@ -467,6 +477,7 @@ __global__ __launch_bounds__(64 * KW) void gemm_bf16_kernel(GemmArgs a) {
           const float xv = yv[j][i] + acc[r][j][i];
           a.y[(size_t)m * a.ldy + n] = xv;
           if (a.tap) ((uint16_t*)a.tap)[(size_t)m * a.ldtap + n] = f2bf(xv);
+          if (a.tap_p) ((uint16_t*)a.tap_p)[frag_index(m, a.tap_col + n, a.ldtap)] = f2bf(xv);
         } else epi_single<uint16_t>(a, EPI, m, n, acc[r][j][i]);
       }
     }

@@ -222,6 +222,13 @@ bool compute_layout(const ssd_cfg& c, Layout& L) {
     L.m_groups = take((16 + max_units * 18) * 4);
     L.m_union = take((size_t)c.n_layers * 4);
   }
+  if (c.dtype == SSD_BF16 && c.n_experts == 0) {   // fragment-order copies of the dense GEMM inputs
+    L.frag = true;
+    L.xn_p = take((size_t)kFragRows * d * 2);
+    L.att_p = take((size_t)kFragRows * hq * hd * 2);
+    L.act_p = take((size_t)kFragRows * c.ffn_dim * 2);
+    if (c.n_feat > 0) L.tap_p = take((size_t)kFragRows * c.n_feat * d * 2);
+  }
   L.wpack = take((size_t)packed_elems(c) * 2);   // bf16 GEMM weights in the packed tile layout
   L.total = off;
   return true;

@@ -10,6 +10,9 @@
 namespace ssd {
 
 constexpr int kAttPT = 64;   // attention key partition width (kernels.h: ATT_PT)
+// Passes of kFragMinM..kFragRows rows of dense bf16 models also keep their
+// GEMM inputs in fragment order (frag_index in device.h): two row tiles.
+constexpr int kFragMinM = 5, kFragRows = 32;
 constexpr int kTestCycles = 4096;   // sampling test cycles per output copy
 // sampling scratch (kernels.h: SMP_CHUNK, SMP_ROWS, SMP_CTL_BYTES)
 constexpr int kSmpChunk = 2048, kSmpRows = 63, kSmpCtlBytes = 64;
@@ -23,6 +26,8 @@ struct Layout {
   size_t tap = 0, feat = 0, amax_v = 0, amax_i = 0, trace = 0, trace_pts = 0, wpack = 0, exit_x = 0, exit_ss = 0, dlog = 0, tout = 0;
   size_t smp_stats = 0, smp_csum = 0, smp_ctl = 0, smp_nch = 0;
   size_t m_rlogits = 0, m_ids = 0, m_gates = 0, m_inject = 0, m_slot_out = 0, m_groups = 0, m_union = 0;
+  size_t xn_p = 0, att_p = 0, act_p = 0, tap_p = 0;   // fragment-order GEMM inputs (frag = true)
+  bool frag = false;
   size_t total = 0;
   int R = 0;        // rows per pass (multiple of 16)
   int n_part = 0;   // attention partitions covering max_ctx

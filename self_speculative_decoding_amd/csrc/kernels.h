@@ -25,6 +25,8 @@ enum Epi {
 struct GemmArgs {
   const void* X;              // activations [M, K], row stride ldx (elements)
   int ldx;
+  const void* Xp;             // optional: the same activations in fragment order (frag_index), read instead of X
+                              // by one-tile-row launches
   const void* W0;             // weights [rows, K] row-major
   const void* W1;
   const void* W2;
@@ -36,6 +38,9 @@ struct GemmArgs {
   int ldo;
   void* tap;                  // RESID: optional copy of the new residual (activation type)
   int ldtap;
+  void* tap_p;                // RESID: optional fragment-order copy of the tap: column tap_col + n of [M, ldtap]
+  int tap_col;
+  void* out_p;                // SWIGLU: optional fragment-order copy of out ([M, N])
   // QKV epilogue
   void* q;                    // [M, hq*hd]
   void* kc;                   // this layer's K cache [hkv][max_ctx][hd]
@@ -61,6 +66,7 @@ struct GemmArgs {
   float* ss_out;
   void* xg_out;
   const void* gain_next;
+  void* xg_out_p;             // optional fragment-order copy of xg_out ([M, N])
   // set by the launcher only: a 1-D launch of remap_gx x remap_rb workgroups
   // of the multi-row-tile kernel mapped XCD-aware (see gemm.hip); 0 otherwise
   int remap_gx, remap_rb;
@@ -74,6 +80,7 @@ struct AttnArgs {
   const void* kc;             // [hkv][max_ctx][hd]
   const void* vc;             // [hkv][hd][max_ctx]
   void* out;                  // [M, hq*hd]
+  void* out_p;                // optional fragment-order copy of out (bf16 only)
   float* part_o;              // [R][hq][pstride][hd]: one row-head's partitions contiguous
   float* part_ml;             // [R][hq][pstride][2]
   const int* state;
@@ -86,9 +93,10 @@ struct AttnArgs {
 // dtype: 0 = f32, 1 = bf16 (uint16 bit patterns)
 hipError_t launch_embed(int dtype, const int* tok, const void* E, float* x, int d, int M, hipStream_t s);
 // bf16 embedding that also leaves the folded-RMSNorm inputs of the first layer:
-// xg = bf16(x * gain) and sums of squares over runs of ssw columns (16, 10 or 8), ss [M][d/ssw]
+// xg = bf16(x * gain) and sums of squares over runs of ssw columns (16, 10 or 8), ss [M][d/ssw];
+// xgp (optional): a fragment-order copy of xg (frag_index)
 hipError_t launch_embed_norm(const int* tok, const void* E, float* x, int d, int M, const void* gain, void* xg,
-                             float* ss, int ssw, hipStream_t s);
+                             float* ss, int ssw, hipStream_t s, void* xgp = nullptr);
 hipError_t launch_rmsnorm(int dtype, const float* x, int ldx, const void* g, void* y, int ldy, int d,
                           float eps, int M, hipStream_t s);
 hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t s);
@@ -101,8 +109,9 @@ hipError_t launch_set_state(int* state, int idx, int value, hipStream_t s);
 hipError_t launch_read_probe(const void* src, size_t bytes, unsigned* sink, int blocks, hipStream_t s);
 hipError_t launch_copy_tokens(const int* src, int* dst, int n, hipStream_t s);
 hipError_t launch_copy_f32(const float* src, float* dst, int n, hipStream_t s);
-// xg[m][n] = bf16(x[m][n] * g[n]) for M rows of d (the folded-norm input)
-hipError_t launch_scale_bf16(const float* x, const void* g, void* xg, int d, int M, hipStream_t s);
+// xg[m][n] = bf16(x[m][n] * g[n]) for M rows of d (the folded-norm input); xgp as in launch_embed_norm
+hipError_t launch_scale_bf16(const float* x, const void* g, void* xg, int d, int M, hipStream_t s,
+                             void* xgp = nullptr);
 
 // MoE (routed experts + shared experts)
 struct MoeArgs {

@@ -25,7 +25,8 @@ __global__ __launch_bounds__(256) void embed_kernel(const int* __restrict__ tok,
 template <int SSW>
 __global__ __launch_bounds__(256) void embed_norm_kernel(const int* __restrict__ tok, const uint16_t* __restrict__ emb,
                                                          float* __restrict__ x, int d, const uint16_t* __restrict__ g,
-                                                         uint16_t* __restrict__ xg, float* __restrict__ ss) {
+                                                         uint16_t* __restrict__ xg, float* __restrict__ ss,
+                                                         uint16_t* __restrict__ xgp) {
   const int m = blockIdx.x;
   const uint16_t* row = emb + (size_t)tok[m] * d;
   for (int c0 = threadIdx.x * SSW; c0 < d; c0 += 256 * SSW) {
@@ -34,7 +35,9 @@ __global__ __launch_bounds__(256) void embed_norm_kernel(const int* __restrict__
     for (int j = 0; j < SSW; ++j) {
       const float v = bf2f(row[c0 + j]);
       x[(size_t)m * d + c0 + j] = v;
-      xg[(size_t)m * d + c0 + j] = f2bf(v * bf2f(g[c0 + j]));
+      const uint16_t vg = f2bf(v * bf2f(g[c0 + j]));
+      xg[(size_t)m * d + c0 + j] = vg;
+      if (xgp) xgp[frag_index(m, c0 + j, d)] = vg;   // fragment-order copy (frag_index)
       q = fmaf(v, v, q);
     }
     ss[(size_t)m * (d / SSW) + c0 / SSW] = q;
@@ -467,7 +470,9 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
     for (int j = 0; j < B; ++j)
       if (p0 + j < np) acc += sw[p0 + j] * v[j];
   }
-  ((E*)a.out)[(size_t)row * a.hq * a.hd + (size_t)head * a.hd + t] = fromf<E>(acc / L);
+  const E ov = fromf<E>(acc / L);
+  ((E*)a.out)[(size_t)row * a.hq * a.hd + (size_t)head * a.hd + t] = ov;
+  if (sizeof(E) == 2 && a.out_p) ((E*)a.out_p)[frag_index(row, head * a.hd + t, a.hq * a.hd)] = ov;
 }
 
 // ---------------------------------------------------------------------------
@@ -595,9 +600,14 @@ __global__ __launch_bounds__(256) void copy_f32_kernel(const float* __restrict__
 }
 
 __global__ __launch_bounds__(256) void scale_bf16_kernel(const float* __restrict__ x, const uint16_t* __restrict__ g,
-                                                         uint16_t* __restrict__ xg, int d, int n) {
+                                                         uint16_t* __restrict__ xg, int d, int n,
+                                                         uint16_t* __restrict__ xgp) {
   const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i < n) xg[i] = f2bf(x[i] * bf2f(g[i % d]));
+  if (i < n) {
+    const uint16_t v = f2bf(x[i] * bf2f(g[i % d]));
+    xg[i] = v;
+    if (xgp) xgp[frag_index(i / d, i % d, d)] = v;   // fragment-order copy (frag_index)
+  }
 }
 
 __global__ void copy_tokens_kernel(const int* src, int* dst, int n) {
@@ -615,13 +625,13 @@ hipError_t launch_embed(int dtype, const int* tok, const void* E, float* x, int 
 }
 
 hipError_t launch_embed_norm(const int* tok, const void* E, float* x, int d, int M, const void* gain, void* xg,
-                             float* ss, int ssw, hipStream_t s) {
+                             float* ss, int ssw, hipStream_t s, void* xgp) {
   if (d % ssw != 0) return hipErrorInvalidValue;
   const uint16_t *e16 = (const uint16_t*)E, *g16 = (const uint16_t*)gain;
   switch (ssw) {   // the residual tile widths (resid_tile_width)
-    case 16: embed_norm_kernel<16><<<M, 256, 0, s>>>(tok, e16, x, d, g16, (uint16_t*)xg, ss); break;
-    case 10: embed_norm_kernel<10><<<M, 256, 0, s>>>(tok, e16, x, d, g16, (uint16_t*)xg, ss); break;
-    case 8: embed_norm_kernel<8><<<M, 256, 0, s>>>(tok, e16, x, d, g16, (uint16_t*)xg, ss); break;
+    case 16: embed_norm_kernel<16><<<M, 256, 0, s>>>(tok, e16, x, d, g16, (uint16_t*)xg, ss, (uint16_t*)xgp); break;
+    case 10: embed_norm_kernel<10><<<M, 256, 0, s>>>(tok, e16, x, d, g16, (uint16_t*)xg, ss, (uint16_t*)xgp); break;
+    case 8: embed_norm_kernel<8><<<M, 256, 0, s>>>(tok, e16, x, d, g16, (uint16_t*)xg, ss, (uint16_t*)xgp); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -699,9 +709,9 @@ hipError_t launch_copy_f32(const float* src, float* dst, int n, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_scale_bf16(const float* x, const void* g, void* xg, int d, int M, hipStream_t s) {
+hipError_t launch_scale_bf16(const float* x, const void* g, void* xg, int d, int M, hipStream_t s, void* xgp) {
   const int n = d * M;
-  scale_bf16_kernel<<<(n + 255) / 256, 256, 0, s>>>(x, (const uint16_t*)g, (uint16_t*)xg, d, n);
+  scale_bf16_kernel<<<(n + 255) / 256, 256, 0, s>>>(x, (const uint16_t*)g, (uint16_t*)xg, d, n, (uint16_t*)xgp);
   return hipGetLastError();
 }
 

@@ -104,6 +104,7 @@ struct ssd_ctx {
   float *x, *ss, *logits, *part_o, *part_ml, *cos_t, *sin_t, *amax_v;
   int* amax_i;
   void *xn, *q, *att, *act, *kc, *vc, *tap, *feat;
+  void *xn_p = nullptr, *att_p = nullptr, *act_p = nullptr, *tap_p = nullptr;   // fragment-order GEMM inputs
   int *block, *post, *toks, *dstate, *result, *outlog;
   int *tblock, *tpost, *tstate, *tresult, *toutlog;
   float *m_rlogits, *m_gates, *m_slot_out;
@@ -180,8 +181,17 @@ hipError_t trace_point(ssd_ctx* c, int l, int pt, const void* src, int M) {
   return launch_copy_f32((const float*)src, (float*)(c->trace_pts + off), (int)(M * row / 4), c->stream);
 }
 
-// One decoder layer over M rows at positions state[0] + pos_off + r.
-ssd_status layer_forward(ssd_ctx* c, int l, int M, int pos_off, bool feats, const void* gain_next) {
+// Passes of kFragMinM..kFragRows rows of dense bf16 models keep a
+// fragment-order copy of every GEMM input (frag_index): their GEMMs then load
+// each A chunk as two 1 KB reads (whole cache lines) instead of 16 rows of 64
+// bytes per load, which costs the wide verify blocks most.  The copy holds
+// the same values, so results do not change; a function of M only.
+inline bool frag_pass(const ssd_ctx* c, int M) { return c->xn_p && M >= kFragMinM && M <= kFragRows; }
+
+// One decoder layer over M rows at positions state[0] + pos_off + r.  fr:
+// every producer also writes the fragment-order copy of the next GEMM's
+// input and every GEMM reads that copy (frag_pass).
+ssd_status layer_forward(ssd_ctx* c, int l, int M, int pos_off, bool feats, const void* gain_next, bool fr) {
   const ssd_cfg& g = c->cfg;
   const LayerW& w = c->L[l];
   const int d = g.d_model, hq = g.n_q_heads, hkv = g.n_kv_heads, hd = g.head_dim;
@@ -197,6 +207,7 @@ ssd_status layer_forward(ssd_ctx* c, int l, int M, int pos_off, bool feats, cons
   {
     GemmArgs a{};
     a.X = c->xn; a.ldx = d; a.W0 = w.wq; a.W1 = w.wk; a.W2 = w.wv;
+    a.Xp = fr ? c->xn_p : nullptr;
     a.n0 = hq * hd; a.n1 = hkv * hd; a.M = M; a.N = (hq + 2 * hkv) * hd; a.K = d;
     a.q = c->q; a.kc = kc; a.vc = vc; a.cos_t = c->cos_t; a.sin_t = c->sin_t;
     a.state = c->dstate; a.pos_off = pos_off; a.hq = hq; a.hkv = hkv; a.hd = hd; a.max_ctx = kv_stride(g);
@@ -207,6 +218,7 @@ ssd_status layer_forward(ssd_ctx* c, int l, int M, int pos_off, bool feats, cons
   {
     AttnArgs a{};
     a.q = c->q; a.kc = kc; a.vc = vc; a.out = c->att; a.part_o = c->part_o; a.part_ml = c->part_ml; a.pstride = c->lay.n_part;
+    a.out_p = fr ? c->att_p : nullptr;
     a.state = c->dstate; a.pos_off = pos_off; a.M = M; a.R = c->lay.R;
     a.hq = hq; a.hkv = hkv; a.hd = hd; a.max_ctx = kv_stride(g);
     a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)hd));
@@ -219,7 +231,9 @@ ssd_status layer_forward(ssd_ctx* c, int l, int M, int pos_off, bool feats, cons
   {
     GemmArgs a{};
     a.X = c->att; a.ldx = hq * hd; a.W0 = w.wo; a.M = M; a.N = d; a.K = hq * hd; a.y = c->x; a.ldy = d;
+    a.Xp = fr ? c->att_p : nullptr;
     if (fold && !w.moe) fold_out(c, a, w.ffn_norm);
+    a.xg_out_p = fr ? c->xn_p : nullptr;
     HIPCHK(run_gemm(c, EPI_RESID, a));
   }
   if (tr) HIPCHK(trace_point(c, l, 3, c->x, M));
@@ -237,16 +251,24 @@ ssd_status layer_forward(ssd_ctx* c, int l, int M, int pos_off, bool feats, cons
     GemmArgs a{};
     a.X = c->xn; a.ldx = d; a.W0 = w.w_gate; a.W1 = w.w_up; a.M = M; a.N = w.ffn; a.K = d;
     a.out = c->act; a.ldo = w.ffn;
+    a.Xp = fr ? c->xn_p : nullptr;
+    a.out_p = fr ? c->act_p : nullptr;
     if (fold) fold_in(c, a, 0);
     HIPCHK(run_gemm(c, EPI_SWIGLU, a));
     if (tr) HIPCHK(trace_point(c, l, 5, c->act, M));
     GemmArgs b{};
     b.X = c->act; b.ldx = w.ffn; b.W0 = w.w_down; b.M = M; b.N = d; b.K = w.ffn; b.y = c->x; b.ldy = d;
+    b.Xp = fr ? c->act_p : nullptr;
     if (feats && w.feat_slot >= 0) {
       b.tap = (char*)c->tap + (size_t)w.feat_slot * d * c->esz;
       b.ldtap = g.n_feat * d;
+      if (fr) {
+        b.tap_p = c->tap_p;
+        b.tap_col = w.feat_slot * d;
+      }
     }
     if (fold) fold_out(c, b, gain_next);
+    b.xg_out_p = fr ? c->xn_p : nullptr;
     HIPCHK(run_gemm(c, EPI_RESID, b));
   }
   if (c->trace_on && M <= g.max_block)
@@ -276,20 +298,23 @@ ssd_status run_pass(ssd_ctx* c, const int* d_tok, int M, int pos_off, const uint
   hipStream_t s = c->stream;
   if (c->moe_inject && M > c->moe_inject)
     return fail(SSD_E_ARG, "pass of %d rows but routing was injected for %d", M, c->moe_inject);
+  const bool fr = frag_pass(c, M);
+  void* xgp = fr ? c->xn_p : nullptr;
   if (ps.load) {
     HIPCHK(launch_copy_f32(c->exit_x, c->x, M * d, s));
     if (fold) {
       HIPCHK(launch_copy_f32(c->exit_ss, c->ss, M * n_ss(g), s));
-      HIPCHK(launch_scale_bf16(c->x, next_gain(c, -1, skip), c->xn, d, M, s));
+      HIPCHK(launch_scale_bf16(c->x, next_gain(c, -1, skip), c->xn, d, M, s, xgp));
     }
   } else if (fold) {
-    HIPCHK(launch_embed_norm(d_tok, c->embed, c->x, d, M, next_gain(c, -1, skip), c->xn, c->ss, resid_tile_width(d), s));
+    HIPCHK(launch_embed_norm(d_tok, c->embed, c->x, d, M, next_gain(c, -1, skip), c->xn, c->ss, resid_tile_width(d), s,
+                             xgp));
   } else {
     HIPCHK(launch_embed(dt, d_tok, c->embed, c->x, d, M, s));
   }
   for (int l = 0; l < g.n_layers; ++l) {
     if (skip && skip[l]) continue;
-    SSDCHK(layer_forward(c, l, M, pos_off, feats, next_gain(c, l, skip)));
+    SSDCHK(layer_forward(c, l, M, pos_off, feats, next_gain(c, l, skip), fr));
   }
   if (ps.save_row >= 0) {
     HIPCHK(launch_copy_f32(c->x, c->exit_x + (size_t)ps.save_row * d, M * d, s));
@@ -302,6 +327,7 @@ ssd_status run_pass(ssd_ctx* c, const int* d_tok, int M, int pos_off, const uint
     GemmArgs a{};
     a.X = fold ? (const void*)((const uint16_t*)c->xn + (size_t)head_row0 * d) : c->xn;
     a.ldx = d; a.W0 = c->lm_head; a.M = head_rows; a.N = g.vocab; a.K = d;
+    a.Xp = fr && head_row0 == 0 ? c->xn_p : nullptr;
     a.y = c->logits; a.ldy = g.vocab;
     if (dt == SSD_BF16) {
       // the LM head epilogue leaves (max, index) per 16 columns; reduce those
@@ -318,6 +344,7 @@ ssd_status run_pass(ssd_ctx* c, const int* d_tok, int M, int pos_off, const uint
   if (feats && g.n_feat > 0) {
     GemmArgs a{};
     a.X = c->tap; a.ldx = g.n_feat * d; a.W0 = c->fc; a.M = M; a.N = d; a.K = g.n_feat * d;
+    a.Xp = fr ? c->tap_p : nullptr;
     a.out = c->feat; a.ldo = d;
     HIPCHK(run_gemm(c, EPI_STORE, a));
     c->feat_rows = M;
@@ -645,6 +672,10 @@ ssd_status ssd_load(const ssd_cfg* cfg, const ssd_buf* weights, int32_t n_weight
   c->tresult = (int*)at(c, lay.tresult); c->toutlog = (int*)at(c, lay.toutlog);
   c->tap = cfg->n_feat ? at(c, lay.tap) : nullptr;
   c->feat = cfg->n_feat ? at(c, lay.feat) : nullptr;
+  if (lay.frag) {
+    c->xn_p = at(c, lay.xn_p); c->att_p = at(c, lay.att_p); c->act_p = at(c, lay.act_p);
+    c->tap_p = cfg->n_feat ? at(c, lay.tap_p) : nullptr;
+  }
   if (cfg->n_experts > 0) {
     c->m_rlogits = (float*)at(c, lay.m_rlogits); c->m_ids = (int*)at(c, lay.m_ids);
     c->m_gates = (float*)at(c, lay.m_gates); c->m_inject = (int*)at(c, lay.m_inject);
@@ -1219,11 +1250,17 @@ ssd_status ssd_time_op(ssd_ctx* c, int32_t op, int32_t layer, int32_t m, int32_t
       at.state = c->dstate; at.pos_off = 0; at.M = m; at.R = c->lay.R;
       at.hq = hq; at.hkv = hkv; at.hd = hd; at.max_ctx = kv_stride(g);
       at.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)hd));
+      at.out_p = frag_pass(c, m) ? c->att_p : nullptr;
       HIPCHK(launch_attention(dt, at, (c->n + m + ATT_PT - 1) / ATT_PT, s));
     } else {
       // bf16 GEMMs carry their folded-norm work as in a pass
       if (dt == SSD_BF16 && (op == 0 || op == 2 || op == 4)) fold_in(c, a, 0);
       if (dt == SSD_BF16 && (op == 1 || op == 3)) fold_out(c, a, w.ffn_norm);
+      if (frag_pass(c, m)) {   // as a pass of m rows: fragment-order inputs and outputs
+        a.Xp = op == 1 ? c->act_p : op == 3 ? c->att_p : c->xn_p;
+        if (op == 0) a.out_p = c->act_p;
+        if (op == 1 || op == 3) a.xg_out_p = c->xn_p;
+      }
       HIPCHK(run_gemm(c, epi, a));
     }
   }
