@@ -142,10 +142,10 @@ __device__ __forceinline__ void epi_resid_fold(const GemmArgs& a, int m, int n, 
 #pragma unroll
   for (int o = 1; o < 16; o <<= 1) sq += __shfl_xor(sq, o);
   if (ok) {
+    const uint16_t xg = f2bf(xv * bf2f(((const uint16_t*)a.gain_next)[n]));
     a.y[(size_t)m * a.ldy + n] = xv;
     if (a.tap) ((uint16_t*)a.tap)[(size_t)m * a.ldtap + n] = f2bf(xv);
     if (a.tap_p) ((uint16_t*)a.tap_p)[frag_index(m, a.tap_col + n, a.ldtap)] = f2bf(xv);
-    const uint16_t xg = f2bf(xv * bf2f(((const uint16_t*)a.gain_next)[n]));
     ((uint16_t*)a.xg_out)[(size_t)m * a.ldy + n] = xg;
     if (a.xg_out_p) ((uint16_t*)a.xg_out_p)[frag_index(m, n, a.N)] = xg;
     if (c == 0) a.ss_out[(size_t)m * ntiles + tt] = sq;

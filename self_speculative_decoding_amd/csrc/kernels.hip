@@ -30,17 +30,28 @@ __global__ __launch_bounds__(256) void embed_norm_kernel(const int* __restrict__
   const int m = blockIdx.x;
   const uint16_t* row = emb + (size_t)tok[m] * d;
   for (int c0 = threadIdx.x * SSW; c0 < d; c0 += 256 * SSW) {
+    // every load before the first store and before the optional copy's
+    // branch, so that they are all in flight together
+    uint16_t e[SSW], gw[SSW], vg[SSW];
+#pragma unroll
+    for (int j = 0; j < SSW; ++j) {
+      e[j] = row[c0 + j];
+      gw[j] = g[c0 + j];
+    }
     float q = 0.f;
 #pragma unroll
     for (int j = 0; j < SSW; ++j) {
-      const float v = bf2f(row[c0 + j]);
+      const float v = bf2f(e[j]);
       x[(size_t)m * d + c0 + j] = v;
-      const uint16_t vg = f2bf(v * bf2f(g[c0 + j]));
-      xg[(size_t)m * d + c0 + j] = vg;
-      if (xgp) xgp[frag_index(m, c0 + j, d)] = vg;   // fragment-order copy (frag_index)
+      vg[j] = f2bf(v * bf2f(gw[j]));
+      xg[(size_t)m * d + c0 + j] = vg[j];
       q = fmaf(v, v, q);
     }
     ss[(size_t)m * (d / SSW) + c0 / SSW] = q;
+    if (xgp) {   // fragment-order copy (frag_index)
+#pragma unroll
+      for (int j = 0; j < SSW; ++j) xgp[frag_index(m, c0 + j, d)] = vg[j];
+    }
   }
 }
 
@@ -644,6 +655,10 @@ hipError_t launch_rmsnorm(int dtype, const float* x, int ldx, const void* g, voi
   return hipGetLastError();
 }
 
+#ifndef SSD_ATT_NT2_MIN   // 16-query tiles per KV head from which one wave takes two of them
+#define SSD_ATT_NT2_MIN 2
+#endif
+
 template <typename E>
 static hipError_t attn_dispatch(AttnArgs a, int n_part, int hd, hipStream_t s) {
   if (n_part < 1 || n_part > a.pstride) return hipErrorInvalidValue;
@@ -658,7 +673,7 @@ static hipError_t attn_dispatch(AttnArgs a, int n_part, int hd, hipStream_t s) {
     const dim3 g1(n_part, a.hkv, tiles), g2(n_part, a.hkv, (tiles + 1) / 2);
 #define SSD_ATTM(Gv)                                                              \
     if (G == Gv) {                                                                \
-      if (tiles >= 2) attn_mfma_kernel<Gv, 2><<<g2, 64, 0, s>>>(a);              \
+      if (tiles >= SSD_ATT_NT2_MIN) attn_mfma_kernel<Gv, 2><<<g2, 64, 0, s>>>(a); \
       else attn_mfma_kernel<Gv, 1><<<g1, 64, 0, s>>>(a);                         \
       done = true;                                                                \
     }
