@@ -32,6 +32,9 @@
 #ifndef SSD_TPW_MIN_M        // tile groups only for passes wider than this
 #define SSD_TPW_MIN_M 8
 #endif
+#ifndef SSD_TPW_MIN_WG       // ... and only where at least this many workgroups remain
+#define SSD_TPW_MIN_WG 256
+#endif
 #ifndef SSD_KW_SWIGLU
 #define SSD_KW_SWIGLU 8
 #endif
@@ -890,14 +893,16 @@ hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t s) {
     }
     // passes wider than 8 rows group 2 or 4 column tiles per workgroup so
     // the A operand is read once for them (results unchanged, see the kernel),
-    // but only where at least 1024 workgroups remain: spreading the weight
-    // stream over every CU matters more than the A reads (measured)
+    // but only where at least SSD_TPW_MIN_WG workgroups remain, one per CU:
+    // spreading the weight stream over every CU matters more than the A reads
+    // (measured at 16 rows: the LM head 250 -> 231 us with 4 tiles, QKV of 512
+    // tiles 13.7 -> 12.1 us with 2; o and down keep their 256 workgroups)
     // (never for long-K narrow tiles: their one-tile kernel splits K over
     // more waves, and a row's K split must not depend on the pass width)
     int tpw = 1;
     const bool tpw_ok = a.M > SSD_TPW_MIN_M && !(a.K >= 8192 && tw < 16);
-    if (tpw_ok && tiles % 4 == 0 && tiles / 4 >= 1024) tpw = 4;
-    else if (tpw_ok && tiles % 2 == 0 && tiles / 2 >= 1024) tpw = 2;
+    if (tpw_ok && tiles % 4 == 0 && tiles / 4 >= SSD_TPW_MIN_WG) tpw = 4;
+    else if (tpw_ok && tiles % 2 == 0 && tiles / 2 >= SSD_TPW_MIN_WG) tpw = 2;
 #define SSD_G1(E, KWN, UN, TWV)                                                                         \
   if (multi) {                                                                                           \
     if (tpm == 4) gemm_bf16_kernel<E, 1, SSD_MT_KW, SSD_MT_MT, 1, 4, TWV><<<grid_mt, 64 * SSD_MT_KW, 0, s>>>(am); \
