@@ -126,15 +126,18 @@ class Model:
         """x [M, in] times W [out, in] transposed."""
         return x @ W.astype(np.float64, copy=False).T
 
-    def normed_lin(self, x: np.ndarray, g: np.ndarray, Ws) -> list[np.ndarray]:
-        """RMSNorm with gain g followed by products with each W of Ws.
-
-        Exact arithmetic gives lin(rmsnorm(x, g), W).  The stored operand is
+    def norm_input(self, x: np.ndarray, g: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+        """RMSNorm with gain g, as it feeds a product: the stored operand is
         the gain-scaled input x * g (rounded like every stored matrix input)
-        and the 1/rms factor multiplies the product: the normalisation is a
-        per-row scalar, so it commutes with the product."""
+        and the per-row 1/rms factor [M, 1] multiplies each product of it.
+        The normalisation is a per-row scalar, so it commutes with the
+        product: in exact arithmetic lin(x * g, W) * rstd = lin(rmsnorm(x, g), W)."""
         rstd = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + self.eps)
-        xg = self.rn(x * g)
+        return self.rn(x * g), rstd
+
+    def normed_lin(self, x: np.ndarray, g: np.ndarray, Ws) -> list[np.ndarray]:
+        """RMSNorm with gain g followed by products with each W of Ws (norm_input)."""
+        xg, rstd = self.norm_input(x, g)
         return [self.lin(xg, W) * rstd for W in Ws]
 
     # -- blocks --------------------------------------------------------------
@@ -180,47 +183,60 @@ class Model:
         act = self.rn(silu(gate) * up)
         return self.lin(act, w[p + "w_down"])
 
-    def expert(self, l: int, e: int, rows: np.ndarray, shared: bool = False) -> np.ndarray:
+    def expert(self, l: int, e: int, rows: np.ndarray, rstd: np.ndarray, shared: bool = False) -> np.ndarray:
+        """SwiGLU expert e of layer l on stored input rows [n, d] whose gate
+        and up products take their rows' 1/rms factors rstd [n, 1]."""
         w, p = self.w, f"l{l}." + ("sh_" if shared else "exp_")
-        act = self.rn(silu(self.lin(rows, w[p + "gate"][e])) * self.lin(rows, w[p + "up"][e]))
+        gate = self.lin(rows, w[p + "gate"][e]) * rstd
+        up = self.lin(rows, w[p + "up"][e]) * rstd
+        act = self.rn(silu(gate) * up)
         return self.lin(act, w[p + "down"][e])
 
-    def route(self, l: int, n2: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
-        """Router probabilities [M, E] and top_k ids [M, top_k] (ties -> lower id)."""
-        probs = softmax(self.lin(n2, self.w[f"l{l}.router"]))
+    def route(self, l: int, xg: np.ndarray, rstd: np.ndarray | None = None) -> tuple[np.ndarray, np.ndarray]:
+        """Router probabilities [M, E] and top_k ids [M, top_k] (ties -> lower
+        id) of stored input rows xg with 1/rms factors rstd (None: 1)."""
+        z = self.lin(xg, self.w[f"l{l}.router"])
+        if rstd is not None:
+            z = z * rstd
+        probs = softmax(z)
         ids = np.argsort(-probs, axis=-1, kind="stable")[:, :self.cfg["top_k"]]
         return probs, ids
 
-    def moe_ffn(self, l: int, n2: np.ndarray, dedup: bool = False) -> np.ndarray:
-        M = n2.shape[0]
-        probs, ids = self.route(l, n2)
+    def moe_ffn(self, l: int, xg: np.ndarray, rstd: np.ndarray | None = None, dedup: bool = False) -> np.ndarray:
+        """Routed and shared experts of layer l over stored input rows xg
+        [M, d]; rstd [M, 1]: the rows' 1/rms factors of the folded ffn norm
+        (norm_input), which multiply the router's and the experts' gate and
+        up products (None: 1, the block applied to xg itself)."""
+        M = xg.shape[0]
+        r = np.ones((M, 1)) if rstd is None else rstd
+        probs, ids = self.route(l, xg, r)
         if self.routing is not None:
             ids = np.asarray(self.routing[l], dtype=np.int64)[:M]
         gate = np.take_along_axis(probs, ids, axis=-1)             # not renormalised
         self.union[l] = len(set(int(e) for e in ids.reshape(-1)))
-        y = np.zeros_like(n2)
+        y = np.zeros(xg.shape)
         if dedup:
             # every expert of the union evaluated once over the rows that chose it
-            per = np.zeros((M, ids.shape[1], n2.shape[1]))
+            per = np.zeros((M, ids.shape[1], xg.shape[1]))
             for e in sorted(set(int(e) for e in ids.reshape(-1))):
                 t, j = np.nonzero(ids == e)
-                per[t, j] = self.expert(l, e, n2[t])
+                per[t, j] = self.expert(l, e, xg[t], r[t])
             for j in range(ids.shape[1]):
                 y = y + gate[:, j:j + 1] * per[:, j]
         else:
             for j in range(ids.shape[1]):
-                outj = np.stack([self.expert(l, int(ids[t, j]), n2[t:t + 1])[0] for t in range(M)])
+                outj = np.stack([self.expert(l, int(ids[t, j]), xg[t:t + 1], r[t:t + 1])[0] for t in range(M)])
                 y = y + gate[:, j:j + 1] * outj
         for s in range(self.cfg["n_shared"]):
-            y = y + self.expert(l, s, n2, shared=True)
+            y = y + self.expert(l, s, xg, r, shared=True)
         return y
 
     def layer(self, l: int, x: np.ndarray, pos0: int, cache: Cache, dedup: bool = False) -> np.ndarray:
         h = self.attention_block(l, x, pos0, cache)
         if self.cfg["n_experts"] > 0 and l >= self.cfg["n_dense_layers"]:
-            # router and experts share one normed input
-            n2 = self.rn(rmsnorm(h, self.w[f"l{l}.ffn_norm"], self.eps))
-            return h + self.moe_ffn(l, n2, dedup)
+            # router and experts share one stored input, the ffn norm folded in
+            xg, rstd = self.norm_input(h, self.w[f"l{l}.ffn_norm"])
+            return h + self.moe_ffn(l, xg, rstd, dedup)
         return h + self.dense_ffn(l, h)
 
     def head(self, x: np.ndarray) -> np.ndarray:

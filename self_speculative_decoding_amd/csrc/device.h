@@ -42,6 +42,27 @@ __device__ __forceinline__ uint4 ld16_nt(const uint16_t* p) {
   return uint4{t[0], t[1], t[2], t[3]};
 }
 
+// Folded RMSNorm (GemmArgs::ss_in): the 1/rms factor of row m of K columns
+// from its nss sums-of-squares partials (one per residual tile).  Lane l
+// holds partials 4l..4l+3; partials from 256 on are added after, 64 apart;
+// then a fixed butterfly over the wave: the order is fixed by nss alone,
+// whatever the pass width.  Every lane of the wave calls both; rows with
+// ok == false read nothing.
+__device__ __forceinline__ float4 norm_part(const float* ss, int nss, bool ok, int m, int lane) {
+  if (!ok || 4 * lane >= nss) return make_float4(0.f, 0.f, 0.f, 0.f);
+  return *(const float4*)(ss + (size_t)m * nss + 4 * lane);
+}
+
+__device__ __forceinline__ float norm_rstd(const float* ss, int nss, int K, float eps, bool ok, int m, int lane,
+                                           float4 v) {
+  float s = ((v.x + v.y) + v.z) + v.w;
+  if (ok)
+    for (int p = 256 + lane; p < nss; p += 64) s += ss[(size_t)m * nss + p];
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) s += __shfl_xor(s, o);
+  return 1.0f / sqrtf(s / (float)K + eps);
+}
+
 // Packed weight tiles.  A bf16 GEMM weight [N, K] is stored as tiles of 16
 // rows (output columns) x 64 K-elements, 1024 elements = 2 KB each, the tiles
 // of one row tile consecutive in K.  Inside a tile, element (row c, k) with

@@ -191,21 +191,12 @@ __device__ __forceinline__ BlockPos block_pos(const GemmArgs& a) {
 // ---------------------------------------------------------------------------
 
 
-// Row m's sum-of-squares partials (one per 16 columns, nss of them): lane l
-// holds partials 4l..4l+3; partials from 256 on are added after, 64 apart.
-// The order is fixed by nss alone, whatever the pass width.
 __device__ __forceinline__ float4 ss_part(const GemmArgs& a, int m, bool row_ok, int lane) {
-  if (!row_ok || m >= a.M || 4 * lane >= a.nss) return make_float4(0.f, 0.f, 0.f, 0.f);
-  return *(const float4*)(a.ss_in + (size_t)m * a.nss + 4 * lane);
+  return norm_part(a.ss_in, a.nss, row_ok && m < a.M, m, lane);
 }
 
 __device__ __forceinline__ float ss_rstd(const GemmArgs& a, int m, bool row_ok, int lane, float4 v) {
-  float s = ((v.x + v.y) + v.z) + v.w;
-  if (row_ok && m < a.M)
-    for (int p = 256 + lane; p < a.nss; p += 64) s += a.ss_in[(size_t)m * a.nss + p];
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) s += __shfl_xor(s, o);
-  return 1.0f / sqrtf(s / (float)a.K + a.eps);
+  return norm_rstd(a.ss_in, a.nss, a.K, a.eps, row_ok && m < a.M, m, lane, v);
 }
 
 // TPW: independent 16-column tiles per workgroup (one-matrix GEMMs of wide

@@ -221,6 +221,7 @@ bool compute_layout(const ssd_cfg& c, Layout& L) {
     const size_t max_units = (size_t)R * c.top_k + (size_t)((R + 15) / 16) * c.n_shared;
     L.m_groups = take((16 + max_units * 18) * 4);
     L.m_union = take((size_t)c.n_layers * 4);
+    L.m_rstd = take((size_t)R * 4);
   }
   if (c.dtype == SSD_BF16 && c.n_experts == 0) {   // fragment-order copies of the dense GEMM inputs
     L.frag = true;

@@ -25,7 +25,7 @@ struct Layout {
   size_t tblock = 0, tpost = 0, tstate = 0, tresult = 0, toutlog = 0;
   size_t tap = 0, feat = 0, amax_v = 0, amax_i = 0, trace = 0, trace_pts = 0, wpack = 0, exit_x = 0, exit_ss = 0, dlog = 0, tout = 0;
   size_t smp_stats = 0, smp_csum = 0, smp_ctl = 0, smp_nch = 0;
-  size_t m_rlogits = 0, m_ids = 0, m_gates = 0, m_inject = 0, m_slot_out = 0, m_groups = 0, m_union = 0;
+  size_t m_rlogits = 0, m_ids = 0, m_gates = 0, m_inject = 0, m_slot_out = 0, m_groups = 0, m_union = 0, m_rstd = 0;
   size_t xn_p = 0, att_p = 0, act_p = 0, tap_p = 0;   // fragment-order GEMM inputs (frag = true)
   bool frag = false;
   size_t total = 0;

@@ -115,7 +115,11 @@ hipError_t launch_scale_bf16(const float* x, const void* g, void* xg, int d, int
 
 // MoE (routed experts + shared experts)
 struct MoeArgs {
-  const void* X;              // normalised input [M, d]
+  const void* X;              // input rows [M, d]: bf16(x * ffn_norm gain) with ss_in set, else normalised
+  const float* ss_in;         // folded RMSNorm (see GemmArgs): router and expert gate/up products of row m
+  int nss;                    // are scaled by its 1/rms, from these nss partials per row
+  float eps;
+  float* rstd;                // [M] scratch: each token's 1/rms (written by the routing kernel)
   int M, d, E, top_k, fe, n_shared;
   const void* router;         // [E, d]
   const void* eg; const void* ed;   // packed: per expert gate/up interleaved [fe x d], down [d x fe]

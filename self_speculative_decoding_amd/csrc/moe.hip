@@ -78,7 +78,9 @@ constexpr int GROUP_IDS_CAP = 2048;
 __global__ __launch_bounds__(512) void moe_route_group_kernel(const float* __restrict__ rlogits, const int* __restrict__ inject,
                                                               int* __restrict__ ids, float* __restrict__ gates, int M,
                                                               int top_k, int E, int n_shared, int dedup,
-                                                              int* __restrict__ groups, int* __restrict__ union_out) {
+                                                              int* __restrict__ groups, int* __restrict__ union_out,
+                                                              const float* __restrict__ ss_in, int nss, int d,
+                                                              float eps, float* __restrict__ rstd) {
   __shared__ int cnt[64], ubase[65];
   __shared__ int sid[GROUP_IDS_CAP];
   const int tid = threadIdx.x;
@@ -86,7 +88,13 @@ __global__ __launch_bounds__(512) void moe_route_group_kernel(const float* __res
   const int P = M * top_k;   // <= GROUP_IDS_CAP (launch_moe checks)
   const int mchunks = (M + 15) / 16;
   int* units = groups + 16;
-  for (int m = tid >> 6; m < M; m += 8) route_token(rlogits, m, E, top_k, inject, ids, gates, sid, tid & 63);
+  for (int m = tid >> 6; m < M; m += 8) {
+    route_token(rlogits, m, E, top_k, inject, ids, gates, sid, tid & 63);
+    if (ss_in) {   // the token's 1/rms of the folded ffn norm, for the expert gate/up products
+      const float f = norm_rstd(ss_in, nss, d, eps, true, m, tid & 63, norm_part(ss_in, nss, true, m, tid & 63));
+      if ((tid & 63) == 0) rstd[m] = f;
+    }
+  }
   __syncthreads();
   for (int e = tid; e < E; e += 512) {
     int n = 0;
@@ -149,7 +157,8 @@ __global__ __launch_bounds__(512) void moe_route_group_kernel(const float* __res
 }
 
 // Expert GEMM over work units.  PHASE 0: act = silu(x.Wg^T) * (x.Wu^T) (bf16,
-// row code's slot of the act buffer); PHASE 1: y = act . Wd^T (float32).
+// row code's slot of the act buffer), both products times the row's 1/rms
+// when the norm is folded (ss_in); PHASE 1: y = act . Wd^T (float32).
 // A workgroup owns TPW output column tiles of 16 (grid: column tile groups x
 // units; units past groups[0] exit); its 4 waves split K and each wave runs
 // every tile of the group on its K range, reusing each A fragment for them.
@@ -193,6 +202,10 @@ __global__ __launch_bounds__(256) void moe_gemm_kernel(MoeArgs a) {
   f32x4 acc[NS];
 #pragma unroll
   for (int j = 0; j < NS; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // folded norm: this lane's row's 1/rms (per token, from the routing kernel),
+  // loaded before the weight stream
+  const bool fold = PHASE == 0 && a.ss_in != nullptr;
+  const float rrow = fold && ok ? a.rstd[code / slots] : 1.0f;
   // a tile's chunks are NW tiles apart (gate/up interleaved), independent tiles one tile apart
   mfma_stream<NS, true, 4, NW * PACK_TILE>(xr, ok, wr, s0, s1, acc);
 
@@ -205,6 +218,9 @@ __global__ __launch_bounds__(256) void moe_gemm_kernel(MoeArgs a) {
   if (wave != 0) return;
 #pragma unroll
   for (int j = 0; j < NS; ++j) acc[j] = ((acc[j] + red[0][j][lane]) + red[1][j][lane]) + red[2][j][lane];
+  float rs[4];   // 1/rms of rows 4kg + i, from the lanes holding those rows
+#pragma unroll
+  for (int i = 0; i < 4; ++i) rs[i] = __shfl(rrow, 4 * kg + i);
 #pragma unroll
   for (int jt = 0; jt < TPW; ++jt)
 #pragma unroll
@@ -214,7 +230,8 @@ __global__ __launch_bounds__(256) void moe_gemm_kernel(MoeArgs a) {
       const int rc = u[2 + r];
       const int n = (t0 + jt) * 16 + c;
       if (PHASE == 0) {
-        const float g = acc[jt * NW][i], up = acc[jt * NW + NW - 1][i];
+        const float g = fold ? acc[jt * NW][i] * rs[i] : acc[jt * NW][i];
+        const float up = fold ? acc[jt * NW + NW - 1][i] * rs[i] : acc[jt * NW + NW - 1][i];
         ((uint16_t*)a.act)[(size_t)rc * a.fe + n] = f2bf(g / (1.0f + expf(-g)) * up);
       } else {
         a.slot_out[(size_t)rc * a.d + n] = acc[jt][i];
@@ -273,10 +290,11 @@ hipError_t launch_moe(int dtype, const MoeArgs& a, hipStream_t s) {
   if (a.top_k > 8 || a.top_k + a.n_shared > MOE_MAX_SLOTS || a.M * a.top_k > GROUP_IDS_CAP) return hipErrorInvalidValue;
   GemmArgs r{};
   r.X = a.X; r.ldx = a.d; r.W0 = a.router; r.M = a.M; r.N = a.E; r.K = a.d; r.y = a.rlogits; r.ldy = a.E;
+  r.ss_in = a.ss_in; r.nss = a.nss; r.eps = a.eps;   // folded norm: logits times the row's 1/rms
   hipError_t e = launch_gemm(1, EPI_F32, r, s);
   if (e != hipSuccess) return e;
   moe_route_group_kernel<<<1, 512, 0, s>>>(a.rlogits, a.inject, a.ids, a.gates, a.M, a.top_k, a.E, a.n_shared, a.dedup,
-                                           a.groups, a.union_out);
+                                           a.groups, a.union_out, a.ss_in, a.nss, a.d, a.eps, a.rstd);
   const int max_units = a.M * a.top_k + ((a.M + 15) / 16) * a.n_shared;
   // one column tile per workgroup in both phases: 4 tiles per workgroup in the
   // down projection (one A read for them) measured slower (the dedup expert

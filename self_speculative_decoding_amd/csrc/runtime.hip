@@ -109,6 +109,7 @@ struct ssd_ctx {
   int *tblock, *tpost, *tstate, *tresult, *toutlog;
   float *m_rlogits, *m_gates, *m_slot_out;
   int *m_ids, *m_inject, *m_groups, *m_union;
+  float* m_rstd = nullptr;   // MoE: per-token 1/rms of the folded ffn norm
 };
 
 namespace {
@@ -133,6 +134,8 @@ MoeArgs moe_args(ssd_ctx* c, int l, int M) {
   a.act = c->act; a.slot_out = c->m_slot_out; a.resid = c->x; a.groups = c->m_groups;
   a.union_out = c->m_union + l; a.dedup = g.moe_dedup;
   a.ssw = resid_tile_width(g.d_model);   // the combine's column runs, also without ss_out
+  // the ffn norm folded in: X holds bf16(x * ffn_norm gain) and ss the partials
+  a.ss_in = c->ss; a.nss = g.d_model / a.ssw; a.eps = g.rms_eps; a.rstd = c->m_rstd;
   return a;
 }
 
@@ -143,11 +146,10 @@ hipError_t run_gemm(ssd_ctx* c, int epi, GemmArgs a) {
   return launch_gemm(c->cfg.dtype, epi, a, c->stream);
 }
 
-// bf16 models fold every RMSNorm that feeds a dense GEMM (QKV, gate/up, LM
-// head) into that GEMM: the residual's producer leaves xn = bf16(x * gain) and
-// per-16-column sums of squares in ss, and the GEMM scales its product by
-// 1/rms.  The MoE feed-forward keeps a standalone norm (router and experts
-// share its output).
+// bf16 models fold every RMSNorm that feeds a GEMM (QKV, gate/up, the MoE
+// router and expert gate/up, LM head) into that GEMM: the residual's producer
+// leaves xn = bf16(x * gain) and per-residual-tile sums of squares in ss, and
+// the GEMM scales its product by 1/rms.
 // Sums-of-squares partials per row: one per column tile of the residual
 // GEMMs (resid_tile_width), as every producer writes them.
 inline int n_ss(const ssd_cfg& g) { return g.d_model / resid_tile_width(g.d_model); }
@@ -232,13 +234,12 @@ ssd_status layer_forward(ssd_ctx* c, int l, int M, int pos_off, bool feats, cons
     GemmArgs a{};
     a.X = c->att; a.ldx = hq * hd; a.W0 = w.wo; a.M = M; a.N = d; a.K = hq * hd; a.y = c->x; a.ldy = d;
     a.Xp = fr ? c->att_p : nullptr;
-    if (fold && !w.moe) fold_out(c, a, w.ffn_norm);
+    if (fold) fold_out(c, a, w.ffn_norm);
     a.xg_out_p = fr ? c->xn_p : nullptr;
     HIPCHK(run_gemm(c, EPI_RESID, a));
   }
   if (tr) HIPCHK(trace_point(c, l, 3, c->x, M));
-  if (w.moe) {
-    HIPCHK(launch_rmsnorm(dt, c->x, d, w.ffn_norm, c->xn, d, d, g.rms_eps, M, s));
+  if (w.moe) {   // bf16 only: the o projection left bf16(x * ffn_norm) and the partials
     if (tr) HIPCHK(trace_point(c, l, 4, c->xn, M));
     MoeArgs a = moe_args(c, l, M);
     a.ss_out = c->ss; a.xg_out = c->xn; a.gain_next = gain_next;
@@ -681,6 +682,7 @@ ssd_status ssd_load(const ssd_cfg* cfg, const ssd_buf* weights, int32_t n_weight
     c->m_gates = (float*)at(c, lay.m_gates); c->m_inject = (int*)at(c, lay.m_inject);
     c->m_slot_out = (float*)at(c, lay.m_slot_out); c->m_groups = (int*)at(c, lay.m_groups);
     c->m_union = (int*)at(c, lay.m_union);
+    c->m_rstd = (float*)at(c, lay.m_rstd);
   }
 
   ssd_status st = SSD_OK;

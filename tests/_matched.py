@@ -93,23 +93,23 @@ class MatchedModel(Model):
 
     # MoE layers: each expert evaluation's activation is checked against the
     # GPU's act buffer [token][slot][expert_ffn] (routed slots, then shared)
-    def expert(self, l, e, rows, shared=False):
+    def expert(self, l, e, rows, rstd, shared=False):
         act = self.moe_act.get(l)
         if act is None:
-            return super().expert(l, e, rows, shared)
-        n2 = self._n2
-        t = np.array([int(np.nonzero(np.all(n2 == r, axis=1))[0][0]) for r in rows])
+            return super().expert(l, e, rows, rstd, shared)
+        xg = self._xg
+        t = np.array([int(np.nonzero(np.all(xg == r, axis=1))[0][0]) for r in rows])
         if shared:
             j = np.full(len(t), self.cfg["top_k"] + e)
         else:
-            ids = np.asarray(self.routing[l])[:n2.shape[0]]
+            ids = np.asarray(self.routing[l])[:xg.shape[0]]
             j = np.array([int(np.nonzero(ids[ti] == e)[0][0]) for ti in t])
         self.expect.insert(0, ("moe_act", act[t, j]))
-        return super().expert(l, e, rows, shared)
+        return super().expert(l, e, rows, rstd, shared)
 
-    def moe_ffn(self, l, n2, dedup=False):
-        self._n2 = n2
-        return super().moe_ffn(l, n2, dedup)
+    def moe_ffn(self, l, xg, rstd=None, dedup=False):
+        self._xg = xg
+        return super().moe_ffn(l, xg, rstd, dedup)
 
     # the residual after each block, for comparison with the GPU's trace
     def attention_block(self, l, x, pos0, cache):
@@ -137,7 +137,7 @@ class MatchedModel(Model):
 def expected_points(eng, cfg, layers, rows, n, kv_rows):
     """The GPU's stored values of the last traced pass, in the oracle's order:
     per run layer the QKV input, q, the new K and V entries, the attention
-    output, the gate/up input (MoE: the normed row) and, for dense layers, the
+    output, the gate/up input (bf16(x * ffn_norm), also in MoE layers) and, for dense layers, the
     activation; then, for a full pass of a feature-tap model, the concat of
     the tapped residuals and the fc output; then the LM head input.  Returns
     (expect, moe_act), moe_act: layer -> [rows, slots, fe] of the MoE layers.

@@ -391,6 +391,48 @@ def _moe_cfg():
                         expert_ffn=24, dense_ffn=80, dtype="f32", max_ctx=64)
 
 
+def _hf_moe_block(w):
+    """transformers' DeepSeek-V2 MoE block (float64) holding layer 1's experts of w."""
+    from transformers import DeepseekV2Config
+    from transformers.models.deepseek_v2.modeling_deepseek_v2 import DeepseekV2Moe
+    c = DeepseekV2Config(hidden_size=64, num_experts=16, num_experts_per_tok=4, n_shared_experts=2,
+                         moe_intermediate_size=24, routed_scaling_factor=1.0, topk_method="greedy",
+                         hidden_act="silu", mlp_bias=False)
+    blk = DeepseekV2Moe(c).double()
+    t = lambda a: torch.from_numpy(np.asarray(a, np.float64))
+    with torch.no_grad():
+        blk.gate.weight.copy_(t(w["l1.router"]))
+        blk.experts.gate_up_proj.copy_(torch.cat([t(w["l1.exp_gate"]), t(w["l1.exp_up"])], dim=1))
+        blk.experts.down_proj.copy_(t(w["l1.exp_down"]))
+        blk.shared_experts.gate_proj.weight.copy_(t(w["l1.sh_gate"]).reshape(48, 64))
+        blk.shared_experts.up_proj.weight.copy_(t(w["l1.sh_up"]).reshape(48, 64))
+        blk.shared_experts.down_proj.weight.copy_(torch.cat([t(w["l1.sh_down"][0]), t(w["l1.sh_down"][1])], dim=1))
+    return blk
+
+
+def test_moe_layer_folded_norm_matches_transformers_on_the_normed_input():
+    """The MoE feed-forward of a layer takes the stored input x * g and the
+    rows' 1/rms factors (the ffn norm folded in, as every norm that feeds a
+    product): it must equal transformers' DeepSeek-V2 MoE block applied to
+    rmsnorm(x, g), router included.  A factor left off the router, the gate
+    or the up product (or applied to the down product) fails it."""
+    cfg = _moe_cfg()
+    w = synth.make_weights(cfg, seed=29)
+    w["l1.router"] = w["l1.router"] * 20            # peaked routing: no near-ties
+    w["l1.ffn_norm"] = np.random.default_rng(31).uniform(0.5, 1.5, 64).astype(np.float32)
+    m = Model(cfg, w)
+    # residual rows with distinct scales, so that a missing 1/rms shows
+    h = np.random.default_rng(30).standard_normal((6, 64)) * np.array([0.3, 1, 2, 5, 0.7, 3])[:, None]
+    blk = _hf_moe_block(m.w)
+    with torch.no_grad():
+        ref = blk(torch.from_numpy(rmsnorm(h, m.w["l1.ffn_norm"], m.eps))[None])[0].numpy()
+    xg, rstd = m.norm_input(h, m.w["l1.ffn_norm"])
+    for dedup in (False, True):
+        np.testing.assert_allclose(m.moe_ffn(1, xg, rstd, dedup=dedup), ref, rtol=2e-5, atol=2e-6)
+    # without the 1/rms factors the output is visibly different
+    assert not np.allclose(m.moe_ffn(1, xg), ref, rtol=1e-3)
+
+
 def test_moe_block_matches_transformers_deepseek_v2():
     from transformers import DeepseekV2Config
     from transformers.models.deepseek_v2.modeling_deepseek_v2 import DeepseekV2Moe
