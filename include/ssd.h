@@ -292,8 +292,8 @@ ssd_status ssd_read_trace(ssd_ctx* ctx, float* host, int32_t rows);
  * row for float32 models) [rows][d], 1 q after the rotary embedding
  * [rows][n_q_heads * head_dim], 2 the attention output [rows][n_q_heads *
  * head_dim], 3 the residual after the attention block, float32 [rows][d],
- * 4 the gate/up GEMM input [rows][d] (MoE layers: the normed row router and
- * experts share), 5 the SwiGLU activation [rows][F] (MoE layers: [rows]
+ * 4 the gate/up GEMM input [rows][d] (bf16(x * ffn_norm) for bf16 models,
+ * also the row the MoE router and experts share), 5 the SwiGLU activation [rows][F] (MoE layers: [rows]
  * [top_k + n_shared][expert_ffn], routed slots then shared experts); cfg
  * dtype except point 3.  layer == n_layers with
  * point 0: the LM head's input of rows [0, rows).  Layers a draft skipped keep
