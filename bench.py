@@ -165,6 +165,29 @@ def bench_pmc_probe(args) -> int:
     return 0
 
 
+def bench_attn_pmc_probe(args) -> int:
+    """Kernel sequence for `rocprofv3 --pmc` runs on the decode attention:
+    3 plain copies of 128 MiB (counter calibration), then the 8B-shaped
+    model (4 layers, headline widths) after a 1024-token prompt, 24 attention
+    launches at m = 4 (the k = 3 verify) and then 24 at m = 1, cycling over
+    the layers.  Prints the K/V bytes each launch reads."""
+    import synth
+    from self_speculative_decoding_amd import Engine, make_cfg
+    cfg = synth.config("llama-8b", n_layers=4)
+    w = synth.make_weights(cfg, progress=_weights_progress)
+    eng = Engine(make_cfg(cfg, max_block=6, prefill_chunk=256), [w[n] for n, _, _ in synth.weight_specs(cfg)])
+    eng.prefill(synth.make_prompt(cfg))
+    ctx = eng.context_length
+    res = {"copy_probe_us": eng.time_op("copy_probe", 0, 128, 3),
+           "attention_m4_us": eng.time_op("attention", 0, 4, 24),
+           "attention_m1_us": eng.time_op("attention", 0, 1, 24)}
+    eng.close()
+    kv = lambda m: cfg["n_kv_heads"] * (ctx + m) * cfg["head_dim"] * 2 * 2
+    res.update({"copy_bytes": 128 << 20, "context": ctx, "kv_bytes_m4": kv(4), "kv_bytes_m1": kv(1)})
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def bench_trace_verify(args) -> int:
     """Kernel sequence for `rocprofv3 --kernel-trace`: the workload's model
     after its full prompt, then groups of 12 verify passes (host blocks of
@@ -659,6 +682,8 @@ def main() -> int:
     ap.add_argument("--moe-pmc-probe", action="store_true",
                     help="MoE expert op kernel sequence for rocprofv3 --pmc (with --moe-dedup)")
     ap.add_argument("--moe-dedup", type=int, default=0, choices=(0, 1))
+    ap.add_argument("--attn-pmc-probe", action="store_true",
+                    help="kernel sequence for rocprofv3 --pmc on the decode attention (8B shape, context 1024)")
     ap.add_argument("--trace-verify", action="store_true",
                     help="kernel sequence for rocprofv3 --kernel-trace: groups of replayed verify graphs after "
                          "the workload's prompt (see bench_trace_verify)")
@@ -684,6 +709,8 @@ def main() -> int:
         return bench_pmc_probe(args)
     if args.moe_pmc_probe:
         return bench_moe_pmc_probe(args)
+    if args.attn_pmc_probe:
+        return bench_attn_pmc_probe(args)
     if args.prefill:
         return bench_prefill(args)
     if args.workload == "qwen3-8b":
