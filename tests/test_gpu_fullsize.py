@@ -3,7 +3,7 @@
 Properties at the full size: self-speculation emits exactly plain greedy over
 the 1024-token prompt and 512 generated tokens; a verify block at context
 1024+ reproduces the decode rows bitwise.  Oracle parity at context 1024 for
-a 4-row verify pass and a draft step, all layers end to end, with every bf16
+4- and 6-row verify passes and a draft step, all layers end to end, with every bf16
 storage decision checked against the oracle's (tests/_matched.py); and the
 whole greedy run's tokens against the plain oracle teacher-forced on them.
 """
@@ -58,19 +58,23 @@ def test_fullsize_verify_rows_equal_decode_rows(big):
     eng.accept()
 
 
-def test_fullsize_verify_pass_matches_oracle_decision_by_decision(big):
-    """4-row verify pass at context 1024 (the workload's prompt), all 32
-    layers, checked end to end from the embedding against the oracle."""
+@pytest.mark.parametrize("rows", [4, 6])
+def test_fullsize_verify_pass_matches_oracle_decision_by_decision(big, rows):
+    """Verify pass at context 1024 (the workload's prompt), all 32 layers,
+    checked end to end from the embedding against the oracle: 4 rows (k = 3)
+    and 6 rows (k = 5: GEMM inputs in fragment order, two 16-query tiles per
+    attention wave)."""
     cfg, w, eng = big
     prompt = synth.make_prompt(cfg)
     eng.reset()
     eng.set_trace(True)
     try:
         t = eng.prefill(prompt)
-        block = [t] + [int(x) for x in synth.make_tokens(cfg["vocab"], 3, seed=1, stream=77)]
+        block = [t] + [int(x) for x in synth.make_tokens(cfg["vocab"], rows - 1, seed=1, stream=77)]
         eng.verify(block)
-        logits = eng.read_logits(4)
-        check_matched("llama-8b verify", cfg, w, eng, block, len(prompt), list(range(cfg["n_layers"])), logits)
+        logits = eng.read_logits(rows)
+        check_matched(f"llama-8b {rows}-row verify", cfg, w, eng, block, len(prompt), list(range(cfg["n_layers"])),
+                      logits)
         eng.accept()
     finally:
         eng.set_trace(False)
