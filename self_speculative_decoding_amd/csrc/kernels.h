@@ -87,6 +87,7 @@ struct AttnArgs {
   int pos_off, M, R, hq, hkv, hd, max_ctx;   // max_ctx: positions per cache row (multiple of 64)
   int n_part;                 // partitions launched (set by launch_attention)
   int pstride;                // partition slots per (row, head) in part_o / part_ml (>= n_part)
+  int xcd;                    // set by the launcher: 1-D XCD-affine grids (attn_xcd_map)
   float scale_log2;           // log2(e) / sqrt(hd)
 };
 
