@@ -109,13 +109,16 @@ def test_degenerate_masks(edge):
         assert out == base, k
 
 
-@pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 4)])
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 4), (8, 8), (32, 16)])
 def test_query_groups_of_one_and_two(hq, hkv):
-    """The attention kernel's other head groupings (G = 1, 2) against the oracle."""
+    """The attention kernel's other head groupings (G = 1, 2) against the
+    oracle; with 8 and 16 kv heads the XCD-aware grids (one and two kv heads
+    per XCD slot).  A 12-row verify (two 16-query tiles per wave at G = 2)
+    reproduces the decode rows bit for bit."""
     cfg = _edge_cfg(n_q_heads=hq, n_kv_heads=hkv, max_ctx=200, prompt_len=90, cid=71 + hq // hkv)
     w = synth.make_weights(cfg, seed=7)
-    print(f"[edge] G = {hq // hkv}", flush=True)
-    eng = engine(cfg, w, max_block=8, prefill_chunk=64)
+    print(f"[edge] G = {hq // hkv}, {hkv} kv heads", flush=True)
+    eng = engine(cfg, w, max_block=12, prefill_chunk=64)
     try:
         prompt = synth.make_prompt(cfg)
         toks, rows = _stepwise(eng, prompt, 32)
@@ -128,6 +131,11 @@ def test_query_groups_of_one_and_two(hq, hkv):
         mask[1] = 1
         spec, _ = eng.generate(prompt, 32, mask, 3)
         assert spec == toks
+        eng.reset()
+        eng.prefill(prompt)
+        post = eng.verify(toks[:12])
+        assert np.array_equal(eng.read_logits(12), rows[1:13]) and post == toks[1:13]
+        eng.accept()
     finally:
         eng.close()
 
