@@ -696,6 +696,7 @@ template <typename E>
 static hipError_t attn_dispatch(AttnArgs a, int n_part, int hd, hipStream_t s) {
   if (n_part < 1 || n_part > a.pstride) return hipErrorInvalidValue;
   a.n_part = n_part;
+  a.xcd = 0;   // set below for the MFMA kernel's 1-D grids only
   const int G = a.hq / a.hkv;
   dim3 grid(n_part, a.hkv, (a.M + ROW_TILE - 1) / ROW_TILE);
   bool done = false;
