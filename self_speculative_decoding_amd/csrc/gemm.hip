@@ -8,8 +8,8 @@
 #include "device.h"
 
 // Build-time tuning of the decode GEMMs: load-batch depth in 64-element
-// chunks (U1 one-matrix, U2 gate/up; the batch depth does not change the
-// accumulation order) and waves per workgroup (gate/up; other
+// chunks (U1 one-matrix, U2 gate/up with tiles that split evenly over the
+// CUs, else 1; the batch depth does not change the accumulation order) and waves per workgroup (gate/up; other
 // GEMMs with fewer than 1024 column tiles; wider GEMMs such as the LM head).
 #ifndef SSD_GEMM_U1
 #define SSD_GEMM_U1 4
@@ -23,6 +23,9 @@
 #ifndef SSD_GEMM_UW         // GEMMs with >= 1024 column tiles (the LM head)
 #define SSD_GEMM_UW 2
 #endif
+#ifndef SSD_GEMM_U_TPW4     // 4-tile workgroups (the LM head of passes wider than 8 rows):
+#define SSD_GEMM_U_TPW4 1   // 84 VGPRs, two workgroups per CU (two chunks: 134, one per CU;
+#endif                      // 16 rows: Qwen3-8B head 230.9 -> 217.6 us, Llama-8B 188.6 -> 181.9)
 #ifndef SSD_MT_KW            // waves (K ranges) of the multi-row-tile kernel
 #define SSD_MT_KW 4
 #endif
@@ -886,8 +889,10 @@ hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t s) {
     // the A operand is read once for them (results unchanged, see the kernel),
     // but only where at least SSD_TPW_MIN_WG workgroups remain, one per CU:
     // spreading the weight stream over every CU matters more than the A reads
-    // (measured at 16 rows: the LM head 250 -> 231 us with 4 tiles, QKV of 512
-    // tiles 13.7 -> 12.1 us with 2; o and down keep their 256 workgroups)
+    // (measured at 16 rows: the LM head 250 -> 231 us with 4 tiles, 218 with
+    // one-chunk batches, QKV of 512 tiles 13.7 -> 12.1 us with 2; o and down
+    // keep their 256 workgroups; at 5-8 rows the grouped LM head is slower,
+    // 191 -> 203 us at 6 rows, whatever the batch depth)
     // (never for long-K narrow tiles: their one-tile kernel splits K over
     // more waves, and a row's K split must not depend on the pass width)
     int tpw = 1;
@@ -902,8 +907,8 @@ hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t s) {
   }                                                                                                      \
   else if (tpw == 4) {                                                                                   \
     const dim3 g4(tiles / 4, mt);                                                                        \
-    if (wide) gemm_bf16_kernel<E, 1, SSD_KW_WIDE, 1, 2, 4, TWV><<<g4, 64 * SSD_KW_WIDE, 0, s>>>(a);      \
-    else gemm_bf16_kernel<E, 1, KWN, 1, 2, 4, TWV><<<g4, 64 * KWN, 0, s>>>(a);                           \
+    if (wide) gemm_bf16_kernel<E, 1, SSD_KW_WIDE, 1, SSD_GEMM_U_TPW4, 4, TWV><<<g4, 64 * SSD_KW_WIDE, 0, s>>>(a); \
+    else gemm_bf16_kernel<E, 1, KWN, 1, SSD_GEMM_U_TPW4, 4, TWV><<<g4, 64 * KWN, 0, s>>>(a);              \
   } else if (tpw == 2) {                                                                                 \
     const dim3 g2(tiles / 2, mt);                                                                        \
     if (wide) gemm_bf16_kernel<E, 1, SSD_KW_WIDE, 1, 2, 2, TWV><<<g2, 64 * SSD_KW_WIDE, 0, s>>>(a);      \
@@ -928,16 +933,27 @@ hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t s) {
         else { SSD_G1(EPI_QKV, SSD_KW_NARROW, SSD_GEMM_U1, 16) }
         break;
       case EPI_STORE: SSD_G1(EPI_STORE, SSD_KW_NARROW, SSD_GEMM_U1, 16) break;
-      case EPI_SWIGLU:
+      case EPI_SWIGLU: {
+        // Load batches of the one-tile kernel: SSD_GEMM_U2 chunks where the
+        // tiles split evenly over the CUs, else one, so that every workgroup
+        // is resident at once (58 instead of 90 VGPRs) and no CU runs a last
+        // round alone (measured: 608 tiles of the Qwen3-4B shape 20.3 ->
+        // 19.2 us; 768 and 1024 tiles faster with two, 33.9 -> 33.0 and
+        // 37.1 -> 36.4 us).  The batch depth never changes a result.
+        const bool u1 = tiles % NUM_CU != 0;
         if (tw == 14) {
           if (multi && tpm == 2) gemm_bf16_kernel<EPI_SWIGLU, 2, SSD_MT_KW, SSD_MT_MT, 1, 2, 14><<<grid_mt, 64 * SSD_MT_KW, 0, s>>>(am);
           else if (multi) gemm_bf16_kernel<EPI_SWIGLU, 2, SSD_MT_KW, SSD_MT_MT, 1, 1, 14><<<grid_mt, 64 * SSD_MT_KW, 0, s>>>(am);
+          else if (u1) gemm_bf16_kernel<EPI_SWIGLU, 2, SSD_KW_SWIGLU, 1, 1, 1, 14><<<grid, 64 * SSD_KW_SWIGLU, 0, s>>>(a);
           else gemm_bf16_kernel<EPI_SWIGLU, 2, SSD_KW_SWIGLU, 1, SSD_GEMM_U2, 1, 14><<<grid, 64 * SSD_KW_SWIGLU, 0, s>>>(a);
         } else if (multi && tpm == 2) gemm_bf16_kernel<EPI_SWIGLU, 2, SSD_MT_KW, SSD_MT_MT, 1, 2><<<grid_mt, 64 * SSD_MT_KW, 0, s>>>(am);
         else if (multi) gemm_bf16_kernel<EPI_SWIGLU, 2, SSD_MT_KW, SSD_MT_MT, 1, 1><<<grid_mt, 64 * SSD_MT_KW, 0, s>>>(am);
+        else if (wide && u1) gemm_bf16_kernel<EPI_SWIGLU, 2, SSD_KW_WIDE, 1, 1, 1><<<grid, 64 * SSD_KW_WIDE, 0, s>>>(a);
         else if (wide) gemm_bf16_kernel<EPI_SWIGLU, 2, SSD_KW_WIDE, 1, SSD_GEMM_U2, 1><<<grid, 64 * SSD_KW_WIDE, 0, s>>>(a);
+        else if (u1) gemm_bf16_kernel<EPI_SWIGLU, 2, SSD_KW_SWIGLU, 1, 1, 1><<<grid, 64 * SSD_KW_SWIGLU, 0, s>>>(a);
         else gemm_bf16_kernel<EPI_SWIGLU, 2, SSD_KW_SWIGLU, 1, SSD_GEMM_U2, 1><<<grid, 64 * SSD_KW_SWIGLU, 0, s>>>(a);
         break;
+      }
       default: return hipErrorInvalidValue;
     }
 #undef SSD_G1
