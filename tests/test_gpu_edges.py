@@ -140,21 +140,23 @@ def test_query_groups_of_one_and_two(hq, hkv):
         eng.close()
 
 
-def test_narrow_gate_up_tiles():
-    """An FFN width whose gate/up weight is packed in 14-row tiles (3584 = 256
-    tiles of 14 columns, one per compute unit) against the oracle; the narrow
-    tiles keep verify rows bitwise equal to decode rows and self-speculation
-    lossless."""
-    cfg = _edge_cfg(ffn_dim=3584, max_ctx=200, prompt_len=90, cid=74)
+@pytest.mark.parametrize("ffn", [3584, 8960])
+def test_narrow_gate_up_tiles(ffn):
+    """FFN widths whose gate/up weight is packed in 14-row tiles against the
+    oracle: 3584 = 256 tiles of 14 columns, one per compute unit (two-chunk
+    load batches), and 8960 = 640 tiles, which do not split evenly over the
+    compute units (one-chunk load batches); the narrow tiles keep verify rows
+    bitwise equal to decode rows and self-speculation lossless."""
+    cfg = _edge_cfg(ffn_dim=ffn, max_ctx=200, prompt_len=90, cid=74)
     w = synth.make_weights(cfg, seed=8)
-    print("[edge] ffn 3584 (14-row gate/up tiles)", flush=True)
+    print(f"[edge] ffn {ffn} (14-row gate/up tiles)", flush=True)
     eng = engine(cfg, w, max_block=8, prefill_chunk=64)
     try:
         prompt = synth.make_prompt(cfg)
         toks, rows = _stepwise(eng, prompt, 33)
         ref = Model(cfg, w).teacher_forced(prompt, toks)
         err = np.max(np.abs(rows - ref))
-        print(f"[edge] ffn 3584: max |dlogit| = {err:.3e}")
+        print(f"[edge] ffn {ffn}: max |dlogit| = {err:.3e}")
         assert err <= BOUND
         assert _gap_ok(toks, ref, BOUND) == []
         eng.reset()
