@@ -140,6 +140,32 @@ def test_query_groups_of_one_and_two(hq, hkv):
         eng.close()
 
 
+def test_grouped_lm_head_tiles():
+    """A vocabulary of 16384 (1024 column tiles): passes wider than 8 rows run
+    the LM head with four column tiles per workgroup, the others one.  Greedy
+    against the oracle, and a 16-row verify reproduces the one-tile decode
+    rows bit for bit."""
+    cfg = _edge_cfg(vocab=16384, max_ctx=200, prompt_len=90, cid=76)
+    w = synth.make_weights(cfg, seed=9)
+    print("[edge] vocab 16384 (grouped LM head tiles)", flush=True)
+    eng = engine(cfg, w, max_block=16, prefill_chunk=64)
+    try:
+        prompt = synth.make_prompt(cfg)
+        toks, rows = _stepwise(eng, prompt, 32)
+        ref = Model(cfg, w).teacher_forced(prompt, toks)
+        err = np.max(np.abs(rows - ref))
+        print(f"[edge] vocab 16384: max |dlogit| = {err:.3e}")
+        assert err <= BOUND
+        assert _gap_ok(toks, ref, BOUND) == []
+        eng.reset()
+        eng.prefill(prompt)
+        post = eng.verify(toks[:16])
+        assert np.array_equal(eng.read_logits(16), rows[1:17]) and post == toks[1:17]
+        eng.accept()
+    finally:
+        eng.close()
+
+
 @pytest.mark.parametrize("ffn", [3584, 8960])
 def test_narrow_gate_up_tiles(ffn):
     """FFN widths whose gate/up weight is packed in 14-row tiles against the
