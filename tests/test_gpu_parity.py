@@ -167,6 +167,29 @@ def test_state_errors_on_gpu(tiny):
     assert e.value.status == -3
 
 
+def test_smallest_requests_on_gpu(tiny):
+    """The degenerate request sizes: an empty prompt and zero new tokens are
+    argument errors; one new token is the prefill's token alone, with or
+    without a draft; two tokens with k = 3 stop inside the first cycle and
+    the output is the greedy prefix (the last cycle's overshoot is cut)."""
+    from self_speculative_decoding_amd import SSDError, skip_mask
+    cfg, w, eng, _ = tiny
+    prompt = synth.make_prompt(cfg)
+    eng.reset()
+    with pytest.raises(SSDError) as e:
+        eng.prefill([])
+    assert e.value.status == -1
+    with pytest.raises(SSDError) as e:
+        eng.generate(prompt, 0)
+    assert e.value.status == -1
+    base, _ = eng.generate(prompt, 8)
+    mask = skip_mask(cfg["n_layers"], 0.5)
+    assert eng.generate(prompt, 1)[0] == base[:1]
+    assert eng.generate(prompt, 1, mask, 3)[0] == base[:1]
+    assert eng.generate(prompt, 2, mask, 3)[0] == base[:2]
+    assert eng.generate(prompt, 8, mask, 3)[0] == base
+
+
 # ---------------------------------------------------------------------------
 # small bf16 workload with the real head geometry (hd 128, 4 q heads per KV head)
 # ---------------------------------------------------------------------------
