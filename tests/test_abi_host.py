@@ -30,6 +30,21 @@ def test_every_declared_symbol_is_exported():
     assert sorted(ssd.EXPORTS) == names
 
 
+def test_binding_fails_loudly_without_the_library(tmp_path):
+    """The binding refuses to import when libssd.so is absent: no CPU or other
+    fallback stands in for the HIP path."""
+    import shutil
+    import subprocess
+    import sys
+    pkg = tmp_path / "self_speculative_decoding_amd"
+    pkg.mkdir()
+    shutil.copy(os.path.join(ROOT, "self_speculative_decoding_amd", "__init__.py"), pkg / "__init__.py")
+    r = subprocess.run([sys.executable, "-c", "import self_speculative_decoding_amd"], cwd=tmp_path,
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0
+    assert "ImportError" in r.stderr and "libssd.so is missing" in r.stderr
+
+
 @pytest.mark.parametrize("name", ["tiny", "qwen3-4b", "llama-8b", "qwen3-8b", "dsv2-lite"])
 def test_workload_cfgs_validate_and_weight_table_matches(name):
     cfg = synth.config(name)
