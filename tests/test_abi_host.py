@@ -45,6 +45,17 @@ def test_binding_fails_loudly_without_the_library(tmp_path):
     assert "ImportError" in r.stderr and "libssd.so is missing" in r.stderr
 
 
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU; --gpus 2 exits non-zero with a message
+    before anything touches a device."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], cwd=ROOT,
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0
+    assert "one GPU only" in r.stdout + r.stderr
+
+
 @pytest.mark.parametrize("name", ["tiny", "qwen3-4b", "llama-8b", "qwen3-8b", "dsv2-lite"])
 def test_workload_cfgs_validate_and_weight_table_matches(name):
     cfg = synth.config(name)
