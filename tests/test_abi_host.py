@@ -56,6 +56,28 @@ def test_bench_refuses_more_than_one_gpu():
     assert "one GPU only" in r.stdout + r.stderr
 
 
+def test_bench_traffic_is_null_once_the_gemm_sources_change(tmp_path, monkeypatch):
+    """roofline.traffic comes from the committed counter summary only while the
+    gate/up kernel's sources hash as they did when the counters were taken."""
+    import hashlib
+    import shutil
+    import sys
+    sys.path.insert(0, ROOT)
+    import bench
+    csrc = tmp_path / "self_speculative_decoding_amd" / "csrc"
+    csrc.mkdir(parents=True)
+    (tmp_path / "profiles").mkdir()
+    for f in ("gemm.hip", "device.h"):
+        shutil.copy(os.path.join(ROOT, "self_speculative_decoding_amd", "csrc", f), csrc / f)
+    sha = hashlib.sha256((csrc / "gemm.hip").read_bytes() + (csrc / "device.h").read_bytes()).hexdigest()
+    (tmp_path / "profiles" / "gemm_swiglu_llama8b_traffic.txt").write_text(
+        f"counter bytes per launch: 235467858 (ratio 1.0019)\nkernel source sha256 (gemm.hip + device.h) when measured: {sha}\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.measured_traffic() == 235467858.0
+    (csrc / "gemm.hip").write_bytes((csrc / "gemm.hip").read_bytes() + b"\n// changed\n")
+    assert bench.measured_traffic() is None
+
+
 @pytest.mark.parametrize("name", ["tiny", "qwen3-4b", "llama-8b", "qwen3-8b", "dsv2-lite"])
 def test_workload_cfgs_validate_and_weight_table_matches(name):
     cfg = synth.config(name)
