@@ -66,6 +66,31 @@ def pass_bytes(cfg: dict, M: int, ctx: float, layers: int | None = None, head: b
     return b
 
 
+def speedup_frame(k: int, c_d: float, alpha: float, t_draft_ms: float, t_verify_ms: float,
+                  t_base_ms: float) -> dict:
+    """Expected-speedup frame of a cycle of k draft steps and one verify (time
+    per pass = bytes / bandwidth + fixed time, MoE speculative decoding
+    abstract; geometric acceptance): a cycle yields sum_{i<=k} alpha^i tokens
+    in k draft steps + one verify.  Ceiling (every draft accepted) from the
+    draft/full byte ratio c_d: (k + 1) / (k c_d + 1); break-even: the
+    smallest alpha with sum_{i<=k} alpha^i >= k c_d + 1; prediction from the
+    measured step times against a plain decode step of t_base_ms."""
+    e_tok = sum(alpha ** i for i in range(k + 1))
+    lo, hi = 0.0, 1.0
+    for _ in range(60):
+        mid = (lo + hi) / 2
+        if sum(mid ** i for i in range(k + 1)) >= k * c_d + 1:
+            hi = mid
+        else:
+            lo = mid
+    return {"draft_byte_ratio": round(c_d, 4),
+            "ceiling_alpha1": round((k + 1) / (k * c_d + 1), 4),
+            "break_even_alpha": round(hi, 4),
+            "alpha": round(alpha, 4),
+            "predicted_speedup": round(e_tok / ((k * t_draft_ms + t_verify_ms) / t_base_ms), 4),
+            "measured_speedup": None}
+
+
 def _weights_progress(frac: float) -> None:
     log(f"weights {frac:.0%} generated")
 
@@ -819,24 +844,7 @@ def main() -> int:
     # and the prediction from measured step times and the measured acceptance
     # under geometric acceptance
     c_d = pass_bytes(cfg, 1, avg_ctx, layers=cfg["n_layers"] - len(skipped)) / bb
-    alpha = acc / max(drafted, 1)
-    e_tok = sum(alpha ** i for i in range(k + 1))
-    t_d = dr_ms / max(drafted, 1)
-    frame = {"draft_byte_ratio": round(c_d, 4),
-             "ceiling_alpha1": round((k + 1) / (k * c_d + 1), 4),
-             "break_even_alpha": None,
-             "alpha": round(alpha, 4),
-             "predicted_speedup": round(e_tok / ((k * t_d + v_ms) / b_ms), 4),
-             "measured_speedup": None}
-    # smallest alpha with (1 - a^(k+1)) / (1 - a) >= k * c_d + 1
-    lo, hi = 0.0, 1.0
-    for _ in range(60):
-        mid = (lo + hi) / 2
-        if sum(mid ** i for i in range(k + 1)) >= k * c_d + 1:
-            hi = mid
-        else:
-            lo = mid
-    frame["break_even_alpha"] = round(hi, 4)
+    frame = speedup_frame(k, c_d, acc / max(drafted, 1), dr_ms / max(drafted, 1), v_ms, b_ms)
 
     # ---- skip x k sweep (one decode each) ----
     sweep = []
