@@ -3,7 +3,10 @@
 Each case draws a model shape (layers, width, head dim 64 or 128, 1/2/4
 query heads per KV head, FFN widths that take 16- or 14-row gate/up tiles,
 QKV widths that take 16- or 12-row tiles), a prompt length, a verify-block
-limit and a prefill chunk.  Bars as in test_gpu_parity: greedy logits within
+limit and a prefill chunk.  The wide cases add 8 KV heads (the XCD-aware
+attention grids), widths with 8- and 10-row residual tiles, FFN widths whose
+14-row tiles do not split evenly over the compute units, a vocabulary whose
+LM head groups column tiles above 8 rows, and verify blocks of up to 16 rows.  Bars as in test_gpu_parity: greedy logits within
 |dlogit| <= 3e-2 of the oracle's teacher-forced logits, tokens equal wherever
 the oracle's top-2 gap exceeds twice that; a verify block's rows equal to the
 decode rows bit for bit; self-speculation equal to greedy for random skip
@@ -35,23 +38,36 @@ def _shape(seed):
     return cfg, int(r.choice([4, 8, 17])), int(r.choice([16, 64, 256])), r
 
 
-@pytest.mark.parametrize("seed", range(6))
-def test_random_shape(seed):
-    cfg, max_block, chunk, r = _shape(seed)
+def _wide_shape(seed):
+    r = np.random.default_rng(5000 + seed)
+    hd = int(r.choice([64, 128]))
+    hkv = int(r.choice([1, 2, 4, 8]))
+    hq = hkv * int(r.choice([1, 2, 4]))
+    P = int(r.integers(1, 300))
+    cfg = synth.config("llama-8b", n_layers=int(r.choice([2, 3])),
+                       d_model=int(r.choice([256, 512, 768, 1280, 2048, 2560])),
+                       n_q_heads=hq, n_kv_heads=hkv, head_dim=hd,
+                       ffn_dim=int(r.choice([512, 1792, 3584, 8960, 4480])),
+                       vocab=int(r.choice([2048, 4096, 16384])), prompt_len=P, max_ctx=P + 80, cid=300 + seed)
+    return cfg, int(r.choice([4, 8, 12, 17])), int(r.choice([16, 64, 256])), r
+
+
+def _run_shape(tag, seed, cfg, max_block, chunk, r, n_tok, max_m):
     keys = ("n_layers", "d_model", "n_q_heads", "n_kv_heads", "head_dim", "ffn_dim", "vocab", "prompt_len")
-    print(f"[shape {seed}] " + " ".join(f"{k}={cfg[k]}" for k in keys) + f" max_block={max_block} chunk={chunk}",
+    print(f"[{tag} {seed}] " + " ".join(f"{k}={cfg[k]}" for k in keys) + f" max_block={max_block} chunk={chunk}",
           flush=True)
     w = synth.make_weights(cfg, seed=seed)
     eng = engine(cfg, w, max_block=max_block, prefill_chunk=chunk)
     try:
         prompt = synth.make_prompt(cfg)
-        toks, rows = _stepwise(eng, prompt, 16)
+        toks, rows = _stepwise(eng, prompt, n_tok)
         ref = Model(cfg, w).teacher_forced(prompt, toks)
         err = float(np.max(np.abs(rows - ref)))
-        print(f"[shape {seed}] max |dlogit| = {err:.3e}", flush=True)
+        print(f"[{tag} {seed}] max |dlogit| = {err:.3e}", flush=True)
         assert err <= BOUND
         assert _gap_ok(toks, ref, BOUND) == []
-        m = min(max_block, 8)
+        m = min(max_block, max_m)
+        assert m + 1 <= len(rows)
         eng.reset()
         eng.prefill(prompt)
         post = eng.verify(toks[:m])
@@ -62,7 +78,19 @@ def test_random_shape(seed):
         for _ in range(2):
             mask = (r.random(L) < 0.5).astype(np.uint8)
             k = int(r.integers(1, max_block))
-            spec, _ = eng.generate(prompt, 16, mask, k)
+            spec, _ = eng.generate(prompt, n_tok, mask, k)
             assert spec == toks, (mask.tolist(), k)
     finally:
         eng.close()
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_shape(seed):
+    cfg, max_block, chunk, r = _shape(seed)
+    _run_shape("shape", seed, cfg, max_block, chunk, r, 16, 8)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_wide_shape(seed):
+    cfg, max_block, chunk, r = _wide_shape(seed)
+    _run_shape("wide", seed, cfg, max_block, chunk, r, 18, 16)
