@@ -173,7 +173,9 @@ typedef struct ssd_ctx ssd_ctx;
  * weight table (LayerSkip summary 4.3.1, self-drafting with the model's own
  * early layers; MLX layer-skip blog, "Code": the draft shares the full model's
  * layer objects).  weights: device buffers, canonical order, n_weights of them,
- * sizes checked; a device workspace of at least ssd_workspace_bytes(cfg)
+ * sizes checked, 16-byte aligned (a zero-byte entry, such as the shared experts
+ * of an MoE model with n_shared = 0, may be NULL); a device workspace of at
+ * least ssd_workspace_bytes(cfg)
  * bytes, 256-byte aligned.  hip_stream: a hipStream_t (NULL = the null stream).
  * Clears the KV cache; for bf16 models packs the weight matrices into the
  * workspace (synchronously) after which the buffers ssd_weight_retained

@@ -603,7 +603,7 @@ ssd_status ssd_load(const ssd_cfg* cfg, const ssd_buf* weights, int32_t n_weight
     return fail(SSD_E_ARG, "expected %d weight buffers, got %d", (int)table.size(), n_weights);
   const size_t esz = cfg->dtype == SSD_BF16 ? 2 : 4;
   for (int i = 0; i < n_weights; ++i) {
-    if (!weights[i].ptr) return fail(SSD_E_ARG, "weight %d is NULL", i);
+    if (!weights[i].ptr && table[i] != 0) return fail(SSD_E_ARG, "weight %d is NULL", i);
     if (weights[i].nbytes != (int64_t)(table[i] * esz))
       return fail(SSD_E_ARG, "weight %d has %lld bytes, expected %lld", i, (long long)weights[i].nbytes,
                   (long long)(table[i] * esz));
