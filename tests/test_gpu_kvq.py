@@ -122,3 +122,30 @@ def test_kvq_other_masks_and_host_blocks_verify_in_full():
     finally:
         eng.set_kvq(False)
         eng.close()
+
+
+def _random_shape(kind, seed):
+    from test_gpu_random_moe_shapes import _shape as moe_shape
+    from test_gpu_random_shapes import _f32_shape, _wide_shape
+    if kind == "moe":
+        cfg, mb, _ = moe_shape(seed)
+        return cfg, mb, dict(prefill_chunk=64, moe_dedup=seed % 2)
+    cfg, mb, chunk, _ = (_wide_shape if kind == "wide" else _f32_shape)(seed)
+    return cfg, mb, dict(prefill_chunk=chunk)
+
+
+@pytest.mark.parametrize("kind,seed", [("wide", s) for s in range(6)] + [("f32", s) for s in (1, 5, 7, 8)] +
+                         [("moe", s) for s in (0, 2, 3, 4)])
+def test_kvq_random_shapes_bitwise_equal_full_verify(kind, seed):
+    """Exit-state reuse on the random shapes of the other GPU tests (bf16
+    wide, float32 ragged, MoE per-slot and dedup): every exit layer E and
+    draft lengths 1 to max_block-1, bitwise equal to the full verify."""
+    cfg, mb, kw = _random_shape(kind, seed)
+    if cfg["n_layers"] < 2 or mb < 2:
+        pytest.skip("needs two layers and room for a draft")
+    w = synth.make_weights(cfg, seed=seed)
+    eng = engine(cfg, w, max_block=mb, **kw)
+    try:
+        _check_model(cfg, eng, range(1, cfg["n_layers"]), sorted({1, min(3, mb - 1), mb - 1}), N=20)
+    finally:
+        eng.close()
