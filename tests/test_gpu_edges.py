@@ -378,3 +378,59 @@ def test_prefill_column_groups_bitwise_across_chunkings():
     err = np.max(np.abs(out[0][1] - last))
     print(f"[edge] prefill 640 rows: max |dlogit| = {err:.3e}")
     assert err <= BOUND
+
+
+def _bucket_shape(seed):
+    r = np.random.default_rng(13000 + seed)
+    hkv = int(r.choice([1, 2, 4, 8]))
+    hq = hkv * int(r.choice([1, 2, 4]))
+    b = int(r.choice([512, 1024]))
+    P = b - int(r.integers(3, 40))              # cross the bucket boundary while decoding
+    cfg = synth.config("llama-8b", n_layers=2, d_model=int(r.choice([256, 512, 1280])),
+                       n_q_heads=hq, n_kv_heads=hkv, head_dim=int(r.choice([64, 128])),
+                       ffn_dim=int(r.choice([512, 1792])), vocab=int(r.choice([2048, 16384])),
+                       prompt_len=P, max_ctx=P + 96, cid=700 + seed, dtype=str(r.choice(["bf16", "f32"])))
+    return cfg, int(r.choice([4, 9, 17])), int(r.choice([64, 256])), r
+
+
+def _decode_rows(eng, prompt, n):
+    eng.reset()
+    t = eng.prefill(prompt)
+    toks, rows = [t], [eng.read_logits(1)[0].copy()]
+    while len(toks) < n:
+        eng.verify([toks[-1]])
+        rows.append(eng.read_logits(1)[0].copy())
+        toks.append(eng.accept()[1][0])
+    return toks, np.stack(rows)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_graphs_across_context_buckets(seed):
+    """Passes replay as HIP graphs keyed by the 512-position context bucket
+    of their last row: decoding from just below a bucket boundary (512 or
+    1024) across it, captured graphs, their later replays and eager
+    launches give the same tokens and logits bit for bit (bf16 and float32,
+    random head groupings), and so does self-speculation."""
+    cfg, mb, chunk, r = _bucket_shape(seed)
+    print(f"[graph {seed}] dtype={cfg['dtype']} d={cfg['d_model']} hq={cfg['n_q_heads']} hkv={cfg['n_kv_heads']} "
+          f"hd={cfg['head_dim']} P={cfg['prompt_len']} max_block={mb}", flush=True)
+    w = synth.make_weights(cfg, seed=seed)
+    eng = engine(cfg, w, max_block=mb, prefill_chunk=chunk)
+    try:
+        prompt = synth.make_prompt(cfg)
+        eng.set_graphs(True)
+        g = _decode_rows(eng, prompt, 60)
+        g2 = _decode_rows(eng, prompt, 60)          # replays of graphs captured in the first run
+        eng.set_graphs(False)
+        e = _decode_rows(eng, prompt, 60)
+        assert g[0] == e[0] == g2[0]
+        assert np.array_equal(g[1], e[1]) and np.array_equal(g2[1], e[1])
+        mask = (r.random(cfg["n_layers"]) < 0.5).astype(np.uint8)
+        k = int(r.integers(1, mb))
+        eng.set_graphs(True)
+        sg, _ = eng.generate(prompt, 60, mask, k)
+        eng.set_graphs(False)
+        se, _ = eng.generate(prompt, 60, mask, k)
+        assert sg == se == g[0]
+    finally:
+        eng.close()
