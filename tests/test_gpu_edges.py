@@ -434,3 +434,56 @@ def test_graphs_across_context_buckets(seed):
         assert sg == se == g[0]
     finally:
         eng.close()
+
+
+def _prefill_shape(seed):
+    r = np.random.default_rng(15000 + seed)
+    hkv = int(r.choice([1, 2, 4, 8]))
+    hq = hkv * int(r.choice([1, 2, 4]))
+    P = int(r.integers(33, 900))
+    cfg = synth.config("llama-8b", n_layers=2, d_model=int(r.choice([256, 512, 1024, 1280, 2560])),
+                       n_q_heads=hq, n_kv_heads=hkv, head_dim=int(r.choice([64, 128])),
+                       ffn_dim=int(r.choice([512, 1792, 3584, 4480, 8960])), vocab=int(r.choice([2048, 16384])),
+                       prompt_len=P, max_ctx=P + 16, cid=800 + seed)
+    chunks = sorted(set(int(c) for c in r.choice([48, 64, 96, 128, 160, 256], size=2, replace=False)))
+    return cfg, chunks
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_prefill_random_shapes_and_chunkings(seed):
+    """Prompts of 33-900 tokens prefilled in chunks of 48-256 rows over random
+    widths, head groupings, FFN widths and vocabularies: the last row's
+    logits against the oracle; where every chunk of both chunkings is wider
+    than 32 rows (the multi-row-tile and prefill tile kernels, whose per-row
+    arithmetic depends on neither the chunk nor the tile grouping), the KV
+    cache and the logits bit for bit across the chunkings.  A tail of 32
+    rows or fewer runs the decode kernels, equal to rounding only."""
+    cfg, chunks = _prefill_shape(seed)
+    print(f"[prefill {seed}] d={cfg['d_model']} hq={cfg['n_q_heads']} hkv={cfg['n_kv_heads']} hd={cfg['head_dim']} "
+          f"F={cfg['ffn_dim']} V={cfg['vocab']} P={cfg['prompt_len']} chunks={chunks}", flush=True)
+    w = synth.make_weights(cfg, seed=seed)
+    prompt = synth.make_prompt(cfg)
+    out = []
+    for chunk in chunks:
+        eng = engine(cfg, w, max_block=4, prefill_chunk=chunk)
+        try:
+            t = eng.prefill(prompt)
+            out.append((t, eng.read_logits(1)[0].copy(),
+                        [eng.read_kv(l, 0, len(prompt)) for l in range(cfg["n_layers"])]))
+        finally:
+            eng.close()
+    P = len(prompt)
+    wide = [(P - 1) % c + 1 > 32 for c in chunks]    # every chunk of the chunking wider than 32 rows
+    print(f"[prefill {seed}] tails {[(P - 1) % c + 1 for c in chunks]}", flush=True)
+    _, _, last = Model(cfg, w).prefill(prompt)
+    for o in out:
+        err = float(np.max(np.abs(o[1] - last)))
+        print(f"[prefill {seed}] max |dlogit| = {err:.3e}", flush=True)
+        assert err <= 3e-2
+    if not all(wide):
+        return
+    for o in out[1:]:
+        assert o[0] == out[0][0]
+        assert np.array_equal(o[1], out[0][1])
+        for (k0, v0), (k1, v1) in zip(out[0][2], o[2]):
+            assert np.array_equal(k0, k1) and np.array_equal(v0, v1)
