@@ -487,3 +487,44 @@ def test_prefill_random_shapes_and_chunkings(seed):
         assert np.array_equal(o[1], out[0][1])
         for (k0, v0), (k1, v1) in zip(out[0][2], o[2]):
             assert np.array_equal(k0, k1) and np.array_equal(v0, v1)
+
+
+def _long_shape(seed):
+    r = np.random.default_rng(17000 + seed)
+    hkv = int(r.choice([1, 2, 4, 8]))
+    hq = min(16, hkv * int(r.choice([1, 2, 4])))
+    P = int(r.integers(2000, 8100))
+    cfg = synth.config("llama-8b", n_layers=2, d_model=int(r.choice([256, 512])), n_q_heads=hq, n_kv_heads=hkv,
+                       head_dim=int(r.choice([64, 128])), ffn_dim=512, vocab=2048,
+                       prompt_len=P, max_ctx=min(8192, P + 40), cid=900 + seed)
+    return cfg, int(r.choice([4, 9, 17])), r
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_long_context_random_shapes(seed):
+    """Contexts of 2000-8100 positions (up to 127 attention partitions, the
+    combine's second load batch, the XCD-aware grids with 8 kv heads) over
+    random head groupings: greedy against the oracle, and a verify block
+    equal to the decode rows bit for bit."""
+    cfg, mb, r = _long_shape(seed)
+    n = min(18, cfg["max_ctx"] - cfg["prompt_len"] - 1)
+    print(f"[edge long {seed}] hq={cfg['n_q_heads']} hkv={cfg['n_kv_heads']} hd={cfg['head_dim']} d={cfg['d_model']} "
+          f"P={cfg['prompt_len']} max_ctx={cfg['max_ctx']} max_block={mb} n={n}", flush=True)
+    w = synth.make_weights(cfg, seed=seed)
+    eng = engine(cfg, w, max_block=mb, prefill_chunk=256)
+    try:
+        prompt = synth.make_prompt(cfg)
+        toks, rows = _stepwise(eng, prompt, n)
+        ref = Model(cfg, w).teacher_forced(prompt, toks)
+        err = float(np.max(np.abs(rows - ref)))
+        print(f"[edge long {seed}] max |dlogit| = {err:.3e}", flush=True)
+        assert err <= 3e-2
+        assert _gap_ok(toks, ref, 3e-2) == []
+        m = min(mb, n - 1)
+        eng.reset()
+        eng.prefill(prompt)
+        post = eng.verify(toks[:m])
+        assert np.array_equal(eng.read_logits(m), rows[1:m + 1]) and post == toks[1:m + 1]
+        eng.accept()
+    finally:
+        eng.close()
