@@ -528,3 +528,86 @@ def test_long_context_random_shapes(seed):
         eng.accept()
     finally:
         eng.close()
+
+
+@pytest.mark.parametrize("kind,seed", [("tiny", 0), ("tiny", 1), ("bf16", 0), ("bf16", 1)])
+def test_random_call_sequences_follow_the_state_machine(kind, seed):
+    """400 random calls (prefill, draft, verify of the drafts, verify of a host
+    block, accept, reset) on a float32 and a bf16 model: each call succeeds
+    exactly when ssd_check_transition allows it and leaves the documented
+    state; a refused call returns SSD_E_STATE and changes neither the state
+    nor the context length; an accept of a drafts advances the committed
+    length by a + 1."""
+    import self_speculative_decoding_amd as S
+    from self_speculative_decoding_amd import SSDError
+    if kind == "tiny":
+        cfg = synth.config("tiny", max_ctx=400)
+    else:
+        cfg = synth.config("llama-8b", n_layers=3, d_model=512, n_q_heads=8, n_kv_heads=2, ffn_dim=1024,
+                           vocab=2048, max_ctx=400, prompt_len=60, cid=950)
+    mb = 6
+    w = synth.make_weights(cfg, seed=seed)
+    eng = engine(cfg, w, max_block=mb, prefill_chunk=64)
+    r = np.random.default_rng(seed)
+    L, V = cfg["n_layers"], cfg["vocab"]
+    try:
+        eng.reset()
+        n_drafted = 0
+        counts = {}
+        for step in range(400):
+            st, n = eng.state, eng.context_length
+            op = str(r.choice(["prefill", "draft", "verify", "block", "accept", "reset"],
+                              p=[0.12, 0.22, 0.18, 0.18, 0.22, 0.08]))
+            code = {"prefill": S.OP_PREFILL, "draft": S.OP_DRAFT, "verify": S.OP_VERIFY,
+                    "block": S.OP_VERIFY_BLOCK, "accept": S.OP_ACCEPT, "reset": S.OP_RESET}[op]
+            want = S.check_transition(st, code)
+            try:
+                if op == "prefill":
+                    P = int(r.integers(1, 80))
+                    eng.prefill(list(synth.make_tokens(V, P, seed=seed, stream=step)))
+                    got_n = P
+                elif op == "draft":
+                    k = int(r.integers(1, mb))
+                    mask = (r.random(L) < 0.5).astype(np.uint8)
+                    d = eng.draft(mask, k)
+                    assert len(d) == k and all(0 <= x < V for x in d)
+                    n_drafted = k
+                    got_n = n
+                elif op == "verify":
+                    post = eng.verify(None, n_drafted + 1)
+                    assert len(post) == n_drafted + 1
+                    got_n = n
+                elif op == "block":
+                    m = int(r.integers(1, mb + 1))
+                    post = eng.verify(list(synth.make_tokens(V, m, seed=seed, stream=1000 + step)))
+                    assert len(post) == m
+                    n_drafted = m - 1
+                    got_n = n
+                elif op == "accept":
+                    a, em = eng.accept()
+                    assert 0 <= a <= n_drafted and len(em) == a + 1
+                    got_n = n + a + 1
+                else:
+                    eng.reset()
+                    got_n = 0
+                ok = True
+            except SSDError as e:
+                ok = False
+                status = e.status
+            if want >= 0:
+                if not ok and status == -3:      # capacity: the state stays
+                    assert eng.state == st and eng.context_length == n
+                    counts["capacity"] = counts.get("capacity", 0) + 1
+                    continue
+                assert ok, (step, op, st, want, status)
+                assert eng.state == want, (step, op, st, want, eng.state)
+                if op != "reset":
+                    assert eng.context_length == got_n, (step, op, n, got_n, eng.context_length)
+                counts[op] = counts.get(op, 0) + 1
+            else:
+                assert not ok and status == want, (step, op, st, want, ok)
+                assert eng.state == st and eng.context_length == n, (step, op)
+                counts["refused"] = counts.get("refused", 0) + 1
+        print(f"[edge fsm {kind} {seed}] {counts}", flush=True)
+    finally:
+        eng.close()
