@@ -53,7 +53,7 @@ def test_engine_churn_leaves_no_growing_allocation():
     w = synth.make_weights(cfg, seed=1)
     prompt = synth.make_prompt(cfg)
     free = {}
-    for i in range(61):
+    for i in range(81):
         eng = engine(cfg, w, max_block=6, prefill_chunk=64)
         eng.generate(prompt, 12, np.array([0, 1], np.uint8), 3)
         eng.close()
@@ -62,7 +62,9 @@ def test_engine_churn_leaves_no_growing_allocation():
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
         free[i] = torch.cuda.mem_get_info()[0]
-    settled = (free[40] - free[60]) / 2**20
-    print(f"[lifecycle] free memory: engines 1-40 {(free[1] - free[40]) / 2**20:.1f} MiB, "
-          f"engines 40-60 {settled:.1f} MiB", flush=True)
-    assert settled < 4.0
+    settled = (free[60] - free[80]) / 2**20
+    total = (free[1] - free[80]) / 2**20
+    print(f"[lifecycle] free memory: engines 1-60 {(free[1] - free[60]) / 2**20:.1f} MiB, "
+          f"engines 60-80 {settled:.1f} MiB", flush=True)
+    assert settled < 8.0            # a graph or buffer kept per engine would show here
+    assert total < 128.0
